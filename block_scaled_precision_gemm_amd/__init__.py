@@ -1,0 +1,329 @@
+"""Python binding of libbsmm (the block-scaled matmul for MI355X).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libbsmm.so``.  The functions take PyTorch tensors (PyTorch is
+used for device memory and streams), check shapes the way ``_scaled_mm``
+states its scaling rules (ValueError), and pass raw pointers, strides and the
+current HIP stream to the C ABI in ``include/bsmm.h``.  There is no fallback:
+if the library is not built, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "load", "lib_path", "BsmmError",
+    "bsmm_int8_rowwise", "bsmm_fp8_blockwise", "bsmm_fp8_mx_bmm",
+    "bsmm_workspace_bytes", "bsmm_query_plan", "bsmm_set_override",
+    "bsmm_variant_names", "bsmm_version",
+    "I32", "F32", "BF16", "OP_INT8_ROWWISE", "OP_FP8_BLOCKWISE", "OP_FP8_MX_BMM",
+    "STATUS",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_PKG, "libbsmm.so")
+
+I32, F32, BF16 = 0, 1, 2
+OP_INT8_ROWWISE, OP_FP8_BLOCKWISE, OP_FP8_MX_BMM = 0, 1, 2
+STATUS = {0: "BSMM_OK", 1: "BSMM_ERR_NULL", 2: "BSMM_ERR_SHAPE",
+          3: "BSMM_ERR_SCALE_SHAPE", 4: "BSMM_ERR_LAYOUT", 5: "BSMM_ERR_ALIGN",
+          6: "BSMM_ERR_DTYPE", 7: "BSMM_ERR_UNSUPPORTED", 8: "BSMM_ERR_HIP",
+          9: "BSMM_ERR_ARG"}
+
+_lib = None
+
+
+class BsmmError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("variant", ctypes.c_char * 48), ("tile_m", ctypes.c_int32),
+                ("tile_n", ctypes.c_int32), ("split_k", ctypes.c_int32),
+                ("m_split", ctypes.c_int32), ("workspace", ctypes.c_int64),
+                ("source", ctypes.c_int32)]
+
+
+def load():
+    """Load the in-tree libbsmm.so (once) and declare its prototypes."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(lib_path):
+        raise RuntimeError(f"{lib_path} is not built; run __graft_entry__.build()")
+    L = ctypes.CDLL(lib_path)
+    i64, vp, sz, st = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    L.bsmm_int8_rowwise.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, st,
+                                    i64, i64, i64, vp, sz, vp]
+    L.bsmm_fp8_blockwise.argtypes = [vp, i64, vp, i64, vp, i64, i64, vp, i64, i64,
+                                     vp, i64, st, i64, i64, i64, vp, sz, vp]
+    L.bsmm_fp8_mx_bmm.argtypes = [vp, i64, i64, vp, i64, i64, vp, i64, i64, vp, i64,
+                                  i64, vp, i64, i64, st, i64, i64, i64, i64, vp, sz, vp]
+    for f in ("bsmm_int8_rowwise", "bsmm_fp8_blockwise", "bsmm_fp8_mx_bmm"):
+        getattr(L, f).restype = st
+    L.bsmm_workspace_bytes.argtypes = [st, i64, i64, i64, i64, st]
+    L.bsmm_workspace_bytes.restype = sz
+    L.bsmm_query_plan.argtypes = [st, i64, i64, i64, i64, st, sz, ctypes.POINTER(PlanInfo)]
+    L.bsmm_query_plan.restype = st
+    L.bsmm_set_override.argtypes = [ctypes.c_char_p, st]
+    L.bsmm_set_override.restype = st
+    L.bsmm_variant_names.restype = ctypes.c_char_p
+    L.bsmm_status_string.argtypes = [st]
+    L.bsmm_status_string.restype = ctypes.c_char_p
+    L.bsmm_last_error.restype = ctypes.c_char_p
+    L.bsmm_version.restype = st
+    _lib = L
+    return L
+
+
+def _check(status):
+    if status != 0:
+        raise BsmmError(status, load().bsmm_last_error().decode())
+
+
+# ----------------------------------------------------------------- helpers --
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+_WS = {}
+
+
+def _workspace(op, G, M, N, K, out_dtype, device):
+    """Workspace for the fastest plan, cached per device (grow-only)."""
+    need = load().bsmm_workspace_bytes(op, G, M, N, K, out_dtype)
+    if need == 0:
+        return None, 0
+    buf = _WS.get(device)
+    if buf is None or buf.numel() < need:
+        buf = _torch().empty(need, dtype=_torch().uint8, device=device)
+        _WS[device] = buf
+    return buf, buf.numel()
+
+
+def _dtype_code(dt):
+    torch = _torch()
+    if dt in (torch.int32, "i32"):
+        return I32
+    if dt in (torch.float32, "f32"):
+        return F32
+    if dt in (torch.bfloat16, "bf16"):
+        return BF16
+    raise ValueError(f"unsupported output dtype {dt}")
+
+
+def _torch_dtype(code):
+    torch = _torch()
+    return {I32: torch.int32, F32: torch.float32, BF16: torch.bfloat16}[code]
+
+
+def _bytes_view(t, name):
+    torch = _torch()
+    if t.dtype in (torch.int8, torch.uint8):
+        return t
+    if t.dtype in (torch.float8_e4m3fn, torch.float8_e8m0fnu):
+        return t.view(torch.uint8)
+    raise ValueError(f"{name}: expected 1-byte codes, got {t.dtype}")
+
+
+def _out(out, shape, code, device):
+    torch = _torch()
+    dt = _torch_dtype(code)
+    if out is None:
+        return torch.empty(shape, dtype=dt, device=device)
+    if tuple(out.shape) != tuple(shape) or out.dtype != dt:
+        raise ValueError(f"out must be {tuple(shape)} {dt}, got {tuple(out.shape)} {out.dtype}")
+    return out
+
+
+def _ws_args(workspace, op, G, M, N, K, code, device):
+    if workspace is False:
+        return None, 0
+    if workspace is None:
+        buf, n = _workspace(op, G, M, N, K, code, device)
+        return (buf.data_ptr() if buf is not None else None), n
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+# ------------------------------------------------------------ entry points --
+
+def bsmm_int8_rowwise(a, b, scale_a=None, scale_b=None, *, out_dtype="bf16",
+                      out=None, workspace=None, stream=None):
+    """int8 rowwise scaled matmul.
+
+    a: int8 [M, K] with unit stride along K.  b: int8 [K, N] column-major
+    (b.stride(0) == 1), e.g. ``b_nk.t()``.  scale_a: fp32 [M, 1] / [M] or a
+    0-d scalar (tensorwise); scale_b: fp32 [1, N] / [N] or 0-d.  out_dtype
+    "i32" returns the raw int32 accumulators and ignores the scales.
+    """
+    torch = _torch()
+    code = _dtype_code(out_dtype)
+    if a.dim() != 2 or b.dim() != 2:
+        raise ValueError("a and b must be 2-D")
+    M, K = a.shape
+    K2, N = b.shape
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    if a.dtype != torch.int8 or b.dtype != torch.int8:
+        raise ValueError("a and b must be int8")
+    if K and a.stride(1) != 1:
+        raise ValueError(f"a must be row-major, got stride {a.stride()}")
+    if K and b.stride(0) != 1:
+        raise ValueError(f"b must be column-major, got stride {b.stride()}")
+    sa_m = sb_n = 0
+    if code != I32:
+        if scale_a is None or scale_b is None:
+            raise ValueError("scale_a and scale_b are required unless out_dtype is int32")
+        if scale_a.dtype != torch.float32 or scale_b.dtype != torch.float32:
+            raise ValueError("scales must be fp32")
+        if scale_a.dim() == 0 and scale_b.dim() == 0:
+            pass                                     # tensorwise
+        elif (tuple(scale_a.shape) in ((M, 1), (M,)) and tuple(scale_b.shape) in ((1, N), (N,))):
+            sa_m = scale_a.stride(0)
+            sb_n = scale_b.stride(-1)
+        else:
+            raise ValueError(
+                "Invalid scaling configuration. For tensorwise scaling, both scales "
+                f"should be scalar. For rowwise scaling, scale_a should be ({M}, 1), "
+                f"scale_b should be (1, {N}). Got scale_a.size()={tuple(scale_a.shape)} "
+                f"and scale_b.size()={tuple(scale_b.shape)}")
+    o = _out(out, (M, N), code, a.device)
+    wsp, wsn = _ws_args(workspace, OP_INT8_ROWWISE, 1, M, N, K, code, a.device)
+    _check(load().bsmm_int8_rowwise(
+        a.data_ptr(), a.stride(0), b.data_ptr(), b.stride(1),
+        scale_a.data_ptr() if scale_a is not None else None, sa_m,
+        scale_b.data_ptr() if scale_b is not None else None, sb_n,
+        o.data_ptr(), o.stride(0), code, M, N, K, wsp, wsn, _stream(stream)))
+    return o
+
+
+def bsmm_fp8_blockwise(a, b, scale_a, scale_b, *, out_dtype="bf16", out=None,
+                       workspace=None, stream=None):
+    """fp8 E4M3 blockwise scaled matmul.
+
+    a: [M, K] E4M3 codes (float8_e4m3fn or uint8), row-major.  b: [K, N]
+    column-major.  scale_a: fp32 [M, K/128]; scale_b: fp32 [K/128, N/128]
+    (any strides).
+    """
+    torch = _torch()
+    code = _dtype_code(out_dtype)
+    a8, b8 = _bytes_view(a, "a"), _bytes_view(b, "b")
+    M, K = a8.shape
+    K2, N = b8.shape
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    if K and a8.stride(1) != 1:
+        raise ValueError(f"a must be row-major, got stride {a8.stride()}")
+    if K and b8.stride(0) != 1:
+        raise ValueError(f"b must be column-major, got stride {b8.stride()}")
+    KB, NB = -(-K // 128), -(-N // 128)
+    if scale_a.dtype != torch.float32 or scale_b.dtype != torch.float32:
+        raise ValueError("blockwise scales must be fp32")
+    if tuple(scale_a.shape) != (M, KB) or tuple(scale_b.shape) != (KB, NB):
+        raise ValueError(
+            "Invalid scaling configuration. For blockwise scaling, scale_a should be "
+            f"({M}, {KB}) and scale_b should be ({KB}, {NB}). Got "
+            f"scale_a.size()={tuple(scale_a.shape)} and scale_b.size()={tuple(scale_b.shape)}")
+    o = _out(out, (M, N), code, a8.device)
+    wsp, wsn = _ws_args(workspace, OP_FP8_BLOCKWISE, 1, M, N, K, code, a8.device)
+    _check(load().bsmm_fp8_blockwise(
+        a8.data_ptr(), a8.stride(0), b8.data_ptr(), b8.stride(1),
+        scale_a.data_ptr(), scale_a.stride(0), scale_a.stride(1),
+        scale_b.data_ptr(), scale_b.stride(0), scale_b.stride(1),
+        o.data_ptr(), o.stride(0), code, M, N, K, wsp, wsn, _stream(stream)))
+    return o
+
+
+def bsmm_fp8_mx_bmm(x, w, x_scale, w_scale, *, layout="m_major", out_dtype="bf16",
+                    out=None, workspace=None, stream=None):
+    """fp8 E4M3 batched matmul with e8m0 per-128-K-block scales.
+
+    layout "m_major": x [M, G, K], x_scale [M, G, K/128], out [M, G, N].
+    layout "batch_first": x [G, M, K], x_scale [G, M, K/128], out [G, M, N].
+    w [G, N, K] and w_scale [G, N/128, K/128] in both.  Arbitrary strides
+    with unit stride along K.
+    """
+    code = _dtype_code(out_dtype)
+    x8, w8 = _bytes_view(x, "x"), _bytes_view(w, "w")
+    xs8, ws8 = _bytes_view(x_scale, "x_scale"), _bytes_view(w_scale, "w_scale")
+    if x8.dim() != 3 or w8.dim() != 3:
+        raise ValueError("x and w must be 3-D")
+    if layout == "m_major":
+        M, G, K = x8.shape
+        x_sg, x_sm = x8.stride(1), x8.stride(0)
+    elif layout == "batch_first":
+        G, M, K = x8.shape
+        x_sg, x_sm = x8.stride(0), x8.stride(1)
+    else:
+        raise ValueError(f"unknown layout {layout}")
+    G2, N, K2 = w8.shape
+    if G2 != G or K2 != K:
+        raise ValueError(f"x {tuple(x8.shape)} and w {tuple(w8.shape)} disagree")
+    if K and (x8.stride(2) != 1 or w8.stride(2) != 1):
+        raise ValueError("x and w must be contiguous along K")
+    KB, NB = -(-K // 128), -(-N // 128)
+    want_xs = (M, G, KB) if layout == "m_major" else (G, M, KB)
+    if tuple(xs8.shape) != want_xs or tuple(ws8.shape) != (G, NB, KB):
+        raise ValueError(
+            f"Invalid scaling configuration. For mxscale BMM ({layout}), x_scale should be "
+            f"{want_xs} and w_scale should be {(G, NB, KB)}. Got x_scale.size()="
+            f"{tuple(xs8.shape)} and w_scale.size()={tuple(ws8.shape)}")
+    if KB and (xs8.stride(2) != 1 or ws8.stride(2) != 1):
+        raise ValueError("scales must be contiguous along K/128")
+    if layout == "m_major":
+        xs_sg, xs_sm = xs8.stride(1), xs8.stride(0)
+        oshape = (M, G, N)
+    else:
+        xs_sg, xs_sm = xs8.stride(0), xs8.stride(1)
+        oshape = (G, M, N)
+    o = _out(out, oshape, code, x8.device)
+    if layout == "m_major":
+        o_sg, o_sm = o.stride(1), o.stride(0)
+    else:
+        o_sg, o_sm = o.stride(0), o.stride(1)
+    if o.stride(2) != 1:
+        raise ValueError("out must be contiguous along N")
+    wsp, wsn = _ws_args(workspace, OP_FP8_MX_BMM, G, M, N, K, code, x8.device)
+    _check(load().bsmm_fp8_mx_bmm(
+        x8.data_ptr(), x_sg, x_sm, w8.data_ptr(), w8.stride(0), w8.stride(1),
+        xs8.data_ptr(), xs_sg, xs_sm, ws8.data_ptr(), ws8.stride(0), ws8.stride(1),
+        o.data_ptr(), o_sg, o_sm, code, G, M, N, K, wsp, wsn, _stream(stream)))
+    return o
+
+
+def bsmm_workspace_bytes(op, G, M, N, K, out_dtype):
+    return load().bsmm_workspace_bytes(op, G, M, N, K, _dtype_code(out_dtype))
+
+
+def bsmm_query_plan(op, G, M, N, K, out_dtype, workspace_bytes=2**62):
+    info = PlanInfo()
+    _check(load().bsmm_query_plan(op, G, M, N, K, _dtype_code(out_dtype),
+                                  workspace_bytes, ctypes.byref(info)))
+    return {"variant": info.variant.decode(), "tile_m": info.tile_m,
+            "tile_n": info.tile_n, "split_k": info.split_k, "m_split": info.m_split,
+            "workspace": info.workspace, "source": info.source}
+
+
+def bsmm_set_override(variant=None, split_k=0):
+    _check(load().bsmm_set_override(variant.encode() if variant else None, split_k))
+
+
+def bsmm_variant_names():
+    return load().bsmm_variant_names().decode().split(",")
+
+
+def bsmm_version():
+    return load().bsmm_version()

@@ -1,0 +1,419 @@
+// Host front end of libbsmm: argument validation, plan selection and the C
+// entry points declared in include/bsmm.h.  Everything here runs on the host
+// before any HIP call, so every error path is testable without a GPU.
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "bsmm.h"
+#include "bsmm_internal.h"
+#include "bsmm_tuned.h"
+
+namespace bsmm {
+namespace {
+
+thread_local char g_err[512] = "";
+
+bsmm_status fail(bsmm_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+// ---- override (tests / tuning) and logging --------------------------------
+struct Override {
+  std::mutex mu;
+  std::string variant;
+  int split = 0;
+  bool env_read = false;
+  int log = 0;
+};
+Override& ovr() {
+  static Override o;
+  return o;
+}
+void read_env_once() {
+  Override& o = ovr();
+  std::lock_guard<std::mutex> g(o.mu);
+  if (o.env_read) return;
+  o.env_read = true;
+  if (const char* v = getenv("BSMM_FORCE_VARIANT")) o.variant = v;
+  if (const char* v = getenv("BSMM_FORCE_SPLITK")) o.split = atoi(v);
+  if (const char* v = getenv("BSMM_LOG")) o.log = atoi(v);
+}
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;
+constexpr int64_t kMaxLd = (int64_t)1 << 23;    // 256 rows * ld + K < 2^32
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+const char* op_name(bsmm_op op) {
+  switch (op) {
+    case BSMM_OP_INT8_ROWWISE: return "int8_rowwise";
+    case BSMM_OP_FP8_BLOCKWISE: return "fp8_blockwise";
+    default: return "fp8_mx_bmm";
+  }
+}
+
+}  // namespace
+
+const Variant* find_variant(const char* name) {
+  int n = 0;
+  const Variant* v = variants(&n);
+  for (int i = 0; i < n; ++i)
+    if (strcmp(v[i].name, name) == 0) return &v[i];
+  return nullptr;
+}
+
+size_t splitk_workspace(const Problem& p, int rows, int split) {
+  if (split <= 1) return 0;
+  return (size_t)split * (size_t)p.G * (size_t)rows * (size_t)p.N * 4u;
+}
+
+static size_t ws_bytes(int G, int rows, int N, int split) {
+  if (split <= 1) return 0;
+  return (size_t)split * (size_t)G * (size_t)rows * (size_t)N * 4u;
+}
+
+// Plan selection (bsmm_plan_info::source):
+//  0  exact hit in the tuned table for (op, out dtype, G, N, K, M);
+//  1  padded-M: the nearest tuned M bucket above M for the same (op, dtype,
+//     G, N, K), run at the real M (every variant masks rows past M);
+//  2  heuristic: tile by M; split-K when the grid would underfill the chip
+//     and K is long compared with the tile (the "K much larger than m, n and
+//     m, n small" rule of Inductor's use_decompose_k_choice); an M-split into
+//     a tile-aligned bulk plus a short tail when the bulk work G*M_bulk is
+//     at least 8192 rows (the break-even the aiter PR's dispatch uses);
+//  3  override.
+// A plan whose workspace exceeds workspace_bytes falls back to split 1.
+Plan make_plan(bsmm_op op, int G, int M, int N, int K, bsmm_dtype dt,
+               size_t workspace_bytes) {
+  read_env_once();
+  Plan pl;
+  const int KB = K / kBlockK;
+  {
+    Override& o = ovr();
+    std::lock_guard<std::mutex> g(o.mu);
+    if (!o.variant.empty() || o.split > 0) {
+      Plan h = make_plan_heuristic(op, G, M, N, K, dt);
+      const Variant* v = o.variant.empty() ? h.v : find_variant(o.variant.c_str());
+      if (!v) v = h.v;
+      pl.v = v;
+      pl.split = o.split > 0 ? o.split : (o.variant.empty() ? h.split : 1);
+      if (pl.split > KB) pl.split = KB > 0 ? KB : 1;
+      if (o.variant.empty() && o.split <= 0) { pl.tail = h.tail; pl.m_split = h.m_split; }
+      pl.source = 3;
+      pl.workspace = ws_bytes(G, pl.m_split ? pl.m_split : M, N, pl.split);
+      if (pl.workspace > workspace_bytes) { pl.split = 1; pl.workspace = 0; }
+      return pl;
+    }
+  }
+  const TunedEntry* best = nullptr;
+  int ntab = 0;
+  const TunedEntry* tab = tuned_table(&ntab);
+  for (int i = 0; i < ntab; ++i) {
+    const TunedEntry& e = tab[i];
+    if (e.op != (int)op || e.out_dtype != (int)dt || e.G != G || e.N != N || e.K != K)
+      continue;
+    if (e.M == M) { best = &e; pl.source = 0; break; }
+    if (e.M > M && (!best || e.M < best->M)) { best = &e; pl.source = 1; }
+  }
+  if (best) {
+    pl.v = find_variant(best->variant);
+    pl.split = best->split;
+    if (pl.source == 0 && best->tail_variant[0] && best->m_split > 0 && best->m_split < M) {
+      pl.tail = find_variant(best->tail_variant);
+      pl.m_split = best->m_split;
+    }
+  }
+  if (!pl.v) {
+    pl = make_plan_heuristic(op, G, M, N, K, dt);
+    pl.source = 2;
+  }
+  if (pl.split > KB) pl.split = KB > 0 ? KB : 1;
+  const int bulk_rows = pl.m_split ? pl.m_split : M;
+  pl.workspace = ws_bytes(G, bulk_rows, N, pl.split);
+  if (pl.workspace > workspace_bytes) { pl.split = 1; pl.workspace = 0; }
+  return pl;
+}
+
+Plan make_plan_heuristic(bsmm_op op, int G, int M, int N, int K, bsmm_dtype dt) {
+  (void)op; (void)dt;
+  Plan pl;
+  const char* name;
+  if (M <= 64) name = N % 256 == 0 ? "t64x256" : "t64x128";
+  else if (M <= 128) name = N % 256 == 0 ? "t128x256" : "t128x128";
+  else name = N % 256 == 0 ? "t256x256" : "t256x128";
+  pl.v = find_variant(name);
+  const int KB = K / kBlockK;
+  const int64_t tiles = (int64_t)((M + pl.v->tile_m - 1) / pl.v->tile_m) *
+                        ((N + pl.v->tile_n - 1) / pl.v->tile_n) * G;
+  pl.split = 1;
+  // Split K only when one pass leaves most CUs idle and each slice keeps at
+  // least 4 K blocks.
+  if (tiles < 128 && KB >= 8) {
+    int s = (int)((256 + tiles - 1) / tiles);
+    if (s > KB / 4) s = KB / 4;
+    if (s < 1) s = 1;
+    pl.split = s;
+  }
+  // M-split: aligned bulk on the big tile plus a narrow tail launch.
+  const int bm = pl.v->tile_m;
+  const int bulk = (M / bm) * bm;
+  const int tail = M - bulk;
+  if (bm == 256 && tail > 0 && tail <= 64 && (int64_t)G * bulk >= 8192) {
+    pl.m_split = bulk;
+    pl.tail = find_variant(N % 256 == 0 ? "t64x256" : "t64x128");
+  }
+  return pl;
+}
+
+static bsmm_status run(const Problem& p, size_t workspace_bytes, void* ws,
+                       void* stream) {
+  Plan pl = make_plan(p.op, p.G, p.M, p.N, p.K, p.out_dtype, workspace_bytes);
+  if (ovr().log)
+    fprintf(stderr, "[bsmm] %s G=%d M=%d N=%d K=%d out=%d -> %s split=%d m_split=%d tail=%s src=%d\n",
+            op_name(p.op), p.G, p.M, p.N, p.K, (int)p.out_dtype, pl.v->name, pl.split,
+            pl.m_split, pl.tail ? pl.tail->name : "-", pl.source);
+  const int bulk_end = pl.m_split ? pl.m_split : p.M;
+  if (pl.v->launch(p, 0, bulk_end, pl.split, ws, stream))
+    return fail(BSMM_ERR_HIP, "kernel launch failed (%s)", pl.v->name);
+  if (pl.m_split && pl.m_split < p.M) {
+    if (pl.tail->launch(p, pl.m_split, p.M, 1, nullptr, stream))
+      return fail(BSMM_ERR_HIP, "kernel launch failed (%s)", pl.tail->name);
+  }
+  return BSMM_OK;
+}
+
+}  // namespace bsmm
+
+using namespace bsmm;
+
+#define CHECK(cond, status, ...) \
+  do { if (!(cond)) return fail(status, __VA_ARGS__); } while (0)
+
+extern "C" {
+
+bsmm_status bsmm_int8_rowwise(const int8_t* a, int64_t lda, const int8_t* b,
+                              int64_t ldb, const float* scale_a, int64_t sa_m,
+                              const float* scale_b, int64_t sb_n, void* out,
+                              int64_t ldo, bsmm_dtype out_dtype, int64_t M,
+                              int64_t N, int64_t K, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  CHECK(M >= 0 && N >= 0 && K >= 0, BSMM_ERR_SHAPE, "negative size M=%lld N=%lld K=%lld",
+        (long long)M, (long long)N, (long long)K);
+  CHECK(M < kMaxDim && N < kMaxDim && K < kMaxDim, BSMM_ERR_UNSUPPORTED, "size beyond 2^31");
+  CHECK(out_dtype == BSMM_I32 || out_dtype == BSMM_F32 || out_dtype == BSMM_BF16,
+        BSMM_ERR_DTYPE, "unknown output dtype %d", (int)out_dtype);
+  if (M == 0 || N == 0) return BSMM_OK;
+  CHECK(K % kBlockK == 0, BSMM_ERR_UNSUPPORTED, "K=%lld is not a multiple of 128", (long long)K);
+  CHECK(K <= 133144, BSMM_ERR_UNSUPPORTED, "K=%lld may overflow the int32 accumulator", (long long)K);
+  CHECK(out != nullptr, BSMM_ERR_NULL, "out is NULL");
+  CHECK(K == 0 || (a != nullptr && b != nullptr), BSMM_ERR_NULL, "a or b is NULL");
+  if (out_dtype != BSMM_I32) {
+    CHECK(scale_a != nullptr && scale_b != nullptr, BSMM_ERR_NULL,
+          "scale_a / scale_b NULL with a scaled output dtype");
+    CHECK(sa_m >= 0 && sb_n >= 0, BSMM_ERR_SCALE_SHAPE,
+          "scale strides must be >= 0 (0 broadcasts one scalar)");
+    CHECK(aligned(scale_a, 4) && aligned(scale_b, 4), BSMM_ERR_ALIGN, "scales not 4-byte aligned");
+    CHECK((M - 1) * sa_m < ((int64_t)1 << 30) && (N - 1) * sb_n < ((int64_t)1 << 30),
+          BSMM_ERR_UNSUPPORTED, "scale index range beyond 2^30");
+  }
+  CHECK(ldo >= N, BSMM_ERR_SHAPE, "ldo=%lld below N", (long long)ldo);
+  if (K > 0) {   // operands are not read when K == 0
+    CHECK(lda >= K && ldb >= K, BSMM_ERR_SHAPE, "leading dimensions lda=%lld ldb=%lld below K",
+          (long long)lda, (long long)ldb);
+    CHECK(lda % 16 == 0 && ldb % 16 == 0, BSMM_ERR_ALIGN, "lda / ldb not multiples of 16 bytes");
+    CHECK(lda <= kMaxLd && ldb <= kMaxLd, BSMM_ERR_UNSUPPORTED, "leading dimension beyond 2^23");
+  }
+  CHECK(K == 0 || (aligned(a, 16) && aligned(b, 16)), BSMM_ERR_ALIGN, "a / b not 16-byte aligned");
+  CHECK(aligned(out, 4), BSMM_ERR_ALIGN, "out not 4-byte aligned");
+  Problem p{};
+  p.op = BSMM_OP_INT8_ROWWISE;
+  p.out_dtype = out_dtype;
+  p.G = 1; p.M = (int)M; p.N = (int)N; p.K = (int)K;
+  p.a = (const uint8_t*)a; p.lda = lda; p.a_sg = 0;
+  p.b = (const uint8_t*)b; p.ldb = ldb; p.b_sg = 0;
+  p.sa = scale_a; p.sa_m = sa_m; p.sa_sg = 0; p.sa_kb = 0;
+  p.sb = scale_b; p.sb_n = sb_n; p.sb_sg = 0; p.sb_kb = 0;
+  p.out = out; p.ldo = ldo; p.o_sg = 0;
+  return run(p, workspace ? workspace_bytes : 0, workspace, stream);
+}
+
+bsmm_status bsmm_fp8_blockwise(const uint8_t* a, int64_t lda, const uint8_t* b,
+                               int64_t ldb, const float* scale_a, int64_t sa_m,
+                               int64_t sa_kb, const float* scale_b, int64_t sb_kb,
+                               int64_t sb_nb, void* out, int64_t ldo,
+                               bsmm_dtype out_dtype, int64_t M, int64_t N, int64_t K,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  CHECK(M >= 0 && N >= 0 && K >= 0, BSMM_ERR_SHAPE, "negative size M=%lld N=%lld K=%lld",
+        (long long)M, (long long)N, (long long)K);
+  CHECK(M < kMaxDim && N < kMaxDim && K < kMaxDim, BSMM_ERR_UNSUPPORTED, "size beyond 2^31");
+  CHECK(out_dtype == BSMM_F32 || out_dtype == BSMM_BF16, BSMM_ERR_DTYPE,
+        "fp8 blockwise writes fp32 or bf16 (got %d)", (int)out_dtype);
+  if (M == 0 || N == 0) return BSMM_OK;
+  CHECK(K % kBlockK == 0, BSMM_ERR_UNSUPPORTED, "K=%lld is not a multiple of 128", (long long)K);
+  CHECK(N % kBlockK == 0, BSMM_ERR_UNSUPPORTED, "N=%lld is not a multiple of 128", (long long)N);
+  CHECK(out != nullptr, BSMM_ERR_NULL, "out is NULL");
+  if (K > 0) {
+    CHECK(a != nullptr && b != nullptr, BSMM_ERR_NULL, "a or b is NULL");
+    CHECK(scale_a != nullptr && scale_b != nullptr, BSMM_ERR_NULL, "scale_a / scale_b is NULL");
+    CHECK(sa_m >= 0 && sa_kb >= 0 && sb_kb >= 0 && sb_nb >= 0, BSMM_ERR_SCALE_SHAPE,
+          "scale strides must be >= 0 (0 broadcasts)");
+    const int64_t KB = K / kBlockK, NB = N / kBlockK;
+    CHECK(((M - 1) * sa_m + (KB - 1) * sa_kb) < ((int64_t)1 << 30) &&
+              ((KB - 1) * sb_kb + (NB - 1) * sb_nb) < ((int64_t)1 << 30),
+          BSMM_ERR_UNSUPPORTED, "scale index range beyond 2^30");
+    CHECK(aligned(scale_a, 4) && aligned(scale_b, 4), BSMM_ERR_ALIGN, "scales not 4-byte aligned");
+    CHECK(aligned(a, 16) && aligned(b, 16), BSMM_ERR_ALIGN, "a / b not 16-byte aligned");
+  }
+  CHECK(ldo >= N, BSMM_ERR_SHAPE, "ldo=%lld below N", (long long)ldo);
+  if (K > 0) {   // operands are not read when K == 0
+    CHECK(lda >= K && ldb >= K, BSMM_ERR_SHAPE, "leading dimensions lda=%lld ldb=%lld below K",
+          (long long)lda, (long long)ldb);
+    CHECK(lda % 16 == 0 && ldb % 16 == 0, BSMM_ERR_ALIGN, "lda / ldb not multiples of 16 bytes");
+    CHECK(lda <= kMaxLd && ldb <= kMaxLd, BSMM_ERR_UNSUPPORTED, "leading dimension beyond 2^23");
+  }
+  CHECK(aligned(out, 4), BSMM_ERR_ALIGN, "out not 4-byte aligned");
+  Problem p{};
+  p.op = BSMM_OP_FP8_BLOCKWISE;
+  p.out_dtype = out_dtype;
+  p.G = 1; p.M = (int)M; p.N = (int)N; p.K = (int)K;
+  p.a = a; p.lda = lda;
+  p.b = b; p.ldb = ldb;
+  p.sa = scale_a; p.sa_m = sa_m; p.sa_kb = sa_kb;
+  p.sb = scale_b; p.sb_kb = sb_kb; p.sb_n = sb_nb;
+  p.out = out; p.ldo = ldo;
+  return run(p, workspace ? workspace_bytes : 0, workspace, stream);
+}
+
+bsmm_status bsmm_fp8_mx_bmm(const uint8_t* x, int64_t x_sg, int64_t x_sm,
+                            const uint8_t* w, int64_t w_sg, int64_t w_sn,
+                            const uint8_t* x_scale, int64_t xs_sg, int64_t xs_sm,
+                            const uint8_t* w_scale, int64_t ws_sg, int64_t ws_snb,
+                            void* out, int64_t o_sg, int64_t o_sm, bsmm_dtype out_dtype,
+                            int64_t G, int64_t M, int64_t N, int64_t K,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  CHECK(G >= 0 && M >= 0 && N >= 0 && K >= 0, BSMM_ERR_SHAPE,
+        "negative size G=%lld M=%lld N=%lld K=%lld", (long long)G, (long long)M,
+        (long long)N, (long long)K);
+  CHECK(G < kMaxDim && M < kMaxDim && N < kMaxDim && K < kMaxDim, BSMM_ERR_UNSUPPORTED,
+        "size beyond 2^31");
+  CHECK(out_dtype == BSMM_F32 || out_dtype == BSMM_BF16, BSMM_ERR_DTYPE,
+        "fp8 mx BMM writes fp32 or bf16 (got %d)", (int)out_dtype);
+  if (G == 0 || M == 0 || N == 0) return BSMM_OK;
+  CHECK(K % kBlockK == 0, BSMM_ERR_UNSUPPORTED, "K=%lld is not a multiple of 128", (long long)K);
+  CHECK(N % kBlockK == 0, BSMM_ERR_UNSUPPORTED, "N=%lld is not a multiple of 128", (long long)N);
+  CHECK(out != nullptr, BSMM_ERR_NULL, "out is NULL");
+  CHECK(x_sg >= 0 && x_sm >= 0 && w_sg >= 0 && w_sn >= 0 && o_sg >= 0 && o_sm >= 0,
+        BSMM_ERR_LAYOUT, "negative stride");
+  CHECK(x_sm >= K && w_sn >= K && o_sm >= N, BSMM_ERR_LAYOUT,
+        "row strides x_sm=%lld w_sn=%lld o_sm=%lld below K / N", (long long)x_sm,
+        (long long)w_sn, (long long)o_sm);
+  if (K > 0) {
+    CHECK(x != nullptr && w != nullptr, BSMM_ERR_NULL, "x or w is NULL");
+    CHECK(x_scale != nullptr && w_scale != nullptr, BSMM_ERR_NULL, "x_scale / w_scale is NULL");
+    CHECK(xs_sg >= 0 && xs_sm >= 0 && ws_sg >= 0 && ws_snb >= 0, BSMM_ERR_SCALE_SHAPE,
+          "scale strides must be >= 0");
+    CHECK(aligned(x, 16) && aligned(w, 16) && x_sg % 16 == 0 && x_sm % 16 == 0 &&
+              w_sg % 16 == 0 && w_sn % 16 == 0,
+          BSMM_ERR_ALIGN, "x / w pointers or strides not 16-byte aligned");
+    CHECK(x_sm <= kMaxLd && w_sn <= kMaxLd, BSMM_ERR_UNSUPPORTED, "row stride beyond 2^23");
+  }
+  CHECK(aligned(out, 4), BSMM_ERR_ALIGN, "out not 4-byte aligned");
+  Problem p{};
+  p.op = BSMM_OP_FP8_MX_BMM;
+  p.out_dtype = out_dtype;
+  p.G = (int)G; p.M = (int)M; p.N = (int)N; p.K = (int)K;
+  p.a = x; p.a_sg = x_sg; p.lda = x_sm;
+  p.b = w; p.b_sg = w_sg; p.ldb = w_sn;
+  p.sa = x_scale; p.sa_sg = xs_sg; p.sa_m = xs_sm; p.sa_kb = 1;
+  p.sb = w_scale; p.sb_sg = ws_sg; p.sb_n = ws_snb; p.sb_kb = 1;
+  p.out = out; p.o_sg = o_sg; p.ldo = o_sm;
+  return run(p, workspace ? workspace_bytes : 0, workspace, stream);
+}
+
+size_t bsmm_workspace_bytes(bsmm_op op, int64_t G, int64_t M, int64_t N, int64_t K,
+                            bsmm_dtype out_dtype) {
+  if (G <= 0 || M <= 0 || N <= 0 || K <= 0 || G >= kMaxDim || M >= kMaxDim ||
+      N >= kMaxDim || K >= kMaxDim || K % kBlockK)
+    return 0;
+  Plan pl = make_plan(op, (int)G, (int)M, (int)N, (int)K, out_dtype, (size_t)-1);
+  return pl.workspace;
+}
+
+bsmm_status bsmm_query_plan(bsmm_op op, int64_t G, int64_t M, int64_t N, int64_t K,
+                            bsmm_dtype out_dtype, size_t workspace_bytes,
+                            bsmm_plan_info* info) {
+  CHECK(info != nullptr, BSMM_ERR_NULL, "info is NULL");
+  CHECK(op == BSMM_OP_INT8_ROWWISE || op == BSMM_OP_FP8_BLOCKWISE || op == BSMM_OP_FP8_MX_BMM,
+        BSMM_ERR_ARG, "unknown op %d", (int)op);
+  CHECK(G > 0 && M > 0 && N > 0 && K >= 0, BSMM_ERR_SHAPE, "sizes must be positive");
+  CHECK(G < kMaxDim && M < kMaxDim && N < kMaxDim && K < kMaxDim, BSMM_ERR_UNSUPPORTED,
+        "size beyond 2^31");
+  CHECK(K % kBlockK == 0, BSMM_ERR_UNSUPPORTED, "K not a multiple of 128");
+  Plan pl = make_plan(op, (int)G, (int)M, (int)N, (int)K, out_dtype, workspace_bytes);
+  memset(info, 0, sizeof(*info));
+  snprintf(info->variant, sizeof(info->variant), "%s", pl.v->name);
+  info->tile_m = pl.v->tile_m;
+  info->tile_n = pl.v->tile_n;
+  info->split_k = pl.split;
+  info->m_split = pl.m_split;
+  info->workspace = (int64_t)pl.workspace;
+  info->source = pl.source;
+  return BSMM_OK;
+}
+
+bsmm_status bsmm_set_override(const char* variant, int split_k) {
+  read_env_once();
+  if (variant && variant[0] && !find_variant(variant))
+    return fail(BSMM_ERR_ARG, "unknown variant '%s'", variant);
+  Override& o = ovr();
+  std::lock_guard<std::mutex> g(o.mu);
+  o.variant = variant ? variant : "";
+  o.split = split_k > 0 ? split_k : 0;
+  return BSMM_OK;
+}
+
+const char* bsmm_variant_names(void) {
+  static std::string names = [] {
+    std::string s;
+    int n = 0;
+    const Variant* v = variants(&n);
+    for (int i = 0; i < n; ++i) {
+      if (i) s += ",";
+      s += v[i].name;
+    }
+    return s;
+  }();
+  return names.c_str();
+}
+
+const char* bsmm_status_string(bsmm_status s) {
+  switch (s) {
+    case BSMM_OK: return "BSMM_OK";
+    case BSMM_ERR_NULL: return "BSMM_ERR_NULL";
+    case BSMM_ERR_SHAPE: return "BSMM_ERR_SHAPE";
+    case BSMM_ERR_SCALE_SHAPE: return "BSMM_ERR_SCALE_SHAPE";
+    case BSMM_ERR_LAYOUT: return "BSMM_ERR_LAYOUT";
+    case BSMM_ERR_ALIGN: return "BSMM_ERR_ALIGN";
+    case BSMM_ERR_DTYPE: return "BSMM_ERR_DTYPE";
+    case BSMM_ERR_UNSUPPORTED: return "BSMM_ERR_UNSUPPORTED";
+    case BSMM_ERR_HIP: return "BSMM_ERR_HIP";
+    case BSMM_ERR_ARG: return "BSMM_ERR_ARG";
+  }
+  return "BSMM_ERR_UNKNOWN";
+}
+
+const char* bsmm_last_error(void) { return g_err; }
+
+int bsmm_version(void) { return BSMM_VERSION; }
+
+}  // extern "C"

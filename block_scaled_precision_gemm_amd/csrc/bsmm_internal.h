@@ -1,0 +1,66 @@
+// Internal interface between the host front end (validation, dispatch) and
+// the HIP kernels.  Plain C++; no HIP types, so the front end is host code.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "bsmm.h"
+
+namespace bsmm {
+
+constexpr int kBlockK = 128;   // K extent of one scale block and one k-step
+
+// One GEMM problem after validation, in a single strided form that covers
+// all three entry points.  Element (g, m, k) of A is at
+// a + g*a_sg + m*lda + k; element (g, n, k) of B at b + g*b_sg + n*ldb + k.
+// Output (g, m, n) at out + (g*o_sg + m*ldo + n) * sizeof(out element).
+struct Problem {
+  bsmm_op op;
+  bsmm_dtype out_dtype;
+  int G, M, N, K;
+  const uint8_t* a; int64_t a_sg, lda;
+  const uint8_t* b; int64_t b_sg, ldb;
+  // scales, strides in elements (float for int8 / blockwise, byte for mx)
+  //   int8:      sa[m*sa_m], sb[n*sb_n]                       (sb_kb unused)
+  //   blockwise: sa[m*sa_m + kb*sa_kb], sb[kb*sb_kb + nb*sb_n]
+  //   mx:        sa[g*sa_sg + m*sa_m + kb], sb[g*sb_sg + nb*sb_n + kb]
+  const void* sa; int64_t sa_sg, sa_m, sa_kb;
+  const void* sb; int64_t sb_sg, sb_n, sb_kb;
+  void* out; int64_t o_sg, ldo;
+};
+
+struct Variant;
+
+struct Plan {
+  const Variant* v = nullptr;      // main launch
+  int split = 1;                   // K slices of the main launch
+  const Variant* tail = nullptr;   // second launch for rows [m_split, M)
+  int m_split = 0;                 // 0: one launch covers all of M
+  size_t workspace = 0;            // bytes used
+  int source = 2;                  // bsmm_plan_info::source
+};
+
+// Kernel variants compiled into the library.
+using LaunchFn = int (*)(const Problem& p, int row_begin, int row_end,
+                         int split, void* ws, void* stream);
+struct Variant {
+  const char* name;
+  int tile_m, tile_n;
+  unsigned op_mask;     // bit i set: usable for bsmm_op i
+  bool masked_tail;     // safe for rows past M (every variant is)
+  LaunchFn launch;
+};
+
+const Variant* variants(int* count);
+const Variant* find_variant(const char* name);
+
+// Bytes of split-K workspace a variant needs for `split` slices.
+size_t splitk_workspace(const Problem& p, int rows, int split);
+
+// Plan selection (host only).
+Plan make_plan(bsmm_op op, int G, int M, int N, int K, bsmm_dtype dt,
+               size_t workspace_bytes);
+Plan make_plan_heuristic(bsmm_op op, int G, int M, int N, int K, bsmm_dtype dt);
+
+}  // namespace bsmm

@@ -1,0 +1,203 @@
+/*
+ * bsmm.h -- block-scaled low-precision matmul for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libbsmm.so.  Every entry point computes a low-precision GEMM or
+ * batched GEMM whose int32 / fp32 accumulator is dequantised by per-row,
+ * per-column or per-block scales.  A scale is a dequantisation multiplier:
+ * the real value of an operand element is code * scale.
+ *
+ * Conventions shared by all entry points
+ * --------------------------------------
+ * Pointers: all operand, scale, output and workspace pointers are device
+ *   pointers owned by the caller; the library allocates and frees nothing.
+ * Operands: A is [M, K] with K contiguous (row-major); B is logically [K, N]
+ *   and stored K-contiguous, i.e. column-major, element (k, n) at
+ *   b[n * ldb + k].  This is the layout rule of Inductor's
+ *   check_supported_striding for _scaled_mm (mat_a row-major, mat_b
+ *   column-major) in torch/_inductor/kernel/mm.py.
+ * Leading dimensions and batch strides are in elements; operand leading
+ *   dimensions (bytes, since operands are 1-byte codes) must be multiples of
+ *   16 and operand/output base pointers 16-byte aligned.
+ * Supported sizes: K % 128 == 0 (the block-scale shapes imply it); the fp8
+ *   entry points also need N % 128 == 0.  Any M >= 0.  M, N, K, G below 2^31;
+ *   128 * (operand leading dimension) below 2^31.
+ * Degenerate sizes: M == 0, N == 0 or G == 0 returns BSMM_OK and launches
+ *   nothing.  K == 0 (which satisfies K % 128 == 0) writes zeros, the value
+ *   of an empty sum.
+ * Stream: `stream` is a hipStream_t (NULL = the null stream).  Calls are
+ *   asynchronous: errors detected from the arguments are returned before
+ *   anything is enqueued; a launch failure reported by the HIP runtime is
+ *   returned as BSMM_ERR_HIP.  No call synchronises the stream or the host.
+ * Workspace: optional device scratch for split-K partial sums.  Pass the size
+ *   from bsmm_workspace_bytes for the fastest plan; with less (or NULL) the
+ *   call still succeeds with a plan that needs none.  Results do not depend on
+ *   the split: int32 accumulators are identical for every split, fp32 sums of
+ *   the split partials are added in ascending split order.
+ * Threads: the library keeps no mutable state across calls except a
+ *   thread-local error message and the optional plan override; calls on
+ *   different streams may run concurrently.  Two calls that write the same
+ *   output or share a workspace on different streams race.
+ */
+#ifndef BSMM_H
+#define BSMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BSMM_VERSION 1
+
+typedef enum {
+  BSMM_OK = 0,
+  BSMM_ERR_NULL = 1,        /* a required pointer is NULL                      */
+  BSMM_ERR_SHAPE = 2,       /* negative size, leading dimension below the row  */
+  BSMM_ERR_SCALE_SHAPE = 3, /* scale pointer / strides do not fit the mode     */
+  BSMM_ERR_LAYOUT = 4,      /* strides describe an impossible layout           */
+  BSMM_ERR_ALIGN = 5,       /* pointer or leading dimension misaligned         */
+  BSMM_ERR_DTYPE = 6,       /* output dtype not available for this entry point */
+  BSMM_ERR_UNSUPPORTED = 7, /* K % 128, N % 128 (fp8) or size limits           */
+  BSMM_ERR_HIP = 8,         /* the HIP runtime reported an error               */
+  BSMM_ERR_ARG = 9          /* any other invalid argument                      */
+} bsmm_status;
+
+typedef enum {
+  BSMM_I32 = 0,  /* raw int32 accumulators (int8 entry point only)  */
+  BSMM_F32 = 1,  /* IEEE binary32                                   */
+  BSMM_BF16 = 2  /* bfloat16, round-to-nearest-even from binary32   */
+} bsmm_dtype;
+
+typedef enum {
+  BSMM_OP_INT8_ROWWISE = 0,
+  BSMM_OP_FP8_BLOCKWISE = 1,
+  BSMM_OP_FP8_MX_BMM = 2
+} bsmm_op;
+
+/*
+ * int8 x int8 -> int32 accumulate, rowwise activation scale and per-column
+ * weight scale.
+ *
+ * Defined by torchao's int_scaled_matmul (PR "Remove int_scaled_mm's
+ * dependency on triton for cpu": an int32 matmul, a cast to the scale dtype,
+ * a multiply) with both scales fused as in the torchao issue "Unify scaled
+ * INT8 matmul" (acc_i32.to(f32) * scale.to(f32)), and by the rowwise scale
+ * shapes scale_a (M, 1), scale_b (1, N) stated in the PyTorch issue on
+ * blockwise _scaled_mm.
+ *
+ *   acc[m,n] = sum_k a[m*lda + k] * b[n*ldb + k]            (exact int32)
+ *   out[m*ldo + n] = (f32(acc) * scale_a[m*sa_m]) * scale_b[n*sb_n]
+ * with f32() round-to-nearest-even and each product rounded to binary32 (no
+ * fused multiply-add); BSMM_BF16 rounds that binary32 value once more.
+ * out_dtype BSMM_I32 stores acc itself; the scales are then ignored and may
+ * be NULL.  A scale stride of 0 broadcasts one scalar (tensorwise scaling).
+ * a, b: int8.  scale_a, scale_b: fp32.  out: int32 / fp32 / bf16.
+ * |acc| must stay below 2^31 (guaranteed for K * 127^2 < 2^31, K <= 133144).
+ */
+bsmm_status bsmm_int8_rowwise(const int8_t* a, int64_t lda,
+                              const int8_t* b, int64_t ldb,
+                              const float* scale_a, int64_t sa_m,
+                              const float* scale_b, int64_t sb_n,
+                              void* out, int64_t ldo, bsmm_dtype out_dtype,
+                              int64_t M, int64_t N, int64_t K,
+                              void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
+ * fp8 E4M3FN x E4M3FN with blockwise fp32 scales: one scale per row per
+ * 128-long K block of A, one per 128 x 128 block of B.  Scale shapes
+ * scale_a (M, K/128) and scale_b (K/128, N/128) as printed in the PyTorch
+ * issue "torch._scaled_mm with blockwise scaling doesn't work with
+ * torch.compile" (bug description).
+ *
+ *   out[m*ldo + n] = sum_kb  scale_a[m*sa_m + kb*sa_kb]
+ *                          * scale_b[kb*sb_kb + (n/128)*sb_nb]
+ *                          * sum_{k in block kb} A[m,k] * B[k,n]
+ * accumulated in fp32 (one fp32 block partial per 128-K block, then one
+ * multiply-add by the block's scale product); rounded to bf16 (RNE) or
+ * stored as fp32.  a, b: E4M3FN bytes (OCP; NaN codes unsupported).  Scale
+ * strides in elements; a stride of 0 broadcasts.
+ */
+bsmm_status bsmm_fp8_blockwise(const uint8_t* a, int64_t lda,
+                               const uint8_t* b, int64_t ldb,
+                               const float* scale_a, int64_t sa_m, int64_t sa_kb,
+                               const float* scale_b, int64_t sb_kb, int64_t sb_nb,
+                               void* out, int64_t ldo, bsmm_dtype out_dtype,
+                               int64_t M, int64_t N, int64_t K,
+                               void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
+ * Batched fp8 E4M3FN GEMM with e8m0 ("mxscale") scales per 128-long K block:
+ * per row of x and per 128 x 128 block of w.  Layouts of the ROCm aiter PR
+ * "Add opus fp8 mxscale BMM kernels for gfx950" (Motivation): m-major
+ * x [M, G, K], w [G, N, K], x_scale [M, G, K/128], w_scale [G, N/128, K/128],
+ * out [M, G, N]; and the batch-first layout x [G, M, K], out [G, M, N] named
+ * in its test plan.  Both are expressed by strides (elements):
+ *
+ *   x       (g, m, k)   at x[g*x_sg + m*x_sm + k]
+ *           m-major: x_sg = K, x_sm = G*K;  batch-first: x_sg = M*K, x_sm = K
+ *   w       (g, n, k)   at w[g*w_sg + n*w_sn + k]
+ *   x_scale (g, m, kb)  at x_scale[g*xs_sg + m*xs_sm + kb]
+ *   w_scale (g, nb, kb) at w_scale[g*ws_sg + nb*ws_snb + kb]
+ *   out     (g, m, n)   at out[g*o_sg + m*o_sm + n]
+ *
+ *   out(g,m,n) = sum_kb 2^(x_scale(g,m,kb) - 127) * 2^(w_scale(g,n/128,kb) - 127)
+ *                       * sum_{k in block kb} x(g,m,k) * w(g,n,k)
+ * accumulated in fp32 and stored as bf16 (RNE) or fp32.  Scale byte 255
+ * (NaN) is unsupported.
+ */
+bsmm_status bsmm_fp8_mx_bmm(const uint8_t* x, int64_t x_sg, int64_t x_sm,
+                            const uint8_t* w, int64_t w_sg, int64_t w_sn,
+                            const uint8_t* x_scale, int64_t xs_sg, int64_t xs_sm,
+                            const uint8_t* w_scale, int64_t ws_sg, int64_t ws_snb,
+                            void* out, int64_t o_sg, int64_t o_sm,
+                            bsmm_dtype out_dtype,
+                            int64_t G, int64_t M, int64_t N, int64_t K,
+                            void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/* Workspace bytes the fastest plan for this problem wants (0 if none). */
+size_t bsmm_workspace_bytes(bsmm_op op, int64_t G, int64_t M, int64_t N,
+                            int64_t K, bsmm_dtype out_dtype);
+
+/* The plan the dispatcher picks for a problem (host only, no GPU needed). */
+typedef struct {
+  char variant[48];   /* kernel variant name                                */
+  int32_t tile_m;     /* rows per workgroup tile                            */
+  int32_t tile_n;     /* columns per workgroup tile                         */
+  int32_t split_k;    /* number of K slices (1 = no split)                  */
+  int32_t m_split;    /* rows handled by the bulk launch when M is split,   */
+                      /* 0 when the whole M runs in one launch              */
+  int64_t workspace;  /* workspace bytes this plan uses                     */
+  int32_t source;     /* 0 table hit, 1 padded-M bucket, 2 heuristic,       */
+                      /* 3 override                                         */
+} bsmm_plan_info;
+
+bsmm_status bsmm_query_plan(bsmm_op op, int64_t G, int64_t M, int64_t N,
+                            int64_t K, bsmm_dtype out_dtype,
+                            size_t workspace_bytes, bsmm_plan_info* info);
+
+/*
+ * Force a variant and/or split for subsequent calls in this process (tests
+ * and tuning): variant NULL or "" keeps the dispatcher's choice, split_k <= 0
+ * keeps its split.  Returns BSMM_ERR_ARG for an unknown variant name.  The
+ * environment variables BSMM_FORCE_VARIANT and BSMM_FORCE_SPLITK set the same
+ * override at load time; BSMM_LOG=1 prints each dispatch decision to stderr.
+ */
+bsmm_status bsmm_set_override(const char* variant, int split_k);
+
+/* Names of all kernel variants, separated by ','. */
+const char* bsmm_variant_names(void);
+
+const char* bsmm_status_string(bsmm_status s);
+/* Thread-local detail of the last non-OK status returned on this thread. */
+const char* bsmm_last_error(void);
+int bsmm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSMM_H */

@@ -1,0 +1,198 @@
+"""C-ABI tests that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments before any HIP call.  Also the
+host-side plan selection and the dispatch table.  Pointers used here are
+never dereferenced: every call fails validation (or is a no-op) first.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_scaled_precision_gemm_amd as bsmm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsmm.h")
+TABLE = os.path.join(ROOT, "block_scaled_precision_gemm_amd", "csrc", "bsmm_tuned_table.inc")
+
+OK, NULL, SHAPE, SCALE, LAYOUT, ALIGN, DTYPE, UNSUP = 0, 1, 2, 3, 4, 5, 6, 7
+P = 0x10000          # a fake, 16-byte-aligned "device pointer" (never touched)
+
+
+@pytest.fixture(scope="module")
+def L():
+    return bsmm.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bsmm_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert "bsmm_fp8_blockwise" in names and len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), f"missing export {n}"
+    assert bsmm.bsmm_version() == 1
+
+
+def test_status_strings(L):
+    for code, name in bsmm.STATUS.items():
+        assert L.bsmm_status_string(code).decode() == name
+
+
+def i8(*, a=P, lda=256, b=P, ldb=256, sa=P, sa_m=1, sb=P, sb_n=1, out=P, ldo=128,
+       dt=bsmm.F32, M=64, N=128, K=256, ws=None, wsb=0):
+    L = bsmm.load()
+    return L.bsmm_int8_rowwise(a, lda, b, ldb, sa, sa_m, sb, sb_n, out, ldo, dt,
+                               M, N, K, ws, wsb, None)
+
+
+def bw(*, a=P, lda=256, b=P, ldb=256, sa=P, sa_m=2, sa_kb=1, sb=P, sb_kb=1, sb_nb=2,
+       out=P, ldo=256, dt=bsmm.BF16, M=64, N=256, K=256):
+    L = bsmm.load()
+    return L.bsmm_fp8_blockwise(a, lda, b, ldb, sa, sa_m, sa_kb, sb, sb_kb, sb_nb,
+                                out, ldo, dt, M, N, K, None, 0, None)
+
+
+def mx(*, x=P, x_sg=512, x_sm=4096, w=P, w_sg=1 << 20, w_sn=512, xs=P, xs_sg=4,
+       xs_sm=32, ws=P, ws_sg=64, ws_snb=4, out=P, o_sg=256, o_sm=2048,
+       dt=bsmm.BF16, G=8, M=16, N=256, K=512):
+    L = bsmm.load()
+    return L.bsmm_fp8_mx_bmm(x, x_sg, x_sm, w, w_sg, w_sn, xs, xs_sg, xs_sm, ws, ws_sg,
+                             ws_snb, out, o_sg, o_sm, dt, G, M, N, K, None, 0, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=-1), SHAPE), (dict(N=-5), SHAPE), (dict(K=-128), SHAPE),
+    (dict(K=200), UNSUP), (dict(K=2**31), UNSUP), (dict(K=133248, lda=133248, ldb=133248), UNSUP),
+    (dict(dt=7), DTYPE),
+    (dict(out=None), NULL), (dict(a=None), NULL), (dict(sa=None), NULL),
+    (dict(sa_m=-1), SCALE), (dict(sb_n=-2), SCALE),
+    (dict(lda=128), SHAPE), (dict(ldo=100), SHAPE),
+    (dict(lda=264), ALIGN), (dict(a=P + 8), ALIGN), (dict(sa=P + 2), ALIGN),
+    (dict(lda=1 << 24, ldb=1 << 24), UNSUP),
+])
+def test_int8_rejects(kw, status):
+    assert i8(**kw) == status
+    assert bsmm.load().bsmm_last_error().decode()
+
+
+def test_int8_noops_and_int32_mode_without_scales():
+    assert i8(M=0) == OK            # nothing to compute: returns before any launch
+    assert i8(N=0, a=None, b=None, out=None) == OK
+    # int32 mode ignores the scales: NULL scales pass validation (then M=0)
+    assert i8(M=0, sa=None, sb=None, dt=bsmm.I32) == OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=bsmm.I32), DTYPE), (dict(N=200, ldo=256), UNSUP), (dict(K=100), UNSUP),
+    (dict(sa=None), NULL), (dict(sb=None), NULL), (dict(out=None), NULL),
+    (dict(sa_kb=-1), SCALE), (dict(sb_nb=-1), SCALE),
+    (dict(ldb=255), SHAPE), (dict(ldb=264), ALIGN), (dict(b=P + 4), ALIGN),
+    (dict(sa_m=1 << 30), UNSUP),
+])
+def test_blockwise_rejects(kw, status):
+    assert bw(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(G=-1), SHAPE), (dict(dt=bsmm.I32), DTYPE), (dict(N=192, o_sm=192), UNSUP),
+    (dict(x_sm=256), LAYOUT), (dict(w_sn=100), LAYOUT), (dict(o_sm=100), LAYOUT),
+    (dict(x_sg=-512), LAYOUT), (dict(xs_sm=-1), SCALE), (dict(x_sm=4104), ALIGN),
+    (dict(w_sg=8), ALIGN), (dict(xs=None), NULL), (dict(w=None), NULL),
+])
+def test_mx_rejects(kw, status):
+    assert mx(**kw) == status
+
+
+def test_mx_noops():
+    assert mx(G=0) == OK and mx(M=0) == OK and mx(N=0) == OK
+
+
+# ----------------------------------------------------------------- binding --
+
+def test_binding_scale_shape_rules_follow_the_page():
+    """The rowwise/tensorwise message and the blockwise shapes of the PyTorch
+    blockwise _scaled_mm issue: (16640, 64) / (64, 40) for M=16640, K=8192,
+    N=5120 are the blockwise scales; rowwise-shaped scales are rejected."""
+    import torch
+    M, N, K = 16640, 5120, 8192
+    a = torch.empty((M, K), dtype=torch.float8_e4m3fn)
+    b = torch.empty((N, K), dtype=torch.float8_e4m3fn).t()
+    with pytest.raises(ValueError, match=r"scale_a should be \(16640, 64\)"):
+        bsmm.bsmm_fp8_blockwise(a, b, torch.empty(M, 1), torch.empty(1, N))
+    ai = torch.empty((M, K), dtype=torch.int8)
+    bi = torch.empty((N, K), dtype=torch.int8).t()
+    with pytest.raises(ValueError, match=r"rowwise scaling, scale_a should be \(16640, 1\)"):
+        bsmm.bsmm_int8_rowwise(ai, bi, torch.empty(M, 64), torch.empty(64, 40))
+    with pytest.raises(ValueError, match="column-major"):
+        bsmm.bsmm_int8_rowwise(ai, torch.empty((K, N), dtype=torch.int8),
+                               torch.empty(M, 1), torch.empty(1, N))
+    x = torch.empty((4, 8, 512), dtype=torch.uint8)
+    w = torch.empty((8, 256, 512), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="x_scale should be"):
+        bsmm.bsmm_fp8_mx_bmm(x, w, torch.empty((4, 8, 3), dtype=torch.uint8),
+                             torch.empty((8, 2, 4), dtype=torch.uint8))
+
+
+# ---------------------------------------------------------------- dispatch --
+
+def test_plan_heuristics():
+    q = bsmm.bsmm_query_plan
+    p = q(bsmm.OP_FP8_BLOCKWISE, 1, 16640, 5120, 8192, "bf16")
+    assert p["tile_m"] in (128, 256) and p["split_k"] >= 1
+    small = q(bsmm.OP_FP8_MX_BMM, 8, 1, 1024, 4096, "bf16")
+    assert small["tile_m"] == 64 and small["split_k"] > 1
+    assert small["workspace"] == small["split_k"] * 8 * 1 * 1024 * 4
+    # without workspace the same problem runs unsplit
+    nows = q(bsmm.OP_FP8_MX_BMM, 8, 1, 1024, 4096, "bf16", workspace_bytes=0)
+    assert nows["split_k"] == 1 and nows["workspace"] == 0
+    assert bsmm.bsmm_workspace_bytes(bsmm.OP_FP8_MX_BMM, 8, 1, 1024, 4096, "bf16") == \
+        small["workspace"]
+
+
+def test_override_roundtrip():
+    try:
+        bsmm.bsmm_set_override("t128x128", 3)
+        p = bsmm.bsmm_query_plan(bsmm.OP_INT8_ROWWISE, 1, 4096, 4096, 4096, "bf16")
+        assert p["variant"] == "t128x128" and p["split_k"] == 3 and p["source"] == 3
+        with pytest.raises(bsmm.BsmmError):
+            bsmm.bsmm_set_override("no_such_variant", 0)
+    finally:
+        bsmm.bsmm_set_override(None, 0)
+    p = bsmm.bsmm_query_plan(bsmm.OP_INT8_ROWWISE, 1, 4096, 4096, 4096, "bf16")
+    assert p["source"] != 3
+
+
+def parse_table():
+    rows = []
+    for line in open(TABLE):
+        line = line.split("//")[0].strip()
+        if not line:
+            continue
+        m = re.match(r"\{(.*)\},?$", line)
+        assert m, line
+        f = [x.strip().strip('"') for x in m.group(1).split(",")]
+        rows.append(f)
+    return rows
+
+
+def test_dispatch_table_keys_unique_and_variants_exist():
+    names = set(bsmm.bsmm_variant_names())
+    keys = set()
+    for f in parse_table():
+        key = tuple(int(x) for x in f[:6])
+        assert key not in keys, f"duplicate dispatch key {key}"
+        keys.add(key)
+        assert f[6] in names
+        if int(f[8]):
+            assert f[9] in names
+    # every table entry is what the dispatcher returns for its key
+    for f in parse_table():
+        op, dt, G, M, N, K = (int(x) for x in f[:6])
+        p = bsmm.bsmm_query_plan(op, G, M, N, K, {0: "i32", 1: "f32", 2: "bf16"}[dt])
+        assert p["source"] == 0 and p["variant"] == f[6]

@@ -1,0 +1,209 @@
+"""GPU parity of the HIP path against the CPU oracle, at sizes that span
+several tiles with ragged M and N tails: every kernel variant, forced split-K,
+both mx layouts, strided and broadcast scales, guard bands around the output,
+degenerate sizes and run-to-run determinism.
+
+Bars: int8 path bit-exact (int32 accumulators, and the fp32/bf16 outputs,
+which are the same binary32 operations in the same order); fp8 paths within
+relative Frobenius error 1e-2 and |Y - C| <= 2^-7 * sum_k |a_deq||b_deq|
+elementwise (Y exactly 0 where that sum is 0).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_precision_gemm_amd as bsmm
+from oracle import scaled_mm as S
+from synth import fp8_blockwise_inputs, fp8_mx_bmm_inputs, int8_rowwise_inputs
+from tests.gpu_util import (DEV, Forced, as_f64, check_blockwise, check_int8, check_mx,
+                            dev, host_out, run_blockwise, run_int8, run_mx, say)
+
+pytestmark = pytest.mark.gpu
+
+VARIANTS = ["t256x256", "t256x128", "t128x256", "t128x128", "t64x256", "t64x128"]
+
+
+@pytest.fixture(autouse=True)
+def _lib(gpu_lib):
+    yield
+
+
+# ------------------------------------------------------------------ int8 ----
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_int8_variants_exact(variant):
+    p = int8_rowwise_inputs(300, 384, 512, 101)
+    for dt in ("i32", "f32", "bf16"):
+        say(f"int8 {variant} {dt} M=300 N=384 K=512")
+        with Forced(variant, 1):
+            y = run_int8(p, dt)
+        check_int8(p, dt, y)
+
+
+def test_int8_tiny_workload_exact():
+    """64x256 @ 256x128, codes uniform in [-127,127], scales in [1e-3,1e-2]:
+    int32 accumulators bit-exact and the fp32 output bit-exact."""
+    p = int8_rowwise_inputs(64, 128, 256, 1)
+    say("int8 tiny i32 + f32")
+    check_int8(p, "i32", run_int8(p, "i32"))
+    check_int8(p, "f32", run_int8(p, "f32"))
+
+
+@pytest.mark.parametrize("split", [2, 3, 4])
+def test_int8_splitk_bit_identical(split):
+    p = int8_rowwise_inputs(200, 256, 1024, 102)
+    say(f"int8 split {split}")
+    with Forced("t128x128", split):
+        y = run_int8(p, "i32")
+        yb = run_int8(p, "bf16")
+    check_int8(p, "i32", y)
+    check_int8(p, "bf16", yb)
+
+
+def test_int8_tensorwise_and_extreme_values():
+    """All codes at +-127 (largest accumulators) and tensorwise (0-d) scales."""
+    M, N, K = 130, 160, 4096
+    rng = np.random.default_rng(7)
+    a = np.where(rng.random((M, K)) < 0.5, -127, 127).astype(np.int8)
+    b = np.where(rng.random((N, K)) < 0.5, -127, 127).astype(np.int8)
+    a[0, :] = 127
+    b[0, :] = 127                                  # acc[0,0] = K * 127^2
+    sa = np.float32(3e-3)
+    sb = np.float32(7e-4)
+    say("int8 tensorwise extreme")
+    y = bsmm.bsmm_int8_rowwise(dev(a), dev(b).t(), torch.tensor(sa, device=DEV),
+                               torch.tensor(sb, device=DEV), out_dtype="f32")
+    yi = bsmm.bsmm_int8_rowwise(dev(a), dev(b).t(), out_dtype="i32")
+    ref = S.int8_rowwise(a, b.T, np.full(M, sa), np.full(N, sb), "f32")
+    assert S.compare(host_out(y), ref, exact=True)["ok"]
+    refi = S.int8_rowwise(a, b.T, out_dtype="i32")
+    assert S.compare(host_out(yi), refi, exact=True)["ok"]
+    assert host_out(yi)[0, 0] == K * 127 * 127
+
+
+def test_int8_guard_bands():
+    """Output written through a strided view inside a sentinel-filled buffer:
+    nothing outside [M, N] changes."""
+    p = int8_rowwise_inputs(75, 200, 256, 103)
+    big = torch.full((75 + 9, 256), -12345, dtype=torch.int32, device=DEV)
+    view = big[3:78, 16:216]
+    say("int8 guard bands")
+    run_int8(p, "i32", out=view)
+    h = host_out(big)
+    check_int8(p, "i32", view)
+    mask = np.ones_like(h, dtype=bool)
+    mask[3:78, 16:216] = False
+    assert (h[mask] == -12345).all()
+
+
+# ------------------------------------------------------------ fp8 blockwise --
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_blockwise_variants(variant):
+    p = fp8_blockwise_inputs(300, 384, 640, 201)
+    for dt in ("bf16", "f32"):
+        say(f"blockwise {variant} {dt} M=300 N=384 K=640")
+        with Forced(variant, 1):
+            y = run_blockwise(p, dt)
+        check_blockwise(p, dt, y)
+
+
+@pytest.mark.parametrize("split", [2, 5])
+def test_blockwise_splitk(split):
+    p = fp8_blockwise_inputs(160, 256, 1280, 202)
+    say(f"blockwise split {split}")
+    with Forced("t128x256", split):
+        y = run_blockwise(p, "f32")
+    check_blockwise(p, "f32", y)
+
+
+def test_blockwise_scale_layouts():
+    """Column-major scale_a (stride along M = 1) and broadcast (stride 0)
+    scale_b give the same results as their dense equivalents."""
+    p = fp8_blockwise_inputs(96, 256, 512, 203)
+    a = dev(p["a"])
+    b = dev(p["b_nk"]).t()
+    sa_cm = dev(np.ascontiguousarray(p["scale_a"].T)).t()          # [M, KB], stride (1, M)
+    sb_one = torch.full((1, 1), 0.03125, device=DEV).expand(4, 2)  # stride (0, 0)
+    say("blockwise strided scales")
+    y = bsmm.bsmm_fp8_blockwise(a, b, sa_cm, sb_one, out_dtype="f32")
+    ref = S.fp8_blockwise(p["a"], p["b_nk"].T, p["scale_a"],
+                          np.full((4, 2), 0.03125, np.float32), "f32")
+    assert S.compare(as_f64(host_out(y)), ref)["ok"]
+
+
+def test_blockwise_guard_bands_and_m1():
+    p = fp8_blockwise_inputs(1, 256, 256, 204)
+    big = torch.full((4, 512), 7.0, dtype=torch.float32, device=DEV)
+    view = big[1:2, 128:384]
+    say("blockwise M=1 guard bands")
+    run_blockwise(p, "f32", out=view)
+    check_blockwise(p, "f32", view)
+    h = host_out(big)
+    mask = np.ones_like(h, dtype=bool)
+    mask[1, 128:384] = False
+    assert (h[mask] == 7.0).all()
+
+
+# -------------------------------------------------------------------- mx ----
+
+@pytest.mark.parametrize("layout", ["m_major", "batch_first"])
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_mx_variants(variant, layout):
+    p = fp8_mx_bmm_inputs(3, 300, 384, 512, 301, layout=layout)
+    say(f"mx {variant} {layout} G=3 M=300 N=384 K=512")
+    with Forced(variant, 1):
+        y = run_mx(p, "bf16")
+    check_mx(p, "bf16", y)
+
+
+@pytest.mark.parametrize("split", [2, 4])
+def test_mx_splitk(split):
+    p = fp8_mx_bmm_inputs(2, 70, 256, 1024, 302, layout="batch_first", dist="t")
+    say(f"mx split {split}")
+    with Forced("t64x256", split):
+        y = run_mx(p, "f32")
+    check_mx(p, "f32", y)
+
+
+def test_mx_layouts_agree():
+    """The same logical problem in m-major and batch-first storage gives the
+    same bits (identical kernels, identical per-element order)."""
+    p = fp8_mx_bmm_inputs(4, 130, 256, 512, 303, layout="m_major")
+    q = dict(p)
+    q["layout"] = "batch_first"
+    q["x"] = np.ascontiguousarray(p["x"].transpose(1, 0, 2))
+    q["x_scale"] = np.ascontiguousarray(p["x_scale"].transpose(1, 0, 2))
+    say("mx layouts agree")
+    y1 = host_out(run_mx(p, "f32"))
+    y2 = host_out(run_mx(q, "f32"))
+    assert np.array_equal(y1.transpose(1, 0, 2).view(np.uint32), y2.view(np.uint32))
+
+
+# --------------------------------------------------------------- edges ----
+
+def test_degenerate_sizes():
+    say("degenerate sizes")
+    z = torch.empty((0, 256), dtype=torch.uint8, device=DEV)
+    b = torch.empty((256, 256), dtype=torch.uint8, device=DEV)
+    y = bsmm.bsmm_fp8_blockwise(z, b.t(), torch.empty((0, 2), device=DEV),
+                                torch.ones((2, 2), device=DEV), out_dtype="f32")
+    assert y.shape == (0, 256)
+    # K = 0: an empty sum is zero
+    a0 = torch.empty((5, 0), dtype=torch.int8, device=DEV)
+    b0 = torch.empty((0, 7), dtype=torch.int8, device=DEV)
+    out = torch.full((5, 7), 99, dtype=torch.int32, device=DEV)
+    bsmm.bsmm_int8_rowwise(a0, b0, out_dtype="i32", out=out)
+    assert (host_out(out) == 0).all()
+
+
+def test_determinism():
+    p = fp8_blockwise_inputs(256, 512, 1024, 401)
+    say("determinism")
+    ys = [host_out(run_blockwise(p, "f32")).view(np.uint32) for _ in range(3)]
+    assert all(np.array_equal(ys[0], y) for y in ys[1:])
+    with Forced("t64x128", 3):
+        z1 = host_out(run_blockwise(p, "f32")).view(np.uint32)
+        z2 = host_out(run_blockwise(p, "f32")).view(np.uint32)
+    assert np.array_equal(z1, z2)
