@@ -82,6 +82,17 @@ static size_t ws_bytes(int G, int rows, int N, int split) {
   return (size_t)split * (size_t)G * (size_t)rows * (size_t)N * 4u;
 }
 
+size_t persistent_workspace(const Variant* v, bsmm_op op) {
+  (void)op;   // int32 and fp32 partials are both 4 bytes
+  return (size_t)kPlanCUs * v->wg_per_cu * ((size_t)v->tile_m * v->tile_n * 4u + 8u);
+}
+
+// Workspace of a plan: split-K partials or stream-K slots.
+static size_t plan_ws(const Plan& pl, bsmm_op op, int G, int rows, int N) {
+  if (pl.v->persistent) return persistent_workspace(pl.v, op);
+  return ws_bytes(G, rows, N, pl.split);
+}
+
 // Plan selection (bsmm_plan_info::source):
 //  0  exact hit in the tuned table for (op, out dtype, G, N, K, M);
 //  1  padded-M: the nearest tuned M bucket above M for the same (op, dtype,
@@ -110,8 +121,13 @@ Plan make_plan(bsmm_op op, int G, int M, int N, int K, bsmm_dtype dt,
       if (pl.split > KB) pl.split = KB > 0 ? KB : 1;
       if (o.variant.empty() && o.split <= 0) { pl.tail = h.tail; pl.m_split = h.m_split; }
       pl.source = 3;
-      pl.workspace = ws_bytes(G, pl.m_split ? pl.m_split : M, N, pl.split);
-      if (pl.workspace > workspace_bytes) { pl.split = 1; pl.workspace = 0; }
+      if (pl.v->persistent) pl.split = 1;
+      pl.workspace = plan_ws(pl, op, G, pl.m_split ? pl.m_split : M, N);
+      if (pl.workspace > workspace_bytes) {
+        pl.split = 1;
+        pl.workspace = 0;
+        if (pl.v->persistent) pl.v = h.v;   // no room for stream-K slots
+      }
       return pl;
     }
   }
@@ -138,9 +154,14 @@ Plan make_plan(bsmm_op op, int G, int M, int N, int K, bsmm_dtype dt,
     pl.source = 2;
   }
   if (pl.split > KB) pl.split = KB > 0 ? KB : 1;
+  if (pl.v->persistent) pl.split = 1;
   const int bulk_rows = pl.m_split ? pl.m_split : M;
-  pl.workspace = ws_bytes(G, bulk_rows, N, pl.split);
-  if (pl.workspace > workspace_bytes) { pl.split = 1; pl.workspace = 0; }
+  pl.workspace = plan_ws(pl, op, G, bulk_rows, N);
+  if (pl.workspace > workspace_bytes) {
+    pl.split = 1;
+    pl.workspace = 0;
+    if (pl.v->persistent) pl = make_plan_heuristic(op, G, M, N, K, dt), pl.split = 1;
+  }
   return pl;
 }
 
@@ -183,10 +204,10 @@ static bsmm_status run(const Problem& p, size_t workspace_bytes, void* ws,
             op_name(p.op), p.G, p.M, p.N, p.K, (int)p.out_dtype, pl.v->name, pl.split,
             pl.m_split, pl.tail ? pl.tail->name : "-", pl.source);
   const int bulk_end = pl.m_split ? pl.m_split : p.M;
-  if (pl.v->launch(p, 0, bulk_end, pl.split, ws, stream))
+  if (pl.v->launch(p, 0, bulk_end, pl.split, ws, workspace_bytes, stream))
     return fail(BSMM_ERR_HIP, "kernel launch failed (%s)", pl.v->name);
   if (pl.m_split && pl.m_split < p.M) {
-    if (pl.tail->launch(p, pl.m_split, p.M, 1, nullptr, stream))
+    if (pl.tail->launch(p, pl.m_split, p.M, 1, nullptr, 0, stream))
       return fail(BSMM_ERR_HIP, "kernel launch failed (%s)", pl.tail->name);
   }
   return BSMM_OK;

@@ -43,14 +43,21 @@ struct Plan {
 
 // Kernel variants compiled into the library.
 using LaunchFn = int (*)(const Problem& p, int row_begin, int row_end,
-                         int split, void* ws, void* stream);
+                         int split, void* ws, size_t ws_bytes, void* stream);
 struct Variant {
   const char* name;
   int tile_m, tile_n;
   unsigned op_mask;     // bit i set: usable for bsmm_op i
   bool masked_tail;     // safe for rows past M (every variant is)
+  bool persistent;      // stream-K: one workgroup per slot of the device
+  int wg_per_cu;        // workgroups one CU holds (LDS / registers)
   LaunchFn launch;
 };
+
+// Workspace a persistent (stream-K) variant wants: one partial tile plus a
+// 64-bit flag per workgroup, for a device of kPlanCUs compute units.
+constexpr int kPlanCUs = 256;
+size_t persistent_workspace(const Variant* v, bsmm_op op);
 
 const Variant* variants(int* count);
 const Variant* find_variant(const char* name);

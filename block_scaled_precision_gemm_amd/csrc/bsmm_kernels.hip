@@ -13,8 +13,8 @@
 // The K extent of one 16x16x128 fp8 instruction is exactly one scale block.
 //
 // Data movement: A and B tiles (both K-contiguous, 128 bytes of K per step)
-// go global -> LDS with direct-to-LDS buffer loads (no staging registers),
-// double-buffered; rows past the end of the matrix fall outside the buffer
+// go global -> LDS with direct-to-LDS buffer loads (no staging registers)
+// into a ring of LDS slots; rows past the end of the matrix fall outside the buffer
 // resource's range and load as zeros, so partial tiles need no masks on the
 // load side.  LDS rows are 128 bytes with the 16-byte chunks XOR-swizzled so
 // that the fragment reads (16 consecutive rows per lane group) hit distinct
@@ -25,11 +25,18 @@
 //     [32*(l/16), +32) of the 128-byte block (the hardware's internal K order
 //     within those bytes is irrelevant because A and B use the same order and
 //     one scale covers the whole block);
-//   16x16 result: lane l, register r -> row 4*(l/16) + r, column l % 16.
+//   16x16 result D = X * Y: lane l, register r -> D[4*(l/16) + r][l % 16].
+// The kernels compute the transposed product (X = B fragment, Y = A
+// fragment), so lane l holds output row (l % 16) and the four consecutive
+// output columns 4*(l/16) .. +3: the epilogue stores 8 or 16 contiguous bytes
+// per lane and each lane needs one row scale per 16-row tile.
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <chrono>
 #include <cstdint>
+#include <type_traits>
 
 #include "bsmm_internal.h"
 
@@ -39,6 +46,7 @@ namespace {
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr int kWave = 64;
@@ -60,16 +68,22 @@ __device__ __forceinline__ int lds_off(int r, int c) {
   return (r << 7) + ((c ^ swz(r)) << 4);
 }
 
-__device__ __forceinline__ void wait_vmem() {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+// Workgroup barrier for the K loop.  Each wave has already waited for its
+// own direct-to-LDS loads and consumed every LDS read of the stage being
+// recycled, so a bare s_barrier suffices (no release fence); the empty asm
+// statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
   if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu))
-    return (uint16_t)((u >> 16) | 0x0040u);          // quiet NaN
+    return (u >> 16) | 0x0040u;                       // quiet NaN
   u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return u >> 16;
 }
 
 // ---------------------------------------------------------------------------
@@ -81,6 +95,7 @@ struct KArgs {
   int row_begin, row_end;
   int tiles_m, tiles_n;
   int splits, kb_per_split;
+  int vec_out;        // output (or workspace) rows allow 8/16-byte stores
   void* ws;           // split-K partials [splits][G][rows][N] (fp32 / int32)
 };
 
@@ -123,8 +138,18 @@ __device__ __forceinline__ TileId decode_tile(const KArgs& k) {
 // ---------------------------------------------------------------------------
 // The tile kernel.  Workgroup tile BM x BN, waves arranged WM x WN, each wave
 // a 64 x 128 sub-tile = 4 x 8 MFMA tiles of 16 x 16.
+//
+// LDS is a ring of NSLOT slots; K block c of the workgroup occupies two
+// "half-stages": h = 2c (its A tile) and h = 2c + 1 (its B tile), in slot
+// h % NSLOT.  While K block c computes from its two slots, the other
+// NSLOT - 2 half-stages are in flight (for 256 x 256 tiles: five 32 KB slots,
+// the whole 160 KB, so 1.5 K blocks stay in flight).  The two slots of block
+// c - 1 are refilled with half-stages 2c + NSLOT - 2 and 2c + NSLOT - 1 as
+// soon as every wave has passed the barrier at the top of block c.  Scales
+// do not go through LDS: each lane loads the ones it needs into registers one
+// K block ahead.
 // ---------------------------------------------------------------------------
-template <int OP, int WM, int WN>
+template <int OP, int WM, int WN, int RING>
 struct Tile {
   static constexpr int NW = WM * WN;
   static constexpr int NT = NW * kWave;
@@ -133,294 +158,515 @@ struct Tile {
   static constexpr int BM = WM * WTM, BN = WN * WTN;
   static constexpr int A_BYTES = BM * kBlockK;
   static constexpr int B_BYTES = BN * kBlockK;
-  // blockwise: BM fp32 row scales + up to 64 fp32 column-block scales
-  static constexpr int S_BYTES = (OP == BSMM_OP_FP8_BLOCKWISE) ? (BM * 4 + 256) : 0;
-  static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
-  static constexpr int LDS = 2 * STAGE;
-  static_assert((BM / 8) % NW == 0 || NW % (BM / 8) == 0, "A loader split");
+  static constexpr int SLOT = A_BYTES > B_BYTES ? A_BYTES : B_BYTES;
+  static constexpr int NSLOT = RING;
+  static constexpr int LDS = NSLOT * SLOT;
+  // direct-to-LDS loads per thread for one A / one B half-stage
+  static constexpr int LA = BM / 8 / NW, LB = BN / 8 / NW;
+  // loads of the half-stages after block c's pair that may still be in
+  // flight when block c starts: h = 2c+2 .. 2c+NSLOT-3 (A, B, A, ...)
+  static constexpr int WAIT = ((NSLOT - 3) / 2) * LA + ((NSLOT - 4) / 2) * LB;
+  static_assert(NSLOT >= 4, "the ring needs at least four slots");
+  static_assert((BM / 8) % NW == 0 && (BN / 8) % NW == 0, "loader split");
+  static_assert(WAIT < 64, "vmcnt range");
 };
 
+// R rows x 128 bytes; one wave instruction moves 8 rows (64 x 16 bytes) to
+// LDS bytes [q*1024, q*1024+1024) of the slot, lane l -> slot byte 16 l.
+// A dead half-stage (past the last K block) is issued with out-of-range
+// offsets: it keeps the per-wave load count uniform and touches no memory.
 template <int R, int NW>
 __device__ __forceinline__ void load_rows(__amdgpu_buffer_rsrc_t rs,
                                           uint8_t* dst, uint32_t ld,
-                                          uint32_t kbyte, int wave, int lane) {
-  // R rows x 128 bytes; one wave instruction moves 8 rows (64 x 16 bytes)
-  // to LDS bytes [q*1024, q*1024+1024) of the tile, lane l -> slot l.
+                                          uint32_t kbyte, int wave, int lane,
+                                          bool live) {
   constexpr int Q = R / 8;
-  if constexpr (Q >= NW) {
 #pragma unroll
-    for (int t = 0; t < Q / NW; ++t) {
-      const int q = t * NW + wave;
-      const int r = q * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ swz(r);
-      const uint32_t vo = (uint32_t)r * ld + kbyte + ((uint32_t)c << 4);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + q * 1024),
-                                               16, vo, 0, 0, 0);
+  for (int t = 0; t < Q / NW; ++t) {
+    const int q = t * NW + wave;
+    const int r = q * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ swz(r);
+    const uint32_t vo = live ? (uint32_t)r * ld + kbyte + ((uint32_t)c << 4) : kOob;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + q * 1024), 16, vo,
+                                             0, 0, 0);
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Store 4 consecutive output values of one row.
+template <int OUT>
+__device__ __forceinline__ void store4(uint8_t* base, int64_t e, const float* y,
+                                       const int* yi, bool vec, int nvalid) {
+  if (OUT == BSMM_BF16) {
+    uint16_t* o = (uint16_t*)base + e;
+    if (vec && nvalid == 4) {
+      u32x2 v;
+      v.x = f32_to_bf16_rne(y[0]) | (f32_to_bf16_rne(y[1]) << 16);
+      v.y = f32_to_bf16_rne(y[2]) | (f32_to_bf16_rne(y[3]) << 16);
+      *(u32x2*)o = v;
+    } else {
+      for (int r = 0; r < nvalid; ++r) o[r] = (uint16_t)f32_to_bf16_rne(y[r]);
     }
+  } else if (OUT == BSMM_F32) {
+    float* o = (float*)base + e;
+    if (vec && nvalid == 4) *(f32x4*)o = f32x4{y[0], y[1], y[2], y[3]};
+    else for (int r = 0; r < nvalid; ++r) o[r] = y[r];
   } else {
-    if (wave < Q) {
-      const int q = wave;
-      const int r = q * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ swz(r);
-      const uint32_t vo = (uint32_t)r * ld + kbyte + ((uint32_t)c << 4);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + q * 1024),
-                                               16, vo, 0, 0, 0);
+    int* o = (int*)base + e;
+    if (vec && nvalid == 4) *(i32x4*)o = i32x4{yi[0], yi[1], yi[2], yi[3]};
+    else for (int r = 0; r < nvalid; ++r) o[r] = yi[r];
+  }
+}
+
+// The K loop: acc += the products of K blocks [kb0, kb0 + nkb) of tile
+// (g, row0, col0).  Shared by the one-tile-per-workgroup kernel and the
+// persistent stream-K kernel.  Every wave of the workgroup must call it with
+// the same arguments; it starts with a barrier (a previous call's LDS reads
+// must be finished before its loads overwrite the ring) and leaves no loads
+// in flight.
+template <int OP, int WM, int WN, int RING>
+struct Mainloop {
+  using T = Tile<OP, WM, WN, RING>;
+  using acc_t = typename OpT<OP>::acc_t;
+  static constexpr int TI = T::TI, TJ = T::TJ;
+
+  __device__ __forceinline__ static void run(const KArgs& k, uint8_t* smem, int g,
+                                             int row0, int col0, int kb0, int nkb,
+                                             acc_t (&acc)[TI][TJ]) {
+    constexpr int BM = T::BM, BN = T::BN;
+    constexpr int NW = T::NW, NSLOT = T::NSLOT, SLOT = T::SLOT;
+    const Problem& p = k.p;
+    const int lane = threadIdx.x & 63;
+    // wave-uniform values live in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int wm = wave / WN, wn = wave % WN;
+
+    // Buffer resources: rows past the launch's end / past N are out of range.
+    const uint32_t lda = (uint32_t)p.lda, ldb = (uint32_t)p.ldb;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(
+        p.a + (int64_t)g * p.a_sg + (int64_t)row0 * p.lda,
+        (uint64_t)(k.row_end - row0) * p.lda);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(
+        p.b + (int64_t)g * p.b_sg + (int64_t)col0 * p.ldb,
+        (uint64_t)(p.N - col0) * p.ldb);
+
+    // half-stage h (relative to kb0): its K block's A (h even) or B tile
+    auto issue_half = [&](int h, int slot) {
+      uint8_t* dst = smem + slot * SLOT;
+      const bool live = h < 2 * nkb;
+      const uint32_t kbyte = (uint32_t)(kb0 + (h >> 1)) * kBlockK;
+      if (h & 1) load_rows<BN, NW>(rb, dst, ldb, kbyte, wave, lane, live);
+      else load_rows<BM, NW>(ra, dst, lda, kbyte, wave, lane, live);
+    };
+
+    // Per-lane fragment addresses (bytes within a slot): row / column
+    // (lane % 16) of the wave's first 16-row tile, chunks 2*(lane/16) + h.
+    const int fr = lane & 15;
+    const int fc = (lane >> 4) * 2;
+    const int a_r = wm * T::WTM + fr;
+    const int b_r = wn * T::WTN + fr;
+    const int a_off0 = lds_off(a_r, fc), a_off1 = lds_off(a_r, fc + 1);
+    const int b_off0 = lds_off(b_r, fc), b_off1 = lds_off(b_r, fc + 1);
+
+    lds_barrier();     // LDS reads of a previous call are finished
+    // Scale pointers.  mx: x_scale bytes of this lane's row in each 16-row
+    // tile and the wave's w_scale block.  blockwise: scale_a of the same rows
+    // and the wave's scale_b column block.  Rows past the end read a valid row
+    // (their results are never stored); so do waves whose columns lie past N.
+    const uint8_t* xs_row[TI];
+    const uint8_t* ws_blk = nullptr;
+    const float* sa_row[TI];
+    const float* sb_blk = nullptr;
+    if constexpr (OP != BSMM_OP_INT8_ROWWISE) {
+      const int nb = min((col0 + wn * T::WTN) / kBlockK, p.N / kBlockK - 1);
+  #pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        const int m = min(row0 + wm * T::WTM + i * 16 + fr, k.row_end - 1);
+        if constexpr (OP == BSMM_OP_FP8_MX_BMM)
+          xs_row[i] = (const uint8_t*)p.sa + (int64_t)g * p.sa_sg + (int64_t)m * p.sa_m;
+        else
+          sa_row[i] = (const float*)p.sa + (int64_t)m * p.sa_m;
+      }
+      if constexpr (OP == BSMM_OP_FP8_MX_BMM)
+        ws_blk = (const uint8_t*)p.sb + (int64_t)g * p.sb_sg + (int64_t)nb * p.sb_n;
+      else
+        sb_blk = (const float*)p.sb + (int64_t)nb * p.sb_n;
+    }
+
+    // Scale registers of the current K block (cur) and the next one (nxt).
+    // Block c+1's are loaded during block c, before that block's refills; the
+    // copy at the end of block c therefore only waits for loads that were
+    // issued a whole block earlier.
+    int xs_cur[TI], xs_nxt[TI];
+    int ws_cur = 127, ws_nxt = 127;
+    float sa_cur[TI], sa_nxt[TI];
+    float sb_cur = 1.f, sb_nxt = 1.f;
+    auto load_scales = [&](int kb) {
+      if constexpr (OP == BSMM_OP_FP8_MX_BMM) {
+  #pragma unroll
+        for (int i = 0; i < TI; ++i) xs_nxt[i] = xs_row[i][kb];
+        ws_nxt = ws_blk[kb];
+      } else if constexpr (OP == BSMM_OP_FP8_BLOCKWISE) {
+  #pragma unroll
+        for (int i = 0; i < TI; ++i) sa_nxt[i] = sa_row[i][(int64_t)kb * p.sa_kb];
+        sb_nxt = sb_blk[(int64_t)kb * p.sb_kb];
+      }
+    };
+
+    if (nkb > 0) {
+      load_scales(kb0);
+  #pragma unroll
+      for (int h = 0; h < NSLOT - 2; ++h) issue_half(h, h);
+    }
+    for (int c = 0; c < nkb; ++c) {
+      const int slot_a = (2 * c) % NSLOT;
+      const int slot_b = slot_a + 1 == NSLOT ? 0 : slot_a + 1;
+      const int refill_a = (2 * c + NSLOT - 2) % NSLOT;
+      const int refill_b = refill_a + 1 == NSLOT ? 0 : refill_a + 1;
+      wait_vmcnt<T::WAIT>();   // block c's two half-stages have landed
+      lds_barrier();           // ... for every wave; block c-1's slots are free
+  #pragma unroll
+      for (int i = 0; i < TI; ++i) { xs_cur[i] = xs_nxt[i]; sa_cur[i] = sa_nxt[i]; }
+      ws_cur = ws_nxt;
+      sb_cur = sb_nxt;
+      const uint8_t* SA = smem + slot_a * SLOT;
+      const uint8_t* SB = smem + slot_b * SLOT;
+
+      // Fragments: B tile 0 and the A tiles first (they gate the first MFMA);
+      // the B tile of column j+1 is read while column j computes.
+      auto read_b = [&](int j) {
+        const i32x4 lo = *(const i32x4*)(SB + b_off0 + j * 2048);
+        const i32x4 hi = *(const i32x4*)(SB + b_off1 + j * 2048);
+        return i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      };
+      i32x8 bcur = read_b(0);
+      i32x8 af[TI];
+  #pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        const i32x4 lo = *(const i32x4*)(SA + a_off0 + i * 2048);
+        const i32x4 hi = *(const i32x4*)(SA + a_off1 + i * 2048);
+        af[i] = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      }
+      // next block's scales (clamped to the last block), then the two slots
+      // block c-1 used are refilled with half-stages 2c+NSLOT-2, 2c+NSLOT-1
+      load_scales(kb0 + min(c + 1, nkb - 1));
+      __builtin_amdgcn_sched_barrier(0);   // scale loads stay ahead of the refills
+      issue_half(2 * c + NSLOT - 2, refill_a);
+      issue_half(2 * c + NSLOT - 1, refill_b);
+      __builtin_amdgcn_sched_barrier(0);
+
+      // blockwise: scale product for this lane's row in each 16-row tile
+      float sc[TI];
+      if constexpr (OP == BSMM_OP_FP8_BLOCKWISE) {
+  #pragma unroll
+        for (int i = 0; i < TI; ++i) sc[i] = sa_cur[i] * sb_cur;
+      }
+
+      // Blockwise: the fp32 partial of MFMA tile t is folded into its
+      // accumulator D steps later, so the multiply-adds never wait on the
+      // MFMA that was just issued.
+      constexpr int D = 4;
+      f32x4 ring[D];
+  #pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        i32x8 bnext = bcur;
+        if (j + 1 < TJ) bnext = read_b(j + 1);
+  #pragma unroll
+        for (int i = 0; i < TI; ++i) {
+          const int tt = j * TI + i;
+          if constexpr (OP == BSMM_OP_INT8_ROWWISE) {
+            const i32x4 alo = i32x4{af[i][0], af[i][1], af[i][2], af[i][3]};
+            const i32x4 ahi = i32x4{af[i][4], af[i][5], af[i][6], af[i][7]};
+            const i32x4 blo = i32x4{bcur[0], bcur[1], bcur[2], bcur[3]};
+            const i32x4 bhi = i32x4{bcur[4], bcur[5], bcur[6], bcur[7]};
+            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(blo, alo, acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bhi, ahi, acc[i][j], 0, 0, 0);
+          } else if constexpr (OP == BSMM_OP_FP8_BLOCKWISE) {
+            // fold tile tt-D (issued D MFMAs ago) out of its ring slot, then
+            // refill the slot with tile tt
+            if (tt >= D) {
+              const int u = tt - D, ui = u % TI, uj = u / TI;
+  #pragma unroll
+              for (int r = 0; r < 4; ++r)
+                acc[ui][uj][r] = __builtin_fmaf(sc[ui], ring[u % D][r], acc[ui][uj][r]);
+            }
+            ring[tt % D] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                bcur, af[i], f32x4{0, 0, 0, 0}, 0, 0, 0, 127, 0, 127);
+          } else {
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                bcur, af[i], acc[i][j], 0, 0, 0, ws_cur, 0, xs_cur[i]);
+          }
+        }
+        bcur = bnext;
+      }
+      if constexpr (OP == BSMM_OP_FP8_BLOCKWISE) {
+  #pragma unroll
+        for (int u = TI * TJ - D; u < TI * TJ; ++u) {
+          const int ui = u % TI, uj = u / TI;
+  #pragma unroll
+          for (int r = 0; r < 4; ++r)
+            acc[ui][uj][r] = __builtin_fmaf(sc[ui], ring[u % D][r], acc[ui][uj][r]);
+        }
+      }
+      // Scheduling: per column j, the MFMAs of j with the two reads of B tile
+      // j+1 right after the first one and, for blockwise, four multiply-adds
+      // after each MFMA.
+      constexpr int kMfma = 0x008, kValu = 0x002, kDsRead = 0x100;
+      constexpr int MF = OP == BSMM_OP_INT8_ROWWISE ? 2 : 1;   // MFMAs per tile
+  #pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+  #pragma unroll
+        for (int i = 0; i < TI; ++i) {
+          __builtin_amdgcn_sched_group_barrier(kMfma, MF, 0);
+          if (i == 0 && j + 1 < TJ) __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
+          if constexpr (OP == BSMM_OP_FP8_BLOCKWISE) __builtin_amdgcn_sched_group_barrier(kValu, 4, 0);
+        }
+      }
+    }
+    // the last refills were out-of-range loads; let them drain
+    wait_vmcnt<0>();
+  }
+};
+
+// Lane (wave wm, wn; lane l) holds output rows row0 + 64 wm + 16 i + l % 16
+// and columns col0 + 128 wn + 16 j + 4 (l / 16) .. +3 of the tile.
+struct LanePos { int mrow, ncol; };
+template <int WM, int WN>
+__device__ __forceinline__ LanePos lane_pos(int row0, int col0) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  return LanePos{row0 + wm * 64 + (lane & 15), col0 + wn * 128 + 4 * (lane >> 4)};
+}
+
+// Final epilogue: scale (int8), convert, store the tile to the output.
+template <int OP, int OUT, int WM, int WN, int TI, int TJ, class acc_t>
+__device__ __forceinline__ void store_output(const KArgs& k, int g, int row0, int col0,
+                                             const acc_t (&acc)[TI][TJ]) {
+  const Problem& p = k.p;
+  const LanePos lp = lane_pos<WM, WN>(row0, col0);
+  const bool vec = k.vec_out != 0;
+  uint8_t* obase = (uint8_t*)p.out;
+  const int64_t og = (int64_t)g * p.o_sg;
+#pragma unroll
+  for (int i = 0; i < TI; ++i) {
+    const int m = lp.mrow + i * 16;
+    if (m >= k.row_end) continue;
+    float sa_m = 1.f;
+    if constexpr (OP == BSMM_OP_INT8_ROWWISE && OUT != BSMM_I32)
+      sa_m = ((const float*)p.sa)[(int64_t)m * p.sa_m];
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int n = lp.ncol + j * 16;
+      const int nvalid = min(4, p.N - n);
+      if (nvalid <= 0) continue;
+      const int64_t e = og + (int64_t)m * p.ldo + n;
+      float y[4];
+      int yi[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if constexpr (OP == BSMM_OP_INT8_ROWWISE) {
+          yi[r] = acc[i][j][r];
+          if constexpr (OUT != BSMM_I32) {
+            // (f32(acc) * sa) * sb, two separately rounded binary32 products
+            const float sb_n = ((const float*)p.sb)[(int64_t)min(n + r, p.N - 1) * p.sb_n];
+            y[r] = __fmul_rn(__fmul_rn((float)acc[i][j][r], sa_m), sb_n);
+          }
+        } else {
+          y[r] = acc[i][j][r];
+        }
+      }
+      store4<OUT>(obase, e, y, yi, vec, nvalid);
     }
   }
 }
 
-template <int OP, int WM, int WN>
-__global__ void __launch_bounds__(64 * WM * WN)
-tile_kernel(const KArgs k) {
-  using T = Tile<OP, WM, WN>;
-  using acc_t = typename OpT<OP>::acc_t;
-  constexpr int BM = T::BM, BN = T::BN, TI = T::TI, TJ = T::TJ;
-  constexpr int NW = T::NW;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS];
-
+// Split-K partial: fp32 / int32 values into workspace [splits][G][rows][N].
+template <int OP, int WM, int WN, int TI, int TJ, class acc_t>
+__device__ __forceinline__ void store_splitk(const KArgs& k, int s, int g, int row0,
+                                             int col0, const acc_t (&acc)[TI][TJ]) {
   const Problem& p = k.p;
-  const TileId t = decode_tile(k);
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int wm = wave / WN, wn = wave % WN;
-
-  const int row0 = k.row_begin + t.tm * BM;
-  const int col0 = t.tn * BN;
-  const int KB = p.K / kBlockK;
-  const int kb0 = t.s * k.kb_per_split;
-  const int kb1 = min(KB, kb0 + k.kb_per_split);
-
-  // Buffer resources: rows past the launch's end / past N are out of range.
-  const uint32_t lda = (uint32_t)p.lda, ldb = (uint32_t)p.ldb;
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(
-      p.a + (int64_t)t.g * p.a_sg + (int64_t)row0 * p.lda,
-      (uint64_t)(k.row_end - row0) * p.lda);
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(
-      p.b + (int64_t)t.g * p.b_sg + (int64_t)col0 * p.ldb,
-      (uint64_t)(p.N - col0) * p.ldb);
-
-  // Blockwise scale resources (fp32): rows of this tile, column blocks.
-  __amdgpu_buffer_rsrc_t rsa, rsb;
-  if constexpr (OP == BSMM_OP_FP8_BLOCKWISE) {
-    const float* sa = (const float*)p.sa + (int64_t)row0 * p.sa_m;
-    const int64_t last = (int64_t)(k.row_end - 1 - row0) * p.sa_m +
-                         (int64_t)(KB - 1) * p.sa_kb + 1;
-    rsa = make_rsrc(sa, (uint64_t)last * 4);
-    const int NB = p.N / kBlockK;
-    const int64_t lastb = (int64_t)(KB - 1) * p.sb_kb + (int64_t)(NB - 1) * p.sb_n + 1;
-    rsb = make_rsrc(p.sb, (uint64_t)lastb * 4);
-  }
-
-  auto issue = [&](int kb, int st) {
-    uint8_t* base = smem + st * T::STAGE;
-    const uint32_t kbyte = (uint32_t)kb * kBlockK;
-    load_rows<BM, NW>(ra, base, lda, kbyte, wave, lane);
-    load_rows<BN, NW>(rb, base + T::A_BYTES, ldb, kbyte, wave, lane);
-    if constexpr (OP == BSMM_OP_FP8_BLOCKWISE) {
-      uint8_t* sdst = base + T::A_BYTES + T::B_BYTES;
-      constexpr int QA = BM / 64;             // 64 row scales per instruction
+  const LanePos lp = lane_pos<WM, WN>(row0, col0);
+  const bool vec = k.vec_out != 0;
+  const int rows = k.row_end - k.row_begin;
+  typedef typename OpT<OP>::elem_t E;
+  uint8_t* ws = (uint8_t*)((E*)k.ws + ((int64_t)s * p.G + g) * (int64_t)rows * p.N);
 #pragma unroll
-      for (int q = 0; q <= QA; ++q) {
-        if (wave == q % NW) {
-          uint32_t vo;
-          if (q < QA) {
-            vo = (uint32_t)(((int64_t)(q * 64 + lane) * p.sa_m +
-                             (int64_t)kb * p.sa_kb) * 4);
-            if (row0 + q * 64 + lane >= k.row_end) vo = kOob;
-          } else {
-            const int nb = col0 / kBlockK + lane;
-            vo = (lane < BN / kBlockK)
-                     ? (uint32_t)(((int64_t)kb * p.sb_kb + (int64_t)nb * p.sb_n) * 4)
-                     : kOob;
-          }
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              q < QA ? rsa : rsb, (lds_ptr_t)(sdst + q * 256), 4, vo, 0, 0, 0);
-        }
-      }
-    }
-  };
-
-  acc_t acc[TI][TJ];
-#pragma unroll
-  for (int i = 0; i < TI; ++i)
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) acc[i][j] = acc_t{0, 0, 0, 0};
-
-  // Per-lane fragment addresses (bytes within a stage): row / column
-  // (lane % 16) of the wave's first 16-row tile, chunks 2*(lane/16) + h.
-  const int fr = lane & 15;
-  const int fc = (lane >> 4) * 2;
-  const int a_r = wm * T::WTM + fr;
-  const int b_r = wn * T::WTN + fr;
-  const int a_off0 = lds_off(a_r, fc), a_off1 = lds_off(a_r, fc + 1);
-  const int b_off0 = T::A_BYTES + lds_off(b_r, fc);
-  const int b_off1 = T::A_BYTES + lds_off(b_r, fc + 1);
-
-  // mx scale bytes: x_scale rows of this lane's 4 row tiles, w_scale block.
-  const uint8_t* xs_row[TI];
-  const uint8_t* ws_blk = nullptr;
-  if constexpr (OP == BSMM_OP_FP8_MX_BMM) {
-#pragma unroll
-    for (int i = 0; i < TI; ++i) {
-      int m = row0 + wm * T::WTM + i * 16 + fr;
-      m = min(m, k.row_end - 1);   // rows past the end: any valid row
-      xs_row[i] = (const uint8_t*)p.sa + (int64_t)t.g * p.sa_sg + (int64_t)m * p.sa_m;
-    }
-    // waves whose columns lie past N (N tail) read the last block's scale;
-    // their results are never stored
-    const int nb = min((col0 + wn * T::WTN) / kBlockK, p.N / kBlockK - 1);
-    ws_blk = (const uint8_t*)p.sb + (int64_t)t.g * p.sb_sg + (int64_t)nb * p.sb_n;
-  }
-
-  // mx scale bytes of the current K block; the next block's are loaded one
-  // step ahead, together with its tiles.
-  int xsc[TI];
-  int wsc = 127;
-  if constexpr (OP == BSMM_OP_FP8_MX_BMM) {
-    if (kb0 < kb1) {
-#pragma unroll
-      for (int i = 0; i < TI; ++i) xsc[i] = xs_row[i][kb0];
-      wsc = ws_blk[kb0];
-    }
-  }
-
-  if (kb0 < kb1) issue(kb0, 0);
-  for (int kb = kb0; kb < kb1; ++kb) {
-    const int st = (kb - kb0) & 1;
-    wait_vmem();
-    __syncthreads();
-    int xsn[TI];
-    int wsn = 127;
-    if (kb + 1 < kb1) {
-      issue(kb + 1, st ^ 1);
-      if constexpr (OP == BSMM_OP_FP8_MX_BMM) {
-#pragma unroll
-        for (int i = 0; i < TI; ++i) xsn[i] = xs_row[i][kb + 1];
-        wsn = ws_blk[kb + 1];
-      }
-    }
-    const uint8_t* S = smem + st * T::STAGE;
-
-    i32x8 af[TI];
-#pragma unroll
-    for (int i = 0; i < TI; ++i) {
-      const i32x4 lo = *(const i32x4*)(S + a_off0 + i * 2048);
-      const i32x4 hi = *(const i32x4*)(S + a_off1 + i * 2048);
-      af[i] = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-    }
-
-    f32x4 sc[TI];
-    if constexpr (OP == BSMM_OP_FP8_BLOCKWISE) {
-      const float* sa_s = (const float*)(S + T::A_BYTES + T::B_BYTES);
-      const float sbv = sa_s[BM + wn];
-#pragma unroll
-      for (int i = 0; i < TI; ++i) {
-        const f32x4 v = *(const f32x4*)(sa_s + wm * T::WTM + i * 16 + 4 * (lane >> 4));
-        sc[i] = v * sbv;
-      }
-    }
-
+  for (int i = 0; i < TI; ++i) {
+    const int m = lp.mrow + i * 16;
+    if (m >= k.row_end) continue;
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
-      const i32x4 blo = *(const i32x4*)(S + b_off0 + j * 2048);
-      const i32x4 bhi = *(const i32x4*)(S + b_off1 + j * 2048);
-      const i32x8 bf = i32x8{blo.x, blo.y, blo.z, blo.w, bhi.x, bhi.y, bhi.z, bhi.w};
-#pragma unroll
-      for (int i = 0; i < TI; ++i) {
-        if constexpr (OP == BSMM_OP_INT8_ROWWISE) {
-          const i32x4 alo = i32x4{af[i][0], af[i][1], af[i][2], af[i][3]};
-          const i32x4 ahi = i32x4{af[i][4], af[i][5], af[i][6], af[i][7]};
-          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(alo, blo, acc[i][j], 0, 0, 0);
-          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ahi, bhi, acc[i][j], 0, 0, 0);
-        } else if constexpr (OP == BSMM_OP_FP8_BLOCKWISE) {
-          const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              af[i], bf, f32x4{0, 0, 0, 0}, 0, 0, 0, 127, 0, 127);
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            acc[i][j][r] = __builtin_fmaf(sc[i][r], part[r], acc[i][j][r]);
-        } else {
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              af[i], bf, acc[i][j], 0, 0, 0, xsc[i], 0, wsc);
-        }
+      const int n = lp.ncol + j * 16;
+      const int nvalid = min(4, p.N - n);
+      if (nvalid <= 0) continue;
+      const int64_t e = (int64_t)(m - k.row_begin) * p.N + n;
+      if constexpr (OP == BSMM_OP_INT8_ROWWISE) {
+        const int yi[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+        store4<BSMM_I32>(ws, e, nullptr, yi, vec, nvalid);
+      } else {
+        const float y[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+        store4<BSMM_F32>(ws, e, y, nullptr, vec, nvalid);
       }
     }
-    if constexpr (OP == BSMM_OP_FP8_MX_BMM) {
-#pragma unroll
-      for (int i = 0; i < TI; ++i) xsc[i] = xsn[i];
-      wsc = wsn;
-    }
   }
+}
 
-  // ------------------------------------------------------------- epilogue --
-  const int mbase = row0 + wm * T::WTM + 4 * (lane >> 4);
-  const int nbase = col0 + wn * T::WTN + fr;
-  if (k.splits > 1) {
-    // fp32 / int32 partials, reduced in split order by splitk_reduce.
-    const int rows = k.row_end - k.row_begin;
-    typedef typename OpT<OP>::elem_t E;
-    E* ws = (E*)k.ws + ((int64_t)t.s * p.G + t.g) * (int64_t)rows * p.N;
+// One output tile (or one K slice of it, with split-K) per workgroup.
+template <int OP, int OUT, int WM, int WN, int RING>
+__global__ void __launch_bounds__(64 * WM * WN)
+tile_kernel(const KArgs k) {
+  using M = Mainloop<OP, WM, WN, RING>;
+  using T = typename M::T;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS];
+  const TileId t = decode_tile(k);
+  const int row0 = k.row_begin + t.tm * T::BM;
+  const int col0 = t.tn * T::BN;
+  const int KB = k.p.K / kBlockK;
+  const int kb0 = t.s * k.kb_per_split;
+  const int nkb = max(0, min(KB, kb0 + k.kb_per_split) - kb0);
+  typename M::acc_t acc[M::TI][M::TJ];
+#pragma unroll
+  for (int i = 0; i < M::TI; ++i)
+#pragma unroll
+    for (int j = 0; j < M::TJ; ++j) acc[i][j] = typename M::acc_t{0, 0, 0, 0};
+  M::run(k, smem, t.g, row0, col0, kb0, nkb, acc);
+  if (k.splits > 1)
+    store_splitk<OP, WM, WN>(k, t.s, t.g, row0, col0, acc);
+  else
+    store_output<OP, OUT, WM, WN>(k, t.g, row0, col0, acc);
+}
+
+// ---------------------------------------------------------------------------
+// Persistent stream-K kernel.  The grid is exactly the number of workgroups
+// the device holds at once.  The work, tiles x K blocks, is cut into equal
+// contiguous ranges, one per workgroup, so every CU gets the same number of
+// K blocks however the tile count divides the CU count.  A tile split between
+// consecutive ranges is finished by the workgroup holding its K block 0 (it
+// reaches that segment last, at the end of its range); every other segment
+// of the tile is the *first* segment of a later range, computed first, and is
+// stored as an fp32 / int32 partial with a flag carrying the launch's epoch.
+// The owner waits for the flags (bounded), adds the partials in K order and
+// stores the tile.  With two segments the sum is exactly order-independent;
+// with more, the fixed K order keeps it deterministic.
+// Workspace: one partial slot of BM x BN elements per workgroup, then one
+// 64-bit flag per workgroup.
+// ---------------------------------------------------------------------------
+struct SkArgs {
+  int64_t units;       // tiles * KB
+  uint64_t epoch;      // distinct per launch
+  int tiles_total;     // tiles_m * tiles_n * G
+};
+
+constexpr int kSpinLimit = 1 << 22;   // ~ seconds of polling; never reached
+                                      // when the grid is co-resident
+
+template <int OP, int OUT, int WM, int WN, int RING>
+__global__ void __launch_bounds__(64 * WM * WN)
+sk_kernel(const KArgs k, const SkArgs sk) {
+  using M = Mainloop<OP, WM, WN, RING>;
+  using T = typename M::T;
+  using acc_t = typename M::acc_t;
+  typedef typename OpT<OP>::elem_t E;
+  constexpr int TI = M::TI, TJ = M::TJ, NT = T::NT;
+  constexpr int SLOT_ELEMS = T::BM * T::BN;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS];
+  const int P = gridDim.x;
+  // XCD-aware: consecutive ranges run on the same XCD
+  const int hw = blockIdx.x;
+  const int per = P >> 3, rem = P & 7;
+  const int xcd = hw & 7, local = hw >> 3;
+  const int w = (xcd < rem) ? xcd * (per + 1) + local
+                            : rem * (per + 1) + (xcd - rem) * per + local;
+  const int KB = k.p.K / kBlockK;
+  auto range_start = [&](int wi) { return (int64_t)wi * sk.units / P; };   // units * P < 2^63
+  E* slots = (E*)k.ws;
+  uint64_t* flags = (uint64_t*)((uint8_t*)k.ws + (size_t)P * SLOT_ELEMS * sizeof(E));
+  const int tid = threadIdx.x;
+
+  int64_t u = range_start(w);
+  const int64_t uend = range_start(w + 1);
+  while (u < uend) {
+    const int tile = (int)(u / KB);
+    const int kb_a = (int)(u - (int64_t)tile * KB);
+    const int kb_b = (int)min((int64_t)KB, (int64_t)kb_a + (uend - u));
+    // tile -> (g, tm, tn): grouped order within each G
+    const int tiles = k.tiles_m * k.tiles_n;
+    const int g = tile / tiles;
+    const int tin = tile - g * tiles;
+    constexpr int GROUP_M = 8;
+    const int width = GROUP_M * k.tiles_n;
+    const int gid = tin / width;
+    const int first_m = gid * GROUP_M;
+    const int gsize = min(k.tiles_m - first_m, GROUP_M);
+    const int in = tin - gid * width;
+    const int tm = first_m + in % gsize, tn = in / gsize;
+    const int row0 = k.row_begin + tm * T::BM;
+    const int col0 = tn * T::BN;
+
+    acc_t acc[TI][TJ];
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int j = 0; j < TJ; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = mbase + i * 16 + r, n = nbase + j * 16;
-          if (m < k.row_end && n < p.N)
-            ws[(int64_t)(m - k.row_begin) * p.N + n] = acc[i][j][r];
-        }
-    return;
-  }
+      for (int j = 0; j < TJ; ++j) acc[i][j] = acc_t{0, 0, 0, 0};
+    M::run(k, smem, g, row0, col0, kb_a, kb_b - kb_a, acc);
 
-  uint8_t* obase = (uint8_t*)p.out;
-  const int osz = p.out_dtype == BSMM_BF16 ? 2 : 4;
-  const int64_t og = (int64_t)t.g * p.o_sg;
+    if (kb_a > 0) {
+      // a later K segment of a split tile: publish the partial (lane-major
+      // slot layout, 16-byte stores) and its flag
+      E* slot = slots + (size_t)w * SLOT_ELEMS;
 #pragma unroll
-  for (int i = 0; i < TI; ++i) {
-    float sa_r[4] = {1.f, 1.f, 1.f, 1.f};
-    if constexpr (OP == BSMM_OP_INT8_ROWWISE) {
-      if (p.out_dtype != BSMM_I32) {
+      for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = min(mbase + i * 16 + r, k.row_end - 1);
-          sa_r[r] = ((const float*)p.sa)[(int64_t)m * p.sa_m];
+        for (int j = 0; j < TJ; ++j) {
+          typedef E e4 __attribute__((ext_vector_type(4)));
+          e4 v = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+          *(e4*)(slot + ((size_t)(i * TJ + j) * NT + tid) * 4) = v;
         }
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-      const int n = nbase + j * 16;
-      float sb_c = 1.f;
-      if constexpr (OP == BSMM_OP_INT8_ROWWISE) {
-        if (p.out_dtype != BSMM_I32)
-          sb_c = ((const float*)p.sb)[(int64_t)min(n, p.N - 1) * p.sb_n];
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = mbase + i * 16 + r;
-        if (m >= k.row_end || n >= p.N) continue;
-        const int64_t e = og + (int64_t)m * p.ldo + n;
-        if constexpr (OP == BSMM_OP_INT8_ROWWISE) {
-          if (p.out_dtype == BSMM_I32) {
-            ((int*)obase)[e] = acc[i][j][r];
-            continue;
+      __threadfence();
+      __syncthreads();
+      if (tid == 0)
+        __hip_atomic_store(&flags[w], sk.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      if (kb_b < KB) {
+        // owner of a split tile: add the later segments' partials, which are
+        // the first segments of the following ranges, in K order
+        int w2 = w + 1;
+        while (w2 < P && range_start(w2) < (int64_t)(tile + 1) * KB) {
+          if (tid == 0) {
+            int spins = 0;
+            while (__hip_atomic_load(&flags[w2], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) !=
+                       sk.epoch &&
+                   ++spins < kSpinLimit)
+              __builtin_amdgcn_s_sleep(2);
           }
-          // (f32(acc) * sa) * sb, two separately rounded binary32 products
-          const float y = __fmul_rn(__fmul_rn((float)acc[i][j][r], sa_r[r]), sb_c);
-          if (osz == 2) ((uint16_t*)obase)[e] = f32_to_bf16_rne(y);
-          else ((float*)obase)[e] = y;
-        } else {
-          const float y = acc[i][j][r];
-          if (osz == 2) ((uint16_t*)obase)[e] = f32_to_bf16_rne(y);
-          else ((float*)obase)[e] = y;
+          __syncthreads();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+          const E* slot = slots + (size_t)w2 * SLOT_ELEMS;
+#pragma unroll
+          for (int i = 0; i < TI; ++i)
+#pragma unroll
+            for (int j = 0; j < TJ; ++j) {
+              typedef E e4 __attribute__((ext_vector_type(4)));
+              const e4 v = *(const e4*)(slot + ((size_t)(i * TJ + j) * NT + tid) * 4);
+#pragma unroll
+              for (int r = 0; r < 4; ++r) acc[i][j][r] += v[r];
+            }
+          ++w2;
         }
       }
+      store_output<OP, OUT, WM, WN>(k, g, row0, col0, acc);
     }
+    u += kb_b - kb_a;
   }
 }
 
 // Split-K reduction: out = epilogue(sum over s of partial[s]) in ascending s.
-template <int OP>
+template <int OP, int OUT>
 __global__ void __launch_bounds__(256)
 splitk_reduce(const KArgs k) {
   const Problem& p = k.p;
@@ -441,13 +687,16 @@ splitk_reduce(const KArgs k) {
     const int64_t o = (int64_t)g * p.o_sg + (int64_t)m * p.ldo + n;
     float y;
     if constexpr (OP == BSMM_OP_INT8_ROWWISE) {
-      if (p.out_dtype == BSMM_I32) { ((int*)p.out)[o] = (int)s; continue; }
+      if constexpr (OUT == BSMM_I32) {
+        ((int*)p.out)[o] = (int)s;
+        continue;
+      }
       y = __fmul_rn(__fmul_rn((float)s, ((const float*)p.sa)[(int64_t)m * p.sa_m]),
                     ((const float*)p.sb)[(int64_t)n * p.sb_n]);
     } else {
       y = (float)s;
     }
-    if (p.out_dtype == BSMM_BF16) ((uint16_t*)p.out)[o] = f32_to_bf16_rne(y);
+    if constexpr (OUT == BSMM_BF16) ((uint16_t*)p.out)[o] = (uint16_t)f32_to_bf16_rne(y);
     else ((float*)p.out)[o] = y;
   }
 }
@@ -477,10 +726,22 @@ int check_launch() {
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
-template <int OP, int WM, int WN>
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+// Output rows allow 8-byte (bf16) / 16-byte (fp32, int32) vector stores.
+template <int OUT>
+bool out_vec_ok(const Problem& p) {
+  const int osz = OUT == BSMM_BF16 ? 2 : 4;
+  const int vbytes = 4 * osz;
+  return ((uintptr_t)p.out % vbytes == 0) && (p.ldo * osz) % vbytes == 0 &&
+         (p.o_sg * osz) % vbytes == 0;
+}
+
+template <int OP, int OUT, int WM, int WN, int RING>
 int launch_tile(const Problem& p, int row_begin, int row_end, int split,
-                void* ws, void* stream) {
-  using T = Tile<OP, WM, WN>;
+                void* ws, size_t ws_bytes, void* stream) {
+  (void)ws_bytes;
+  using T = Tile<OP, WM, WN, RING>;
   KArgs k;
   k.p = p;
   k.row_begin = row_begin;
@@ -494,6 +755,7 @@ int launch_tile(const Problem& p, int row_begin, int row_end, int split,
   if (KB == 0) {              // empty sum: the output is zero
     k.splits = 1;
     k.kb_per_split = 0;
+    k.vec_out = 0;
     hipLaunchKernelGGL(zero_out, dim3(1024), dim3(256), 0, s, k);
     return check_launch();
   }
@@ -501,48 +763,116 @@ int launch_tile(const Problem& p, int row_begin, int row_end, int split,
   if (split > KB) split = KB;
   k.kb_per_split = (KB + split - 1) / split;
   k.splits = (KB + k.kb_per_split - 1) / k.kb_per_split;
+  if (k.splits > 1) {
+    // workspace rows are N elements of 4 bytes
+    k.vec_out = aligned16(ws) && p.N % 4 == 0;
+  } else {
+    k.vec_out = out_vec_ok<OUT>(p);
+  }
   const int64_t grid = (int64_t)k.tiles_m * k.tiles_n * p.G * k.splits;
-  hipLaunchKernelGGL((tile_kernel<OP, WM, WN>), dim3((unsigned)grid), dim3(T::NT), 0, s, k);
+  hipLaunchKernelGGL((tile_kernel<OP, OUT, WM, WN, RING>), dim3((unsigned)grid), dim3(T::NT), 0, s, k);
   if (check_launch()) return 1;
   if (k.splits > 1) {
     const int64_t total = (int64_t)rows * p.N * p.G;
     int64_t blocks = (total + 255) / 256;
     if (blocks > 65536) blocks = 65536;
-    hipLaunchKernelGGL(splitk_reduce<OP>, dim3((unsigned)blocks), dim3(256), 0, s, k);
+    hipLaunchKernelGGL((splitk_reduce<OP, OUT>), dim3((unsigned)blocks), dim3(256), 0, s, k);
     return check_launch();
   }
   return 0;
 }
 
+// Distinct per launch for the stream-K flags; seeded from the clock so that
+// flags left in a reused workspace by another process do not match.
+uint64_t next_epoch() {
+  static std::atomic<uint64_t> ctr{
+      ((uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() << 16) | 1u};
+  return ctr.fetch_add(1, std::memory_order_relaxed);
+}
+
+template <int OP, int OUT, int WM, int WN, int RING>
+int launch_sk(const Problem& p, int row_begin, int row_end, int split, void* ws,
+              size_t ws_bytes, void* stream) {
+  using T = Tile<OP, WM, WN, RING>;
+  const int KB = p.K / kBlockK;
+  typedef typename OpT<OP>::elem_t E;
+  const size_t per_wg = (size_t)T::BM * T::BN * sizeof(E) + sizeof(uint64_t);
+  if (KB == 0 || !aligned16(ws))
+    return launch_tile<OP, OUT, WM, WN, RING>(p, row_begin, row_end, split, ws, ws_bytes, stream);
+  // co-resident capacity of this kernel on the current device (cached)
+  static std::atomic<int> cap_cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
+  int cap = cap_cache[dev].load(std::memory_order_relaxed);
+  if (cap == 0) {
+    int cus = 0, occ = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &occ, reinterpret_cast<const void*>(&sk_kernel<OP, OUT, WM, WN, RING>), T::NT, 0) !=
+        hipSuccess)
+      return 1;
+    cap = cus * (occ > 0 ? occ : 1);
+    cap_cache[dev].store(cap, std::memory_order_relaxed);
+  }
+  KArgs k;
+  k.p = p;
+  k.row_begin = row_begin;
+  k.row_end = row_end;
+  const int rows = row_end - row_begin;
+  k.tiles_m = (rows + T::BM - 1) / T::BM;
+  k.tiles_n = (p.N + T::BN - 1) / T::BN;
+  k.splits = 1;
+  k.kb_per_split = KB;
+  k.vec_out = out_vec_ok<OUT>(p);
+  k.ws = ws;
+  SkArgs sk;
+  sk.tiles_total = k.tiles_m * k.tiles_n * p.G;
+  sk.units = (int64_t)sk.tiles_total * KB;
+  int P = cap;
+  if ((int64_t)P > sk.units) P = (int)sk.units;
+  if ((size_t)P * per_wg > ws_bytes) P = (int)(ws_bytes / per_wg);
+  if (P < 1)
+    return launch_tile<OP, OUT, WM, WN, RING>(p, row_begin, row_end, split, ws, ws_bytes, stream);
+  sk.epoch = next_epoch();
+  hipLaunchKernelGGL((sk_kernel<OP, OUT, WM, WN, RING>), dim3((unsigned)P), dim3(T::NT), 0,
+                     (hipStream_t)stream, k, sk);
+  return check_launch();
+}
+
+template <int WM, int WN, int RING, bool SK>
+int launch_variant(const Problem& p, int rb, int re, int sp, void* ws, size_t wsb, void* st) {
+#define BSMM_L(OPX, OUTX)                                                           \
+  return SK ? launch_sk<OPX, OUTX, WM, WN, RING>(p, rb, re, sp, ws, wsb, st)       \
+            : launch_tile<OPX, OUTX, WM, WN, RING>(p, rb, re, sp, ws, wsb, st)
+  switch (p.op) {
+    case BSMM_OP_INT8_ROWWISE:
+      if (p.out_dtype == BSMM_I32) BSMM_L(BSMM_OP_INT8_ROWWISE, BSMM_I32);
+      if (p.out_dtype == BSMM_F32) BSMM_L(BSMM_OP_INT8_ROWWISE, BSMM_F32);
+      BSMM_L(BSMM_OP_INT8_ROWWISE, BSMM_BF16);
+    case BSMM_OP_FP8_BLOCKWISE:
+      if (p.out_dtype == BSMM_F32) BSMM_L(BSMM_OP_FP8_BLOCKWISE, BSMM_F32);
+      BSMM_L(BSMM_OP_FP8_BLOCKWISE, BSMM_BF16);
+    default:
+      if (p.out_dtype == BSMM_F32) BSMM_L(BSMM_OP_FP8_MX_BMM, BSMM_F32);
+      BSMM_L(BSMM_OP_FP8_MX_BMM, BSMM_BF16);
+  }
+#undef BSMM_L
+}
+
 constexpr unsigned kAllOps = 7u;
 
-#define BSMM_VARIANT(NAME, WM, WN)                                              \
-  static int NAME##_launch(const Problem& p, int rb, int re, int sp, void* ws,  \
-                           void* st) {                                          \
-    switch (p.op) {                                                             \
-      case BSMM_OP_INT8_ROWWISE:                                                \
-        return launch_tile<BSMM_OP_INT8_ROWWISE, WM, WN>(p, rb, re, sp, ws, st); \
-      case BSMM_OP_FP8_BLOCKWISE:                                               \
-        return launch_tile<BSMM_OP_FP8_BLOCKWISE, WM, WN>(p, rb, re, sp, ws, st); \
-      default:                                                                  \
-        return launch_tile<BSMM_OP_FP8_MX_BMM, WM, WN>(p, rb, re, sp, ws, st);  \
-    }                                                                           \
-  }
-
-BSMM_VARIANT(t256x256, 4, 2)
-BSMM_VARIANT(t256x128, 4, 1)
-BSMM_VARIANT(t128x256, 2, 2)
-BSMM_VARIANT(t128x128, 2, 1)
-BSMM_VARIANT(t64x256, 1, 2)
-BSMM_VARIANT(t64x128, 1, 1)
-
+// name, tile_m, tile_n, ops, masked tail, persistent, workgroups per CU, launch
 const Variant kVariants[] = {
-    {"t256x256", 256, 256, kAllOps, true, t256x256_launch},
-    {"t256x128", 256, 128, kAllOps, true, t256x128_launch},
-    {"t128x256", 128, 256, kAllOps, true, t128x256_launch},
-    {"t128x128", 128, 128, kAllOps, true, t128x128_launch},
-    {"t64x256", 64, 256, kAllOps, true, t64x256_launch},
-    {"t64x128", 64, 128, kAllOps, true, t64x128_launch},
+    {"t256x256", 256, 256, kAllOps, true, false, 1, launch_variant<4, 2, 5, false>},
+    {"t256x128", 256, 128, kAllOps, true, false, 1, launch_variant<4, 1, 5, false>},
+    {"t128x256", 128, 256, kAllOps, true, false, 1, launch_variant<2, 2, 5, false>},
+    {"t128x128", 128, 128, kAllOps, true, false, 2, launch_variant<2, 1, 5, false>},
+    {"t64x256", 64, 256, kAllOps, true, false, 1, launch_variant<1, 2, 5, false>},
+    {"t64x128", 64, 128, kAllOps, true, false, 2, launch_variant<1, 1, 5, false>},
+    {"t256x256sk", 256, 256, kAllOps, true, true, 1, launch_variant<4, 2, 5, true>},
+    {"t256x128sk", 256, 128, kAllOps, true, true, 1, launch_variant<4, 1, 5, true>},
+    {"t128x128sk", 128, 128, kAllOps, true, true, 2, launch_variant<2, 1, 5, true>},
 };
 
 }  // namespace

@@ -21,7 +21,9 @@ from tests.gpu_util import (DEV, Forced, as_f64, check_blockwise, check_int8, ch
 
 pytestmark = pytest.mark.gpu
 
-VARIANTS = ["t256x256", "t256x128", "t128x256", "t128x128", "t64x256", "t64x128"]
+VARIANTS = ["t256x256", "t256x128", "t128x256", "t128x128", "t64x256", "t64x128",
+            "t256x256sk", "t256x128sk", "t128x128sk"]
+SK_VARIANTS = ["t256x256sk", "t256x128sk", "t128x128sk"]
 
 
 @pytest.fixture(autouse=True)
@@ -207,3 +209,37 @@ def test_determinism():
         z1 = host_out(run_blockwise(p, "f32")).view(np.uint32)
         z2 = host_out(run_blockwise(p, "f32")).view(np.uint32)
     assert np.array_equal(z1, z2)
+
+
+# ------------------------------------------------------------- stream-K ----
+
+@pytest.mark.parametrize("variant", SK_VARIANTS)
+def test_streamk_many_segments(variant):
+    """Few tiles, many workgroups: every tile is cut into several K
+    segments whose partials the owning workgroup adds in K order."""
+    p = int8_rowwise_inputs(300, 384, 1280, 501)
+    q = fp8_blockwise_inputs(300, 384, 1280, 502)
+    r = fp8_mx_bmm_inputs(2, 200, 256, 1280, 503, layout="m_major")
+    say(f"stream-K {variant} many segments")
+    with Forced(variant, 0):
+        yi = run_int8(p, "i32")
+        yb = run_blockwise(q, "f32")
+        ym = run_mx(r, "bf16")
+    check_int8(p, "i32", yi)
+    check_blockwise(q, "f32", yb)
+    check_mx(r, "bf16", ym)
+
+
+def test_streamk_small_workspace_two_way_splits():
+    """A workspace that holds three slots: three workgroups, tiles split in
+    two.  Results match the oracle and repeat bit for bit."""
+    q = fp8_blockwise_inputs(520, 512, 1280, 504)
+    a, b = dev(q["a"]), dev(q["b_nk"]).t()
+    sa, sb = dev(q["scale_a"]), dev(q["scale_b"])
+    ws = torch.empty(3 * (256 * 256 * 4 + 8), dtype=torch.uint8, device=DEV)
+    say("stream-K 3-slot workspace")
+    with Forced("t256x256sk", 0):
+        y1 = bsmm.bsmm_fp8_blockwise(a, b, sa, sb, out_dtype="f32", workspace=ws)
+        y2 = bsmm.bsmm_fp8_blockwise(a, b, sa, sb, out_dtype="f32", workspace=ws)
+    check_blockwise(q, "f32", y1)
+    assert np.array_equal(host_out(y1).view(np.uint32), host_out(y2).view(np.uint32))
