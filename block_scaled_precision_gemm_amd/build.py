@@ -21,8 +21,12 @@ LIB = os.path.join(PKG, "libbsmm.so")
 OBJDIR = os.path.join(PKG, "_build")
 ARCH = "gfx950"
 
-HOST_SOURCES = ["bsmm_api.cpp", "bsmm_tuned.cpp"]
-HIP_SOURCES = ["bsmm_kernels.hip"]
+HOST_SOURCES = ["bsmm_api.cpp", "bsmm_tuned.cpp", "bsmm_variants.cpp"]
+HIP_SOURCE = "bsmm_kernels.hip"
+# The kernel source is compiled once per (operation, output type) pair, in
+# parallel; each object holds that pair's kernels for every configuration.
+#   ops: 0 int8 rowwise, 1 fp8 blockwise, 2 fp8 mx; outputs: 0 i32, 1 f32, 2 bf16
+KERNEL_UNITS = [(0, 0), (0, 1), (0, 2), (1, 1), (1, 2), (2, 1), (2, 2)]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-I" + INCLUDE, "-I" + CSRC, "-Wall",
           "-Wno-unused-function"]
@@ -53,10 +57,11 @@ def build(verbose: bool = False) -> str:
     for s in HOST_SOURCES:
         o = os.path.join(OBJDIR, s + ".o")
         jobs.append([hipcc, *COMMON, "-c", os.path.join(CSRC, s), "-o", o])
-    for s in HIP_SOURCES:
-        o = os.path.join(OBJDIR, s + ".o")
-        jobs.append([hipcc, *COMMON, *HIP_FLAGS, "-x", "hip", "-c",
-                     os.path.join(CSRC, s), "-o", o])
+    for op, out in KERNEL_UNITS:
+        o = os.path.join(OBJDIR, f"bsmm_kernels_{op}_{out}.o")
+        jobs.append([hipcc, *COMMON, *HIP_FLAGS, f"-DBSMM_TU_OP={op}",
+                     f"-DBSMM_TU_OUT={out}", "-x", "hip", "-c",
+                     os.path.join(CSRC, HIP_SOURCE), "-o", o])
     workers = min(len(jobs), max(1, min(8, os.cpu_count() or 1)))
     with ThreadPoolExecutor(workers) as ex:
         list(ex.map(_run, jobs))

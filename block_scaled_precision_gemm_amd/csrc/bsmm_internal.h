@@ -60,6 +60,13 @@ constexpr int kPlanCUs = 256;
 size_t persistent_workspace(const Variant* v, bsmm_op op);
 
 const Variant* variants(int* count);
+
+// One kernel configuration for one (operation, output type); defined in the
+// HIP translation units, one per (OP, OUT) pair, for every configuration in
+// bsmm_variants.inc.
+template <int OP, int OUT, int WM, int WN, int RING, bool SK>
+int launch_kernel(const Problem& p, int row_begin, int row_end, int split, void* ws,
+                  size_t ws_bytes, void* stream);
 const Variant* find_variant(const char* name);
 
 // Bytes of split-K workspace a variant needs for `split` slices.

@@ -173,23 +173,18 @@ struct Tile {
 
 // R rows x 128 bytes; one wave instruction moves 8 rows (64 x 16 bytes) to
 // LDS bytes [q*1024, q*1024+1024) of the slot, lane l -> slot byte 16 l.
+// Wave `wave` of NW issues instructions t = 0 .. R/8/NW - 1, q = t*NW + wave.
 // A dead half-stage (past the last K block) is issued with out-of-range
 // offsets: it keeps the per-wave load count uniform and touches no memory.
-template <int R, int NW>
-__device__ __forceinline__ void load_rows(__amdgpu_buffer_rsrc_t rs,
-                                          uint8_t* dst, uint32_t ld,
-                                          uint32_t kbyte, int wave, int lane,
-                                          bool live) {
-  constexpr int Q = R / 8;
-#pragma unroll
-  for (int t = 0; t < Q / NW; ++t) {
-    const int q = t * NW + wave;
-    const int r = q * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ swz(r);
-    const uint32_t vo = live ? (uint32_t)r * ld + kbyte + ((uint32_t)c << 4) : kOob;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + q * 1024), 16, vo,
-                                             0, 0, 0);
-  }
+template <int NW>
+__device__ __forceinline__ void load_row_group(__amdgpu_buffer_rsrc_t rs, uint8_t* dst,
+                                               uint32_t ld, uint32_t kbyte, int wave,
+                                               int lane, bool live, int t) {
+  const int q = t * NW + wave;
+  const int r = q * 8 + (lane >> 3);
+  const int c = (lane & 7) ^ swz(r);
+  const uint32_t vo = live ? (uint32_t)r * ld + kbyte + ((uint32_t)c << 4) : kOob;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + q * 1024), 16, vo, 0, 0, 0);
 }
 
 template <int N>
@@ -233,6 +228,7 @@ struct Mainloop {
   using T = Tile<OP, WM, WN, RING>;
   using acc_t = typename OpT<OP>::acc_t;
   static constexpr int TI = T::TI, TJ = T::TJ;
+  static constexpr int kLoadsPerBlock = T::LA + T::LB;   // per wave
 
   __device__ __forceinline__ static void run(const KArgs& k, uint8_t* smem, int g,
                                              int row0, int col0, int kb0, int nkb,
@@ -254,13 +250,18 @@ struct Mainloop {
         p.b + (int64_t)g * p.b_sg + (int64_t)col0 * p.ldb,
         (uint64_t)(p.N - col0) * p.ldb);
 
-    // half-stage h (relative to kb0): its K block's A (h even) or B tile
-    auto issue_half = [&](int h, int slot) {
+    // Load t of half-stage h (relative to kb0): its K block's A tile (h
+    // even, LA loads per wave) or B tile (h odd, LB loads), into `slot`.
+    auto issue_load = [&](int h, int slot, int t) {
       uint8_t* dst = smem + slot * SLOT;
       const bool live = h < 2 * nkb;
       const uint32_t kbyte = (uint32_t)(kb0 + (h >> 1)) * kBlockK;
-      if (h & 1) load_rows<BN, NW>(rb, dst, ldb, kbyte, wave, lane, live);
-      else load_rows<BM, NW>(ra, dst, lda, kbyte, wave, lane, live);
+      if (h & 1) load_row_group<NW>(rb, dst, ldb, kbyte, wave, lane, live, t);
+      else load_row_group<NW>(ra, dst, lda, kbyte, wave, lane, live, t);
+    };
+    auto issue_half = [&](int h, int slot) {
+      const int n = (h & 1) ? T::LB : T::LA;
+      for (int t = 0; t < n; ++t) issue_load(h, slot, t);
     };
 
     // Per-lane fragment addresses (bytes within a slot): row / column
@@ -297,14 +298,13 @@ struct Mainloop {
         sb_blk = (const float*)p.sb + (int64_t)nb * p.sb_n;
     }
 
-    // Scale registers of the current K block (cur) and the next one (nxt).
-    // Block c+1's are loaded during block c, before that block's refills; the
-    // copy at the end of block c therefore only waits for loads that were
-    // issued a whole block earlier.
+    // Scale registers of the current K block (cur) and the next one (nxt),
+    // loaded at least half a K block before they are used.
     int xs_cur[TI], xs_nxt[TI];
     int ws_cur = 127, ws_nxt = 127;
-    float sa_cur[TI], sa_nxt[TI];
-    float sb_cur = 1.f, sb_nxt = 1.f;
+    float sa_nxt[TI];
+    float sb_nxt = 1.f;
+    float sc[TI];     // blockwise: scale product of this lane's row in each 16-row tile
     auto load_scales = [&](int kb) {
       if constexpr (OP == BSMM_OP_FP8_MX_BMM) {
   #pragma unroll
@@ -316,65 +316,53 @@ struct Mainloop {
         sb_nxt = sb_blk[(int64_t)kb * p.sb_kb];
       }
     };
-
-    if (nkb > 0) {
-      load_scales(kb0);
+    auto use_scales = [&]() {
+      if constexpr (OP == BSMM_OP_FP8_MX_BMM) {
   #pragma unroll
-      for (int h = 0; h < NSLOT - 2; ++h) issue_half(h, h);
-    }
-    for (int c = 0; c < nkb; ++c) {
-      const int slot_a = (2 * c) % NSLOT;
-      const int slot_b = slot_a + 1 == NSLOT ? 0 : slot_a + 1;
-      const int refill_a = (2 * c + NSLOT - 2) % NSLOT;
-      const int refill_b = refill_a + 1 == NSLOT ? 0 : refill_a + 1;
-      wait_vmcnt<T::WAIT>();   // block c's two half-stages have landed
-      lds_barrier();           // ... for every wave; block c-1's slots are free
+        for (int i = 0; i < TI; ++i) xs_cur[i] = xs_nxt[i];
+        ws_cur = ws_nxt;
+      } else if constexpr (OP == BSMM_OP_FP8_BLOCKWISE) {
   #pragma unroll
-      for (int i = 0; i < TI; ++i) { xs_cur[i] = xs_nxt[i]; sa_cur[i] = sa_nxt[i]; }
-      ws_cur = ws_nxt;
-      sb_cur = sb_nxt;
-      const uint8_t* SA = smem + slot_a * SLOT;
-      const uint8_t* SB = smem + slot_b * SLOT;
+        for (int i = 0; i < TI; ++i) sc[i] = sa_nxt[i] * sb_nxt;
+      }
+    };
 
-      // Fragments: B tile 0 and the A tiles first (they gate the first MFMA);
-      // the B tile of column j+1 is read while column j computes.
-      auto read_b = [&](int j) {
-        const i32x4 lo = *(const i32x4*)(SB + b_off0 + j * 2048);
-        const i32x4 hi = *(const i32x4*)(SB + b_off1 + j * 2048);
-        return i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-      };
-      i32x8 bcur = read_b(0);
-      i32x8 af[TI];
+    // Fragments of the current K block: all A tiles, and the B tile of the
+    // column being computed (bcur); the B tile of column j+1 is read while
+    // column j computes.
+    const uint8_t* SA = smem;
+    const uint8_t* SB = smem;
+    i32x8 af[TI];
+    i32x8 bcur;
+    auto read_b = [&](int j) {
+      const i32x4 lo = *(const i32x4*)(SB + b_off0 + j * 2048);
+      const i32x4 hi = *(const i32x4*)(SB + b_off1 + j * 2048);
+      return i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    };
+    auto read_frags = [&](int slot_a, int slot_b) {
+      SA = smem + slot_a * SLOT;
+      SB = smem + slot_b * SLOT;
+      bcur = read_b(0);
   #pragma unroll
       for (int i = 0; i < TI; ++i) {
         const i32x4 lo = *(const i32x4*)(SA + a_off0 + i * 2048);
         const i32x4 hi = *(const i32x4*)(SA + a_off1 + i * 2048);
         af[i] = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
       }
-      // next block's scales (clamped to the last block), then the two slots
-      // block c-1 used are refilled with half-stages 2c+NSLOT-2, 2c+NSLOT-1
-      load_scales(kb0 + min(c + 1, nkb - 1));
-      __builtin_amdgcn_sched_barrier(0);   // scale loads stay ahead of the refills
-      issue_half(2 * c + NSLOT - 2, refill_a);
-      issue_half(2 * c + NSLOT - 1, refill_b);
-      __builtin_amdgcn_sched_barrier(0);
+    };
 
-      // blockwise: scale product for this lane's row in each 16-row tile
-      float sc[TI];
-      if constexpr (OP == BSMM_OP_FP8_BLOCKWISE) {
-  #pragma unroll
-        for (int i = 0; i < TI; ++i) sc[i] = sa_cur[i] * sb_cur;
-      }
-
-      // Blockwise: the fp32 partial of MFMA tile t is folded into its
-      // accumulator D steps later, so the multiply-adds never wait on the
-      // MFMA that was just issued.
-      constexpr int D = 4;
-      f32x4 ring[D];
+    // Columns [J0, J1) of the current K block.  Blockwise: the fp32 partial
+    // of MFMA tile t is folded into its accumulator D steps later, so the
+    // multiply-adds never wait on the MFMA that was just issued; the ring is
+    // drained at the end of the block.
+    constexpr int D = 4;
+    f32x4 ring[D];
+    auto columns = [&](auto refill) {
   #pragma unroll
       for (int j = 0; j < TJ; ++j) {
         i32x8 bnext = bcur;
         if (j + 1 < TJ) bnext = read_b(j + 1);
+        refill(j);
   #pragma unroll
         for (int i = 0; i < TI; ++i) {
           const int tt = j * TI + i;
@@ -413,19 +401,63 @@ struct Mainloop {
         }
       }
       // Scheduling: per column j, the MFMAs of j with the two reads of B tile
-      // j+1 right after the first one and, for blockwise, four multiply-adds
-      // after each MFMA.
-      constexpr int kMfma = 0x008, kValu = 0x002, kDsRead = 0x100;
+      // j+1 and the column's refill loads right after the first one and, for
+      // blockwise, four multiply-adds after each MFMA.
+      constexpr int kMfma = 0x008, kValu = 0x002, kVmemRead = 0x020, kDsRead = 0x100;
       constexpr int MF = OP == BSMM_OP_INT8_ROWWISE ? 2 : 1;   // MFMAs per tile
   #pragma unroll
       for (int j = 0; j < TJ; ++j) {
   #pragma unroll
         for (int i = 0; i < TI; ++i) {
           __builtin_amdgcn_sched_group_barrier(kMfma, MF, 0);
-          if (i == 0 && j + 1 < TJ) __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
+          if (i == 0) {
+            if (j + 1 < TJ) __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
+            const int nl = kLoadsPerBlock * (j + 1) / TJ - kLoadsPerBlock * j / TJ;
+            if (nl == 1) __builtin_amdgcn_sched_group_barrier(kVmemRead, 1, 0);
+            if (nl == 2) __builtin_amdgcn_sched_group_barrier(kVmemRead, 2, 0);
+            if (nl == 3) __builtin_amdgcn_sched_group_barrier(kVmemRead, 3, 0);
+            if (nl >= 4) __builtin_amdgcn_sched_group_barrier(kVmemRead, 4, 0);
+          }
           if constexpr (OP == BSMM_OP_FP8_BLOCKWISE) __builtin_amdgcn_sched_group_barrier(kValu, 4, 0);
         }
       }
+    };
+
+    if (nkb <= 0) return;
+    // Ring schedule.  K block c occupies half-stages 2c (A) and 2c+1 (B) in
+    // slots h % NSLOT.  At the top of block c (after the barrier that frees
+    // block c-1's two slots) those slots start to be refilled with the next
+    // two half-stages, h1 = 2c+NSLOT-2 and h2 = 2c+NSLOT-1, whose loads are
+    // spread over the block's columns (h1 first, it is needed first): issued
+    // in one burst they would queue in the texture unit and stall the
+    // issuing waves' MFMAs.  At the top of block c+1 only h2's loads may
+    // still be in flight.
+    load_scales(kb0);
+  #pragma unroll
+    for (int h = 0; h < NSLOT - 2; ++h) issue_half(h, h);
+    for (int c = 0; c < nkb; ++c) {
+      const int slot_a = (2 * c) % NSLOT;
+      const int slot_b = slot_a + 1 == NSLOT ? 0 : slot_a + 1;
+      const int h1 = 2 * c + NSLOT - 2, h2 = h1 + 1;
+      const int slot1 = h1 % NSLOT;
+      const int slot2 = slot1 + 1 == NSLOT ? 0 : slot1 + 1;
+      constexpr int L1 = (NSLOT % 2) ? T::LB : T::LA;    // h1 is odd iff NSLOT is odd
+      wait_vmcnt<T::WAIT>();   // block c's two half-stages have landed
+      lds_barrier();           // ... for every wave; block c-1's slots are free
+      use_scales();
+      read_frags(slot_a, slot_b);
+      // Next block's scales (clamped), issued before this block's refills: at
+      // the top of block c+1 they are then waited for together with h1 only,
+      // not with h2's loads issued after them.
+      load_scales(kb0 + min(c + 1, nkb - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      columns([&](int j) {
+  #pragma unroll
+        for (int u = kLoadsPerBlock * j / TJ; u < kLoadsPerBlock * (j + 1) / TJ; ++u) {
+          if (u < L1) issue_load(h1, slot1, u);
+          else issue_load(h2, slot2, u - L1);
+        }
+      });
     }
     // the last refills were out-of-range loads; let them drain
     wait_vmcnt<0>();
@@ -840,46 +872,26 @@ int launch_sk(const Problem& p, int row_begin, int row_end, int split, void* ws,
   return check_launch();
 }
 
-template <int WM, int WN, int RING, bool SK>
-int launch_variant(const Problem& p, int rb, int re, int sp, void* ws, size_t wsb, void* st) {
-#define BSMM_L(OPX, OUTX)                                                           \
-  return SK ? launch_sk<OPX, OUTX, WM, WN, RING>(p, rb, re, sp, ws, wsb, st)       \
-            : launch_tile<OPX, OUTX, WM, WN, RING>(p, rb, re, sp, ws, wsb, st)
-  switch (p.op) {
-    case BSMM_OP_INT8_ROWWISE:
-      if (p.out_dtype == BSMM_I32) BSMM_L(BSMM_OP_INT8_ROWWISE, BSMM_I32);
-      if (p.out_dtype == BSMM_F32) BSMM_L(BSMM_OP_INT8_ROWWISE, BSMM_F32);
-      BSMM_L(BSMM_OP_INT8_ROWWISE, BSMM_BF16);
-    case BSMM_OP_FP8_BLOCKWISE:
-      if (p.out_dtype == BSMM_F32) BSMM_L(BSMM_OP_FP8_BLOCKWISE, BSMM_F32);
-      BSMM_L(BSMM_OP_FP8_BLOCKWISE, BSMM_BF16);
-    default:
-      if (p.out_dtype == BSMM_F32) BSMM_L(BSMM_OP_FP8_MX_BMM, BSMM_F32);
-      BSMM_L(BSMM_OP_FP8_MX_BMM, BSMM_BF16);
-  }
-#undef BSMM_L
-}
-
-constexpr unsigned kAllOps = 7u;
-
-// name, tile_m, tile_n, ops, masked tail, persistent, workgroups per CU, launch
-const Variant kVariants[] = {
-    {"t256x256", 256, 256, kAllOps, true, false, 1, launch_variant<4, 2, 5, false>},
-    {"t256x128", 256, 128, kAllOps, true, false, 1, launch_variant<4, 1, 5, false>},
-    {"t128x256", 128, 256, kAllOps, true, false, 1, launch_variant<2, 2, 5, false>},
-    {"t128x128", 128, 128, kAllOps, true, false, 2, launch_variant<2, 1, 5, false>},
-    {"t64x256", 64, 256, kAllOps, true, false, 1, launch_variant<1, 2, 5, false>},
-    {"t64x128", 64, 128, kAllOps, true, false, 2, launch_variant<1, 1, 5, false>},
-    {"t256x256sk", 256, 256, kAllOps, true, true, 1, launch_variant<4, 2, 5, true>},
-    {"t256x128sk", 256, 128, kAllOps, true, true, 1, launch_variant<4, 1, 5, true>},
-    {"t128x128sk", 128, 128, kAllOps, true, true, 2, launch_variant<2, 1, 5, true>},
-};
-
 }  // namespace
 
-const Variant* variants(int* count) {
-  *count = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
-  return kVariants;
+// Entry used by the variant table: one kernel configuration for one
+// (operation, output type).  Instantiated below for the pair this
+// translation unit is compiled for.
+template <int OP, int OUT, int WM, int WN, int RING, bool SK>
+int launch_kernel(const Problem& p, int row_begin, int row_end, int split, void* ws,
+                  size_t ws_bytes, void* stream) {
+  if constexpr (SK)
+    return launch_sk<OP, OUT, WM, WN, RING>(p, row_begin, row_end, split, ws, ws_bytes, stream);
+  else
+    return launch_tile<OP, OUT, WM, WN, RING>(p, row_begin, row_end, split, ws, ws_bytes, stream);
 }
+
+#if defined(BSMM_TU_OP) && defined(BSMM_TU_OUT)
+#define BSMM_VARIANT(NAME, TM, TN, WM, WN, RING, SK, WPC)                                  \
+  template int launch_kernel<BSMM_TU_OP, BSMM_TU_OUT, WM, WN, RING, SK>(                  \
+      const Problem&, int, int, int, void*, size_t, void*);
+#include "bsmm_variants.inc"
+#undef BSMM_VARIANT
+#endif
 
 }  // namespace bsmm

@@ -1,0 +1,46 @@
+// The table of kernel configurations compiled into the library, and the
+// per-configuration dispatch on (operation, output type).  Host code; the
+// kernels themselves are instantiated in the HIP translation units.
+#include "bsmm_internal.h"
+
+namespace bsmm {
+namespace {
+
+template <int WM, int WN, int RING, bool SK>
+int launch_variant(const Problem& p, int rb, int re, int sp, void* ws, size_t wsb, void* st) {
+  switch (p.op) {
+    case BSMM_OP_INT8_ROWWISE:
+      if (p.out_dtype == BSMM_I32)
+        return launch_kernel<BSMM_OP_INT8_ROWWISE, BSMM_I32, WM, WN, RING, SK>(p, rb, re, sp, ws, wsb, st);
+      if (p.out_dtype == BSMM_F32)
+        return launch_kernel<BSMM_OP_INT8_ROWWISE, BSMM_F32, WM, WN, RING, SK>(p, rb, re, sp, ws, wsb, st);
+      return launch_kernel<BSMM_OP_INT8_ROWWISE, BSMM_BF16, WM, WN, RING, SK>(p, rb, re, sp, ws, wsb, st);
+    case BSMM_OP_FP8_BLOCKWISE:
+      if (p.out_dtype == BSMM_F32)
+        return launch_kernel<BSMM_OP_FP8_BLOCKWISE, BSMM_F32, WM, WN, RING, SK>(p, rb, re, sp, ws, wsb, st);
+      return launch_kernel<BSMM_OP_FP8_BLOCKWISE, BSMM_BF16, WM, WN, RING, SK>(p, rb, re, sp, ws, wsb, st);
+    default:
+      if (p.out_dtype == BSMM_F32)
+        return launch_kernel<BSMM_OP_FP8_MX_BMM, BSMM_F32, WM, WN, RING, SK>(p, rb, re, sp, ws, wsb, st);
+      return launch_kernel<BSMM_OP_FP8_MX_BMM, BSMM_BF16, WM, WN, RING, SK>(p, rb, re, sp, ws, wsb, st);
+  }
+}
+
+constexpr unsigned kAllOps = 7u;
+
+// name, tile_m, tile_n, ops, masked tail, persistent, workgroups per CU, launch
+const Variant kVariants[] = {
+#define BSMM_VARIANT(NAME, TM, TN, WM, WN, RING, SK, WPC) \
+  {NAME, TM, TN, kAllOps, true, SK, WPC, launch_variant<WM, WN, RING, SK>},
+#include "bsmm_variants.inc"
+#undef BSMM_VARIANT
+};
+
+}  // namespace
+
+const Variant* variants(int* count) {
+  *count = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
+  return kVariants;
+}
+
+}  // namespace bsmm
