@@ -87,10 +87,35 @@ size_t persistent_workspace(const Variant* v, bsmm_op op) {
   return (size_t)kPlanCUs * v->wg_per_cu * ((size_t)v->tile_m * v->tile_n * 4u + 8u);
 }
 
-// Workspace of a plan: split-K partials or stream-K slots.
-static size_t plan_ws(const Plan& pl, bsmm_op op, int G, int rows, int N) {
-  if (pl.v->persistent) return persistent_workspace(pl.v, op);
-  return ws_bytes(G, rows, N, pl.split);
+// Workspace of a plan: packed scale_a (packed-scale variants), then split-K
+// partials or stream-K slots.
+static size_t plan_ws(const Plan& pl, bsmm_op op, int G, int M, int rows, int N, int K) {
+  const size_t pack = pl.v->packed_scales ? packed_scale_bytes(op, G, M, K) : 0;
+  if (pl.v->persistent) return pack + persistent_workspace(pl.v, op);
+  return pack + ws_bytes(G, rows, N, pl.split);
+}
+
+// Shrink a plan until its workspace fits: drop split-K, then the stream-K
+// slots, then the packed scales.
+static void fit_workspace(Plan& pl, bsmm_op op, int G, int M, int N, int K, bsmm_dtype dt,
+                          size_t workspace_bytes) {
+  const int rows = pl.m_split ? pl.m_split : M;
+  pl.workspace = plan_ws(pl, op, G, M, rows, N, K);
+  if (pl.workspace <= workspace_bytes) return;
+  pl.split = 1;
+  pl.workspace = plan_ws(pl, op, G, M, rows, N, K);
+  if (pl.workspace <= workspace_bytes) return;
+  if (pl.v->persistent) {
+    Plan h = make_plan_heuristic(op, G, M, N, K, dt);
+    pl.v = h.v;
+    pl.tail = h.tail;
+    pl.m_split = h.m_split;
+    pl.split = 1;
+    pl.workspace = plan_ws(pl, op, G, M, pl.m_split ? pl.m_split : M, N, K);
+    if (pl.workspace <= workspace_bytes) return;
+  }
+  if (pl.v->packed_scales && pl.v->unpacked) pl.v = find_variant(pl.v->unpacked);
+  pl.workspace = plan_ws(pl, op, G, M, pl.m_split ? pl.m_split : M, N, K);
 }
 
 // Plan selection (bsmm_plan_info::source):
@@ -122,12 +147,7 @@ Plan make_plan(bsmm_op op, int G, int M, int N, int K, bsmm_dtype dt,
       if (o.variant.empty() && o.split <= 0) { pl.tail = h.tail; pl.m_split = h.m_split; }
       pl.source = 3;
       if (pl.v->persistent) pl.split = 1;
-      pl.workspace = plan_ws(pl, op, G, pl.m_split ? pl.m_split : M, N);
-      if (pl.workspace > workspace_bytes) {
-        pl.split = 1;
-        pl.workspace = 0;
-        if (pl.v->persistent) pl.v = h.v;   // no room for stream-K slots
-      }
+      fit_workspace(pl, op, G, M, N, K, dt, workspace_bytes);
       return pl;
     }
   }
@@ -155,23 +175,21 @@ Plan make_plan(bsmm_op op, int G, int M, int N, int K, bsmm_dtype dt,
   }
   if (pl.split > KB) pl.split = KB > 0 ? KB : 1;
   if (pl.v->persistent) pl.split = 1;
-  const int bulk_rows = pl.m_split ? pl.m_split : M;
-  pl.workspace = plan_ws(pl, op, G, bulk_rows, N);
-  if (pl.workspace > workspace_bytes) {
-    pl.split = 1;
-    pl.workspace = 0;
-    if (pl.v->persistent) pl = make_plan_heuristic(op, G, M, N, K, dt), pl.split = 1;
-  }
+  fit_workspace(pl, op, G, M, N, K, dt, workspace_bytes);
   return pl;
 }
 
 Plan make_plan_heuristic(bsmm_op op, int G, int M, int N, int K, bsmm_dtype dt) {
-  (void)op; (void)dt;
+  (void)dt;
   Plan pl;
+  // fp8 with enough rows: the K loop reads scale_a repacked once per call
+  // (one small load per wave and K block instead of one per row group)
+  const bool pack = op != BSMM_OP_INT8_ROWWISE && (int64_t)G * M >= 1024;
   const char* name;
   if (M <= 64) name = N % 256 == 0 ? "t64x256" : "t64x128";
-  else if (M <= 128) name = N % 256 == 0 ? "t128x256" : "t128x128";
-  else name = N % 256 == 0 ? "t256x256" : "t256x128";
+  else if (M <= 128) name = N % 256 == 0 ? (pack ? "t128x256p" : "t128x256") : "t128x128";
+  else if (N % 256 == 0) name = pack ? "t256x256p" : "t256x256";
+  else name = pack ? "t256x128p" : "t256x128";
   pl.v = find_variant(name);
   const int KB = K / kBlockK;
   const int64_t tiles = (int64_t)((M + pl.v->tile_m - 1) / pl.v->tile_m) *

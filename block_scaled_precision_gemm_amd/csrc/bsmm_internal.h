@@ -50,9 +50,25 @@ struct Variant {
   unsigned op_mask;     // bit i set: usable for bsmm_op i
   bool masked_tail;     // safe for rows past M (every variant is)
   bool persistent;      // stream-K: one workgroup per slot of the device
+  bool packed_scales;   // fp8: repacks scale_a into the workspace first
   int wg_per_cu;        // workgroups one CU holds (LDS / registers)
+  const char* unpacked; // the same kernel without packed scales (or null)
   LaunchFn launch;
 };
+
+// Packed scale_a for the fp8 kernels: K block major, rows padded to a
+// multiple of 256, and within every 64 rows the element of row
+// 64q + 16i + f stored at position 64q + 4f + i, so that one 16-byte
+// (fp32) or 4-byte (e8m0) load gives a lane the scales of its four rows
+// f, f+16, f+32, f+48.  Layout [G][KB][Mp] (G = 1 for blockwise).
+inline int packed_rows(int M) { return (M + 255) / 256 * 256; }
+inline size_t packed_scale_bytes(bsmm_op op, int G, int M, int K) {
+  if (op == BSMM_OP_INT8_ROWWISE) return 0;
+  const size_t elem = op == BSMM_OP_FP8_BLOCKWISE ? 4u : 1u;
+  const size_t n = (size_t)(op == BSMM_OP_FP8_MX_BMM ? G : 1) * (size_t)(K / kBlockK) *
+                   (size_t)packed_rows(M) * elem;
+  return (n + 255) / 256 * 256;
+}
 
 // Workspace a persistent (stream-K) variant wants: one partial tile plus a
 // 64-bit flag per workgroup, for a device of kPlanCUs compute units.
@@ -63,8 +79,9 @@ const Variant* variants(int* count);
 
 // One kernel configuration for one (operation, output type); defined in the
 // HIP translation units, one per (OP, OUT) pair, for every configuration in
-// bsmm_variants.inc.
-template <int OP, int OUT, int WM, int WN, int RING, bool SK>
+// bsmm_variants.inc.  PK: the fp8 main loop reads packed scale_a, which the
+// launch first writes to the start of the workspace.
+template <int OP, int OUT, int WM, int WN, int RING, bool SK, bool PK>
 int launch_kernel(const Problem& p, int row_begin, int row_end, int split, void* ws,
                   size_t ws_bytes, void* stream);
 const Variant* find_variant(const char* name);

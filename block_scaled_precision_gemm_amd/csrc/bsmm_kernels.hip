@@ -97,6 +97,8 @@ struct KArgs {
   int splits, kb_per_split;
   int vec_out;        // output (or workspace) rows allow 8/16-byte stores
   void* ws;           // split-K partials [splits][G][rows][N] (fp32 / int32)
+  const void* psa;    // packed scale_a [G][KB][psa_ld] (packed-scale kernels)
+  int64_t psa_ld;
 };
 
 template <int OP> struct OpT;
@@ -169,6 +171,7 @@ struct Tile {
   static_assert(NSLOT >= 4, "the ring needs at least four slots");
   static_assert((BM / 8) % NW == 0 && (BN / 8) % NW == 0, "loader split");
   static_assert(WAIT < 64, "vmcnt range");
+  static_assert(TI == 4, "packed scales hold four rows per lane");
 };
 
 // R rows x 128 bytes; one wave instruction moves 8 rows (64 x 16 bytes) to
@@ -223,7 +226,7 @@ __device__ __forceinline__ void store4(uint8_t* base, int64_t e, const float* y,
 // the same arguments; it starts with a barrier (a previous call's LDS reads
 // must be finished before its loads overwrite the ring) and leaves no loads
 // in flight.
-template <int OP, int WM, int WN, int RING>
+template <int OP, int WM, int WN, int RING, bool PK>
 struct Mainloop {
   using T = Tile<OP, WM, WN, RING>;
   using acc_t = typename OpT<OP>::acc_t;
@@ -282,15 +285,21 @@ struct Mainloop {
     const uint8_t* ws_blk = nullptr;
     const float* sa_row[TI];
     const float* sb_blk = nullptr;
+    // packed scale_a: this lane's four rows are at one 4-byte (mx) or 16-byte
+    // (blockwise) position of each K block's row
+    const int64_t pk_lane = (int64_t)(row0 + wm * T::WTM) + 4 * fr;
+    const int64_t pk_g = PK && OP == BSMM_OP_FP8_MX_BMM ? (int64_t)g * (p.K / kBlockK) : 0;
     if constexpr (OP != BSMM_OP_INT8_ROWWISE) {
       const int nb = min((col0 + wn * T::WTN) / kBlockK, p.N / kBlockK - 1);
+      if constexpr (!PK) {
   #pragma unroll
-      for (int i = 0; i < TI; ++i) {
-        const int m = min(row0 + wm * T::WTM + i * 16 + fr, k.row_end - 1);
-        if constexpr (OP == BSMM_OP_FP8_MX_BMM)
-          xs_row[i] = (const uint8_t*)p.sa + (int64_t)g * p.sa_sg + (int64_t)m * p.sa_m;
-        else
-          sa_row[i] = (const float*)p.sa + (int64_t)m * p.sa_m;
+        for (int i = 0; i < TI; ++i) {
+          const int m = min(row0 + wm * T::WTM + i * 16 + fr, k.row_end - 1);
+          if constexpr (OP == BSMM_OP_FP8_MX_BMM)
+            xs_row[i] = (const uint8_t*)p.sa + (int64_t)g * p.sa_sg + (int64_t)m * p.sa_m;
+          else
+            sa_row[i] = (const float*)p.sa + (int64_t)m * p.sa_m;
+        }
       }
       if constexpr (OP == BSMM_OP_FP8_MX_BMM)
         ws_blk = (const uint8_t*)p.sb + (int64_t)g * p.sb_sg + (int64_t)nb * p.sb_n;
@@ -307,12 +316,25 @@ struct Mainloop {
     float sc[TI];     // blockwise: scale product of this lane's row in each 16-row tile
     auto load_scales = [&](int kb) {
       if constexpr (OP == BSMM_OP_FP8_MX_BMM) {
+        if constexpr (PK) {
+          const uint32_t v = *(const uint32_t*)((const uint8_t*)k.psa +
+                                                (pk_g + kb) * k.psa_ld + pk_lane);
   #pragma unroll
-        for (int i = 0; i < TI; ++i) xs_nxt[i] = xs_row[i][kb];
+          for (int i = 0; i < TI; ++i) xs_nxt[i] = (int)((v >> (8 * i)) & 0xFFu);
+        } else {
+  #pragma unroll
+          for (int i = 0; i < TI; ++i) xs_nxt[i] = xs_row[i][kb];
+        }
         ws_nxt = ws_blk[kb];
       } else if constexpr (OP == BSMM_OP_FP8_BLOCKWISE) {
+        if constexpr (PK) {
+          const f32x4 v = *(const f32x4*)((const float*)k.psa + (int64_t)kb * k.psa_ld + pk_lane);
   #pragma unroll
-        for (int i = 0; i < TI; ++i) sa_nxt[i] = sa_row[i][(int64_t)kb * p.sa_kb];
+          for (int i = 0; i < TI; ++i) sa_nxt[i] = v[i];
+        } else {
+  #pragma unroll
+          for (int i = 0; i < TI; ++i) sa_nxt[i] = sa_row[i][(int64_t)kb * p.sa_kb];
+        }
         sb_nxt = sb_blk[(int64_t)kb * p.sb_kb];
       }
     };
@@ -549,10 +571,10 @@ __device__ __forceinline__ void store_splitk(const KArgs& k, int s, int g, int r
 }
 
 // One output tile (or one K slice of it, with split-K) per workgroup.
-template <int OP, int OUT, int WM, int WN, int RING>
+template <int OP, int OUT, int WM, int WN, int RING, bool PK>
 __global__ void __launch_bounds__(64 * WM * WN)
 tile_kernel(const KArgs k) {
-  using M = Mainloop<OP, WM, WN, RING>;
+  using M = Mainloop<OP, WM, WN, RING, PK>;
   using T = typename M::T;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS];
   const TileId t = decode_tile(k);
@@ -597,10 +619,10 @@ struct SkArgs {
 constexpr int kSpinLimit = 1 << 22;   // ~ seconds of polling; never reached
                                       // when the grid is co-resident
 
-template <int OP, int OUT, int WM, int WN, int RING>
+template <int OP, int OUT, int WM, int WN, int RING, bool PK>
 __global__ void __launch_bounds__(64 * WM * WN)
 sk_kernel(const KArgs k, const SkArgs sk) {
-  using M = Mainloop<OP, WM, WN, RING>;
+  using M = Mainloop<OP, WM, WN, RING, PK>;
   using T = typename M::T;
   using acc_t = typename M::acc_t;
   typedef typename OpT<OP>::elem_t E;
@@ -733,6 +755,42 @@ splitk_reduce(const KArgs k) {
   }
 }
 
+// Packed scale_a (layout in bsmm_internal.h): one workgroup per 64 rows x 32
+// K blocks (x G), transposed through LDS so that both the reads (along K
+// blocks) and the writes (along rows) are contiguous.  Rows past M repeat
+// row M-1; the kernels never store their results.
+template <int OP>
+__global__ void __launch_bounds__(256) pack_scales(const KArgs k) {
+  __shared__ uint32_t t[32][65];
+  const Problem& p = k.p;
+  const int KB = p.K / kBlockK;
+  const int q = blockIdx.x, kb0 = blockIdx.y * 32, g = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int kl = tid & 31;
+  for (int rl = tid >> 5; rl < 64; rl += 8) {
+    const int m = min(q * 64 + rl, p.M - 1);
+    const int kb = kb0 + kl;
+    uint32_t v = 0;
+    if (kb < KB) {
+      if constexpr (OP == BSMM_OP_FP8_MX_BMM)
+        v = ((const uint8_t*)p.sa)[(int64_t)g * p.sa_sg + (int64_t)m * p.sa_m + kb];
+      else
+        v = __float_as_uint(((const float*)p.sa)[(int64_t)m * p.sa_m + (int64_t)kb * p.sa_kb]);
+    }
+    t[kl][rl] = v;
+  }
+  __syncthreads();
+  const int pl = tid & 63;
+  const int rl = 16 * (pl & 3) + (pl >> 2);     // position 4f + i <- row 16i + f
+  for (int kl2 = tid >> 6; kl2 < 32; kl2 += 4) {
+    const int kb = kb0 + kl2;
+    if (kb >= KB) break;
+    const int64_t o = ((int64_t)g * KB + kb) * k.psa_ld + (int64_t)q * 64 + pl;
+    if constexpr (OP == BSMM_OP_FP8_MX_BMM) ((uint8_t*)k.psa)[o] = (uint8_t)t[kl2][rl];
+    else ((uint32_t*)k.psa)[o] = t[kl2][rl];
+  }
+}
+
 // Output for K == 0: zeros.
 __global__ void zero_out(const KArgs k) {
   const Problem& p = k.p;
@@ -769,28 +827,51 @@ bool out_vec_ok(const Problem& p) {
          (p.o_sg * osz) % vbytes == 0;
 }
 
-template <int OP, int OUT, int WM, int WN, int RING>
+// Packed-scale launches: repack scale_a into the start of the workspace and
+// return the workspace left after it (nullptr, 0 if it does not fit).
+template <int OP>
+int prepare_packed(KArgs& k, void*& ws, size_t& ws_bytes, hipStream_t s) {
+  const Problem& p = k.p;
+  const size_t need = packed_scale_bytes(p.op, p.G, p.M, p.K);
+  if (ws == nullptr || ws_bytes < need || !aligned16(ws) || k.row_begin % 64 != 0) return 1;
+  k.psa = ws;
+  k.psa_ld = packed_rows(p.M);
+  const int KB = p.K / kBlockK;
+  const int G = OP == BSMM_OP_FP8_MX_BMM ? p.G : 1;
+  hipLaunchKernelGGL(pack_scales<OP>, dim3((unsigned)(k.psa_ld / 64), (unsigned)((KB + 31) / 32), (unsigned)G),
+                     dim3(256), 0, s, k);
+  if (check_launch()) return 1;
+  ws = ws_bytes > need ? (void*)((uint8_t*)ws + need) : nullptr;
+  ws_bytes -= need;
+  return 0;
+}
+
+template <int OP, int OUT, int WM, int WN, int RING, bool PK>
 int launch_tile(const Problem& p, int row_begin, int row_end, int split,
                 void* ws, size_t ws_bytes, void* stream) {
-  (void)ws_bytes;
   using T = Tile<OP, WM, WN, RING>;
   KArgs k;
   k.p = p;
+  k.psa = nullptr;
+  k.psa_ld = 0;
   k.row_begin = row_begin;
   k.row_end = row_end;
   const int rows = row_end - row_begin;
   k.tiles_m = (rows + T::BM - 1) / T::BM;
   k.tiles_n = (p.N + T::BN - 1) / T::BN;
   const int KB = p.K / kBlockK;
-  k.ws = ws;
   hipStream_t s = (hipStream_t)stream;
   if (KB == 0) {              // empty sum: the output is zero
+    k.ws = ws;
     k.splits = 1;
     k.kb_per_split = 0;
     k.vec_out = 0;
     hipLaunchKernelGGL(zero_out, dim3(1024), dim3(256), 0, s, k);
     return check_launch();
   }
+  if constexpr (PK)
+    if (prepare_packed<OP>(k, ws, ws_bytes, s)) return 1;
+  k.ws = ws;
   if (split < 1) split = 1;
   if (split > KB) split = KB;
   k.kb_per_split = (KB + split - 1) / split;
@@ -802,7 +883,7 @@ int launch_tile(const Problem& p, int row_begin, int row_end, int split,
     k.vec_out = out_vec_ok<OUT>(p);
   }
   const int64_t grid = (int64_t)k.tiles_m * k.tiles_n * p.G * k.splits;
-  hipLaunchKernelGGL((tile_kernel<OP, OUT, WM, WN, RING>), dim3((unsigned)grid), dim3(T::NT), 0, s, k);
+  hipLaunchKernelGGL((tile_kernel<OP, OUT, WM, WN, RING, PK>), dim3((unsigned)grid), dim3(T::NT), 0, s, k);
   if (check_launch()) return 1;
   if (k.splits > 1) {
     const int64_t total = (int64_t)rows * p.N * p.G;
@@ -822,15 +903,16 @@ uint64_t next_epoch() {
   return ctr.fetch_add(1, std::memory_order_relaxed);
 }
 
-template <int OP, int OUT, int WM, int WN, int RING>
+template <int OP, int OUT, int WM, int WN, int RING, bool PK>
 int launch_sk(const Problem& p, int row_begin, int row_end, int split, void* ws,
               size_t ws_bytes, void* stream) {
   using T = Tile<OP, WM, WN, RING>;
   const int KB = p.K / kBlockK;
   typedef typename OpT<OP>::elem_t E;
   const size_t per_wg = (size_t)T::BM * T::BN * sizeof(E) + sizeof(uint64_t);
-  if (KB == 0 || !aligned16(ws))
-    return launch_tile<OP, OUT, WM, WN, RING>(p, row_begin, row_end, split, ws, ws_bytes, stream);
+  const size_t pack = PK ? packed_scale_bytes(p.op, p.G, p.M, p.K) : 0;
+  if (KB == 0 || !aligned16(ws) || ws_bytes < pack + per_wg)
+    return launch_tile<OP, OUT, WM, WN, RING, PK>(p, row_begin, row_end, split, ws, ws_bytes, stream);
   // co-resident capacity of this kernel on the current device (cached)
   static std::atomic<int> cap_cache[64];
   int dev = 0;
@@ -841,14 +923,16 @@ int launch_sk(const Problem& p, int row_begin, int row_end, int split, void* ws,
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return 1;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &occ, reinterpret_cast<const void*>(&sk_kernel<OP, OUT, WM, WN, RING>), T::NT, 0) !=
-        hipSuccess)
+            &occ, reinterpret_cast<const void*>(&sk_kernel<OP, OUT, WM, WN, RING, PK>), T::NT,
+            0) != hipSuccess)
       return 1;
     cap = cus * (occ > 0 ? occ : 1);
     cap_cache[dev].store(cap, std::memory_order_relaxed);
   }
   KArgs k;
   k.p = p;
+  k.psa = nullptr;
+  k.psa_ld = 0;
   k.row_begin = row_begin;
   k.row_end = row_end;
   const int rows = row_end - row_begin;
@@ -857,6 +941,9 @@ int launch_sk(const Problem& p, int row_begin, int row_end, int split, void* ws,
   k.splits = 1;
   k.kb_per_split = KB;
   k.vec_out = out_vec_ok<OUT>(p);
+  hipStream_t s = (hipStream_t)stream;
+  if constexpr (PK)
+    if (prepare_packed<OP>(k, ws, ws_bytes, s)) return 1;
   k.ws = ws;
   SkArgs sk;
   sk.tiles_total = k.tiles_m * k.tiles_n * p.G;
@@ -864,11 +951,9 @@ int launch_sk(const Problem& p, int row_begin, int row_end, int split, void* ws,
   int P = cap;
   if ((int64_t)P > sk.units) P = (int)sk.units;
   if ((size_t)P * per_wg > ws_bytes) P = (int)(ws_bytes / per_wg);
-  if (P < 1)
-    return launch_tile<OP, OUT, WM, WN, RING>(p, row_begin, row_end, split, ws, ws_bytes, stream);
   sk.epoch = next_epoch();
-  hipLaunchKernelGGL((sk_kernel<OP, OUT, WM, WN, RING>), dim3((unsigned)P), dim3(T::NT), 0,
-                     (hipStream_t)stream, k, sk);
+  hipLaunchKernelGGL((sk_kernel<OP, OUT, WM, WN, RING, PK>), dim3((unsigned)P), dim3(T::NT), 0, s,
+                     k, sk);
   return check_launch();
 }
 
@@ -877,18 +962,20 @@ int launch_sk(const Problem& p, int row_begin, int row_end, int split, void* ws,
 // Entry used by the variant table: one kernel configuration for one
 // (operation, output type).  Instantiated below for the pair this
 // translation unit is compiled for.
-template <int OP, int OUT, int WM, int WN, int RING, bool SK>
+template <int OP, int OUT, int WM, int WN, int RING, bool SK, bool PK>
 int launch_kernel(const Problem& p, int row_begin, int row_end, int split, void* ws,
                   size_t ws_bytes, void* stream) {
+  // the int8 K loop reads no scales: packed variants run the plain kernel
+  constexpr bool PKX = PK && OP != BSMM_OP_INT8_ROWWISE;
   if constexpr (SK)
-    return launch_sk<OP, OUT, WM, WN, RING>(p, row_begin, row_end, split, ws, ws_bytes, stream);
+    return launch_sk<OP, OUT, WM, WN, RING, PKX>(p, row_begin, row_end, split, ws, ws_bytes, stream);
   else
-    return launch_tile<OP, OUT, WM, WN, RING>(p, row_begin, row_end, split, ws, ws_bytes, stream);
+    return launch_tile<OP, OUT, WM, WN, RING, PKX>(p, row_begin, row_end, split, ws, ws_bytes, stream);
 }
 
 #if defined(BSMM_TU_OP) && defined(BSMM_TU_OUT)
-#define BSMM_VARIANT(NAME, TM, TN, WM, WN, RING, SK, WPC)                                  \
-  template int launch_kernel<BSMM_TU_OP, BSMM_TU_OUT, WM, WN, RING, SK>(                  \
+#define BSMM_VARIANT(NAME, TM, TN, WM, WN, RING, SK, PK, WPC, UNPACKED)                     \
+  template int launch_kernel<BSMM_TU_OP, BSMM_TU_OUT, WM, WN, RING, SK, PK>(              \
       const Problem&, int, int, int, void*, size_t, void*);
 #include "bsmm_variants.inc"
 #undef BSMM_VARIANT

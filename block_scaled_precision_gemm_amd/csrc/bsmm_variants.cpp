@@ -6,32 +6,33 @@
 namespace bsmm {
 namespace {
 
-template <int WM, int WN, int RING, bool SK>
+template <int WM, int WN, int RING, bool SK, bool PK>
 int launch_variant(const Problem& p, int rb, int re, int sp, void* ws, size_t wsb, void* st) {
   switch (p.op) {
     case BSMM_OP_INT8_ROWWISE:
       if (p.out_dtype == BSMM_I32)
-        return launch_kernel<BSMM_OP_INT8_ROWWISE, BSMM_I32, WM, WN, RING, SK>(p, rb, re, sp, ws, wsb, st);
+        return launch_kernel<BSMM_OP_INT8_ROWWISE, BSMM_I32, WM, WN, RING, SK, PK>(p, rb, re, sp, ws, wsb, st);
       if (p.out_dtype == BSMM_F32)
-        return launch_kernel<BSMM_OP_INT8_ROWWISE, BSMM_F32, WM, WN, RING, SK>(p, rb, re, sp, ws, wsb, st);
-      return launch_kernel<BSMM_OP_INT8_ROWWISE, BSMM_BF16, WM, WN, RING, SK>(p, rb, re, sp, ws, wsb, st);
+        return launch_kernel<BSMM_OP_INT8_ROWWISE, BSMM_F32, WM, WN, RING, SK, PK>(p, rb, re, sp, ws, wsb, st);
+      return launch_kernel<BSMM_OP_INT8_ROWWISE, BSMM_BF16, WM, WN, RING, SK, PK>(p, rb, re, sp, ws, wsb, st);
     case BSMM_OP_FP8_BLOCKWISE:
       if (p.out_dtype == BSMM_F32)
-        return launch_kernel<BSMM_OP_FP8_BLOCKWISE, BSMM_F32, WM, WN, RING, SK>(p, rb, re, sp, ws, wsb, st);
-      return launch_kernel<BSMM_OP_FP8_BLOCKWISE, BSMM_BF16, WM, WN, RING, SK>(p, rb, re, sp, ws, wsb, st);
+        return launch_kernel<BSMM_OP_FP8_BLOCKWISE, BSMM_F32, WM, WN, RING, SK, PK>(p, rb, re, sp, ws, wsb, st);
+      return launch_kernel<BSMM_OP_FP8_BLOCKWISE, BSMM_BF16, WM, WN, RING, SK, PK>(p, rb, re, sp, ws, wsb, st);
     default:
       if (p.out_dtype == BSMM_F32)
-        return launch_kernel<BSMM_OP_FP8_MX_BMM, BSMM_F32, WM, WN, RING, SK>(p, rb, re, sp, ws, wsb, st);
-      return launch_kernel<BSMM_OP_FP8_MX_BMM, BSMM_BF16, WM, WN, RING, SK>(p, rb, re, sp, ws, wsb, st);
+        return launch_kernel<BSMM_OP_FP8_MX_BMM, BSMM_F32, WM, WN, RING, SK, PK>(p, rb, re, sp, ws, wsb, st);
+      return launch_kernel<BSMM_OP_FP8_MX_BMM, BSMM_BF16, WM, WN, RING, SK, PK>(p, rb, re, sp, ws, wsb, st);
   }
 }
 
 constexpr unsigned kAllOps = 7u;
 
-// name, tile_m, tile_n, ops, masked tail, persistent, workgroups per CU, launch
+// name, tile_m, tile_n, ops, masked tail, persistent, packed scales,
+// workgroups per CU, unpacked sibling, launch
 const Variant kVariants[] = {
-#define BSMM_VARIANT(NAME, TM, TN, WM, WN, RING, SK, WPC) \
-  {NAME, TM, TN, kAllOps, true, SK, WPC, launch_variant<WM, WN, RING, SK>},
+#define BSMM_VARIANT(NAME, TM, TN, WM, WN, RING, SK, PK, WPC, UNPACKED) \
+  {NAME, TM, TN, kAllOps, true, SK, PK, WPC, UNPACKED, launch_variant<WM, WN, RING, SK, PK>},
 #include "bsmm_variants.inc"
 #undef BSMM_VARIANT
 };

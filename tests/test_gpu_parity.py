@@ -22,8 +22,10 @@ from tests.gpu_util import (DEV, Forced, as_f64, check_blockwise, check_int8, ch
 pytestmark = pytest.mark.gpu
 
 VARIANTS = ["t256x256", "t256x128", "t128x256", "t128x128", "t64x256", "t64x128",
-            "t256x256sk", "t256x128sk", "t128x128sk"]
-SK_VARIANTS = ["t256x256sk", "t256x128sk", "t128x128sk"]
+            "t256x256p", "t256x128p", "t128x256p",
+            "t256x256sk", "t256x128sk", "t128x128sk", "t256x256skp"]
+SK_VARIANTS = ["t256x256sk", "t256x128sk", "t128x128sk", "t256x256skp"]
+PACKED_VARIANTS = ["t256x256p", "t256x128p", "t128x256p", "t256x256skp"]
 
 
 @pytest.fixture(autouse=True)
@@ -243,3 +245,43 @@ def test_streamk_small_workspace_two_way_splits():
         y2 = bsmm.bsmm_fp8_blockwise(a, b, sa, sb, out_dtype="f32", workspace=ws)
     check_blockwise(q, "f32", y1)
     assert np.array_equal(host_out(y1).view(np.uint32), host_out(y2).view(np.uint32))
+
+
+# ------------------------------------------------------- packed scales ----
+
+@pytest.mark.parametrize("variant", PACKED_VARIANTS)
+def test_packed_scales_strided_and_ragged(variant):
+    """Packed-scale kernels: scale_a repacked from a column-major (stride 1
+    along M) tensor and from a broadcast one, M not a multiple of 64, mx
+    with several batches in both layouts."""
+    q = fp8_blockwise_inputs(300, 384, 640, 601)
+    a, b = dev(q["a"]), dev(q["b_nk"]).t()
+    sa_cm = dev(np.ascontiguousarray(q["scale_a"].T)).t()            # [M, KB], stride (1, M)
+    sa_bc = torch.full((1, 1), 0.0625, device=DEV).expand(300, 5)     # stride (0, 0)
+    say(f"packed {variant} blockwise strided / broadcast scale_a")
+    with Forced(variant, 0):
+        y1 = bsmm.bsmm_fp8_blockwise(a, b, sa_cm, dev(q["scale_b"]), out_dtype="f32")
+        y2 = bsmm.bsmm_fp8_blockwise(a, b, sa_bc, dev(q["scale_b"]), out_dtype="bf16")
+    check_blockwise(q, "f32", y1)
+    q2 = dict(q)
+    q2["scale_a"] = np.full((300, 5), 0.0625, np.float32)
+    check_blockwise(q2, "bf16", y2)
+    for layout in ("m_major", "batch_first"):
+        r = fp8_mx_bmm_inputs(3, 300, 256, 640, 602, layout=layout)
+        say(f"packed {variant} mx {layout} G=3 M=300")
+        with Forced(variant, 0):
+            ym = run_mx(r, "f32")
+        check_mx(r, "f32", ym)
+
+
+def test_packed_bulk_with_unpacked_tail():
+    """The default plan for a large fp8 call: a packed 256-row bulk launch
+    followed by a 64-row tail launch that reads scale_a directly."""
+    M, N, K = 8232, 256, 512
+    plan = bsmm.bsmm_query_plan(bsmm.OP_FP8_BLOCKWISE, 1, M, N, K, "f32")
+    assert plan["variant"].endswith("p") and plan["m_split"] == 8192, plan
+    q = fp8_blockwise_inputs(M, N, K, 603)
+    say("packed bulk + unpacked tail")
+    y = run_blockwise(q, "f32")
+    rows = np.r_[0:300, 8100:M]
+    check_blockwise(q, "f32", y, rows=rows)
