@@ -5,7 +5,8 @@
 
 A step is one call of the scaled matmul (validation, dispatch and every
 kernel of the plan) on one batch of synthetic input that is already resident
-in HBM.  W untimed steps, then exactly K timed steps bracketed by device
+in HBM.  About half a second of untimed calls lets the GPU clock settle, then
+W untimed warm-up steps, then exactly K timed steps bracketed by device
 synchronisation; HIP events on the stream the kernels are launched on time
 every step.  Rank 0 prints one JSON line.
 
@@ -145,6 +146,8 @@ def main():
     ap.add_argument("--config", default="c3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--settle", type=float, default=0.5,
+                    help="seconds of untimed calls before the warm-up steps")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the scaled matmul "
@@ -170,6 +173,14 @@ def main():
     flops = 2.0 * G * M * N * K
     kind = "int8" if c["op"] == "int8" else "fp8"
 
+    # Settle: the GPU raises its clock over the first few hundred ms under
+    # load, so the call runs for about half a second before the W warm-up
+    # steps (untimed, like them) and the timed steps see the steady state.
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle:
+        for _ in range(8):
+            call()
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()

@@ -45,7 +45,8 @@ class PlanInfo(ctypes.Structure):
     _fields_ = [("variant", ctypes.c_char * 48), ("tile_m", ctypes.c_int32),
                 ("tile_n", ctypes.c_int32), ("split_k", ctypes.c_int32),
                 ("m_split", ctypes.c_int32), ("workspace", ctypes.c_int64),
-                ("source", ctypes.c_int32)]
+                ("source", ctypes.c_int32), ("tail_variant", ctypes.c_char * 48),
+                ("tail_split_k", ctypes.c_int32)]
 
 
 def load():
@@ -314,7 +315,8 @@ def bsmm_query_plan(op, G, M, N, K, out_dtype, workspace_bytes=2**62):
                                   workspace_bytes, ctypes.byref(info)))
     return {"variant": info.variant.decode(), "tile_m": info.tile_m,
             "tile_n": info.tile_n, "split_k": info.split_k, "m_split": info.m_split,
-            "workspace": info.workspace, "source": info.source}
+            "workspace": info.workspace, "source": info.source,
+            "tail_variant": info.tail_variant.decode(), "tail_split_k": info.tail_split_k}
 
 
 def bsmm_set_override(variant=None, split_k=0):

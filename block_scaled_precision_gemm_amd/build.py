@@ -62,6 +62,9 @@ def build(verbose: bool = False) -> str:
         jobs.append([hipcc, *COMMON, *HIP_FLAGS, f"-DBSMM_TU_OP={op}",
                      f"-DBSMM_TU_OUT={out}", "-x", "hip", "-c",
                      os.path.join(CSRC, HIP_SOURCE), "-o", o])
+    o = os.path.join(OBJDIR, "bsmm_pack.o")
+    jobs.append([hipcc, *COMMON, *HIP_FLAGS, "-x", "hip", "-c",
+                 os.path.join(CSRC, "bsmm_pack.hip"), "-o", o])
     workers = min(len(jobs), max(1, min(8, os.cpu_count() or 1)))
     with ThreadPoolExecutor(workers) as ex:
         list(ex.map(_run, jobs))

@@ -87,23 +87,35 @@ size_t persistent_workspace(const Variant* v, bsmm_op op) {
   return (size_t)kPlanCUs * v->wg_per_cu * ((size_t)v->tile_m * v->tile_n * 4u + 8u);
 }
 
-// Workspace of a plan: packed scale_a (packed-scale variants), then split-K
-// partials or stream-K slots.
-static size_t plan_ws(const Plan& pl, bsmm_op op, int G, int M, int rows, int N, int K) {
-  const size_t pack = pl.v->packed_scales ? packed_scale_bytes(op, G, M, K) : 0;
-  if (pl.v->persistent) return pack + persistent_workspace(pl.v, op);
-  return pack + ws_bytes(G, rows, N, pl.split);
+static bool plan_packed(const Plan& pl, bsmm_op op) {
+  return op != BSMM_OP_INT8_ROWWISE &&
+         (pl.v->packed_scales || (pl.tail && pl.tail->packed_scales));
+}
+
+// Workspace of a plan: packed scale_a (packed-scale variants), then the
+// split-K partials or stream-K slots of the bulk launch or of the tail
+// launch (they run one after the other on the stream and share the space).
+static size_t plan_ws(const Plan& pl, bsmm_op op, int G, int M, int N, int K) {
+  const size_t pack = plan_packed(pl, op) ? packed_scale_bytes(op, G, M, K) : 0;
+  const int rows = pl.m_split ? pl.m_split : M;
+  size_t main = pl.v->persistent ? persistent_workspace(pl.v, op) : ws_bytes(G, rows, N, pl.split);
+  if (pl.tail && pl.m_split) {
+    const size_t t = pl.tail->persistent ? persistent_workspace(pl.tail, op)
+                                         : ws_bytes(G, M - pl.m_split, N, pl.tail_split);
+    if (t > main) main = t;
+  }
+  return pack + main;
 }
 
 // Shrink a plan until its workspace fits: drop split-K, then the stream-K
 // slots, then the packed scales.
 static void fit_workspace(Plan& pl, bsmm_op op, int G, int M, int N, int K, bsmm_dtype dt,
                           size_t workspace_bytes) {
-  const int rows = pl.m_split ? pl.m_split : M;
-  pl.workspace = plan_ws(pl, op, G, M, rows, N, K);
+  pl.workspace = plan_ws(pl, op, G, M, N, K);
   if (pl.workspace <= workspace_bytes) return;
   pl.split = 1;
-  pl.workspace = plan_ws(pl, op, G, M, rows, N, K);
+  pl.tail_split = 1;
+  pl.workspace = plan_ws(pl, op, G, M, N, K);
   if (pl.workspace <= workspace_bytes) return;
   if (pl.v->persistent) {
     Plan h = make_plan_heuristic(op, G, M, N, K, dt);
@@ -111,11 +123,13 @@ static void fit_workspace(Plan& pl, bsmm_op op, int G, int M, int N, int K, bsmm
     pl.tail = h.tail;
     pl.m_split = h.m_split;
     pl.split = 1;
-    pl.workspace = plan_ws(pl, op, G, M, pl.m_split ? pl.m_split : M, N, K);
+    pl.tail_split = 1;
+    pl.workspace = plan_ws(pl, op, G, M, N, K);
     if (pl.workspace <= workspace_bytes) return;
   }
   if (pl.v->packed_scales && pl.v->unpacked) pl.v = find_variant(pl.v->unpacked);
-  pl.workspace = plan_ws(pl, op, G, M, pl.m_split ? pl.m_split : M, N, K);
+  if (pl.tail && pl.tail->packed_scales && pl.tail->unpacked) pl.tail = find_variant(pl.tail->unpacked);
+  pl.workspace = plan_ws(pl, op, G, M, N, K);
 }
 
 // Plan selection (bsmm_plan_info::source):
@@ -167,6 +181,7 @@ Plan make_plan(bsmm_op op, int G, int M, int N, int K, bsmm_dtype dt,
     if (pl.source == 0 && best->tail_variant[0] && best->m_split > 0 && best->m_split < M) {
       pl.tail = find_variant(best->tail_variant);
       pl.m_split = best->m_split;
+      pl.tail_split = best->tail_split > 0 ? best->tail_split : 1;
     }
   }
   if (!pl.v) {
@@ -203,8 +218,28 @@ Plan make_plan_heuristic(bsmm_op op, int G, int M, int N, int K, bsmm_dtype dt) 
     if (s < 1) s = 1;
     pl.split = s;
   }
-  // M-split: aligned bulk on the big tile plus a narrow tail launch.
   const int bm = pl.v->tile_m;
+  const int64_t per_row = (int64_t)((N + pl.v->tile_n - 1) / pl.v->tile_n) * G;
+  const int64_t rounds = tiles / kPlanCUs, rem = tiles % kPlanCUs;
+  if (rounds >= 1 && rem > 0 && rem <= kPlanCUs / 2 && KB >= 8) {
+    // Whole rounds: the last round would leave most CUs idle.  The bulk
+    // launch takes the tile rows that fill whole rounds; the remaining rows
+    // run as a second launch of the same kernel with split K across the chip.
+    const int64_t bulk_tile_rows = rounds * kPlanCUs / per_row;
+    const int m_split = (int)(bulk_tile_rows * bm);
+    if (bulk_tile_rows >= 1 && m_split < M) {
+      const int64_t tail_tiles = (int64_t)((M - m_split + bm - 1) / bm) * per_row;
+      int s = (int)(kPlanCUs / tail_tiles);     // tail_tiles * s fits one round
+      if (s > KB / 4) s = KB / 4;
+      if (s >= 2) {
+        pl.m_split = m_split;
+        pl.tail = pl.v;
+        pl.tail_split = s;
+        return pl;
+      }
+    }
+  }
+  // M-split: aligned bulk on the big tile plus a narrow tail launch.
   const int bulk = (M / bm) * bm;
   const int tail = M - bulk;
   if (bm == 256 && tail > 0 && tail <= 64 && (int64_t)G * bulk >= 8192) {
@@ -218,14 +253,34 @@ static bsmm_status run(const Problem& p, size_t workspace_bytes, void* ws,
                        void* stream) {
   Plan pl = make_plan(p.op, p.G, p.M, p.N, p.K, p.out_dtype, workspace_bytes);
   if (ovr().log)
-    fprintf(stderr, "[bsmm] %s G=%d M=%d N=%d K=%d out=%d -> %s split=%d m_split=%d tail=%s src=%d\n",
+    fprintf(stderr, "[bsmm] %s G=%d M=%d N=%d K=%d out=%d -> %s split=%d m_split=%d tail=%s/%d src=%d\n",
             op_name(p.op), p.G, p.M, p.N, p.K, (int)p.out_dtype, pl.v->name, pl.split,
-            pl.m_split, pl.tail ? pl.tail->name : "-", pl.source);
-  const int bulk_end = pl.m_split ? pl.m_split : p.M;
-  if (pl.v->launch(p, 0, bulk_end, pl.split, ws, workspace_bytes, stream))
+            pl.m_split, pl.tail ? pl.tail->name : "-", pl.tail_split, pl.source);
+  // packed scale_a first (shared by both launches), then the launches, which
+  // share the rest of the workspace
+  Launch l;
+  l.psa = nullptr;
+  l.stream = stream;
+  l.ws = ws;
+  l.ws_bytes = ws ? workspace_bytes : 0;
+  if (plan_packed(pl, p.op)) {
+    const size_t pack = packed_scale_bytes(p.op, p.G, p.M, p.K);
+    if (!ws || l.ws_bytes < pack) return fail(BSMM_ERR_ARG, "workspace too small for the plan");
+    if (pack_scale_a(p, ws, stream)) return fail(BSMM_ERR_HIP, "scale packing launch failed");
+    l.psa = ws;
+    l.ws_bytes -= pack;
+    l.ws = l.ws_bytes ? (void*)((uint8_t*)ws + pack) : nullptr;
+  }
+  l.row_begin = 0;
+  l.row_end = pl.m_split ? pl.m_split : p.M;
+  l.split = pl.split;
+  if (pl.v->launch(p, l))
     return fail(BSMM_ERR_HIP, "kernel launch failed (%s)", pl.v->name);
   if (pl.m_split && pl.m_split < p.M) {
-    if (pl.tail->launch(p, pl.m_split, p.M, 1, nullptr, 0, stream))
+    l.row_begin = pl.m_split;
+    l.row_end = p.M;
+    l.split = pl.tail_split;
+    if (pl.tail->launch(p, l))
       return fail(BSMM_ERR_HIP, "kernel launch failed (%s)", pl.tail->name);
   }
   return BSMM_OK;
@@ -407,6 +462,9 @@ bsmm_status bsmm_query_plan(bsmm_op op, int64_t G, int64_t M, int64_t N, int64_t
   info->m_split = pl.m_split;
   info->workspace = (int64_t)pl.workspace;
   info->source = pl.source;
+  snprintf(info->tail_variant, sizeof(info->tail_variant), "%s",
+           pl.m_split && pl.tail ? pl.tail->name : "");
+  info->tail_split_k = pl.m_split && pl.tail ? pl.tail_split : 0;
   return BSMM_OK;
 }
 

@@ -37,13 +37,23 @@ struct Plan {
   int split = 1;                   // K slices of the main launch
   const Variant* tail = nullptr;   // second launch for rows [m_split, M)
   int m_split = 0;                 // 0: one launch covers all of M
+  int tail_split = 1;              // K slices of the tail launch
   size_t workspace = 0;            // bytes used
   int source = 2;                  // bsmm_plan_info::source
 };
 
+// One kernel launch over rows [row_begin, row_end) of a problem.
+struct Launch {
+  int row_begin, row_end;
+  int split;             // K slices (split-K partials in ws)
+  void* ws;              // split-K partials / stream-K slots
+  size_t ws_bytes;
+  const void* psa;       // packed scale_a, already written (packed variants)
+  void* stream;
+};
+
 // Kernel variants compiled into the library.
-using LaunchFn = int (*)(const Problem& p, int row_begin, int row_end,
-                         int split, void* ws, size_t ws_bytes, void* stream);
+using LaunchFn = int (*)(const Problem& p, const Launch& l);
 struct Variant {
   const char* name;
   int tile_m, tile_n;
@@ -82,8 +92,11 @@ const Variant* variants(int* count);
 // bsmm_variants.inc.  PK: the fp8 main loop reads packed scale_a, which the
 // launch first writes to the start of the workspace.
 template <int OP, int OUT, int WM, int WN, int RING, bool SK, bool PK>
-int launch_kernel(const Problem& p, int row_begin, int row_end, int split, void* ws,
-                  size_t ws_bytes, void* stream);
+int launch_kernel(const Problem& p, const Launch& l);
+
+// Write packed scale_a (layout above) for an fp8 problem to dst, which holds
+// packed_scale_bytes(...) bytes and is 16-byte aligned.  Returns 0 on success.
+int pack_scale_a(const Problem& p, void* dst, void* stream);
 const Variant* find_variant(const char* name);
 
 // Bytes of split-K workspace a variant needs for `split` slices.

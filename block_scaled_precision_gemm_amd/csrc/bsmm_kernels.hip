@@ -755,42 +755,6 @@ splitk_reduce(const KArgs k) {
   }
 }
 
-// Packed scale_a (layout in bsmm_internal.h): one workgroup per 64 rows x 32
-// K blocks (x G), transposed through LDS so that both the reads (along K
-// blocks) and the writes (along rows) are contiguous.  Rows past M repeat
-// row M-1; the kernels never store their results.
-template <int OP>
-__global__ void __launch_bounds__(256) pack_scales(const KArgs k) {
-  __shared__ uint32_t t[32][65];
-  const Problem& p = k.p;
-  const int KB = p.K / kBlockK;
-  const int q = blockIdx.x, kb0 = blockIdx.y * 32, g = blockIdx.z;
-  const int tid = threadIdx.x;
-  const int kl = tid & 31;
-  for (int rl = tid >> 5; rl < 64; rl += 8) {
-    const int m = min(q * 64 + rl, p.M - 1);
-    const int kb = kb0 + kl;
-    uint32_t v = 0;
-    if (kb < KB) {
-      if constexpr (OP == BSMM_OP_FP8_MX_BMM)
-        v = ((const uint8_t*)p.sa)[(int64_t)g * p.sa_sg + (int64_t)m * p.sa_m + kb];
-      else
-        v = __float_as_uint(((const float*)p.sa)[(int64_t)m * p.sa_m + (int64_t)kb * p.sa_kb]);
-    }
-    t[kl][rl] = v;
-  }
-  __syncthreads();
-  const int pl = tid & 63;
-  const int rl = 16 * (pl & 3) + (pl >> 2);     // position 4f + i <- row 16i + f
-  for (int kl2 = tid >> 6; kl2 < 32; kl2 += 4) {
-    const int kb = kb0 + kl2;
-    if (kb >= KB) break;
-    const int64_t o = ((int64_t)g * KB + kb) * k.psa_ld + (int64_t)q * 64 + pl;
-    if constexpr (OP == BSMM_OP_FP8_MX_BMM) ((uint8_t*)k.psa)[o] = (uint8_t)t[kl2][rl];
-    else ((uint32_t*)k.psa)[o] = t[kl2][rl];
-  }
-}
-
 // Output for K == 0: zeros.
 __global__ void zero_out(const KArgs k) {
   const Problem& p = k.p;
@@ -827,40 +791,31 @@ bool out_vec_ok(const Problem& p) {
          (p.o_sg * osz) % vbytes == 0;
 }
 
-// Packed-scale launches: repack scale_a into the start of the workspace and
-// return the workspace left after it (nullptr, 0 if it does not fit).
-template <int OP>
-int prepare_packed(KArgs& k, void*& ws, size_t& ws_bytes, hipStream_t s) {
-  const Problem& p = k.p;
-  const size_t need = packed_scale_bytes(p.op, p.G, p.M, p.K);
-  if (ws == nullptr || ws_bytes < need || !aligned16(ws) || k.row_begin % 64 != 0) return 1;
-  k.psa = ws;
-  k.psa_ld = packed_rows(p.M);
-  const int KB = p.K / kBlockK;
-  const int G = OP == BSMM_OP_FP8_MX_BMM ? p.G : 1;
-  hipLaunchKernelGGL(pack_scales<OP>, dim3((unsigned)(k.psa_ld / 64), (unsigned)((KB + 31) / 32), (unsigned)G),
-                     dim3(256), 0, s, k);
-  if (check_launch()) return 1;
-  ws = ws_bytes > need ? (void*)((uint8_t*)ws + need) : nullptr;
-  ws_bytes -= need;
-  return 0;
+// Packed-scale kernels: the launch brings scale_a already packed; rows of a
+// launch must start on a multiple of 64 (packed groups).
+template <bool PK>
+bool set_packed(KArgs& k, const Launch& l) {
+  k.psa = l.psa;
+  k.psa_ld = packed_rows(k.p.M);
+  return !PK || (l.psa != nullptr && l.row_begin % 64 == 0);
 }
 
 template <int OP, int OUT, int WM, int WN, int RING, bool PK>
-int launch_tile(const Problem& p, int row_begin, int row_end, int split,
-                void* ws, size_t ws_bytes, void* stream) {
+int launch_tile(const Problem& p, const Launch& l) {
   using T = Tile<OP, WM, WN, RING>;
+  const int row_begin = l.row_begin, row_end = l.row_end;
+  int split = l.split;
+  void* ws = l.ws;
   KArgs k;
   k.p = p;
-  k.psa = nullptr;
-  k.psa_ld = 0;
+  if (!set_packed<PK>(k, l)) return 1;
   k.row_begin = row_begin;
   k.row_end = row_end;
   const int rows = row_end - row_begin;
   k.tiles_m = (rows + T::BM - 1) / T::BM;
   k.tiles_n = (p.N + T::BN - 1) / T::BN;
   const int KB = p.K / kBlockK;
-  hipStream_t s = (hipStream_t)stream;
+  hipStream_t s = (hipStream_t)l.stream;
   if (KB == 0) {              // empty sum: the output is zero
     k.ws = ws;
     k.splits = 1;
@@ -869,8 +824,6 @@ int launch_tile(const Problem& p, int row_begin, int row_end, int split,
     hipLaunchKernelGGL(zero_out, dim3(1024), dim3(256), 0, s, k);
     return check_launch();
   }
-  if constexpr (PK)
-    if (prepare_packed<OP>(k, ws, ws_bytes, s)) return 1;
   k.ws = ws;
   if (split < 1) split = 1;
   if (split > KB) split = KB;
@@ -904,15 +857,13 @@ uint64_t next_epoch() {
 }
 
 template <int OP, int OUT, int WM, int WN, int RING, bool PK>
-int launch_sk(const Problem& p, int row_begin, int row_end, int split, void* ws,
-              size_t ws_bytes, void* stream) {
+int launch_sk(const Problem& p, const Launch& l) {
   using T = Tile<OP, WM, WN, RING>;
   const int KB = p.K / kBlockK;
   typedef typename OpT<OP>::elem_t E;
   const size_t per_wg = (size_t)T::BM * T::BN * sizeof(E) + sizeof(uint64_t);
-  const size_t pack = PK ? packed_scale_bytes(p.op, p.G, p.M, p.K) : 0;
-  if (KB == 0 || !aligned16(ws) || ws_bytes < pack + per_wg)
-    return launch_tile<OP, OUT, WM, WN, RING, PK>(p, row_begin, row_end, split, ws, ws_bytes, stream);
+  if (KB == 0 || !aligned16(l.ws) || l.ws_bytes < per_wg)
+    return launch_tile<OP, OUT, WM, WN, RING, PK>(p, l);
   // co-resident capacity of this kernel on the current device (cached)
   static std::atomic<int> cap_cache[64];
   int dev = 0;
@@ -931,26 +882,23 @@ int launch_sk(const Problem& p, int row_begin, int row_end, int split, void* ws,
   }
   KArgs k;
   k.p = p;
-  k.psa = nullptr;
-  k.psa_ld = 0;
-  k.row_begin = row_begin;
-  k.row_end = row_end;
-  const int rows = row_end - row_begin;
+  if (!set_packed<PK>(k, l)) return 1;
+  k.row_begin = l.row_begin;
+  k.row_end = l.row_end;
+  const int rows = l.row_end - l.row_begin;
   k.tiles_m = (rows + T::BM - 1) / T::BM;
   k.tiles_n = (p.N + T::BN - 1) / T::BN;
   k.splits = 1;
   k.kb_per_split = KB;
   k.vec_out = out_vec_ok<OUT>(p);
-  hipStream_t s = (hipStream_t)stream;
-  if constexpr (PK)
-    if (prepare_packed<OP>(k, ws, ws_bytes, s)) return 1;
-  k.ws = ws;
+  hipStream_t s = (hipStream_t)l.stream;
+  k.ws = l.ws;
   SkArgs sk;
   sk.tiles_total = k.tiles_m * k.tiles_n * p.G;
   sk.units = (int64_t)sk.tiles_total * KB;
   int P = cap;
   if ((int64_t)P > sk.units) P = (int)sk.units;
-  if ((size_t)P * per_wg > ws_bytes) P = (int)(ws_bytes / per_wg);
+  if ((size_t)P * per_wg > l.ws_bytes) P = (int)(l.ws_bytes / per_wg);
   sk.epoch = next_epoch();
   hipLaunchKernelGGL((sk_kernel<OP, OUT, WM, WN, RING, PK>), dim3((unsigned)P), dim3(T::NT), 0, s,
                      k, sk);
@@ -963,20 +911,19 @@ int launch_sk(const Problem& p, int row_begin, int row_end, int split, void* ws,
 // (operation, output type).  Instantiated below for the pair this
 // translation unit is compiled for.
 template <int OP, int OUT, int WM, int WN, int RING, bool SK, bool PK>
-int launch_kernel(const Problem& p, int row_begin, int row_end, int split, void* ws,
-                  size_t ws_bytes, void* stream) {
+int launch_kernel(const Problem& p, const Launch& l) {
   // the int8 K loop reads no scales: packed variants run the plain kernel
   constexpr bool PKX = PK && OP != BSMM_OP_INT8_ROWWISE;
   if constexpr (SK)
-    return launch_sk<OP, OUT, WM, WN, RING, PKX>(p, row_begin, row_end, split, ws, ws_bytes, stream);
+    return launch_sk<OP, OUT, WM, WN, RING, PKX>(p, l);
   else
-    return launch_tile<OP, OUT, WM, WN, RING, PKX>(p, row_begin, row_end, split, ws, ws_bytes, stream);
+    return launch_tile<OP, OUT, WM, WN, RING, PKX>(p, l);
 }
 
 #if defined(BSMM_TU_OP) && defined(BSMM_TU_OUT)
 #define BSMM_VARIANT(NAME, TM, TN, WM, WN, RING, SK, PK, WPC, UNPACKED)                     \
   template int launch_kernel<BSMM_TU_OP, BSMM_TU_OUT, WM, WN, RING, SK, PK>(              \
-      const Problem&, int, int, int, void*, size_t, void*);
+      const Problem&, const Launch&);
 #include "bsmm_variants.inc"
 #undef BSMM_VARIANT
 #endif

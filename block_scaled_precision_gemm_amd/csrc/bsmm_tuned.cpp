@@ -4,7 +4,7 @@ namespace bsmm {
 
 static const TunedEntry kTable[] = {
 #include "bsmm_tuned_table.inc"
-    {-1, -1, 0, 0, 0, 0, "", 0, 0, ""},   // sentinel (never matches)
+    {-1, -1, 0, 0, 0, 0, "", 0, 0, "", 1},   // sentinel (never matches)
 };
 
 const TunedEntry* tuned_table(int* count) {

@@ -14,6 +14,7 @@ struct TunedEntry {
   int split;            // K slices of the main launch
   int m_split;          // rows of the bulk launch (0: no M-split)
   const char* tail_variant;  // "" when m_split == 0
+  int tail_split;       // K slices of the tail launch (1: none)
 };
 
 const TunedEntry* tuned_table(int* count);

@@ -7,22 +7,22 @@ namespace bsmm {
 namespace {
 
 template <int WM, int WN, int RING, bool SK, bool PK>
-int launch_variant(const Problem& p, int rb, int re, int sp, void* ws, size_t wsb, void* st) {
+int launch_variant(const Problem& p, const Launch& l) {
   switch (p.op) {
     case BSMM_OP_INT8_ROWWISE:
       if (p.out_dtype == BSMM_I32)
-        return launch_kernel<BSMM_OP_INT8_ROWWISE, BSMM_I32, WM, WN, RING, SK, PK>(p, rb, re, sp, ws, wsb, st);
+        return launch_kernel<BSMM_OP_INT8_ROWWISE, BSMM_I32, WM, WN, RING, SK, PK>(p, l);
       if (p.out_dtype == BSMM_F32)
-        return launch_kernel<BSMM_OP_INT8_ROWWISE, BSMM_F32, WM, WN, RING, SK, PK>(p, rb, re, sp, ws, wsb, st);
-      return launch_kernel<BSMM_OP_INT8_ROWWISE, BSMM_BF16, WM, WN, RING, SK, PK>(p, rb, re, sp, ws, wsb, st);
+        return launch_kernel<BSMM_OP_INT8_ROWWISE, BSMM_F32, WM, WN, RING, SK, PK>(p, l);
+      return launch_kernel<BSMM_OP_INT8_ROWWISE, BSMM_BF16, WM, WN, RING, SK, PK>(p, l);
     case BSMM_OP_FP8_BLOCKWISE:
       if (p.out_dtype == BSMM_F32)
-        return launch_kernel<BSMM_OP_FP8_BLOCKWISE, BSMM_F32, WM, WN, RING, SK, PK>(p, rb, re, sp, ws, wsb, st);
-      return launch_kernel<BSMM_OP_FP8_BLOCKWISE, BSMM_BF16, WM, WN, RING, SK, PK>(p, rb, re, sp, ws, wsb, st);
+        return launch_kernel<BSMM_OP_FP8_BLOCKWISE, BSMM_F32, WM, WN, RING, SK, PK>(p, l);
+      return launch_kernel<BSMM_OP_FP8_BLOCKWISE, BSMM_BF16, WM, WN, RING, SK, PK>(p, l);
     default:
       if (p.out_dtype == BSMM_F32)
-        return launch_kernel<BSMM_OP_FP8_MX_BMM, BSMM_F32, WM, WN, RING, SK, PK>(p, rb, re, sp, ws, wsb, st);
-      return launch_kernel<BSMM_OP_FP8_MX_BMM, BSMM_BF16, WM, WN, RING, SK, PK>(p, rb, re, sp, ws, wsb, st);
+        return launch_kernel<BSMM_OP_FP8_MX_BMM, BSMM_F32, WM, WN, RING, SK, PK>(p, l);
+      return launch_kernel<BSMM_OP_FP8_MX_BMM, BSMM_BF16, WM, WN, RING, SK, PK>(p, l);
   }
 }
 

@@ -173,6 +173,9 @@ typedef struct {
   int64_t workspace;  /* workspace bytes this plan uses                     */
   int32_t source;     /* 0 table hit, 1 padded-M bucket, 2 heuristic,       */
                       /* 3 override                                         */
+  char tail_variant[48]; /* variant of the launch for rows [m_split, M),   */
+                         /* "" without an M-split                          */
+  int32_t tail_split_k;  /* K slices of that launch (0 without M-split)    */
 } bsmm_plan_info;
 
 bsmm_status bsmm_query_plan(bsmm_op op, int64_t G, int64_t M, int64_t N,

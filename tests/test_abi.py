@@ -196,3 +196,15 @@ def test_dispatch_table_keys_unique_and_variants_exist():
         op, dt, G, M, N, K = (int(x) for x in f[:6])
         p = bsmm.bsmm_query_plan(op, G, M, N, K, {0: "i32", 1: "f32", 2: "bf16"}[dt])
         assert p["source"] == 0 and p["variant"] == f[6]
+
+
+def test_int8_packed_variant_needs_no_workspace():
+    """Packed variants only repack fp8 scales: an int8 plan on one needs no
+    workspace."""
+    import block_scaled_precision_gemm_amd as b
+    b.bsmm_set_override("t256x256p", 0)
+    try:
+        assert b.bsmm_query_plan(b.OP_INT8_ROWWISE, 1, 4096, 4096, 4096, "bf16")["workspace"] == 0
+        assert b.bsmm_query_plan(b.OP_FP8_BLOCKWISE, 1, 4096, 4096, 4096, "bf16")["workspace"] > 0
+    finally:
+        b.bsmm_set_override(None, 0)

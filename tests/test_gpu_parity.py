@@ -285,3 +285,19 @@ def test_packed_bulk_with_unpacked_tail():
     y = run_blockwise(q, "f32")
     rows = np.r_[0:300, 8100:M]
     check_blockwise(q, "f32", y, rows=rows)
+
+
+def test_whole_rounds_bulk_with_split_k_tail():
+    """A call whose last round of 256-row tiles would leave most CUs idle:
+    the bulk launch covers whole rounds and the remaining rows (ragged)
+    run with split K, both from one packed copy of scale_a."""
+    M, N, K = 16534, 1024, 2048
+    plan = bsmm.bsmm_query_plan(bsmm.OP_FP8_BLOCKWISE, 1, M, N, K, "bf16")
+    assert plan["m_split"] == 16384 and plan["tail_split_k"] > 1, plan
+    q = fp8_blockwise_inputs(M, N, K, 604)
+    say("whole-rounds bulk + split-K tail")
+    y = run_blockwise(q, "bf16")
+    rows = np.r_[0:64, 16300:M]
+    check_blockwise(q, "bf16", y, rows=rows)
+    y2 = run_blockwise(q, "bf16")
+    assert np.array_equal(host_out(y), host_out(y2))
