@@ -39,7 +39,8 @@ sys.path.insert(0, ROOT)
 
 PEAK = {"fp8": 5.0e15, "int8": 5.0e15}    # MI355X dense MFMA, ops/s
 HBM_PEAK = 8.0e12                          # bytes/s
-KERNEL_SOURCES = ["block_scaled_precision_gemm_amd/csrc/bsmm_kernels.hip"]
+KERNEL_SOURCES = ["block_scaled_precision_gemm_amd/csrc/bsmm_kernels.hip",
+                  "block_scaled_precision_gemm_amd/csrc/bsmm_pack.hip"]
 
 
 def kernel_hash():
@@ -74,6 +75,21 @@ def alg_bytes(c):
     else:
         sc = G * (M * (K // 128) + (N // 128) * (K // 128))
     return G * (M * K + N * K) + sc + G * M * N * ob
+
+
+def launch_bytes(c, rows):
+    """Algorithmic HBM bytes of one launch over `rows` of the M rows: its rows
+    of A and of scale_a, all of B and scale_b, its rows of the output."""
+    G = c.get("G", 1)
+    N, K = c["N"], c["K"]
+    ob = 2 if c["out"] == "bf16" else 4
+    if c["op"] == "int8":
+        sa, sb = 4 * rows, 4 * N
+    elif c["op"] == "fp8_blockwise":
+        sa, sb = 4 * rows * (K // 128), 4 * (K // 128) * (N // 128)
+    else:
+        sa, sb = G * rows * (K // 128), G * (N // 128) * (K // 128)
+    return G * (rows * K + N * K) + sa + sb + G * rows * N * ob
 
 
 def make_call(name, c, p, torch, bsmm):
@@ -125,9 +141,10 @@ def cpu_baseline(name, c, p, budget_s=15.0):
 
     rows = min(M, 16)
     t = run(rows)
-    # grow the sample toward the time budget
-    while rows < M and t < budget_s / 3:
-        rows = min(M, int(rows * max(2.0, min(8.0, budget_s / 2 / max(t, 1e-3)))))
+    # grow the sample toward the time budget (the last sample takes roughly
+    # 0.6 to 1 times the budget)
+    while rows < M and t < budget_s * 0.6:
+        rows = min(M, int(rows * max(1.5, min(8.0, budget_s * 0.8 / max(t, 1e-3)))))
         t = run(rows)
     flops = 2.0 * G * rows * N * K
     threads = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
@@ -136,6 +153,115 @@ def cpu_baseline(name, c, p, budget_s=15.0):
             "sample": f"{rows} of {M} output rows (all {G}x{N} columns), full K={K}; "
                       f"{t:.2f} s; numpy/OpenBLAS fp64 incl. the error-bound GEMM",
             "seconds": t}
+
+
+# ---------------------------------------------------------------------------
+# Profile helpers: the summaries under profiles/ are made with these modes.
+#   python bench.py --copy-kernel            (counter calibration workload)
+#   python bench.py --summarize DIR          (rocprofv3 --kernel-trace --stats)
+#   python bench.py --traffic F W CF CW      (FETCH_SIZE / WRITE_SIZE runs of
+#                                             the bench and of --copy-kernel)
+# ---------------------------------------------------------------------------
+COPY_BYTES = 256 << 20
+
+
+def copy_kernel():
+    """A plain device copy of COPY_BYTES, three times: the reference workload
+    that scales the FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 3}))
+
+
+def _csvs(d, suffix):
+    import glob
+    return sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True))
+
+
+def _main_kernel(name):
+    return "tile_kernel" in name or "sk_kernel" in name
+
+
+def summarize(d):
+    """Kernel statistics of a rocprofv3 run plus the main kernel's dispatches
+    grouped by grid size (the bulk and the tail launch of an M-split plan run
+    the same kernel with different grids)."""
+    import csv
+    out = []
+    for f in _csvs(d, "kernel_stats.csv"):
+        rows = list(csv.DictReader(open(f)))
+        out.append("kernel statistics (rocprofv3 --stats)")
+        out.append(f"{'calls':>6} {'avg us':>10} {'min us':>10} {'max us':>10} {'total %':>8}  kernel")
+        for r in rows:
+            out.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
+                       f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} "
+                       f"{float(r['Percentage']):8.2f}  {r['Name'][:110]}")
+    for f in _csvs(d, "kernel_trace.csv"):
+        rows = list(csv.DictReader(open(f)))
+        groups = {}
+        for r in rows:
+            if not _main_kernel(r["Kernel_Name"]):
+                continue
+            grid = int(r.get("Grid_Size_X") or r.get("Grid_Size") or 0)
+            key = (r["Kernel_Name"][:110], grid)
+            groups.setdefault(key, []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        out.append("")
+        out.append("main-kernel dispatches by grid size (rocprofv3 --kernel-trace)")
+        out.append(f"{'grid':>9} {'calls':>6} {'avg us':>10} {'min us':>10} {'max us':>10}  kernel")
+        for (k, grid), v in sorted(groups.items(), key=lambda kv: -kv[0][1]):
+            out.append(f"{grid:9d} {len(v):6d} {sum(v) / len(v):10.2f} {min(v):10.2f} "
+                       f"{max(v):10.2f}  {k}")
+    print("\n".join(out))
+
+
+def _counter(d, counter, pick):
+    """Per-dispatch values of one counter (summed over its instances) for the
+    dispatches `pick` selects; returns (values, grid)."""
+    import csv
+    per = {}
+    for f in _csvs(d, "counter_collection.csv"):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != counter or not pick(r):
+                continue
+            key = (f, r["Dispatch_Id"])
+            grid = int(r.get("Grid_Size") or 0)
+            v, _ = per.get(key, (0.0, grid))
+            per[key] = (v + float(r["Counter_Value"]), grid)
+    return per
+
+
+def traffic(name, fdir, wdir, cfdir, cwdir):
+    """HBM bytes per launch of the main kernel from FETCH_SIZE / WRITE_SIZE
+    (KiB per dispatch), each scaled by what the counter reads for the plain
+    copy of COPY_BYTES."""
+    def largest_main(per):
+        # the bulk launch is the main kernel's largest grid
+        grid = max(g for (_, g) in per.values())
+        return [v for (v, g) in per.values() if g == grid], grid
+    copy = lambda r: "copy" in r["Kernel_Name"].lower()
+    cf = [v for v, _ in _counter(cfdir, "FETCH_SIZE", copy).values()]
+    cw = [v for v, _ in _counter(cwdir, "WRITE_SIZE", copy).values()]
+    f_scale = COPY_BYTES / (sum(cf) / len(cf) * 1024)
+    w_scale = COPY_BYTES / (sum(cw) / len(cw) * 1024)
+    main = lambda r: _main_kernel(r["Kernel_Name"])
+    fv, grid = largest_main(_counter(fdir, "FETCH_SIZE", main))
+    wv, _ = largest_main(_counter(wdir, "WRITE_SIZE", main))
+    fetch = sum(fv) / len(fv) * 1024 * f_scale
+    write = sum(wv) / len(wv) * 1024 * w_scale
+    res = {"config": name, "kernel_hash": kernel_hash(), "grid": grid,
+           "dispatches": len(fv), "fetch_bytes_per_launch": fetch,
+           "write_bytes_per_launch": write, "hbm_bytes_per_launch": fetch + write,
+           "fetch_scale": f_scale, "write_scale": w_scale,
+           "copy_fetch_kib": sum(cf) / len(cf), "copy_write_kib": sum(cw) / len(cw)}
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+    with open(path, "w") as fh:
+        json.dump(res, fh, indent=1)
+    print(json.dumps(res))
 
 
 def main():
@@ -148,7 +274,17 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--settle", type=float, default=0.5,
                     help="seconds of untimed calls before the warm-up steps")
+    ap.add_argument("--copy-kernel", action="store_true")
+    ap.add_argument("--summarize", metavar="DIR")
+    ap.add_argument("--traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
+                                                   "COPY_WRITE_DIR"))
     args = ap.parse_args()
+    if args.summarize:
+        return summarize(args.summarize)
+    if args.traffic:
+        return traffic(args.config, *args.traffic)
+    if args.copy_kernel:
+        return copy_kernel()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the scaled matmul "
               "shards along M, N or G with no exchange, so per-GPU work is the one-GPU "
@@ -188,6 +324,7 @@ def main():
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
     torch.cuda.synchronize()
+    bsmm.bsmm_timing_enable(True)       # events around each step's main launch
     t_wall = time.perf_counter()
     for s, e in ev:
         s.record(stream)
@@ -195,22 +332,27 @@ def main():
         e.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
+    kern_ms, kern_n, kern_variant = bsmm.bsmm_timing_read()
+    bsmm.bsmm_timing_enable(False)
     durs = sorted(s.elapsed_time(e) for s, e in ev)       # ms per step
-    mean_ms = sum(durs) / len(durs)
-    med_ms = durs[len(durs) // 2]
+    step_ms_mean = sum(durs) / len(durs)
     ms_per_step = wall * 1e3 / args.steps
     value = flops / (ms_per_step * 1e-3) / 1e12
 
-    plan = bsmm.bsmm_query_plan({"int8": 0, "fp8_blockwise": 1, "mx": 2}[c["op"]], G, M, N, K,
-                                c["out"])
-    abytes = alg_bytes(c)
-    intensity = flops / abytes
+    op = {"int8": 0, "fp8_blockwise": 1, "mx": 2}[c["op"]]
+    plan = bsmm.bsmm_query_plan(op, G, M, N, K, c["out"])
+    # dominant kernel: the main launch of the plan (all rows, or the bulk rows
+    # of an M-split plan); its algorithmic work is its share of the rows
+    rows = plan["m_split"] or M
+    kflops = flops * rows / M
+    kbytes = launch_bytes(c, rows)
+    intensity = flops / alg_bytes(c)
     hbm_bound = intensity < PEAK[kind] / HBM_PEAK
     if hbm_bound:
-        roof = {"bound": "hbm", "achieved": abytes / (mean_ms * 1e-3) / 1e9,
+        roof = {"bound": "hbm", "achieved": kbytes / (kern_ms * 1e-3) / 1e9,
                 "peak": HBM_PEAK / 1e9, "unit": "GB/s"}
     else:
-        roof = {"bound": "mfma", "achieved": flops / (mean_ms * 1e-3) / 1e12,
+        roof = {"bound": "mfma", "achieved": kflops / (kern_ms * 1e-3) / 1e12,
                 "peak": PEAK[kind] / 1e12, "unit": "TFLOP/s" if kind == "fp8" else "TOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = None
@@ -219,10 +361,16 @@ def main():
         t = json.load(open(tf))
         if t.get("kernel_hash") == kernel_hash():
             roof["traffic"] = t["hbm_bytes_per_launch"]
-    roof["alg_bytes"] = abytes
-    roof["kernel_ms_mean"] = mean_ms
-    roof["kernel_ms_median"] = med_ms
-    roof["plan"] = plan["variant"] + (f" split{plan['split_k']}" if plan["split_k"] > 1 else "")
+    roof["kernel"] = kern_variant
+    roof["kernel_ms_mean"] = kern_ms
+    roof["kernel_launches"] = kern_n
+    roof["kernel_rows"] = rows
+    roof["kernel_alg_flops"] = kflops
+    roof["kernel_alg_bytes"] = kbytes
+    roof["step_ms_mean"] = step_ms_mean
+    roof["plan"] = (plan["variant"] + (f" split{plan['split_k']}" if plan["split_k"] > 1 else "")
+                    + (f" + rows {plan['m_split']}..{M}: {plan['tail_variant']}"
+                       f" split{plan['tail_split_k']}" if plan["m_split"] else ""))
 
     line = {
         "metric": "TFLOP/s and % of MI355X peak fp8/int8 MFMA, block-scaled GEMM/BMM",

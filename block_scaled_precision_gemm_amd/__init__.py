@@ -17,7 +17,7 @@ __all__ = [
     "load", "lib_path", "BsmmError",
     "bsmm_int8_rowwise", "bsmm_fp8_blockwise", "bsmm_fp8_mx_bmm",
     "bsmm_workspace_bytes", "bsmm_query_plan", "bsmm_set_override",
-    "bsmm_variant_names", "bsmm_version",
+    "bsmm_variant_names", "bsmm_version", "bsmm_timing_enable", "bsmm_timing_read",
     "I32", "F32", "BF16", "OP_INT8_ROWWISE", "OP_FP8_BLOCKWISE", "OP_FP8_MX_BMM",
     "STATUS",
 ]
@@ -77,6 +77,11 @@ def load():
     L.bsmm_status_string.restype = ctypes.c_char_p
     L.bsmm_last_error.restype = ctypes.c_char_p
     L.bsmm_version.restype = st
+    L.bsmm_timing_enable.argtypes = [ctypes.c_int]
+    L.bsmm_timing_enable.restype = st
+    L.bsmm_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64),
+                                   ctypes.c_char_p, sz]
+    L.bsmm_timing_read.restype = st
     _lib = L
     return L
 
@@ -321,6 +326,19 @@ def bsmm_query_plan(op, G, M, N, K, out_dtype, workspace_bytes=2**62):
 
 def bsmm_set_override(variant=None, split_k=0):
     _check(load().bsmm_set_override(variant.encode() if variant else None, split_k))
+
+
+def bsmm_timing_enable(enable=True):
+    """Time the main launch of every following call with HIP events."""
+    _check(load().bsmm_timing_enable(1 if enable else 0))
+
+
+def bsmm_timing_read():
+    """(mean ms, launches, variant) of the launches timed since enabling."""
+    ms, n = ctypes.c_double(), ctypes.c_int64()
+    name = ctypes.create_string_buffer(64)
+    _check(load().bsmm_timing_read(ctypes.byref(ms), ctypes.byref(n), name, 64))
+    return ms.value, n.value, name.value.decode()
 
 
 def bsmm_variant_names():

@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libbsmm.so")
 OBJDIR = os.path.join(PKG, "_build")
 ARCH = "gfx950"
 
-HOST_SOURCES = ["bsmm_api.cpp", "bsmm_tuned.cpp", "bsmm_variants.cpp"]
+HOST_SOURCES = ["bsmm_api.cpp", "bsmm_tuned.cpp", "bsmm_variants.cpp", "bsmm_timing.cpp"]
 HIP_SOURCE = "bsmm_kernels.hip"
 # The kernel source is compiled once per (operation, output type) pair, in
 # parallel; each object holds that pair's kernels for every configuration.

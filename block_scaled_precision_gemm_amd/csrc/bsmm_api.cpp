@@ -274,8 +274,11 @@ static bsmm_status run(const Problem& p, size_t workspace_bytes, void* ws,
   l.row_begin = 0;
   l.row_end = pl.m_split ? pl.m_split : p.M;
   l.split = pl.split;
+  const bool timed = timing_on();
+  if (timed) timing_mark(stream, pl.v->name, true);
   if (pl.v->launch(p, l))
     return fail(BSMM_ERR_HIP, "kernel launch failed (%s)", pl.v->name);
+  if (timed) timing_mark(stream, pl.v->name, false);
   if (pl.m_split && pl.m_split < p.M) {
     l.row_begin = pl.m_split;
     l.row_end = p.M;

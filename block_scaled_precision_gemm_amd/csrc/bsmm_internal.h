@@ -102,6 +102,10 @@ const Variant* find_variant(const char* name);
 // Bytes of split-K workspace a variant needs for `split` slices.
 size_t splitk_workspace(const Problem& p, int rows, int split);
 
+// Benchmark timing of the main launch of each call (bsmm_timing.cpp).
+bool timing_on();
+void timing_mark(void* stream, const char* name, bool begin);
+
 // Plan selection (host only).
 Plan make_plan(bsmm_op op, int G, int M, int N, int K, bsmm_dtype dt,
                size_t workspace_bytes);

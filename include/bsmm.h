@@ -191,6 +191,21 @@ bsmm_status bsmm_query_plan(bsmm_op op, int64_t G, int64_t M, int64_t N,
  */
 bsmm_status bsmm_set_override(const char* variant, int split_k);
 
+/*
+ * Kernel timing for benchmarks.  While enabled (enable != 0), the main launch
+ * of every call -- the one launch of a single-launch plan, the bulk launch
+ * of an M-split plan; without the split-K reduction -- is bracketed by two
+ * HIP events recorded on the call's stream.  Enabling (or disabling) clears
+ * the record.  bsmm_timing_read waits for the recorded events and returns
+ * the mean duration in milliseconds, the number of timed launches and the
+ * variant name of the last one (truncated to name_len, may be NULL).
+ * Returns BSMM_ERR_NULL for a NULL mean_ms or count, BSMM_ERR_HIP if an
+ * event cannot be created or read.  Not meant for concurrent callers.
+ */
+bsmm_status bsmm_timing_enable(int enable);
+bsmm_status bsmm_timing_read(double* mean_ms, int64_t* count, char* name,
+                             size_t name_len);
+
 /* Names of all kernel variants, separated by ','. */
 const char* bsmm_variant_names(void);
 

@@ -208,3 +208,12 @@ def test_int8_packed_variant_needs_no_workspace():
         assert b.bsmm_query_plan(b.OP_FP8_BLOCKWISE, 1, 4096, 4096, 4096, "bf16")["workspace"] > 0
     finally:
         b.bsmm_set_override(None, 0)
+
+
+def test_timing_hook_host_paths(L):
+    """Timing hook without a GPU: enabling clears the record, reading an empty
+    record returns zero launches, NULL outputs are rejected."""
+    bsmm.bsmm_timing_enable(True)
+    assert bsmm.bsmm_timing_read() == (0.0, 0, "")
+    bsmm.bsmm_timing_enable(False)
+    assert L.bsmm_timing_read(None, None, None, 0) == 1   # BSMM_ERR_NULL
