@@ -91,7 +91,7 @@ const Variant* variants(int* count);
 // HIP translation units, one per (OP, OUT) pair, for every configuration in
 // bsmm_variants.inc.  PK: the fp8 main loop reads packed scale_a, which the
 // launch first writes to the start of the workspace.
-template <int OP, int OUT, int WM, int WN, int RING, bool SK, bool PK>
+template <int OP, int OUT, int WM, int WN, int RING, bool SK, bool PK, int KIND>
 int launch_kernel(const Problem& p, const Launch& l);
 
 // Write packed scale_a (layout above) for an fp8 problem to dst, which holds

@@ -99,6 +99,7 @@ struct KArgs {
   void* ws;           // split-K partials [splits][G][rows][N] (fp32 / int32)
   const void* psa;    // packed scale_a [G][KB][psa_ld] (packed-scale kernels)
   int64_t psa_ld;
+  int units;          // tiles_m * tiles_n * G * splits work units of the launch
 };
 
 template <int OP> struct OpT;
@@ -106,20 +107,25 @@ template <> struct OpT<BSMM_OP_INT8_ROWWISE> { typedef i32x4 acc_t; typedef int 
 template <> struct OpT<BSMM_OP_FP8_BLOCKWISE> { typedef f32x4 acc_t; typedef float elem_t; };
 template <> struct OpT<BSMM_OP_FP8_MX_BMM> { typedef f32x4 acc_t; typedef float elem_t; };
 
-// Map the flat workgroup id to (split, group, tile_m, tile_n).
+// Map a work unit (flat workgroup id) to (split, group, tile_m, tile_n).
 //  1. XCD-aware remap: consecutive hardware ids land on different XCDs
 //     (round robin over 8), so contiguous runs of logical ids are given to
 //     one XCD and share its L2.
 //  2. GROUP_M rasterisation over the tiles (the grouped program-id order of
 //     the Triton mm template in Inductor's mm.py) for L2 reuse.
+//  3. A grid smaller than the number of units (one workgroup per slot of the
+//     device) is persistent: workgroup slot w takes units w, w + grid, ...,
+//     so while a tile's stores drain the workgroup already loads its next
+//     tile, and the CUs drift out of step instead of all storing at once.
 struct TileId { int s, g, tm, tn; };
-__device__ __forceinline__ TileId decode_tile(const KArgs& k) {
+__device__ __forceinline__ int first_unit() {
   const int total = gridDim.x;
   const int hw = blockIdx.x;
   const int per = total >> 3, rem = total & 7;
   const int xcd = hw & 7, local = hw >> 3;
-  int pid = (xcd < rem) ? xcd * (per + 1) + local
-                        : rem * (per + 1) + (xcd - rem) * per + local;
+  return (xcd < rem) ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+}
+__device__ __forceinline__ TileId decode_tile(const KArgs& k, int pid) {
   const int tiles = k.tiles_m * k.tiles_n;
   TileId t;
   int tile = pid % tiles;
@@ -188,6 +194,40 @@ __device__ __forceinline__ void load_row_group(__amdgpu_buffer_rsrc_t rs, uint8_
   const int c = (lane & 7) ^ swz(r);
   const uint32_t vo = live ? (uint32_t)r * ld + kbyte + ((uint32_t)c << 4) : kOob;
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + q * 1024), 16, vo, 0, 0, 0);
+}
+
+// mx MFMA: scale byte-select `sel` (0..3, a constant after unrolling) picks the
+// B-side (A-fragment) e8m0 scale from the lane's packed four row scales.
+__device__ __forceinline__ f32x4 mfma_mx(i32x8 x, i32x8 y, f32x4 c, int sx, int sel,
+                                         uint32_t sy) {
+  switch (sel) {
+    case 0: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, c, 0, 0, 0, sx, 0, (int)sy);
+    case 1: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, c, 0, 0, 0, sx, 1, (int)sy);
+    case 2: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, c, 0, 0, 0, sx, 2, (int)sy);
+    default: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, c, 0, 0, 0, sx, 3, (int)sy);
+  }
+}
+
+// Lane part of a tile load's offset, (8 wave + l/8) * ld + 16 * chunk, for
+// rows 8q + l/8 with q of parity qpar (see load_row_group); the rest of the
+// offset, 8 t NW ld + the K-block byte offset, is wave-uniform.
+__device__ __forceinline__ uint32_t lane_base(uint32_t ld, int wave, int lane, int qpar) {
+  const int c = (lane & 7) ^ (lane >> 3) ^ qpar;
+  return (uint32_t)(wave * 8 + (lane >> 3)) * ld + ((uint32_t)c << 4);
+}
+
+__device__ __forceinline__ void load_tile_rows(__amdgpu_buffer_rsrc_t rs, uint8_t* dst,
+                                               uint32_t base, uint32_t uniform_off,
+                                               bool live) {
+  // opaque to the optimiser, which would otherwise keep one loop-invariant
+  // base + offset sum per load in a VGPR for the whole K loop
+  asm volatile("" : "+s"(uniform_off));
+  const uint32_t vo = live ? base + uniform_off : kOob;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)dst, 16, vo, 0, 0, 0);
+}
+
+__device__ __forceinline__ void wait_lgkm0() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
 template <int N>
@@ -309,7 +349,9 @@ struct Mainloop {
 
     // Scale registers of the current K block (cur) and the next one (nxt),
     // loaded at least half a K block before they are used.
-    int xs_cur[TI], xs_nxt[TI];
+    // mx: the four row scale bytes of a lane, byte i for 16-row tile i (the
+    // MFMA's scale byte-select picks it)
+    uint32_t xs_cur = 0x7F7F7F7Fu, xs_nxt = 0x7F7F7F7Fu;
     int ws_cur = 127, ws_nxt = 127;
     float sa_nxt[TI];
     float sb_nxt = 1.f;
@@ -317,13 +359,12 @@ struct Mainloop {
     auto load_scales = [&](int kb) {
       if constexpr (OP == BSMM_OP_FP8_MX_BMM) {
         if constexpr (PK) {
-          const uint32_t v = *(const uint32_t*)((const uint8_t*)k.psa +
-                                                (pk_g + kb) * k.psa_ld + pk_lane);
-  #pragma unroll
-          for (int i = 0; i < TI; ++i) xs_nxt[i] = (int)((v >> (8 * i)) & 0xFFu);
+          xs_nxt = *(const uint32_t*)((const uint8_t*)k.psa + (pk_g + kb) * k.psa_ld + pk_lane);
         } else {
+          uint32_t v = 0;
   #pragma unroll
-          for (int i = 0; i < TI; ++i) xs_nxt[i] = xs_row[i][kb];
+          for (int i = 0; i < TI; ++i) v |= (uint32_t)xs_row[i][kb] << (8 * i);
+          xs_nxt = v;
         }
         ws_nxt = ws_blk[kb];
       } else if constexpr (OP == BSMM_OP_FP8_BLOCKWISE) {
@@ -340,8 +381,7 @@ struct Mainloop {
     };
     auto use_scales = [&]() {
       if constexpr (OP == BSMM_OP_FP8_MX_BMM) {
-  #pragma unroll
-        for (int i = 0; i < TI; ++i) xs_cur[i] = xs_nxt[i];
+        xs_cur = xs_nxt;
         ws_cur = ws_nxt;
       } else if constexpr (OP == BSMM_OP_FP8_BLOCKWISE) {
   #pragma unroll
@@ -407,8 +447,7 @@ struct Mainloop {
             ring[tt % D] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                 bcur, af[i], f32x4{0, 0, 0, 0}, 0, 0, 0, 127, 0, 127);
           } else {
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                bcur, af[i], acc[i][j], 0, 0, 0, ws_cur, 0, xs_cur[i]);
+            acc[i][j] = mfma_mx(bcur, af[i], acc[i][j], ws_cur, i, xs_cur);
           }
         }
         bcur = bnext;
@@ -486,15 +525,16 @@ struct Mainloop {
   }
 };
 
-// Lane (wave wm, wn; lane l) holds output rows row0 + 64 wm + 16 i + l % 16
-// and columns col0 + 128 wn + 16 j + 4 (l / 16) .. +3 of the tile.
+// Lane (wave wm, wn; lane l) holds output rows row0 + 16 TI wm + 16 i + l % 16
+// and columns col0 + 16 TJ wn + 16 j + 4 (l / 16) .. +3 of the tile (a wave
+// owns TI x TJ MFMA tiles of 16 x 16).
 struct LanePos { int mrow, ncol; };
-template <int WM, int WN>
+template <int WN, int TI, int TJ>
 __device__ __forceinline__ LanePos lane_pos(int row0, int col0) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave / WN, wn = wave % WN;
-  return LanePos{row0 + wm * 64 + (lane & 15), col0 + wn * 128 + 4 * (lane >> 4)};
+  return LanePos{row0 + wm * 16 * TI + (lane & 15), col0 + wn * 16 * TJ + 4 * (lane >> 4)};
 }
 
 // Final epilogue: scale (int8), convert, store the tile to the output.
@@ -502,7 +542,7 @@ template <int OP, int OUT, int WM, int WN, int TI, int TJ, class acc_t>
 __device__ __forceinline__ void store_output(const KArgs& k, int g, int row0, int col0,
                                              const acc_t (&acc)[TI][TJ]) {
   const Problem& p = k.p;
-  const LanePos lp = lane_pos<WM, WN>(row0, col0);
+  const LanePos lp = lane_pos<WN, TI, TJ>(row0, col0);
   const bool vec = k.vec_out != 0;
   uint8_t* obase = (uint8_t*)p.out;
   const int64_t og = (int64_t)g * p.o_sg;
@@ -544,7 +584,7 @@ template <int OP, int WM, int WN, int TI, int TJ, class acc_t>
 __device__ __forceinline__ void store_splitk(const KArgs& k, int s, int g, int row0,
                                              int col0, const acc_t (&acc)[TI][TJ]) {
   const Problem& p = k.p;
-  const LanePos lp = lane_pos<WM, WN>(row0, col0);
+  const LanePos lp = lane_pos<WN, TI, TJ>(row0, col0);
   const bool vec = k.vec_out != 0;
   const int rows = k.row_end - k.row_begin;
   typedef typename OpT<OP>::elem_t E;
@@ -570,6 +610,324 @@ __device__ __forceinline__ void store_splitk(const KArgs& k, int s, int g, int r
   }
 }
 
+// Epilogue through LDS.  Stored straight from the MFMA layout, a wave's
+// store instruction writes 16 rows x 32 or 64 bytes -- sixteen partial cache
+// lines -- and a round of 256 tiles took ~13 us of pure write time.  Here
+// each wave stages 32 rows x (16 TJ) columns of 4-byte values in LDS (idle
+// after the K loop; rows padded by 16 bytes), reads them back as contiguous
+// 4-element groups and stores whole row segments.  int8: the row scale is
+// applied while staging, the column scale after reading back (the order
+// (f32(acc) * sa) * sb is unchanged).  PARTIAL: split-K partials (int32 /
+// fp32) into the workspace [splits][G][rows][N] instead of the output.
+template <int OP, int OUT, int NW, int WN, bool PARTIAL, int TI, int TJ, class acc_t>
+__device__ __forceinline__ void store_staged(const KArgs& k, int s, int g, int row0, int col0,
+                                             const acc_t (&acc)[TI][TJ], uint8_t* smem) {
+  constexpr int ROWS = 32;                       // staged rows per pass
+  constexpr int PITCH = 16 * TJ * 4 + 16;        // bytes per staged row
+  constexpr int GROUPS = ROWS * 16 * TJ / 4;     // 4-element groups per pass
+  constexpr int PER_ROW = 16 * TJ / 4;           // groups per row
+  static_assert(TI % 2 == 0 && GROUPS % kWave == 0, "staging layout");
+  typedef typename OpT<OP>::elem_t E;
+  const Problem& p = k.p;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int wm = wave / WN, wn = wave % WN;
+  uint8_t* st = smem + wave * (ROWS * PITCH);
+  const int fr = lane & 15, fq = lane >> 4;
+  const int wrow0 = row0 + wm * 16 * TI, wcol0 = col0 + wn * 16 * TJ;
+  const bool vec = k.vec_out != 0;
+  uint8_t* obase;
+  int64_t og, ldo;
+  if constexpr (PARTIAL) {
+    const int rows = k.row_end - k.row_begin;
+    obase = (uint8_t*)((E*)k.ws + ((int64_t)s * p.G + g) * (int64_t)rows * p.N);
+    og = -(int64_t)k.row_begin * p.N;
+    ldo = p.N;
+  } else {
+    obase = (uint8_t*)p.out;
+    og = (int64_t)g * p.o_sg;
+    ldo = p.ldo;
+  }
+  constexpr bool SCALE = OP == BSMM_OP_INT8_ROWWISE && OUT != BSMM_I32 && !PARTIAL;
+  const bool sb_vec = SCALE && p.sb_n == 1 && (((uintptr_t)p.sb) & 15u) == 0;
+  lds_barrier();     // every wave's K-loop reads of LDS are done
+#pragma unroll
+  for (int pass = 0; pass < TI / 2; ++pass) {
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) {
+      const int i = 2 * pass + ii;
+      float sa_m = 1.f;
+      if constexpr (SCALE)
+        sa_m = ((const float*)p.sa)[(int64_t)min(wrow0 + 16 * i + fr, k.row_end - 1) * p.sa_m];
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        i32x4 v;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if constexpr (SCALE)
+            v[r] = __float_as_int(__fmul_rn((float)acc[i][j][r], sa_m));
+          else if constexpr (OP == BSMM_OP_INT8_ROWWISE)
+            v[r] = acc[i][j][r];
+          else
+            v[r] = __float_as_int(acc[i][j][r]);
+        }
+        *(i32x4*)(st + (16 * ii + fr) * PITCH + (16 * j + 4 * fq) * 4) = v;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < GROUPS / kWave; ++q) {
+      const int gi = q * kWave + lane;
+      const int r = gi / PER_ROW, cg = gi % PER_ROW;
+      const i32x4 v = *(const i32x4*)(st + r * PITCH + cg * 16);
+      const int m = wrow0 + ROWS * pass + r;
+      const int n = wcol0 + 4 * cg;
+      const int nvalid = min(4, p.N - n);
+      if (m >= k.row_end || nvalid <= 0) continue;
+      const int64_t e = og + (int64_t)m * ldo + n;
+      float y[4];
+      int yi[4];
+      if constexpr (SCALE) {
+        float sb[4];
+        if (sb_vec && nvalid == 4) {
+          const f32x4 t = *(const f32x4*)((const float*)p.sb + n);
+          sb[0] = t[0]; sb[1] = t[1]; sb[2] = t[2]; sb[3] = t[3];
+        } else {
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            sb[c] = ((const float*)p.sb)[(int64_t)min(n + c, p.N - 1) * p.sb_n];
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) y[c] = __fmul_rn(__int_as_float(v[c]), sb[c]);
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          y[c] = __int_as_float(v[c]);
+          yi[c] = v[c];
+        }
+      }
+      if constexpr (PARTIAL)
+        store4<OP == BSMM_OP_INT8_ROWWISE ? BSMM_I32 : BSMM_F32>(obase, e, y, yi, vec, nvalid);
+      else
+        store4<OUT>(obase, e, y, yi, vec, nvalid);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Wide-wave K loop: four waves (one per SIMD), a 256 x 256 tile, each wave a
+// 128 x 128 sub-tile = 8 x 8 MFMA tiles whose 256 accumulator registers the
+// compiler keeps in AGPRs.  For the paths without per-element work in the
+// K loop (int8, mx).
+//
+// Per K block and wave: 64 MFMA tiles in row order (A tile i with B tiles
+// 0..7), 16 direct-to-LDS loads and 32 fragment reads, each of them for the
+// NEXT block and into the register it replaces: the next block's A tile i
+// after row i (a whole block ahead of its use), its B tile j right after
+// the last MFMA that uses B tile j (row 7; eight MFMAs ahead of its first
+// use in row 0).  The only synchronisation is one barrier per block,
+// placed after row 0.
+//
+// LDS ring of five 32 KB half-stages, half-stage h (2c: A of block c,
+// 2c+1: B) in slot h % 5.  Barrier #c (after row 0 of block c) certifies
+// that block c+1 has landed (it is read during block c) and that every
+// wave has finished reading block c (read during block c-1): block c's two
+// slots are refilled with half-stages 2c+5 (block c+2's B, rows 1..4) and
+// 2c+6 (block c+3's A, rows 5..7).  At barrier #c only half-stage 2c+4's
+// loads (block c+2's A, issued during block c-1) may still be in flight.
+// ---------------------------------------------------------------------------
+template <int OP, bool PK>
+struct Mainloop4 {
+  static constexpr int NW = 4, WN = 2, TI = 8, TJ = 8, WTM = 128, WTN = 128;
+  static constexpr int BM = 256, BN = 256, NT = NW * kWave;
+  static constexpr int SLOT = BM * kBlockK, NSLOT = 5, LDS = NSLOT * SLOT;
+  static constexpr int LA = BM / 8 / NW, LB = BN / 8 / NW;    // loads per half-stage per wave
+  using acc_t = typename OpT<OP>::acc_t;
+  static_assert(OP != BSMM_OP_FP8_BLOCKWISE, "blockwise needs its accumulators in VGPRs");
+
+  __device__ __forceinline__ static void run(const KArgs& k, uint8_t* smem, int g,
+                                             int row0, int col0, int kb0, int nkb,
+                                             acc_t (&acc)[TI][TJ]) {
+    const Problem& p = k.p;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int wm = wave / WN, wn = wave % WN;
+    const uint32_t lda = (uint32_t)p.lda, ldb = (uint32_t)p.ldb;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(
+        p.a + (int64_t)g * p.a_sg + (int64_t)row0 * p.lda,
+        (uint64_t)(k.row_end - row0) * p.lda);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(
+        p.b + (int64_t)g * p.b_sg + (int64_t)col0 * p.ldb,
+        (uint64_t)(p.N - col0) * p.ldb);
+    // lane part of the load offsets (the chunk swizzle of row 8q + l/8
+    // depends on q's parity, which is the wave's for four waves)
+    const uint32_t base_a = lane_base(lda, wave, lane, wave & 1);
+    const uint32_t base_b = lane_base(ldb, wave, lane, wave & 1);
+    auto issue_load = [&](int h, int t) {
+      uint8_t* dst = smem + (h % NSLOT) * SLOT + (t * NW + wave) * 1024;
+      const bool live = h < 2 * nkb;
+      const uint32_t kbyte = (uint32_t)(kb0 + (h >> 1)) * kBlockK;
+      if (h & 1) load_tile_rows(rb, dst, base_b, (uint32_t)(t * NW * 8) * ldb + kbyte, live);
+      else load_tile_rows(ra, dst, base_a, (uint32_t)(t * NW * 8) * lda + kbyte, live);
+    };
+
+    const int fr = lane & 15;
+    const int fc = (lane >> 4) * 2;
+    const int a_r = wm * WTM + fr, b_r = wn * WTN + fr;
+    const int a_off0 = lds_off(a_r, fc), a_off1 = lds_off(a_r, fc + 1);
+    const int b_off0 = lds_off(b_r, fc), b_off1 = lds_off(b_r, fc + 1);
+    auto frag = [&](int h, int off0, int off1, int t) {
+      const uint8_t* S = smem + (h % NSLOT) * SLOT;
+      const i32x4 lo = *(const i32x4*)(S + off0 + t * 2048);
+      const i32x4 hi = *(const i32x4*)(S + off1 + t * 2048);
+      return i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    };
+
+    lds_barrier();     // LDS reads of a previous call are finished
+    // mx scales: the lane's rows f + 16 i, i = 0..7, as two packed dwords
+    // (byte i % 4 of word i / 4), and the wave's w_scale block
+    const uint8_t* xs_row[TI];
+    const uint8_t* ws_blk = nullptr;
+    const int64_t pk_lane = (int64_t)(row0 + wm * WTM) + 4 * fr;
+    const int64_t pk_g = PK ? (int64_t)g * (p.K / kBlockK) : 0;
+    if constexpr (OP == BSMM_OP_FP8_MX_BMM) {
+      const int nb = min((col0 + wn * WTN) / kBlockK, p.N / kBlockK - 1);
+      ws_blk = (const uint8_t*)p.sb + (int64_t)g * p.sb_sg + (int64_t)nb * p.sb_n;
+      if constexpr (!PK) {
+  #pragma unroll
+        for (int i = 0; i < TI; ++i) {
+          const int m = min(row0 + wm * WTM + i * 16 + fr, k.row_end - 1);
+          xs_row[i] = (const uint8_t*)p.sa + (int64_t)g * p.sa_sg + (int64_t)m * p.sa_m;
+        }
+      }
+    }
+    uint32_t xs_cur[2] = {0x7F7F7F7Fu, 0x7F7F7F7Fu}, xs_nxt[2] = {0x7F7F7F7Fu, 0x7F7F7F7Fu};
+    int ws_cur = 127, ws_nxt = 127;
+    auto load_scales = [&](int kb) {
+      if constexpr (OP == BSMM_OP_FP8_MX_BMM) {
+        if constexpr (PK) {
+          const uint8_t* q = (const uint8_t*)k.psa + (pk_g + kb) * k.psa_ld + pk_lane;
+          xs_nxt[0] = *(const uint32_t*)q;
+          xs_nxt[1] = *(const uint32_t*)(q + 64);
+        } else {
+  #pragma unroll
+          for (int w = 0; w < 2; ++w) {
+            uint32_t v = 0;
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) v |= (uint32_t)xs_row[4 * w + i][kb] << (8 * i);
+            xs_nxt[w] = v;
+          }
+        }
+        ws_nxt = ws_blk[kb];
+      }
+    };
+    auto use_scales = [&]() {
+      xs_cur[0] = xs_nxt[0];
+      xs_cur[1] = xs_nxt[1];
+      ws_cur = ws_nxt;
+    };
+
+    if (nkb <= 0) return;
+    i32x8 af[TI], bf[TJ];
+    // prologue: blocks 0, 1 and block 2's A in flight; block 0 read
+    load_scales(kb0);
+  #pragma unroll
+    for (int h = 0; h < 5; ++h)
+  #pragma unroll
+      for (int t = 0; t < ((h & 1) ? LB : LA); ++t) issue_load(h, t);
+    wait_vmcnt<LA + LB + LA>();         // block 0 landed
+    lds_barrier();
+  #pragma unroll
+    for (int i = 0; i < TI; ++i) af[i] = frag(0, a_off0, a_off1, i);
+  #pragma unroll
+    for (int j = 0; j < TJ; ++j) bf[j] = frag(1, b_off0, b_off1, j);
+
+    constexpr int kMfma = 0x008, kVmemRead = 0x020, kDsRead = 0x100;
+    constexpr int MF = OP == BSMM_OP_INT8_ROWWISE ? 2 : 1;
+    auto mfma_tile = [&](int i, int j) {
+      if constexpr (OP == BSMM_OP_INT8_ROWWISE) {
+        const i32x4 alo = i32x4{af[i][0], af[i][1], af[i][2], af[i][3]};
+        const i32x4 ahi = i32x4{af[i][4], af[i][5], af[i][6], af[i][7]};
+        const i32x4 blo = i32x4{bf[j][0], bf[j][1], bf[j][2], bf[j][3]};
+        const i32x4 bhi = i32x4{bf[j][4], bf[j][5], bf[j][6], bf[j][7]};
+        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(blo, alo, acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bhi, ahi, acc[i][j], 0, 0, 0);
+      } else {
+        acc[i][j] = mfma_mx(bf[j], af[i], acc[i][j], ws_cur, i & 3, xs_cur[i >> 2]);
+      }
+    };
+    for (int c = 0; c < nkb; ++c) {
+      use_scales();
+  #pragma unroll
+      for (int j = 0; j < TJ; ++j) mfma_tile(0, j);
+      wait_vmcnt<LA>();                 // block c+1 landed
+      wait_lgkm0();                     // this wave's reads of block c are done
+      lds_barrier();                    // ... every wave's: block c's slots are free
+      load_scales(kb0 + min(c + 1, nkb - 1));
+      af[0] = frag(2 * c + 2, a_off0, a_off1, 0);
+      __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+      for (int i = 1; i < TI; ++i) {
+  #pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          mfma_tile(i, j);
+          // row 7: B tile j is done for this block; read the next block's
+          if (i == TI - 1) bf[j] = frag(2 * c + 3, b_off0, b_off1, j);
+        }
+        af[i] = frag(2 * c + 2, a_off0, a_off1, i);
+        // refills: block c+2's B over rows 1..4, block c+3's A over rows 5..7
+        if (i <= 4) {
+          issue_load(2 * c + 5, 2 * (i - 1));
+          issue_load(2 * c + 5, 2 * (i - 1) + 1);
+        } else {
+  #pragma unroll
+          for (int t = LA * (i - 5) / 3; t < LA * (i - 4) / 3; ++t) issue_load(2 * c + 6, t);
+        }
+        // schedule: MFMAs with the fragment reads and loads spread among them
+  #pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          __builtin_amdgcn_sched_group_barrier(kMfma, MF, 0);
+          if (i == TI - 1) __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
+          if (j == 1 && i < TI - 1) __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
+          if (j == 4) {
+            constexpr int kA = LA;   // block c+3's A loads over rows 5..7
+            const int nl = i <= 4 ? 2 : kA * (i - 4) / 3 - kA * (i - 5) / 3;
+            if (nl == 2) __builtin_amdgcn_sched_group_barrier(kVmemRead, 2, 0);
+            if (nl == 3) __builtin_amdgcn_sched_group_barrier(kVmemRead, 3, 0);
+          }
+        }
+        if (i == TI - 1) __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    wait_vmcnt<0>();     // the last refills were out-of-range loads
+  }
+};
+
+template <int OP, int OUT, bool PK>
+__global__ void __launch_bounds__(256)
+tile4_kernel(const KArgs k) {
+  using M = Mainloop4<OP, PK>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[M::LDS];
+  const int KB = k.p.K / kBlockK;
+  for (int u = first_unit(); u < k.units; u += gridDim.x) {
+    const TileId t = decode_tile(k, u);
+    const int row0 = k.row_begin + t.tm * M::BM;
+    const int col0 = t.tn * M::BN;
+    const int kb0 = t.s * k.kb_per_split;
+    const int nkb = max(0, min(KB, kb0 + k.kb_per_split) - kb0);
+    typename M::acc_t acc[M::TI][M::TJ];
+#pragma unroll
+    for (int i = 0; i < M::TI; ++i)
+#pragma unroll
+      for (int j = 0; j < M::TJ; ++j) acc[i][j] = typename M::acc_t{0, 0, 0, 0};
+    M::run(k, smem, t.g, row0, col0, kb0, nkb, acc);
+    if (k.splits > 1)
+      store_staged<OP, OUT, 4, 2, true>(k, t.s, t.g, row0, col0, acc, smem);
+    else
+      store_staged<OP, OUT, 4, 2, false>(k, t.s, t.g, row0, col0, acc, smem);
+  }
+}
+
 // One output tile (or one K slice of it, with split-K) per workgroup.
 template <int OP, int OUT, int WM, int WN, int RING, bool PK>
 __global__ void __launch_bounds__(64 * WM * WN)
@@ -577,22 +935,24 @@ tile_kernel(const KArgs k) {
   using M = Mainloop<OP, WM, WN, RING, PK>;
   using T = typename M::T;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS];
-  const TileId t = decode_tile(k);
-  const int row0 = k.row_begin + t.tm * T::BM;
-  const int col0 = t.tn * T::BN;
   const int KB = k.p.K / kBlockK;
-  const int kb0 = t.s * k.kb_per_split;
-  const int nkb = max(0, min(KB, kb0 + k.kb_per_split) - kb0);
-  typename M::acc_t acc[M::TI][M::TJ];
+  for (int u = first_unit(); u < k.units; u += gridDim.x) {
+    const TileId t = decode_tile(k, u);
+    const int row0 = k.row_begin + t.tm * T::BM;
+    const int col0 = t.tn * T::BN;
+    const int kb0 = t.s * k.kb_per_split;
+    const int nkb = max(0, min(KB, kb0 + k.kb_per_split) - kb0);
+    typename M::acc_t acc[M::TI][M::TJ];
 #pragma unroll
-  for (int i = 0; i < M::TI; ++i)
+    for (int i = 0; i < M::TI; ++i)
 #pragma unroll
-    for (int j = 0; j < M::TJ; ++j) acc[i][j] = typename M::acc_t{0, 0, 0, 0};
-  M::run(k, smem, t.g, row0, col0, kb0, nkb, acc);
-  if (k.splits > 1)
-    store_splitk<OP, WM, WN>(k, t.s, t.g, row0, col0, acc);
-  else
-    store_output<OP, OUT, WM, WN>(k, t.g, row0, col0, acc);
+      for (int j = 0; j < M::TJ; ++j) acc[i][j] = typename M::acc_t{0, 0, 0, 0};
+    M::run(k, smem, t.g, row0, col0, kb0, nkb, acc);
+    if (k.splits > 1)
+      store_staged<OP, OUT, WM * WN, WN, true>(k, t.s, t.g, row0, col0, acc, smem);
+    else
+      store_staged<OP, OUT, WM * WN, WN, false>(k, t.s, t.g, row0, col0, acc, smem);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -800,6 +1160,31 @@ bool set_packed(KArgs& k, const Launch& l) {
   return !PK || (l.psa != nullptr && l.row_begin % 64 == 0);
 }
 
+// Workgroups of a kernel the current device holds at once (0 on error),
+// cached per device in `cache`.
+int device_slots(const void* kernel, int threads, std::atomic<int>* cache) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int cap = cache[dev].load(std::memory_order_relaxed);
+  if (cap == 0) {
+    int cus = 0, occ = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, threads, 0) != hipSuccess)
+      return 0;
+    cap = cus * (occ > 0 ? occ : 1);
+    cache[dev].store(cap, std::memory_order_relaxed);
+  }
+  return cap;
+}
+
+// Grid of a tile launch: one workgroup per unit, or -- with more units than
+// the device holds at once -- one per slot, each looping over units.
+int64_t tile_grid(int64_t units, const void* kernel, int threads, std::atomic<int>* cache) {
+  const int cap = device_slots(kernel, threads, cache);
+  return cap > 0 && units > cap ? cap : units;
+}
+
 template <int OP, int OUT, int WM, int WN, int RING, bool PK>
 int launch_tile(const Problem& p, const Launch& l) {
   using T = Tile<OP, WM, WN, RING>;
@@ -835,8 +1220,65 @@ int launch_tile(const Problem& p, const Launch& l) {
   } else {
     k.vec_out = out_vec_ok<OUT>(p);
   }
-  const int64_t grid = (int64_t)k.tiles_m * k.tiles_n * p.G * k.splits;
+  const int64_t units = (int64_t)k.tiles_m * k.tiles_n * p.G * k.splits;
+  k.units = (int)units;
+  static std::atomic<int> slots[64];
+  const int64_t grid = tile_grid(
+      units, reinterpret_cast<const void*>(&tile_kernel<OP, OUT, WM, WN, RING, PK>), T::NT, slots);
   hipLaunchKernelGGL((tile_kernel<OP, OUT, WM, WN, RING, PK>), dim3((unsigned)grid), dim3(T::NT), 0, s, k);
+  if (check_launch()) return 1;
+  if (k.splits > 1) {
+    const int64_t total = (int64_t)rows * p.N * p.G;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL((splitk_reduce<OP, OUT>), dim3((unsigned)blocks), dim3(256), 0, s, k);
+    return check_launch();
+  }
+  return 0;
+}
+
+// The wide-wave kernel (four waves of 128 x 128, int8 / mx).
+template <int OP, int OUT, bool PK>
+int launch_tile4(const Problem& p, const Launch& l) {
+  using T = Mainloop4<OP, PK>;
+  const int row_begin = l.row_begin, row_end = l.row_end;
+  int split = l.split;
+  void* ws = l.ws;
+  KArgs k;
+  k.p = p;
+  if (!set_packed<PK>(k, l)) return 1;
+  k.row_begin = row_begin;
+  k.row_end = row_end;
+  const int rows = row_end - row_begin;
+  k.tiles_m = (rows + T::BM - 1) / T::BM;
+  k.tiles_n = (p.N + T::BN - 1) / T::BN;
+  const int KB = p.K / kBlockK;
+  hipStream_t s = (hipStream_t)l.stream;
+  if (KB == 0) {              // empty sum: the output is zero
+    k.ws = ws;
+    k.splits = 1;
+    k.kb_per_split = 0;
+    k.vec_out = 0;
+    hipLaunchKernelGGL(zero_out, dim3(1024), dim3(256), 0, s, k);
+    return check_launch();
+  }
+  k.ws = ws;
+  if (split < 1) split = 1;
+  if (split > KB) split = KB;
+  k.kb_per_split = (KB + split - 1) / split;
+  k.splits = (KB + k.kb_per_split - 1) / k.kb_per_split;
+  if (k.splits > 1) {
+    // workspace rows are N elements of 4 bytes
+    k.vec_out = aligned16(ws) && p.N % 4 == 0;
+  } else {
+    k.vec_out = out_vec_ok<OUT>(p);
+  }
+  const int64_t units = (int64_t)k.tiles_m * k.tiles_n * p.G * k.splits;
+  k.units = (int)units;
+  static std::atomic<int> slots[64];
+  const int64_t grid = tile_grid(units, reinterpret_cast<const void*>(&tile4_kernel<OP, OUT, PK>),
+                                 T::NT, slots);
+  hipLaunchKernelGGL((tile4_kernel<OP, OUT, PK>), dim3((unsigned)grid), dim3(T::NT), 0, s, k);
   if (check_launch()) return 1;
   if (k.splits > 1) {
     const int64_t total = (int64_t)rows * p.N * p.G;
@@ -866,20 +1308,9 @@ int launch_sk(const Problem& p, const Launch& l) {
     return launch_tile<OP, OUT, WM, WN, RING, PK>(p, l);
   // co-resident capacity of this kernel on the current device (cached)
   static std::atomic<int> cap_cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
-  int cap = cap_cache[dev].load(std::memory_order_relaxed);
-  if (cap == 0) {
-    int cus = 0, occ = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return 1;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &occ, reinterpret_cast<const void*>(&sk_kernel<OP, OUT, WM, WN, RING, PK>), T::NT,
-            0) != hipSuccess)
-      return 1;
-    cap = cus * (occ > 0 ? occ : 1);
-    cap_cache[dev].store(cap, std::memory_order_relaxed);
-  }
+  const int cap = device_slots(reinterpret_cast<const void*>(&sk_kernel<OP, OUT, WM, WN, RING, PK>),
+                               T::NT, cap_cache);
+  if (cap <= 0) return 1;
   KArgs k;
   k.p = p;
   if (!set_packed<PK>(k, l)) return 1;
@@ -890,6 +1321,7 @@ int launch_sk(const Problem& p, const Launch& l) {
   k.tiles_n = (p.N + T::BN - 1) / T::BN;
   k.splits = 1;
   k.kb_per_split = KB;
+  k.units = 0;
   k.vec_out = out_vec_ok<OUT>(p);
   hipStream_t s = (hipStream_t)l.stream;
   k.ws = l.ws;
@@ -910,19 +1342,25 @@ int launch_sk(const Problem& p, const Launch& l) {
 // Entry used by the variant table: one kernel configuration for one
 // (operation, output type).  Instantiated below for the pair this
 // translation unit is compiled for.
-template <int OP, int OUT, int WM, int WN, int RING, bool SK, bool PK>
+template <int OP, int OUT, int WM, int WN, int RING, bool SK, bool PK, int KIND>
 int launch_kernel(const Problem& p, const Launch& l) {
   // the int8 K loop reads no scales: packed variants run the plain kernel
   constexpr bool PKX = PK && OP != BSMM_OP_INT8_ROWWISE;
-  if constexpr (SK)
+  if constexpr (KIND == 1) {
+    // wide waves for int8 / mx; blockwise runs the 256 x 256 eight-wave kernel
+    if constexpr (OP == BSMM_OP_FP8_BLOCKWISE)
+      return launch_tile<OP, OUT, 4, 2, 5, PKX>(p, l);
+    else
+      return launch_tile4<OP, OUT, PKX>(p, l);
+  } else if constexpr (SK)
     return launch_sk<OP, OUT, WM, WN, RING, PKX>(p, l);
   else
     return launch_tile<OP, OUT, WM, WN, RING, PKX>(p, l);
 }
 
 #if defined(BSMM_TU_OP) && defined(BSMM_TU_OUT)
-#define BSMM_VARIANT(NAME, TM, TN, WM, WN, RING, SK, PK, WPC, UNPACKED)                     \
-  template int launch_kernel<BSMM_TU_OP, BSMM_TU_OUT, WM, WN, RING, SK, PK>(              \
+#define BSMM_VARIANT(NAME, TM, TN, WM, WN, RING, SK, PK, WPC, UNPACKED, KIND)               \
+  template int launch_kernel<BSMM_TU_OP, BSMM_TU_OUT, WM, WN, RING, SK, PK, KIND>(        \
       const Problem&, const Launch&);
 #include "bsmm_variants.inc"
 #undef BSMM_VARIANT

@@ -6,23 +6,23 @@
 namespace bsmm {
 namespace {
 
-template <int WM, int WN, int RING, bool SK, bool PK>
+template <int WM, int WN, int RING, bool SK, bool PK, int KIND>
 int launch_variant(const Problem& p, const Launch& l) {
   switch (p.op) {
     case BSMM_OP_INT8_ROWWISE:
       if (p.out_dtype == BSMM_I32)
-        return launch_kernel<BSMM_OP_INT8_ROWWISE, BSMM_I32, WM, WN, RING, SK, PK>(p, l);
+        return launch_kernel<BSMM_OP_INT8_ROWWISE, BSMM_I32, WM, WN, RING, SK, PK, KIND>(p, l);
       if (p.out_dtype == BSMM_F32)
-        return launch_kernel<BSMM_OP_INT8_ROWWISE, BSMM_F32, WM, WN, RING, SK, PK>(p, l);
-      return launch_kernel<BSMM_OP_INT8_ROWWISE, BSMM_BF16, WM, WN, RING, SK, PK>(p, l);
+        return launch_kernel<BSMM_OP_INT8_ROWWISE, BSMM_F32, WM, WN, RING, SK, PK, KIND>(p, l);
+      return launch_kernel<BSMM_OP_INT8_ROWWISE, BSMM_BF16, WM, WN, RING, SK, PK, KIND>(p, l);
     case BSMM_OP_FP8_BLOCKWISE:
       if (p.out_dtype == BSMM_F32)
-        return launch_kernel<BSMM_OP_FP8_BLOCKWISE, BSMM_F32, WM, WN, RING, SK, PK>(p, l);
-      return launch_kernel<BSMM_OP_FP8_BLOCKWISE, BSMM_BF16, WM, WN, RING, SK, PK>(p, l);
+        return launch_kernel<BSMM_OP_FP8_BLOCKWISE, BSMM_F32, WM, WN, RING, SK, PK, KIND>(p, l);
+      return launch_kernel<BSMM_OP_FP8_BLOCKWISE, BSMM_BF16, WM, WN, RING, SK, PK, KIND>(p, l);
     default:
       if (p.out_dtype == BSMM_F32)
-        return launch_kernel<BSMM_OP_FP8_MX_BMM, BSMM_F32, WM, WN, RING, SK, PK>(p, l);
-      return launch_kernel<BSMM_OP_FP8_MX_BMM, BSMM_BF16, WM, WN, RING, SK, PK>(p, l);
+        return launch_kernel<BSMM_OP_FP8_MX_BMM, BSMM_F32, WM, WN, RING, SK, PK, KIND>(p, l);
+      return launch_kernel<BSMM_OP_FP8_MX_BMM, BSMM_BF16, WM, WN, RING, SK, PK, KIND>(p, l);
   }
 }
 
@@ -31,8 +31,8 @@ constexpr unsigned kAllOps = 7u;
 // name, tile_m, tile_n, ops, masked tail, persistent, packed scales,
 // workgroups per CU, unpacked sibling, launch
 const Variant kVariants[] = {
-#define BSMM_VARIANT(NAME, TM, TN, WM, WN, RING, SK, PK, WPC, UNPACKED) \
-  {NAME, TM, TN, kAllOps, true, SK, PK, WPC, UNPACKED, launch_variant<WM, WN, RING, SK, PK>},
+#define BSMM_VARIANT(NAME, TM, TN, WM, WN, RING, SK, PK, WPC, UNPACKED, KIND) \
+  {NAME, TM, TN, kAllOps, true, SK, PK, WPC, UNPACKED, launch_variant<WM, WN, RING, SK, PK, KIND>},
 #include "bsmm_variants.inc"
 #undef BSMM_VARIANT
 };

@@ -22,10 +22,10 @@ from tests.gpu_util import (DEV, Forced, as_f64, check_blockwise, check_int8, ch
 pytestmark = pytest.mark.gpu
 
 VARIANTS = ["t256x256", "t256x128", "t128x256", "t128x128", "t64x256", "t64x128",
-            "t256x256p", "t256x128p", "t128x256p",
+            "t256x256p", "t256x128p", "t128x256p", "w256x256", "w256x256p",
             "t256x256sk", "t256x128sk", "t128x128sk", "t256x256skp"]
 SK_VARIANTS = ["t256x256sk", "t256x128sk", "t128x128sk", "t256x256skp"]
-PACKED_VARIANTS = ["t256x256p", "t256x128p", "t128x256p", "t256x256skp"]
+PACKED_VARIANTS = ["t256x256p", "t256x128p", "t128x256p", "t256x256skp", "w256x256p"]
 
 
 @pytest.fixture(autouse=True)
