@@ -154,13 +154,13 @@ Plan make_plan(bsmm_op op, int G, int M, int N, int K, bsmm_dtype dt,
     if (!o.variant.empty() || o.split > 0) {
       Plan h = make_plan_heuristic(op, G, M, N, K, dt);
       const Variant* v = o.variant.empty() ? h.v : find_variant(o.variant.c_str());
-      if (!v) v = h.v;
+      if (!v || (v->max_m && M > v->max_m)) v = h.v;
       pl.v = v;
       pl.split = o.split > 0 ? o.split : (o.variant.empty() ? h.split : 1);
       if (pl.split > KB) pl.split = KB > 0 ? KB : 1;
       if (o.variant.empty() && o.split <= 0) { pl.tail = h.tail; pl.m_split = h.m_split; }
       pl.source = 3;
-      if (pl.v->persistent) pl.split = 1;
+      if (pl.v->persistent || pl.v->max_m) pl.split = 1;
       fit_workspace(pl, op, G, M, N, K, dt, workspace_bytes);
       return pl;
     }
@@ -175,11 +175,16 @@ Plan make_plan(bsmm_op op, int G, int M, int N, int K, bsmm_dtype dt,
     if (e.M == M) { best = &e; pl.source = 0; break; }
     if (e.M > M && (!best || e.M < best->M)) { best = &e; pl.source = 1; }
   }
-  if (best) {
-    pl.v = find_variant(best->variant);
+  // a tuned entry is used only where its kernels take this M (the skinny
+  // kernel takes M <= 16 in a single launch, so it is never a tail)
+  const Variant* bv = best ? find_variant(best->variant) : nullptr;
+  if (bv && bv->max_m && M > bv->max_m) bv = nullptr;
+  if (bv) {
+    pl.v = bv;
     pl.split = best->split;
-    if (pl.source == 0 && best->tail_variant[0] && best->m_split > 0 && best->m_split < M) {
-      pl.tail = find_variant(best->tail_variant);
+    const Variant* tv = best->tail_variant[0] ? find_variant(best->tail_variant) : nullptr;
+    if (pl.source == 0 && tv && !tv->max_m && best->m_split > 0 && best->m_split < M) {
+      pl.tail = tv;
       pl.m_split = best->m_split;
       pl.tail_split = best->tail_split > 0 ? best->tail_split : 1;
     }
@@ -189,7 +194,7 @@ Plan make_plan(bsmm_op op, int G, int M, int N, int K, bsmm_dtype dt,
     pl.source = 2;
   }
   if (pl.split > KB) pl.split = KB > 0 ? KB : 1;
-  if (pl.v->persistent) pl.split = 1;
+  if (pl.v->persistent || pl.v->max_m) pl.split = 1;
   fit_workspace(pl, op, G, M, N, K, dt, workspace_bytes);
   return pl;
 }
@@ -199,8 +204,13 @@ Plan make_plan_heuristic(bsmm_op op, int G, int M, int N, int K, bsmm_dtype dt) 
   Plan pl;
   // fp8 with enough rows: the K loop reads scale_a repacked once per call
   // (one small load per wave and K block instead of one per row group)
-  const bool pack = op != BSMM_OP_INT8_ROWWISE && (int64_t)G * M >= 1024;
+  const bool pack = op != BSMM_OP_INT8_ROWWISE && M > 128 && (int64_t)G * M >= 1024;
   const char* name;
+  if (M <= 16) {
+    // decode-sized: one pass over B with K split inside each workgroup
+    pl.v = find_variant("s16x16");
+    return pl;
+  }
   if (M <= 64) name = N % 256 == 0 ? "t64x256" : "t64x128";
   else if (M <= 128) name = N % 256 == 0 ? (pack ? "t128x256p" : "t128x256") : "t128x128";
   else if (N % 256 == 0) name = pack ? "t256x256p" : "t256x256";

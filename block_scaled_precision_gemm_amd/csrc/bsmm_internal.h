@@ -63,6 +63,7 @@ struct Variant {
   bool packed_scales;   // fp8: repacks scale_a into the workspace first
   int wg_per_cu;        // workgroups one CU holds (LDS / registers)
   const char* unpacked; // the same kernel without packed scales (or null)
+  int max_m;            // largest M the kernel takes in one launch (0: any)
   LaunchFn launch;
 };
 

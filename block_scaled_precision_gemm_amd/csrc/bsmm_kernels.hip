@@ -272,6 +272,11 @@ struct Mainloop {
   using acc_t = typename OpT<OP>::acc_t;
   static constexpr int TI = T::TI, TJ = T::TJ;
   static constexpr int kLoadsPerBlock = T::LA + T::LB;   // per wave
+#ifndef BSMM_B_PREFETCH
+#define BSMM_B_PREFETCH 1
+#endif
+  // B tiles are read this many columns ahead of their use
+  static constexpr int BPF = BSMM_B_PREFETCH;
 
   __device__ __forceinline__ static void run(const KArgs& k, uint8_t* smem, int g,
                                              int row0, int col0, int kb0, int nkb,
@@ -395,7 +400,7 @@ struct Mainloop {
     const uint8_t* SA = smem;
     const uint8_t* SB = smem;
     i32x8 af[TI];
-    i32x8 bcur;
+    i32x8 bcur, bnx;     // B tiles of the current and the next column
     auto read_b = [&](int j) {
       const i32x4 lo = *(const i32x4*)(SB + b_off0 + j * 2048);
       const i32x4 hi = *(const i32x4*)(SB + b_off1 + j * 2048);
@@ -405,6 +410,7 @@ struct Mainloop {
       SA = smem + slot_a * SLOT;
       SB = smem + slot_b * SLOT;
       bcur = read_b(0);
+      if constexpr (BPF == 2) bnx = read_b(1);
   #pragma unroll
       for (int i = 0; i < TI; ++i) {
         const i32x4 lo = *(const i32x4*)(SA + a_off0 + i * 2048);
@@ -422,8 +428,9 @@ struct Mainloop {
     auto columns = [&](auto refill) {
   #pragma unroll
       for (int j = 0; j < TJ; ++j) {
+        // B tile of column j + BPF read while column j computes
         i32x8 bnext = bcur;
-        if (j + 1 < TJ) bnext = read_b(j + 1);
+        if (j + BPF < TJ) bnext = read_b(j + BPF);
         refill(j);
   #pragma unroll
         for (int i = 0; i < TI; ++i) {
@@ -450,7 +457,12 @@ struct Mainloop {
             acc[i][j] = mfma_mx(bcur, af[i], acc[i][j], ws_cur, i, xs_cur);
           }
         }
-        bcur = bnext;
+        if constexpr (BPF == 2) {
+          bcur = bnx;
+          bnx = bnext;
+        } else {
+          bcur = bnext;
+        }
       }
       if constexpr (OP == BSMM_OP_FP8_BLOCKWISE) {
   #pragma unroll
@@ -472,7 +484,7 @@ struct Mainloop {
         for (int i = 0; i < TI; ++i) {
           __builtin_amdgcn_sched_group_barrier(kMfma, MF, 0);
           if (i == 0) {
-            if (j + 1 < TJ) __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
+            if (j + BPF < TJ) __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
             const int nl = kLoadsPerBlock * (j + 1) / TJ - kLoadsPerBlock * j / TJ;
             if (nl == 1) __builtin_amdgcn_sched_group_barrier(kVmemRead, 1, 0);
             if (nl == 2) __builtin_amdgcn_sched_group_barrier(kVmemRead, 2, 0);
@@ -608,6 +620,125 @@ __device__ __forceinline__ void store_splitk(const KArgs& k, int s, int g, int r
       }
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Skinny kernel for M <= 16 (decode-sized calls, bound by reading B once).
+// One workgroup per 16 output columns of one batch; its four waves split
+// the K blocks four ways.  Each wave streams its B fragments (16 rows x 32
+// bytes per lane-group, 2 KB per K block) and the A fragment (the <= 16 rows
+// of A, zero-filled past M by the buffer range) straight from memory into
+// registers, SPF K blocks ahead (a template argument) -- no LDS staging, every B byte is used once
+// -- and does one 16 x 16 x 128 MFMA step per K block with the operation's
+// scale handling.  The four partial tiles are added in wave order in LDS and
+// wave 0 runs the epilogue.
+// ---------------------------------------------------------------------------
+template <int OP, int OUT, int SPF>
+__global__ void __launch_bounds__(256)
+skinny_kernel(const KArgs k) {
+  using acc_t = typename OpT<OP>::acc_t;
+  __shared__ acc_t red[4][kWave];
+  const Problem& p = k.p;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int ntiles = (p.N + 15) / 16;
+  const int g = blockIdx.x / ntiles;
+  const int n0 = (blockIdx.x - g * ntiles) * 16;
+  const int KB = p.K / kBlockK;
+  const int kbA = wave * KB / 4, kbB = (wave + 1) * KB / 4;
+  const int r16 = lane & 15;             // B row n0 + r16, A row r16
+  const uint32_t co = (uint32_t)(lane >> 4) * 32;
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(
+      p.b + (int64_t)g * p.b_sg + (int64_t)n0 * p.ldb, (uint64_t)(p.N - n0) * p.ldb);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(
+      p.a + (int64_t)g * p.a_sg, (uint64_t)(p.M - 1) * p.lda + (uint64_t)p.K);
+  const uint32_t wrow = (uint32_t)r16 * (uint32_t)p.ldb + co;
+  const bool xlive = r16 < p.M;
+  const uint32_t xrow = (uint32_t)r16 * (uint32_t)p.lda + co;
+  const int m_s = min(r16, p.M - 1);     // scale row (rows past M: any valid one)
+  const int nb = n0 / kBlockK;
+
+  i32x8 wf[SPF], xf[SPF];
+  float s_blk[SPF];                      // blockwise: sa * sb
+  int xs_blk[SPF], ws_blk[SPF];          // mx: e8m0 bytes
+  auto load = [&](int kb, int slot) {
+    const uint32_t kbyte = (uint32_t)kb * kBlockK;
+    const i32x4 wl = __builtin_amdgcn_raw_buffer_load_b128(rw, wrow + kbyte, 0, 0);
+    const i32x4 wh = __builtin_amdgcn_raw_buffer_load_b128(rw, wrow + kbyte + 16, 0, 0);
+    const uint32_t xo = xlive ? xrow + kbyte : kOob;   // rows past M read as zero
+    const i32x4 xl = __builtin_amdgcn_raw_buffer_load_b128(rx, xo, 0, 0);
+    const i32x4 xh = __builtin_amdgcn_raw_buffer_load_b128(rx, xlive ? xo + 16 : kOob, 0, 0);
+    wf[slot] = i32x8{wl.x, wl.y, wl.z, wl.w, wh.x, wh.y, wh.z, wh.w};
+    xf[slot] = i32x8{xl.x, xl.y, xl.z, xl.w, xh.x, xh.y, xh.z, xh.w};
+    if constexpr (OP == BSMM_OP_FP8_MX_BMM) {
+      xs_blk[slot] = ((const uint8_t*)p.sa)[(int64_t)g * p.sa_sg + (int64_t)m_s * p.sa_m + kb];
+      ws_blk[slot] = ((const uint8_t*)p.sb)[(int64_t)g * p.sb_sg + (int64_t)nb * p.sb_n + kb];
+    } else if constexpr (OP == BSMM_OP_FP8_BLOCKWISE) {
+      s_blk[slot] = ((const float*)p.sa)[(int64_t)m_s * p.sa_m + (int64_t)kb * p.sa_kb] *
+                    ((const float*)p.sb)[(int64_t)kb * p.sb_kb + (int64_t)nb * p.sb_n];
+    }
+  };
+  acc_t acc = acc_t{0, 0, 0, 0};
+  auto step = [&](int slot) {
+    const i32x8 w = wf[slot], x = xf[slot];
+    if constexpr (OP == BSMM_OP_INT8_ROWWISE) {
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(i32x4{w[0], w[1], w[2], w[3]},
+                                                   i32x4{x[0], x[1], x[2], x[3]}, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(i32x4{w[4], w[5], w[6], w[7]},
+                                                   i32x4{x[4], x[5], x[6], x[7]}, acc, 0, 0, 0);
+    } else if constexpr (OP == BSMM_OP_FP8_BLOCKWISE) {
+      const f32x4 pp = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+          w, x, f32x4{0, 0, 0, 0}, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(s_blk[slot], pp[r], acc[r]);
+    } else {
+      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w, x, acc, 0, 0, 0, ws_blk[slot], 0,
+                                                             xs_blk[slot]);
+    }
+  };
+#pragma unroll
+  for (int s0 = 0; s0 < SPF; ++s0)
+    if (kbA + s0 < kbB) load(kbA + s0, s0);
+  for (int b = kbA; b < kbB; b += SPF) {
+#pragma unroll
+    for (int s0 = 0; s0 < SPF; ++s0) {
+      if (b + s0 < kbB) {
+        step(s0);
+        if (b + s0 + SPF < kbB) load(b + s0 + SPF, s0);
+      }
+    }
+  }
+  // the four waves' partial tiles, added in wave order
+  red[wave][lane] = acc;
+  __syncthreads();
+  if (wave != 0) return;
+  acc_t sum = red[0][lane];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) {
+    const acc_t v = red[w][lane];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sum[r] += v[r];
+  }
+  // lane: output row r16, columns n0 + 4 (lane / 16) .. +3
+  const int m = r16;
+  const int n = n0 + 4 * (lane >> 4);
+  const int nvalid = min(4, p.N - n);
+  if (m >= p.M || nvalid <= 0) return;
+  float y[4];
+  int yi[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    if constexpr (OP == BSMM_OP_INT8_ROWWISE) {
+      yi[r] = sum[r];
+      if constexpr (OUT != BSMM_I32)
+        y[r] = __fmul_rn(__fmul_rn((float)sum[r], ((const float*)p.sa)[(int64_t)m * p.sa_m]),
+                         ((const float*)p.sb)[(int64_t)min(n + r, p.N - 1) * p.sb_n]);
+    } else {
+      y[r] = sum[r];
+    }
+  }
+  store4<OUT>((uint8_t*)p.out, (int64_t)g * p.o_sg + (int64_t)m * p.ldo + n, y, yi,
+              k.vec_out != 0, nvalid);
 }
 
 // Epilogue through LDS.  Stored straight from the MFMA layout, a wave's
@@ -1342,11 +1473,40 @@ int launch_sk(const Problem& p, const Launch& l) {
 // Entry used by the variant table: one kernel configuration for one
 // (operation, output type).  Instantiated below for the pair this
 // translation unit is compiled for.
+// Skinny launch (M <= 16): one workgroup per 16 columns of each batch.
+template <int OP, int OUT, int SPF>
+int launch_skinny(const Problem& p, const Launch& l) {
+  if (p.M > 16 || l.row_begin != 0 || l.row_end != p.M) return 1;
+  KArgs k;
+  k.p = p;
+  k.row_begin = 0;
+  k.row_end = p.M;
+  k.psa = nullptr;
+  k.psa_ld = 0;
+  k.ws = nullptr;
+  k.splits = 1;
+  k.kb_per_split = p.K / kBlockK;
+  k.units = 0;
+  k.tiles_m = 1;
+  k.tiles_n = (p.N + 15) / 16;
+  k.vec_out = out_vec_ok<OUT>(p);
+  hipStream_t s = (hipStream_t)l.stream;
+  if (p.K / kBlockK == 0) {
+    hipLaunchKernelGGL(zero_out, dim3(1024), dim3(256), 0, s, k);
+    return check_launch();
+  }
+  const int64_t grid = (int64_t)k.tiles_n * p.G;
+  hipLaunchKernelGGL((skinny_kernel<OP, OUT, SPF>), dim3((unsigned)grid), dim3(256), 0, s, k);
+  return check_launch();
+}
+
 template <int OP, int OUT, int WM, int WN, int RING, bool SK, bool PK, int KIND>
 int launch_kernel(const Problem& p, const Launch& l) {
   // the int8 K loop reads no scales: packed variants run the plain kernel
   constexpr bool PKX = PK && OP != BSMM_OP_INT8_ROWWISE;
-  if constexpr (KIND == 1) {
+  if constexpr (KIND == 2) {
+    return launch_skinny<OP, OUT, RING>(p, l);
+  } else if constexpr (KIND == 1) {
     // wide waves for int8 / mx; blockwise runs the 256 x 256 eight-wave kernel
     if constexpr (OP == BSMM_OP_FP8_BLOCKWISE)
       return launch_tile<OP, OUT, 4, 2, 5, PKX>(p, l);

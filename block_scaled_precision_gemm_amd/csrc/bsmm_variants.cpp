@@ -29,10 +29,12 @@ int launch_variant(const Problem& p, const Launch& l) {
 constexpr unsigned kAllOps = 7u;
 
 // name, tile_m, tile_n, ops, masked tail, persistent, packed scales,
-// workgroups per CU, unpacked sibling, launch
+// workgroups per CU, unpacked sibling, largest M (the skinny kernel: 16),
+// launch
 const Variant kVariants[] = {
 #define BSMM_VARIANT(NAME, TM, TN, WM, WN, RING, SK, PK, WPC, UNPACKED, KIND) \
-  {NAME, TM, TN, kAllOps, true, SK, PK, WPC, UNPACKED, launch_variant<WM, WN, RING, SK, PK, KIND>},
+  {NAME, TM, TN, kAllOps, true, SK, PK, WPC, UNPACKED, KIND == 2 ? 16 : 0,                      \
+   launch_variant<WM, WN, RING, SK, PK, KIND>},
 #include "bsmm_variants.inc"
 #undef BSMM_VARIANT
 };

@@ -145,14 +145,33 @@ def test_plan_heuristics():
     q = bsmm.bsmm_query_plan
     p = q(bsmm.OP_FP8_BLOCKWISE, 1, 16640, 5120, 8192, "bf16")
     assert p["tile_m"] in (128, 256) and p["split_k"] >= 1
-    small = q(bsmm.OP_FP8_MX_BMM, 8, 1, 1024, 4096, "bf16")
+    small = q(bsmm.OP_FP8_MX_BMM, 8, 40, 1024, 4096, "bf16")
     assert small["tile_m"] == 64 and small["split_k"] > 1
-    assert small["workspace"] == small["split_k"] * 8 * 1 * 1024 * 4
+    assert small["workspace"] == small["split_k"] * 8 * 40 * 1024 * 4
     # without workspace the same problem runs unsplit
-    nows = q(bsmm.OP_FP8_MX_BMM, 8, 1, 1024, 4096, "bf16", workspace_bytes=0)
+    nows = q(bsmm.OP_FP8_MX_BMM, 8, 40, 1024, 4096, "bf16", workspace_bytes=0)
     assert nows["split_k"] == 1 and nows["workspace"] == 0
-    assert bsmm.bsmm_workspace_bytes(bsmm.OP_FP8_MX_BMM, 8, 1, 1024, 4096, "bf16") == \
+    assert bsmm.bsmm_workspace_bytes(bsmm.OP_FP8_MX_BMM, 8, 40, 1024, 4096, "bf16") == \
         small["workspace"]
+
+
+def test_plan_skinny_m():
+    """M <= 16 runs the skinny kernel for every operation, unsplit and
+    without workspace; M = 17 does not, and forcing it on a taller M falls
+    back to the regular plan."""
+    q = bsmm.bsmm_query_plan
+    for op in (bsmm.OP_INT8_ROWWISE, bsmm.OP_FP8_BLOCKWISE, bsmm.OP_FP8_MX_BMM):
+        for M in (1, 16):
+            p = q(op, 8 if op == bsmm.OP_FP8_MX_BMM else 1, M, 1024, 4096, "bf16")
+            assert p["variant"] == "s16x16" and p["split_k"] == 1 and p["workspace"] == 0, p
+            assert p["m_split"] == 0
+        assert q(op, 1, 17, 1024, 4096, "bf16")["variant"] != "s16x16"
+    try:
+        bsmm.bsmm_set_override("s16x16", 4)
+        assert q(bsmm.OP_INT8_ROWWISE, 1, 8, 1024, 4096, "bf16")["split_k"] == 1
+        assert q(bsmm.OP_INT8_ROWWISE, 1, 40, 1024, 4096, "bf16")["variant"] != "s16x16"
+    finally:
+        bsmm.bsmm_set_override(None, 0)
 
 
 def test_override_roundtrip():

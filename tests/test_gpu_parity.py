@@ -301,3 +301,61 @@ def test_whole_rounds_bulk_with_split_k_tail():
     check_blockwise(q, "bf16", y, rows=rows)
     y2 = run_blockwise(q, "bf16")
     assert np.array_equal(host_out(y), host_out(y2))
+
+
+# ------------------------------------------------------------- skinny M ----
+
+@pytest.mark.parametrize("M", [1, 5, 16])
+def test_skinny_all_ops(M):
+    """The M <= 16 kernel (K split over the four waves of a workgroup, B
+    read straight into registers): the default plan for these M, with K
+    blocks not a multiple of four, a ragged int8 N and several mx batches in
+    both layouts."""
+    plan = bsmm.bsmm_query_plan(bsmm.OP_FP8_MX_BMM, 3, M, 384, 640, "bf16")
+    assert plan["variant"] == "s16x16", plan
+    p = int8_rowwise_inputs(M, 200, 640, 701 + M)
+    for dt in ("i32", "f32", "bf16"):
+        say(f"skinny int8 {dt} M={M} N=200 K=640")
+        check_int8(p, dt, run_int8(p, dt))
+    q = fp8_blockwise_inputs(M, 384, 896, 711 + M)
+    for dt in ("bf16", "f32"):
+        say(f"skinny blockwise {dt} M={M} N=384 K=896")
+        check_blockwise(q, dt, run_blockwise(q, dt))
+    for layout in ("m_major", "batch_first"):
+        r = fp8_mx_bmm_inputs(3, M, 384, 640, 721 + M, layout=layout, dist="t")
+        say(f"skinny mx {layout} G=3 M={M} N=384 K=640")
+        check_mx(r, "bf16", run_mx(r, "bf16"))
+        check_mx(r, "f32", run_mx(r, "f32"))
+
+
+def test_skinny_short_k_and_guard_bands():
+    """One and two K blocks (three or two waves with no K work) and a
+    strided output inside a sentinel buffer."""
+    for K in (128, 256):
+        p = int8_rowwise_inputs(3, 130, K, 731)
+        say(f"skinny int8 K={K}")
+        check_int8(p, "i32", run_int8(p, "i32"))
+        r = fp8_mx_bmm_inputs(2, 9, 256, K, 732, layout="m_major")
+        say(f"skinny mx K={K}")
+        check_mx(r, "f32", run_mx(r, "f32"))
+    q = fp8_blockwise_inputs(7, 256, 512, 733)
+    big = torch.full((12, 512), 7.0, dtype=torch.float32, device=DEV)
+    view = big[2:9, 128:384]
+    say("skinny blockwise guard bands")
+    run_blockwise(q, "f32", out=view)
+    check_blockwise(q, "f32", view)
+    h = host_out(big)
+    mask = np.ones_like(h, dtype=bool)
+    mask[2:9, 128:384] = False
+    assert (h[mask] == 7.0).all()
+
+
+def test_skinny_forced_on_tall_m_falls_back():
+    """Forcing the skinny kernel on M > 16 takes the regular plan."""
+    p = int8_rowwise_inputs(40, 256, 512, 741)
+    say("skinny forced on M=40")
+    with Forced("s16x16", 0):
+        plan = bsmm.bsmm_query_plan(bsmm.OP_INT8_ROWWISE, 1, 40, 256, 512, "i32")
+        y = run_int8(p, "i32")
+    assert plan["variant"] != "s16x16", plan
+    check_int8(p, "i32", y)
