@@ -241,9 +241,11 @@ Plan make_plan_heuristic(bsmm_op op, int G, int M, int N, int K, bsmm_dtype dt) 
       const int64_t tail_tiles = (int64_t)((M - m_split + bm - 1) / bm) * per_row;
       int s = (int)(kPlanCUs / tail_tiles);     // tail_tiles * s fits one round
       if (s > KB / 4) s = KB / 4;
+      if (const char* e = getenv("BSMM_TAIL_SPLIT")) { const int c = atoi(e); if (c > 0 && s > c) s = c; }
       if (s >= 2) {
         pl.m_split = m_split;
         pl.tail = pl.v;
+        if (const char* e = getenv("BSMM_TAIL_VARIANT")) if (const Variant* tv = find_variant(e)) pl.tail = tv;
         pl.tail_split = s;
         return pl;
       }

@@ -169,13 +169,20 @@ struct Tile {
   static constexpr int SLOT = A_BYTES > B_BYTES ? A_BYTES : B_BYTES;
   static constexpr int NSLOT = RING;
   static constexpr int LDS = NSLOT * SLOT;
-  // direct-to-LDS loads per thread for one A / one B half-stage
-  static constexpr int LA = BM / 8 / NW, LB = BN / 8 / NW;
+#ifndef BSMM_LOADER_SPLIT
+#define BSMM_LOADER_SPLIT 1
+#endif
+  // Waves that issue the tile loads: the first half, one per SIMD, so that
+  // while a loading wave waits to issue a load its SIMD sibling keeps the
+  // matrix core busy.
+  static constexpr int NLD = BSMM_LOADER_SPLIT && NW >= 8 ? NW / 2 : NW;
+  // direct-to-LDS loads per loading wave for one A / one B half-stage
+  static constexpr int LA = BM / 8 / NLD, LB = BN / 8 / NLD;
   // loads of the half-stages after block c's pair that may still be in
   // flight when block c starts: h = 2c+2 .. 2c+NSLOT-3 (A, B, A, ...)
   static constexpr int WAIT = ((NSLOT - 3) / 2) * LA + ((NSLOT - 4) / 2) * LB;
   static_assert(NSLOT >= 4, "the ring needs at least four slots");
-  static_assert((BM / 8) % NW == 0 && (BN / 8) % NW == 0, "loader split");
+  static_assert((BM / 8) % NLD == 0 && (BN / 8) % NLD == 0, "loader split");
   static_assert(WAIT < 64, "vmcnt range");
   static_assert(TI == 4, "packed scales hold four rows per lane");
 };
@@ -192,7 +199,11 @@ __device__ __forceinline__ void load_row_group(__amdgpu_buffer_rsrc_t rs, uint8_
   const int q = t * NW + wave;
   const int r = q * 8 + (lane >> 3);
   const int c = (lane & 7) ^ swz(r);
-  const uint32_t vo = live ? (uint32_t)r * ld + kbyte + ((uint32_t)c << 4) : kOob;
+  // dead: an offset past any range, as a max with a uniform floor rather
+  // than a per-lane select (which the compiler may turn into a branch that
+  // splits the K loop's scheduling region)
+  const uint32_t floor = live ? 0u : kOob;
+  const uint32_t vo = max((uint32_t)r * ld + kbyte + ((uint32_t)c << 4), floor);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + q * 1024), 16, vo, 0, 0, 0);
 }
 
@@ -272,11 +283,6 @@ struct Mainloop {
   using acc_t = typename OpT<OP>::acc_t;
   static constexpr int TI = T::TI, TJ = T::TJ;
   static constexpr int kLoadsPerBlock = T::LA + T::LB;   // per wave
-#ifndef BSMM_B_PREFETCH
-#define BSMM_B_PREFETCH 1
-#endif
-  // B tiles are read this many columns ahead of their use
-  static constexpr int BPF = BSMM_B_PREFETCH;
 
   __device__ __forceinline__ static void run(const KArgs& k, uint8_t* smem, int g,
                                              int row0, int col0, int kb0, int nkb,
@@ -304,8 +310,8 @@ struct Mainloop {
       uint8_t* dst = smem + slot * SLOT;
       const bool live = h < 2 * nkb;
       const uint32_t kbyte = (uint32_t)(kb0 + (h >> 1)) * kBlockK;
-      if (h & 1) load_row_group<NW>(rb, dst, ldb, kbyte, wave, lane, live, t);
-      else load_row_group<NW>(ra, dst, lda, kbyte, wave, lane, live, t);
+      if (h & 1) load_row_group<T::NLD>(rb, dst, ldb, kbyte, wave, lane, live, t);
+      else load_row_group<T::NLD>(ra, dst, lda, kbyte, wave, lane, live, t);
     };
     auto issue_half = [&](int h, int slot) {
       const int n = (h & 1) ? T::LB : T::LA;
@@ -387,7 +393,7 @@ struct Mainloop {
     auto use_scales = [&]() {
       if constexpr (OP == BSMM_OP_FP8_MX_BMM) {
         xs_cur = xs_nxt;
-        ws_cur = ws_nxt;
+        ws_cur = __builtin_amdgcn_readfirstlane(ws_nxt);   // wave-uniform; taken here, not sunk into the next iteration
       } else if constexpr (OP == BSMM_OP_FP8_BLOCKWISE) {
   #pragma unroll
         for (int i = 0; i < TI; ++i) sc[i] = sa_nxt[i] * sb_nxt;
@@ -400,7 +406,7 @@ struct Mainloop {
     const uint8_t* SA = smem;
     const uint8_t* SB = smem;
     i32x8 af[TI];
-    i32x8 bcur, bnx;     // B tiles of the current and the next column
+    i32x8 bcur;          // B tile of the current column
     auto read_b = [&](int j) {
       const i32x4 lo = *(const i32x4*)(SB + b_off0 + j * 2048);
       const i32x4 hi = *(const i32x4*)(SB + b_off1 + j * 2048);
@@ -410,7 +416,6 @@ struct Mainloop {
       SA = smem + slot_a * SLOT;
       SB = smem + slot_b * SLOT;
       bcur = read_b(0);
-      if constexpr (BPF == 2) bnx = read_b(1);
   #pragma unroll
       for (int i = 0; i < TI; ++i) {
         const i32x4 lo = *(const i32x4*)(SA + a_off0 + i * 2048);
@@ -425,44 +430,49 @@ struct Mainloop {
     // drained at the end of the block.
     constexpr int D = 4;
     f32x4 ring[D];
-    auto columns = [&](auto refill) {
+    auto columns = [&](auto refill, auto is_loader) {
+      constexpr bool LOADER = decltype(is_loader)::value;
+      (void)LOADER;
+      // The order is fixed by hard scheduling fences: per column j, its first
+      // MFMA, then the reads of B tile j+1 and the column's refill loads, then
+      // its other MFMAs, each preceded (blockwise) by the four multiply-adds
+      // that fold tile tt-D out of the ring slot the MFMA is about to refill.
+      // Left to itself the scheduler hoists the reads and folds each partial
+      // right behind its own MFMA, which serialises MFMA and VALU.
+      auto tile = [&](int i, int j) {
+        const int tt = j * TI + i;
+        if constexpr (OP == BSMM_OP_INT8_ROWWISE) {
+          const i32x4 alo = i32x4{af[i][0], af[i][1], af[i][2], af[i][3]};
+          const i32x4 ahi = i32x4{af[i][4], af[i][5], af[i][6], af[i][7]};
+          const i32x4 blo = i32x4{bcur[0], bcur[1], bcur[2], bcur[3]};
+          const i32x4 bhi = i32x4{bcur[4], bcur[5], bcur[6], bcur[7]};
+          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(blo, alo, acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bhi, ahi, acc[i][j], 0, 0, 0);
+        } else if constexpr (OP == BSMM_OP_FP8_BLOCKWISE) {
+          if (tt >= D) {
+            const int u = tt - D, ui = u % TI, uj = u / TI;
+  #pragma unroll
+            for (int r = 0; r < 4; ++r)
+              acc[ui][uj][r] = __builtin_fmaf(sc[ui], ring[u % D][r], acc[ui][uj][r]);
+          }
+          ring[tt % D] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              bcur, af[i], f32x4{0, 0, 0, 0}, 0, 0, 0, 127, 0, 127);
+        } else {
+          acc[i][j] = mfma_mx(bcur, af[i], acc[i][j], ws_cur, i, xs_cur);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      };
   #pragma unroll
       for (int j = 0; j < TJ; ++j) {
-        // B tile of column j + BPF read while column j computes
+        tile(0, j);
+        // B tile of column j+1, read while column j computes, and refills
         i32x8 bnext = bcur;
-        if (j + BPF < TJ) bnext = read_b(j + BPF);
+        if (j + 1 < TJ) bnext = read_b(j + 1);
         refill(j);
+        __builtin_amdgcn_sched_barrier(0);
   #pragma unroll
-        for (int i = 0; i < TI; ++i) {
-          const int tt = j * TI + i;
-          if constexpr (OP == BSMM_OP_INT8_ROWWISE) {
-            const i32x4 alo = i32x4{af[i][0], af[i][1], af[i][2], af[i][3]};
-            const i32x4 ahi = i32x4{af[i][4], af[i][5], af[i][6], af[i][7]};
-            const i32x4 blo = i32x4{bcur[0], bcur[1], bcur[2], bcur[3]};
-            const i32x4 bhi = i32x4{bcur[4], bcur[5], bcur[6], bcur[7]};
-            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(blo, alo, acc[i][j], 0, 0, 0);
-            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bhi, ahi, acc[i][j], 0, 0, 0);
-          } else if constexpr (OP == BSMM_OP_FP8_BLOCKWISE) {
-            // fold tile tt-D (issued D MFMAs ago) out of its ring slot, then
-            // refill the slot with tile tt
-            if (tt >= D) {
-              const int u = tt - D, ui = u % TI, uj = u / TI;
-  #pragma unroll
-              for (int r = 0; r < 4; ++r)
-                acc[ui][uj][r] = __builtin_fmaf(sc[ui], ring[u % D][r], acc[ui][uj][r]);
-            }
-            ring[tt % D] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                bcur, af[i], f32x4{0, 0, 0, 0}, 0, 0, 0, 127, 0, 127);
-          } else {
-            acc[i][j] = mfma_mx(bcur, af[i], acc[i][j], ws_cur, i, xs_cur);
-          }
-        }
-        if constexpr (BPF == 2) {
-          bcur = bnx;
-          bnx = bnext;
-        } else {
-          bcur = bnext;
-        }
+        for (int i = 1; i < TI; ++i) tile(i, j);
+        bcur = bnext;
       }
       if constexpr (OP == BSMM_OP_FP8_BLOCKWISE) {
   #pragma unroll
@@ -473,67 +483,62 @@ struct Mainloop {
             acc[ui][uj][r] = __builtin_fmaf(sc[ui], ring[u % D][r], acc[ui][uj][r]);
         }
       }
-      // Scheduling: per column j, the MFMAs of j with the two reads of B tile
-      // j+1 and the column's refill loads right after the first one and, for
-      // blockwise, four multiply-adds after each MFMA.
-      constexpr int kMfma = 0x008, kValu = 0x002, kVmemRead = 0x020, kDsRead = 0x100;
-      constexpr int MF = OP == BSMM_OP_INT8_ROWWISE ? 2 : 1;   // MFMAs per tile
-  #pragma unroll
-      for (int j = 0; j < TJ; ++j) {
-  #pragma unroll
-        for (int i = 0; i < TI; ++i) {
-          __builtin_amdgcn_sched_group_barrier(kMfma, MF, 0);
-          if (i == 0) {
-            if (j + BPF < TJ) __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
-            const int nl = kLoadsPerBlock * (j + 1) / TJ - kLoadsPerBlock * j / TJ;
-            if (nl == 1) __builtin_amdgcn_sched_group_barrier(kVmemRead, 1, 0);
-            if (nl == 2) __builtin_amdgcn_sched_group_barrier(kVmemRead, 2, 0);
-            if (nl == 3) __builtin_amdgcn_sched_group_barrier(kVmemRead, 3, 0);
-            if (nl >= 4) __builtin_amdgcn_sched_group_barrier(kVmemRead, 4, 0);
-          }
-          if constexpr (OP == BSMM_OP_FP8_BLOCKWISE) __builtin_amdgcn_sched_group_barrier(kValu, 4, 0);
-        }
-      }
     };
 
     if (nkb <= 0) return;
-    // Ring schedule.  K block c occupies half-stages 2c (A) and 2c+1 (B) in
-    // slots h % NSLOT.  At the top of block c (after the barrier that frees
-    // block c-1's two slots) those slots start to be refilled with the next
-    // two half-stages, h1 = 2c+NSLOT-2 and h2 = 2c+NSLOT-1, whose loads are
-    // spread over the block's columns (h1 first, it is needed first): issued
-    // in one burst they would queue in the texture unit and stall the
-    // issuing waves' MFMAs.  At the top of block c+1 only h2's loads may
-    // still be in flight.
-    load_scales(kb0);
-  #pragma unroll
-    for (int h = 0; h < NSLOT - 2; ++h) issue_half(h, h);
-    for (int c = 0; c < nkb; ++c) {
-      const int slot_a = (2 * c) % NSLOT;
-      const int slot_b = slot_a + 1 == NSLOT ? 0 : slot_a + 1;
-      const int h1 = 2 * c + NSLOT - 2, h2 = h1 + 1;
-      const int slot1 = h1 % NSLOT;
-      const int slot2 = slot1 + 1 == NSLOT ? 0 : slot1 + 1;
-      constexpr int L1 = (NSLOT % 2) ? T::LB : T::LA;    // h1 is odd iff NSLOT is odd
-      wait_vmcnt<T::WAIT>();   // block c's two half-stages have landed
-      lds_barrier();           // ... for every wave; block c-1's slots are free
+    // The loading waves and the others run the same K loop; only the
+    // former issue tile loads (the others' vmcnt waits are then trivially
+    // met: they have at most their scale loads in flight).
+    auto body = [&](auto is_loader) {
+      constexpr bool LOADER = decltype(is_loader)::value;
+      // Ring schedule.  K block c occupies half-stages 2c (A) and 2c+1 (B) in
+      // slots h % NSLOT.  At the top of block c (after the barrier that frees
+      // block c-1's two slots) those slots start to be refilled with the next
+      // two half-stages, h1 = 2c+NSLOT-2 and h2 = 2c+NSLOT-1, whose loads are
+      // spread over the block's columns (h1 first, it is needed first): issued
+      // in one burst they would queue in the texture unit and stall the
+      // issuing waves' MFMAs.  At the top of block c+1 only h2's loads may
+      // still be in flight.
+      load_scales(kb0);
+      if constexpr (LOADER) {
+    #pragma unroll
+        for (int h = 0; h < NSLOT - 2; ++h) issue_half(h, h);
+      }
+      // Scale registers are always consumed in the iteration that loaded them
+      // (block c+1's at the end of block c): a loaded value read across the
+      // loop's back edge makes the compiler wait for nearly every load in
+      // flight, this block's refills included.
       use_scales();
-      read_frags(slot_a, slot_b);
-      // Next block's scales (clamped), issued before this block's refills: at
-      // the top of block c+1 they are then waited for together with h1 only,
-      // not with h2's loads issued after them.
-      load_scales(kb0 + min(c + 1, nkb - 1));
-      __builtin_amdgcn_sched_barrier(0);
-      columns([&](int j) {
-  #pragma unroll
-        for (int u = kLoadsPerBlock * j / TJ; u < kLoadsPerBlock * (j + 1) / TJ; ++u) {
-          if (u < L1) issue_load(h1, slot1, u);
-          else issue_load(h2, slot2, u - L1);
-        }
-      });
-    }
-    // the last refills were out-of-range loads; let them drain
-    wait_vmcnt<0>();
+      for (int c = 0; c < nkb; ++c) {
+        const int slot_a = (2 * c) % NSLOT;
+        const int slot_b = slot_a + 1 == NSLOT ? 0 : slot_a + 1;
+        const int h1 = 2 * c + NSLOT - 2, h2 = h1 + 1;
+        const int slot1 = h1 % NSLOT;
+        const int slot2 = slot1 + 1 == NSLOT ? 0 : slot1 + 1;
+        constexpr int L1 = (NSLOT % 2) ? T::LB : T::LA;    // h1 is odd iff NSLOT is odd
+        wait_vmcnt<T::WAIT>();   // block c's two half-stages have landed
+        lds_barrier();           // ... for every wave; block c-1's slots are free
+        read_frags(slot_a, slot_b);
+        // Next block's scales (clamped), issued before this block's refills,
+        // taken into use after its last MFMA.
+        load_scales(kb0 + min(c + 1, nkb - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        columns([&](int j) {
+          if constexpr (LOADER) {
+    #pragma unroll
+            for (int u = kLoadsPerBlock * j / TJ; u < kLoadsPerBlock * (j + 1) / TJ; ++u) {
+              if (u < L1) issue_load(h1, slot1, u);
+              else issue_load(h2, slot2, u - L1);
+            }
+          }
+        }, is_loader);
+        use_scales();
+      }
+      // the last refills were out-of-range loads; let them drain
+      wait_vmcnt<0>();
+    };
+    if (wave < T::NLD) body(std::true_type());
+    else body(std::false_type());
   }
 };
 
@@ -954,7 +959,7 @@ struct Mainloop4 {
     auto use_scales = [&]() {
       xs_cur[0] = xs_nxt[0];
       xs_cur[1] = xs_nxt[1];
-      ws_cur = ws_nxt;
+      ws_cur = __builtin_amdgcn_readfirstlane(ws_nxt);   // wave-uniform; taken here, not sunk into the next iteration
     };
 
     if (nkb <= 0) return;
@@ -971,6 +976,7 @@ struct Mainloop4 {
     for (int i = 0; i < TI; ++i) af[i] = frag(0, a_off0, a_off1, i);
   #pragma unroll
     for (int j = 0; j < TJ; ++j) bf[j] = frag(1, b_off0, b_off1, j);
+    use_scales();     // consumed where loaded, never across the back edge
 
     constexpr int kMfma = 0x008, kVmemRead = 0x020, kDsRead = 0x100;
     constexpr int MF = OP == BSMM_OP_INT8_ROWWISE ? 2 : 1;
@@ -987,7 +993,6 @@ struct Mainloop4 {
       }
     };
     for (int c = 0; c < nkb; ++c) {
-      use_scales();
   #pragma unroll
       for (int j = 0; j < TJ; ++j) mfma_tile(0, j);
       wait_vmcnt<LA>();                 // block c+1 landed
@@ -1029,6 +1034,7 @@ struct Mainloop4 {
         if (i == TI - 1) __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
+      use_scales();     // block c+1's, after block c's last MFMA
     }
     wait_vmcnt<0>();     // the last refills were out-of-range loads
   }
