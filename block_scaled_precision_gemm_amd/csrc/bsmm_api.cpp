@@ -34,6 +34,8 @@ struct Override {
   int split = 0;
   bool env_read = false;
   int log = 0;
+  int tail_split_cap = 0;          // BSMM_TAIL_SPLIT: cap on the tail launch's K slices
+  std::string tail_variant;        // BSMM_TAIL_VARIANT: kernel of the tail launch
 };
 Override& ovr() {
   static Override o;
@@ -47,6 +49,8 @@ void read_env_once() {
   if (const char* v = getenv("BSMM_FORCE_VARIANT")) o.variant = v;
   if (const char* v = getenv("BSMM_FORCE_SPLITK")) o.split = atoi(v);
   if (const char* v = getenv("BSMM_LOG")) o.log = atoi(v);
+  if (const char* v = getenv("BSMM_TAIL_SPLIT")) o.tail_split_cap = atoi(v);
+  if (const char* v = getenv("BSMM_TAIL_VARIANT")) o.tail_variant = v;
 }
 
 constexpr int64_t kMaxDim = (int64_t)1 << 31;
@@ -241,11 +245,12 @@ Plan make_plan_heuristic(bsmm_op op, int G, int M, int N, int K, bsmm_dtype dt) 
       const int64_t tail_tiles = (int64_t)((M - m_split + bm - 1) / bm) * per_row;
       int s = (int)(kPlanCUs / tail_tiles);     // tail_tiles * s fits one round
       if (s > KB / 4) s = KB / 4;
-      if (const char* e = getenv("BSMM_TAIL_SPLIT")) { const int c = atoi(e); if (c > 0 && s > c) s = c; }
+      if (ovr().tail_split_cap > 0 && s > ovr().tail_split_cap) s = ovr().tail_split_cap;
       if (s >= 2) {
         pl.m_split = m_split;
         pl.tail = pl.v;
-        if (const char* e = getenv("BSMM_TAIL_VARIANT")) if (const Variant* tv = find_variant(e)) pl.tail = tv;
+        if (!ovr().tail_variant.empty())
+          if (const Variant* tv = find_variant(ovr().tail_variant.c_str())) pl.tail = tv;
         pl.tail_split = s;
         return pl;
       }

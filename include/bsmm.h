@@ -188,6 +188,8 @@ bsmm_status bsmm_query_plan(bsmm_op op, int64_t G, int64_t M, int64_t N,
  * keeps its split.  Returns BSMM_ERR_ARG for an unknown variant name.  The
  * environment variables BSMM_FORCE_VARIANT and BSMM_FORCE_SPLITK set the same
  * override at load time; BSMM_LOG=1 prints each dispatch decision to stderr.
+ * For plans with a split-K tail launch, BSMM_TAIL_SPLIT caps the tail's K
+ * slices and BSMM_TAIL_VARIANT names its kernel (tuning only).
  */
 bsmm_status bsmm_set_override(const char* variant, int split_k);
 
