@@ -755,13 +755,33 @@ skinny_kernel(const KArgs k) {
 // applied while staging, the column scale after reading back (the order
 // (f32(acc) * sa) * sb is unchanged).  PARTIAL: split-K partials (int32 /
 // fp32) into the workspace [splits][G][rows][N] instead of the output.
-template <int OP, int OUT, int NW, int WN, bool PARTIAL, int TI, int TJ, class acc_t>
+// Epilogue destinations (MODE):
+//   kOut     the output (int8: both scales applied);
+//   kSplitK  split-K partials (int32 / fp32) into the workspace
+//            [splits][G][rows][N];
+//   kSlot    a stream-K partial: the whole BM x BN tile, row-major, into
+//            the slot `sl.base` (int32 / fp32);
+//   kOutAdd  the output after adding, in K order, the partials of the
+//            tile's later K segments from slots sl.first .. sl.first +
+//            sl.count - 1 (int8: the raw sums are staged and both scales
+//            applied after the adds, so the operations are those of kOut).
+enum { kOut = 0, kSplitK = 1, kSlot = 2, kOutAdd = 3 };
+struct SlotRef {
+  void* base = nullptr;       // slot 0
+  int first = 0, count = 0;   // kOutAdd: slots to add
+  int64_t stride = 0;         // elements per slot
+};
+
+template <int OP, int OUT, int NW, int WN, int MODE, int BM, int BN, int TI, int TJ,
+          class acc_t>
 __device__ __forceinline__ void store_staged(const KArgs& k, int s, int g, int row0, int col0,
-                                             const acc_t (&acc)[TI][TJ], uint8_t* smem) {
+                                             const acc_t (&acc)[TI][TJ], uint8_t* smem,
+                                             const SlotRef& sl = SlotRef()) {
   constexpr int ROWS = 32;                       // staged rows per pass
   constexpr int PITCH = 16 * TJ * 4 + 16;        // bytes per staged row
   constexpr int GROUPS = ROWS * 16 * TJ / 4;     // 4-element groups per pass
   constexpr int PER_ROW = 16 * TJ / 4;           // groups per row
+  constexpr bool PARTIAL = MODE == kSplitK || MODE == kSlot;
   static_assert(TI % 2 == 0 && GROUPS % kWave == 0, "staging layout");
   typedef typename OpT<OP>::elem_t E;
   const Problem& p = k.p;
@@ -774,17 +794,24 @@ __device__ __forceinline__ void store_staged(const KArgs& k, int s, int g, int r
   const bool vec = k.vec_out != 0;
   uint8_t* obase;
   int64_t og, ldo;
-  if constexpr (PARTIAL) {
+  if constexpr (MODE == kSplitK) {
     const int rows = k.row_end - k.row_begin;
     obase = (uint8_t*)((E*)k.ws + ((int64_t)s * p.G + g) * (int64_t)rows * p.N);
     og = -(int64_t)k.row_begin * p.N;
     ldo = p.N;
+  } else if constexpr (MODE == kSlot) {
+    obase = (uint8_t*)sl.base;
+    og = -(int64_t)row0 * BN - col0;
+    ldo = BN;
   } else {
     obase = (uint8_t*)p.out;
     og = (int64_t)g * p.o_sg;
     ldo = p.ldo;
   }
+  // int8 scales: the row scale while staging (kOut), or both after the
+  // slot adds (kOutAdd)
   constexpr bool SCALE = OP == BSMM_OP_INT8_ROWWISE && OUT != BSMM_I32 && !PARTIAL;
+  constexpr bool SCALE_A_STAGED = SCALE && MODE == kOut;
   const bool sb_vec = SCALE && p.sb_n == 1 && (((uintptr_t)p.sb) & 15u) == 0;
   lds_barrier();     // every wave's K-loop reads of LDS are done
 #pragma unroll
@@ -793,14 +820,14 @@ __device__ __forceinline__ void store_staged(const KArgs& k, int s, int g, int r
     for (int ii = 0; ii < 2; ++ii) {
       const int i = 2 * pass + ii;
       float sa_m = 1.f;
-      if constexpr (SCALE)
+      if constexpr (SCALE_A_STAGED)
         sa_m = ((const float*)p.sa)[(int64_t)min(wrow0 + 16 * i + fr, k.row_end - 1) * p.sa_m];
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
         i32x4 v;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          if constexpr (SCALE)
+          if constexpr (SCALE_A_STAGED)
             v[r] = __float_as_int(__fmul_rn((float)acc[i][j][r], sa_m));
           else if constexpr (OP == BSMM_OP_INT8_ROWWISE)
             v[r] = acc[i][j][r];
@@ -814,12 +841,25 @@ __device__ __forceinline__ void store_staged(const KArgs& k, int s, int g, int r
     for (int q = 0; q < GROUPS / kWave; ++q) {
       const int gi = q * kWave + lane;
       const int r = gi / PER_ROW, cg = gi % PER_ROW;
-      const i32x4 v = *(const i32x4*)(st + r * PITCH + cg * 16);
+      i32x4 v = *(const i32x4*)(st + r * PITCH + cg * 16);
       const int m = wrow0 + ROWS * pass + r;
       const int n = wcol0 + 4 * cg;
-      const int nvalid = min(4, p.N - n);
-      if (m >= k.row_end || nvalid <= 0) continue;
+      // a slot holds the whole tile: every group is stored
+      const int nvalid = MODE == kSlot ? 4 : min(4, p.N - n);
+      if (MODE != kSlot && (m >= k.row_end || nvalid <= 0)) continue;
       const int64_t e = og + (int64_t)m * ldo + n;
+      if constexpr (MODE == kOutAdd) {
+        typedef E e4 __attribute__((ext_vector_type(4)));
+        const int64_t off = (int64_t)(m - row0) * BN + (n - col0);
+        for (int q2 = 0; q2 < sl.count; ++q2) {
+          const e4 t = *(const e4*)((const E*)sl.base + (int64_t)(sl.first + q2) * sl.stride + off);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            if constexpr (OP == BSMM_OP_INT8_ROWWISE) v[c] += t[c];
+            else v[c] = __float_as_int(__int_as_float(v[c]) + t[c]);
+          }
+        }
+      }
       float y[4];
       int yi[4];
       if constexpr (SCALE) {
@@ -832,8 +872,14 @@ __device__ __forceinline__ void store_staged(const KArgs& k, int s, int g, int r
           for (int c = 0; c < 4; ++c)
             sb[c] = ((const float*)p.sb)[(int64_t)min(n + c, p.N - 1) * p.sb_n];
         }
+        if constexpr (SCALE_A_STAGED) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) y[c] = __fmul_rn(__int_as_float(v[c]), sb[c]);
+          for (int c = 0; c < 4; ++c) y[c] = __fmul_rn(__int_as_float(v[c]), sb[c]);
+        } else {
+          const float sa_m = ((const float*)p.sa)[(int64_t)m * p.sa_m];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) y[c] = __fmul_rn(__fmul_rn((float)v[c], sa_m), sb[c]);
+        }
       } else {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -1059,9 +1105,9 @@ tile4_kernel(const KArgs k) {
       for (int j = 0; j < M::TJ; ++j) acc[i][j] = typename M::acc_t{0, 0, 0, 0};
     M::run(k, smem, t.g, row0, col0, kb0, nkb, acc);
     if (k.splits > 1)
-      store_staged<OP, OUT, 4, 2, true>(k, t.s, t.g, row0, col0, acc, smem);
+      store_staged<OP, OUT, 4, 2, kSplitK, 256, 256>(k, t.s, t.g, row0, col0, acc, smem);
     else
-      store_staged<OP, OUT, 4, 2, false>(k, t.s, t.g, row0, col0, acc, smem);
+      store_staged<OP, OUT, 4, 2, kOut, 256, 256>(k, t.s, t.g, row0, col0, acc, smem);
   }
 }
 
@@ -1086,9 +1132,9 @@ tile_kernel(const KArgs k) {
       for (int j = 0; j < M::TJ; ++j) acc[i][j] = typename M::acc_t{0, 0, 0, 0};
     M::run(k, smem, t.g, row0, col0, kb0, nkb, acc);
     if (k.splits > 1)
-      store_staged<OP, OUT, WM * WN, WN, true>(k, t.s, t.g, row0, col0, acc, smem);
+      store_staged<OP, OUT, WM * WN, WN, kSplitK, T::BM, T::BN>(k, t.s, t.g, row0, col0, acc, smem);
     else
-      store_staged<OP, OUT, WM * WN, WN, false>(k, t.s, t.g, row0, col0, acc, smem);
+      store_staged<OP, OUT, WM * WN, WN, kOut, T::BM, T::BN>(k, t.s, t.g, row0, col0, acc, smem);
   }
 }
 
@@ -1108,9 +1154,10 @@ tile_kernel(const KArgs k) {
 // 64-bit flag per workgroup.
 // ---------------------------------------------------------------------------
 struct SkArgs {
-  int64_t units;       // tiles * KB
+  int64_t units;       // K-block units of the stream-K phase: sk tiles * KB
   uint64_t epoch;      // distinct per launch
   int tiles_total;     // tiles_m * tiles_n * G
+  int dp_tiles;        // whole tiles before the stream-K phase
 };
 
 constexpr int kSpinLimit = 1 << 22;   // ~ seconds of polling; never reached
@@ -1139,12 +1186,25 @@ sk_kernel(const KArgs k, const SkArgs sk) {
   uint64_t* flags = (uint64_t*)((uint8_t*)k.ws + (size_t)P * SLOT_ELEMS * sizeof(E));
   const int tid = threadIdx.x;
 
+  // Data-parallel phase: whole tiles dp_tiles in the persistent order
+  // (workgroup w takes tiles w, w + P, ...: at any time the workgroups of an
+  // XCD hold a compact block of the grouped raster).  Then the stream-K phase
+  // over the remaining tiles' K blocks, contiguous ranges per workgroup.
+  int dp = w;
   int64_t u = range_start(w);
   const int64_t uend = range_start(w + 1);
-  while (u < uend) {
-    const int tile = (int)(u / KB);
-    const int kb_a = (int)(u - (int64_t)tile * KB);
-    const int kb_b = (int)min((int64_t)KB, (int64_t)kb_a + (uend - u));
+  while (dp < sk.dp_tiles || u < uend) {
+    int tile, kb_a, kb_b;
+    if (dp < sk.dp_tiles) {
+      tile = dp;
+      kb_a = 0;
+      kb_b = KB;
+    } else {
+      const int st = (int)(u / KB);
+      tile = sk.dp_tiles + st;
+      kb_a = (int)(u - (int64_t)st * KB);
+      kb_b = (int)min((int64_t)KB, (int64_t)kb_a + (uend - u));
+    }
     // tile -> (g, tm, tn): grouped order within each G
     const int tiles = k.tiles_m * k.tiles_n;
     const int g = tile / tiles;
@@ -1166,53 +1226,47 @@ sk_kernel(const KArgs k, const SkArgs sk) {
       for (int j = 0; j < TJ; ++j) acc[i][j] = acc_t{0, 0, 0, 0};
     M::run(k, smem, g, row0, col0, kb_a, kb_b - kb_a, acc);
 
+    SlotRef sl;
+    sl.base = slots;
+    sl.stride = SLOT_ELEMS;
     if (kb_a > 0) {
-      // a later K segment of a split tile: publish the partial (lane-major
-      // slot layout, 16-byte stores) and its flag
-      E* slot = slots + (size_t)w * SLOT_ELEMS;
-#pragma unroll
-      for (int i = 0; i < TI; ++i)
-#pragma unroll
-        for (int j = 0; j < TJ; ++j) {
-          typedef E e4 __attribute__((ext_vector_type(4)));
-          e4 v = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
-          *(e4*)(slot + ((size_t)(i * TJ + j) * NT + tid) * 4) = v;
-        }
+      // a later K segment of a split tile: publish the partial (the staged
+      // tile into this workgroup's slot) and its flag
+      sl.base = slots + (size_t)w * SLOT_ELEMS;
+      store_staged<OP, OUT, WM * WN, WN, kSlot, T::BM, T::BN>(k, 0, g, row0, col0, acc, smem, sl);
       __threadfence();
       __syncthreads();
       if (tid == 0)
         __hip_atomic_store(&flags[w], sk.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     } else {
-      if (kb_b < KB) {
-        // owner of a split tile: add the later segments' partials, which are
-        // the first segments of the following ranges, in K order
-        int w2 = w + 1;
-        while (w2 < P && range_start(w2) < (int64_t)(tile + 1) * KB) {
-          if (tid == 0) {
+      // owner (K blocks from 0): the tile's later K segments are the first
+      // segments of the following ranges, computed first.  A split tile
+      // waits for their flags, then adds their partials, in K order, while
+      // storing the output.
+      int w_end = w + 1;
+      if (kb_b < KB)
+        while (w_end < P && range_start(w_end) < (int64_t)(tile - sk.dp_tiles + 1) * KB) ++w_end;
+      if (w_end > w + 1) {
+        if (tid == 0) {
+          for (int w2 = w + 1; w2 < w_end; ++w2) {
             int spins = 0;
             while (__hip_atomic_load(&flags[w2], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) !=
                        sk.epoch &&
                    ++spins < kSpinLimit)
               __builtin_amdgcn_s_sleep(2);
           }
-          __syncthreads();
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-          const E* slot = slots + (size_t)w2 * SLOT_ELEMS;
-#pragma unroll
-          for (int i = 0; i < TI; ++i)
-#pragma unroll
-            for (int j = 0; j < TJ; ++j) {
-              typedef E e4 __attribute__((ext_vector_type(4)));
-              const e4 v = *(const e4*)(slot + ((size_t)(i * TJ + j) * NT + tid) * 4);
-#pragma unroll
-              for (int r = 0; r < 4; ++r) acc[i][j][r] += v[r];
-            }
-          ++w2;
         }
+        __syncthreads();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        sl.first = w + 1;
+        sl.count = w_end - (w + 1);
+        store_staged<OP, OUT, WM * WN, WN, kOutAdd, T::BM, T::BN>(k, 0, g, row0, col0, acc, smem, sl);
+      } else {
+        store_staged<OP, OUT, WM * WN, WN, kOut, T::BM, T::BN>(k, 0, g, row0, col0, acc, smem);
       }
-      store_output<OP, OUT, WM, WN>(k, g, row0, col0, acc);
     }
-    u += kb_b - kb_a;
+    if (dp < sk.dp_tiles) dp += P;
+    else u += kb_b - kb_a;
   }
 }
 
@@ -1464,10 +1518,16 @@ int launch_sk(const Problem& p, const Launch& l) {
   k.ws = l.ws;
   SkArgs sk;
   sk.tiles_total = k.tiles_m * k.tiles_n * p.G;
-  sk.units = (int64_t)sk.tiles_total * KB;
   int P = cap;
-  if ((int64_t)P > sk.units) P = (int)sk.units;
+  if ((int64_t)P > (int64_t)sk.tiles_total * KB) P = (int)((int64_t)sk.tiles_total * KB);
   if ((size_t)P * per_wg > l.ws_bytes) P = (int)(l.ws_bytes / per_wg);
+  // whole rounds of tiles run data-parallel, except that the last P or more
+  // tiles (a round and the remainder) are spread as K blocks over all P
+  // workgroups; a whole number of rounds runs data-parallel throughout
+  const int rounds = sk.tiles_total / P;
+  if (sk.tiles_total % P == 0) sk.dp_tiles = sk.tiles_total;
+  else sk.dp_tiles = rounds >= 1 ? (rounds - 1) * P : 0;
+  sk.units = (int64_t)(sk.tiles_total - sk.dp_tiles) * KB;
   sk.epoch = next_epoch();
   hipLaunchKernelGGL((sk_kernel<OP, OUT, WM, WN, RING, PK>), dim3((unsigned)P), dim3(T::NT), 0, s,
                      k, sk);

@@ -247,6 +247,33 @@ def test_streamk_small_workspace_two_way_splits():
     assert np.array_equal(host_out(y1).view(np.uint32), host_out(y2).view(np.uint32))
 
 
+def test_streamk_data_parallel_rounds_then_split_tiles():
+    """A four-slot workspace over nine 256 x 256 tiles: one data-parallel
+    round of four whole tiles, then the other five tiles' K blocks spread
+    over the four workgroups (tiles split across two of them), for every
+    operation, several mx batches included; repeatable bit for bit."""
+    q = fp8_blockwise_inputs(600, 640, 1280, 505)
+    p = int8_rowwise_inputs(600, 640, 1280, 506)
+    r = fp8_mx_bmm_inputs(3, 300, 640, 1280, 507, layout="batch_first")
+    ws = torch.empty(4 * (256 * 256 * 4 + 8), dtype=torch.uint8, device=DEV)
+    a, b = dev(q["a"]), dev(q["b_nk"]).t()
+    sa, sb = dev(q["scale_a"]), dev(q["scale_b"])
+    say("stream-K data-parallel rounds + split tiles (4 slots)")
+    with Forced("t256x256sk", 0):
+        y1 = bsmm.bsmm_fp8_blockwise(a, b, sa, sb, out_dtype="bf16", workspace=ws)
+        y2 = bsmm.bsmm_fp8_blockwise(a, b, sa, sb, out_dtype="bf16", workspace=ws)
+        yi = bsmm.bsmm_int8_rowwise(dev(p["a"]), dev(p["b_nk"]).t(),
+                                    dev(p["scale_a"]).reshape(-1, 1),
+                                    dev(p["scale_b"]).reshape(1, -1), out_dtype="f32",
+                                    workspace=ws)
+        ym = bsmm.bsmm_fp8_mx_bmm(dev(r["x"]), dev(r["w"]), dev(r["x_scale"]), dev(r["w_scale"]),
+                                  layout="batch_first", out_dtype="f32", workspace=ws)
+    check_blockwise(q, "bf16", y1)
+    assert np.array_equal(host_out(y1), host_out(y2))
+    check_int8(p, "f32", yi)
+    check_mx(r, "f32", ym)
+
+
 # ------------------------------------------------------- packed scales ----
 
 @pytest.mark.parametrize("variant", PACKED_VARIANTS)
