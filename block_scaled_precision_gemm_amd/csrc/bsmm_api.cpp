@@ -180,9 +180,11 @@ Plan make_plan(bsmm_op op, int G, int M, int N, int K, bsmm_dtype dt,
     if (e.M > M && (!best || e.M < best->M)) { best = &e; pl.source = 1; }
   }
   // a tuned entry is used only where its kernels take this M (the skinny
-  // kernel takes M <= 16 in a single launch, so it is never a tail)
+  // kernel takes M <= 16 in a single launch, so it is never a tail); a
+  // padded-M bucket never displaces the skinny kernel for M <= 16
   const Variant* bv = best ? find_variant(best->variant) : nullptr;
   if (bv && bv->max_m && M > bv->max_m) bv = nullptr;
+  if (bv && pl.source == 1 && M <= 16 && !bv->max_m) bv = nullptr;
   if (bv) {
     pl.v = bv;
     pl.split = best->split;

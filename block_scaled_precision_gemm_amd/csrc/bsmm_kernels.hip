@@ -246,7 +246,9 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Store 4 consecutive output values of one row.
+// Store 4 consecutive output values of one row.  The vector stores are
+// non-temporal: a round of tile epilogues writes as much as an XCD's L2
+// holds, and would otherwise evict the A and B slices the next tiles read.
 template <int OUT>
 __device__ __forceinline__ void store4(uint8_t* base, int64_t e, const float* y,
                                        const int* yi, bool vec, int nvalid) {
@@ -256,17 +258,17 @@ __device__ __forceinline__ void store4(uint8_t* base, int64_t e, const float* y,
       u32x2 v;
       v.x = f32_to_bf16_rne(y[0]) | (f32_to_bf16_rne(y[1]) << 16);
       v.y = f32_to_bf16_rne(y[2]) | (f32_to_bf16_rne(y[3]) << 16);
-      *(u32x2*)o = v;
+      __builtin_nontemporal_store(v, (u32x2*)o);
     } else {
       for (int r = 0; r < nvalid; ++r) o[r] = (uint16_t)f32_to_bf16_rne(y[r]);
     }
   } else if (OUT == BSMM_F32) {
     float* o = (float*)base + e;
-    if (vec && nvalid == 4) *(f32x4*)o = f32x4{y[0], y[1], y[2], y[3]};
+    if (vec && nvalid == 4) __builtin_nontemporal_store(f32x4{y[0], y[1], y[2], y[3]}, (f32x4*)o);
     else for (int r = 0; r < nvalid; ++r) o[r] = y[r];
   } else {
     int* o = (int*)base + e;
-    if (vec && nvalid == 4) *(i32x4*)o = i32x4{yi[0], yi[1], yi[2], yi[3]};
+    if (vec && nvalid == 4) __builtin_nontemporal_store(i32x4{yi[0], yi[1], yi[2], yi[3]}, (i32x4*)o);
     else for (int r = 0; r < nvalid; ++r) o[r] = yi[r];
   }
 }
@@ -1274,35 +1276,59 @@ sk_kernel(const KArgs k, const SkArgs sk) {
 template <int OP, int OUT>
 __global__ void __launch_bounds__(256)
 splitk_reduce(const KArgs k) {
+  // Work items (row of [G][rows], 1024-column chunk) strided over the grid,
+  // 4-column groups over the workgroup's threads; one division per item.
   const Problem& p = k.p;
   const int rows = k.row_end - k.row_begin;
-  const int64_t per_g = (int64_t)rows * p.N;
-  const int64_t total = per_g * p.G;
+  const int64_t nrows = (int64_t)rows * p.G;
+  const int64_t split_stride = nrows * p.N;
   typedef typename OpT<OP>::elem_t E;
+  typedef E e4 __attribute__((ext_vector_type(4)));
   const E* ws = (const E*)k.ws;
-  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
-       e += (int64_t)gridDim.x * blockDim.x) {
-    const int g = (int)(e / per_g);
-    const int64_t rem = e - (int64_t)g * per_g;
-    const int mr = (int)(rem / p.N);
-    const int n = (int)(rem - (int64_t)mr * p.N);
-    E s = 0;
-    for (int q = 0; q < k.splits; ++q) s += ws[(int64_t)q * total + e];
+  const bool v4 = (p.N & 3) == 0;     // partial rows are 16-byte aligned
+  const bool vec = k.vec_out != 0;
+  const int chunks = (p.N + 1023) / 1024;
+  const int64_t items = nrows * chunks;
+  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    const int64_t r = it / chunks;
+    const int n0 = (int)(it - r * chunks) * 1024;
+    const int g = (int)(r / rows);
+    const int mr = (int)(r - (int64_t)g * rows);
     const int m = k.row_begin + mr;
-    const int64_t o = (int64_t)g * p.o_sg + (int64_t)m * p.ldo + n;
-    float y;
-    if constexpr (OP == BSMM_OP_INT8_ROWWISE) {
-      if constexpr (OUT == BSMM_I32) {
-        ((int*)p.out)[o] = (int)s;
-        continue;
+    const E* src = ws + r * p.N;
+    float sa_m = 1.f;
+    if constexpr (OP == BSMM_OP_INT8_ROWWISE && OUT != BSMM_I32)
+      sa_m = ((const float*)p.sa)[(int64_t)m * p.sa_m];
+    uint8_t* obase = (uint8_t*)p.out;
+    const int64_t orow = (int64_t)g * p.o_sg + (int64_t)m * p.ldo;
+    for (int n = n0 + 4 * (int)threadIdx.x; n < min(p.N, n0 + 1024); n += 4 * (int)blockDim.x) {
+      const int nvalid = min(4, p.N - n);
+      E s[4] = {0, 0, 0, 0};
+      for (int q = 0; q < k.splits; ++q) {
+        const E* sq = src + (int64_t)q * split_stride + n;
+        if (v4) {
+          const e4 t = *(const e4*)sq;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) s[c] += t[c];
+        } else {
+          for (int c = 0; c < nvalid; ++c) s[c] += sq[c];
+        }
       }
-      y = __fmul_rn(__fmul_rn((float)s, ((const float*)p.sa)[(int64_t)m * p.sa_m]),
-                    ((const float*)p.sb)[(int64_t)n * p.sb_n]);
-    } else {
-      y = (float)s;
+      float y[4];
+      int yi[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if constexpr (OP == BSMM_OP_INT8_ROWWISE) {
+          yi[c] = (int)s[c];
+          if constexpr (OUT != BSMM_I32)
+            y[c] = __fmul_rn(__fmul_rn((float)s[c], sa_m),
+                             ((const float*)p.sb)[(int64_t)min(n + c, p.N - 1) * p.sb_n]);
+        } else {
+          y[c] = (float)s[c];
+        }
+      }
+      store4<OUT>(obase, orow + n, y, yi, vec, nvalid);
     }
-    if constexpr (OUT == BSMM_BF16) ((uint16_t*)p.out)[o] = (uint16_t)f32_to_bf16_rne(y);
-    else ((float*)p.out)[o] = y;
   }
 }
 
@@ -1419,8 +1445,7 @@ int launch_tile(const Problem& p, const Launch& l) {
   hipLaunchKernelGGL((tile_kernel<OP, OUT, WM, WN, RING, PK>), dim3((unsigned)grid), dim3(T::NT), 0, s, k);
   if (check_launch()) return 1;
   if (k.splits > 1) {
-    const int64_t total = (int64_t)rows * p.N * p.G;
-    int64_t blocks = (total + 255) / 256;
+    int64_t blocks = (int64_t)rows * p.G * ((p.N + 1023) / 1024);   // (row, chunk) items
     if (blocks > 65536) blocks = 65536;
     hipLaunchKernelGGL((splitk_reduce<OP, OUT>), dim3((unsigned)blocks), dim3(256), 0, s, k);
     return check_launch();
@@ -1472,8 +1497,7 @@ int launch_tile4(const Problem& p, const Launch& l) {
   hipLaunchKernelGGL((tile4_kernel<OP, OUT, PK>), dim3((unsigned)grid), dim3(T::NT), 0, s, k);
   if (check_launch()) return 1;
   if (k.splits > 1) {
-    const int64_t total = (int64_t)rows * p.N * p.G;
-    int64_t blocks = (total + 255) / 256;
+    int64_t blocks = (int64_t)rows * p.G * ((p.N + 1023) / 1024);   // (row, chunk) items
     if (blocks > 65536) blocks = 65536;
     hipLaunchKernelGGL((splitk_reduce<OP, OUT>), dim3((unsigned)blocks), dim3(256), 0, s, k);
     return check_launch();

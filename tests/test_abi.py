@@ -236,3 +236,23 @@ def test_timing_hook_host_paths(L):
     assert bsmm.bsmm_timing_read() == (0.0, 0, "")
     bsmm.bsmm_timing_enable(False)
     assert L.bsmm_timing_read(None, None, None, 0) == 1   # BSMM_ERR_NULL
+
+
+def test_tuner_candidates_and_table_format(tmp_path, monkeypatch):
+    """The tuning tool's host side: shape parsing, the distinct plans the
+    override yields (every one a known variant, skinny only for M <= 16),
+    and a table it writes parses back with unique keys."""
+    from block_scaled_precision_gemm_amd import tune
+    sh = tune.parse_shape("mx,bf16,8,128,1024,4096,m_major")
+    assert (sh["G"], sh["M"], sh["N"], sh["K"], sh["layout"]) == (8, 128, 1024, 4096, "m_major")
+    names = set(bsmm.bsmm_variant_names())
+    cands = tune.candidates(sh)
+    assert len(cands) > 5 and all(v in names for v, _ in cands)
+    assert all(v != "s16x16" for v, _ in cands)
+    assert ("s16x16", 1) in tune.candidates(tune.parse_shape("int8,bf16,1,4,4096,4096"))
+    monkeypatch.setattr(tune, "TABLE", str(tmp_path / "t.inc"))
+    rows = {(2, 2, 8, 128, 1024, 4096): '{2, 2, 8, 128, 1024, 4096, "t128x128", 4, 0, "", 1}'}
+    tune.write_table(rows)
+    assert tune.read_table() == rows
+    with pytest.raises(SystemExit):
+        tune.parse_shape("fp16,bf16,1,2,3,4")
