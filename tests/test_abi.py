@@ -145,13 +145,15 @@ def test_plan_heuristics():
     q = bsmm.bsmm_query_plan
     p = q(bsmm.OP_FP8_BLOCKWISE, 1, 16640, 5120, 8192, "bf16")
     assert p["tile_m"] in (128, 256) and p["split_k"] >= 1
-    small = q(bsmm.OP_FP8_MX_BMM, 8, 40, 1024, 4096, "bf16")
+    # (a shape with no tuned-table entry, so the heuristic decides)
+    small = q(bsmm.OP_FP8_MX_BMM, 8, 40, 2048, 4096, "bf16")
+    assert small["source"] == 2
     assert small["tile_m"] == 64 and small["split_k"] > 1
-    assert small["workspace"] == small["split_k"] * 8 * 40 * 1024 * 4
+    assert small["workspace"] == small["split_k"] * 8 * 40 * 2048 * 4
     # without workspace the same problem runs unsplit
-    nows = q(bsmm.OP_FP8_MX_BMM, 8, 40, 1024, 4096, "bf16", workspace_bytes=0)
+    nows = q(bsmm.OP_FP8_MX_BMM, 8, 40, 2048, 4096, "bf16", workspace_bytes=0)
     assert nows["split_k"] == 1 and nows["workspace"] == 0
-    assert bsmm.bsmm_workspace_bytes(bsmm.OP_FP8_MX_BMM, 8, 40, 1024, 4096, "bf16") == \
+    assert bsmm.bsmm_workspace_bytes(bsmm.OP_FP8_MX_BMM, 8, 40, 2048, 4096, "bf16") == \
         small["workspace"]
 
 
@@ -172,6 +174,25 @@ def test_plan_skinny_m():
         assert q(bsmm.OP_INT8_ROWWISE, 1, 40, 1024, 4096, "bf16")["variant"] != "s16x16"
     finally:
         bsmm.bsmm_set_override(None, 0)
+
+
+def test_tuned_table_exact_and_padded_m():
+    """A tuned entry serves its exact shape (source 0) and, as the padded-M
+    bucket, smaller M of the same (op, dtype, G, N, K) (source 1), but never
+    M <= 16, which keeps the skinny kernel, and never for stream-K entries."""
+    rows = parse_table()
+    q = bsmm.bsmm_query_plan
+    dts = {0: "i32", 1: "f32", 2: "bf16"}
+    for f in rows:
+        op, dt, G, M, N, K = (int(x) for x in f[:6])
+        assert q(op, G, M, N, K, dts[dt])["source"] == 0
+        if M > 17:
+            below = q(op, G, M - 1, N, K, dts[dt])
+            if "sk" in f[6]:      # stream-K entries serve their exact shape only
+                assert below["source"] == 2
+            else:
+                assert below["source"] == 1 and below["variant"] == f[6]
+            assert q(op, G, 8, N, K, dts[dt])["variant"] == "s16x16"
 
 
 def test_override_roundtrip():
