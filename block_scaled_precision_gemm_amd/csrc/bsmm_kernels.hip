@@ -285,6 +285,10 @@ struct Mainloop {
   using acc_t = typename OpT<OP>::acc_t;
   static constexpr int TI = T::TI, TJ = T::TJ;
   static constexpr int kLoadsPerBlock = T::LA + T::LB;   // per wave
+  // shared memory: the ring, or the epilogue's 32-row strips of every wave
+  // if those need more (a four-slot ring of 256 x 256 tiles does)
+  static constexpr int STAGE = T::NW * 32 * (16 * T::TJ * 4 + 16);
+  static constexpr int SMEM = T::LDS > STAGE ? T::LDS : STAGE;
 
   __device__ __forceinline__ static void run(const KArgs& k, uint8_t* smem, int g,
                                              int row0, int col0, int kb0, int nkb,
@@ -467,13 +471,19 @@ struct Mainloop {
   #pragma unroll
       for (int j = 0; j < TJ; ++j) {
         tile(0, j);
-        // B tile of column j+1, read while column j computes, and refills
+        // B tile of column j+1, read while column j computes; the refill
+        // loads spread one after every few MFMAs (in bursts they queue in the
+        // texture unit and hold up the issuing wave)
         i32x8 bnext = bcur;
         if (j + 1 < TJ) bnext = read_b(j + 1);
-        refill(j);
+        refill(j * TI);
         __builtin_amdgcn_sched_barrier(0);
   #pragma unroll
-        for (int i = 1; i < TI; ++i) tile(i, j);
+        for (int i = 1; i < TI; ++i) {
+          tile(i, j);
+          refill(j * TI + i);
+          __builtin_amdgcn_sched_barrier(0);
+        }
         bcur = bnext;
       }
       if constexpr (OP == BSMM_OP_FP8_BLOCKWISE) {
@@ -518,17 +528,20 @@ struct Mainloop {
         const int slot1 = h1 % NSLOT;
         const int slot2 = slot1 + 1 == NSLOT ? 0 : slot1 + 1;
         constexpr int L1 = (NSLOT % 2) ? T::LB : T::LA;    // h1 is odd iff NSLOT is odd
-        wait_vmcnt<T::WAIT>();   // block c's two half-stages have landed
+        // block c's two half-stages have landed (a wave that issues no tile
+        // loads has only its scale loads to wait for, which the compiler does)
+        if constexpr (LOADER) wait_vmcnt<T::WAIT>();
         lds_barrier();           // ... for every wave; block c-1's slots are free
         read_frags(slot_a, slot_b);
         // Next block's scales (clamped), issued before this block's refills,
         // taken into use after its last MFMA.
         load_scales(kb0 + min(c + 1, nkb - 1));
         __builtin_amdgcn_sched_barrier(0);
-        columns([&](int j) {
+        columns([&](int q) {   // after the block's MFMA q of TI * TJ
           if constexpr (LOADER) {
+            constexpr int NQ = TI * TJ;
     #pragma unroll
-            for (int u = kLoadsPerBlock * j / TJ; u < kLoadsPerBlock * (j + 1) / TJ; ++u) {
+            for (int u = kLoadsPerBlock * q / NQ; u < kLoadsPerBlock * (q + 1) / NQ; ++u) {
               if (u < L1) issue_load(h1, slot1, u);
               else issue_load(h2, slot2, u - L1);
             }
@@ -537,7 +550,7 @@ struct Mainloop {
         use_scales();
       }
       // the last refills were out-of-range loads; let them drain
-      wait_vmcnt<0>();
+      if constexpr (LOADER) wait_vmcnt<0>();
     };
     if (wave < T::NLD) body(std::true_type());
     else body(std::false_type());
@@ -1119,7 +1132,7 @@ __global__ void __launch_bounds__(64 * WM * WN)
 tile_kernel(const KArgs k) {
   using M = Mainloop<OP, WM, WN, RING, PK>;
   using T = typename M::T;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[M::SMEM];
   const int KB = k.p.K / kBlockK;
   for (int u = first_unit(); u < k.units; u += gridDim.x) {
     const TileId t = decode_tile(k, u);
@@ -1174,7 +1187,7 @@ sk_kernel(const KArgs k, const SkArgs sk) {
   typedef typename OpT<OP>::elem_t E;
   constexpr int TI = M::TI, TJ = M::TJ, NT = T::NT;
   constexpr int SLOT_ELEMS = T::BM * T::BN;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[M::SMEM];
   const int P = gridDim.x;
   // XCD-aware: consecutive ranges run on the same XCD
   const int hw = blockIdx.x;
