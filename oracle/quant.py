@@ -133,4 +133,5 @@ def quant_fp8_mx(x):
     amax = np.abs(xb).max(axis=2)
     ex = e8m0_exponent(amax)
     codes = e4m3_encode_rne(np.ldexp(xb.astype(np.float64), -ex[:, :, None]))
+    codes = np.where((amax == 0)[:, :, None], np.uint8(0), codes).astype(np.uint8)
     return codes.reshape(x.shape), (ex + 127).astype(np.uint8)

@@ -164,6 +164,7 @@ def test_fp8_blockwise_hand_blocks():
     x[0, 0], x[0, 1], x[0, 2] = 448.0, -1.0625, 1.1875       # block (0,0): scale 1
     x[0, 128], x[0, 129] = -896.0, 3.0                       # block (0,1): scale 2
     x[1, 5] = 0.5                                            # block (1,0): 0.5/448
+    x[1, 130] = -0.0                                         # block (1,1): all zero
     codes, s = Q.quant_fp8_blockwise(x)
     assert s.tolist() == [[1.0, 2.0], [np.float32(0.5 / 448), 1.0]]
     assert codes[0, :3].tolist() == [0x7E, 0xB8, 0x3A]
@@ -268,3 +269,7 @@ def test_fp8_mx_bottom_clamp_and_zero_block():
     codes, e = Q.quant_fp8_mx(x)
     assert e[0, 0] == 0 and codes[0, 3] == 0x20      # exponent field 4
     assert not codes[0, 128:].any()
+    x[0, 130] = -0.0                               # an all-zero block: +0 codes
+    assert not Q.quant_fp8_mx(x)[0][0, 128:].any()
+    x[0, 5] = -0.0                                 # in a live block -0 keeps its sign
+    assert Q.quant_fp8_mx(x)[0][0, 5] == 0x80
