@@ -13,7 +13,9 @@ every step.  Rank 0 prints one JSON line.
 Default workload: the fp8 E4M3 blockwise GEMM M=16640, N=5120, K=8192 with
 1x128 activation and 128x128 weight fp32 scales and bf16 output (the large
 blockwise GEMM whose throughput is the headline target).  Other workloads:
---config c1 | c2 | c4_m1 | c4_m128 | c4_m8192 | c5.
+--config c1 | c2 | c4_m1 | c4_m128 | c4_m8192 | c5, and the dynamic
+quantisers of their bf16 activations --config q_int8 | q_fp8 | q_mx | q_mx_t
+(one quantiser call per step, GB/s against 8 TB/s).
 
 The JSON line also carries
   roofline      achieved / peak for the dominant kernel (MFMA-bound shapes
@@ -41,11 +43,21 @@ PEAK = {"fp8": 5.0e15, "int8": 5.0e15}    # MI355X dense MFMA, ops/s
 HBM_PEAK = 8.0e12                          # bytes/s
 KERNEL_SOURCES = ["block_scaled_precision_gemm_amd/csrc/bsmm_kernels.hip",
                   "block_scaled_precision_gemm_amd/csrc/bsmm_pack.hip"]
+QUANT_SOURCES = ["block_scaled_precision_gemm_amd/csrc/bsmm_quant.hip"]
+
+# Dynamic-quantisation workloads: the bf16 activations of the matmul
+# workloads (kind, shape, distribution, seed).
+QUANT_CONFIGS = {
+    "q_int8": ("int8", (8192, 4096), "normal", 2),        # X of the int8 8192x4096x4096 GEMM
+    "q_fp8": ("fp8", (16640, 8192), "normal", 3),         # A of the fp8 16640x5120x8192 GEMM
+    "q_mx": ("mx", (8192, 8, 4096), "normal", 43),        # x of the mx BMM, M=8192, G=8
+    "q_mx_t": ("mx", (2, 9000, 7168), "t", 5),            # x of the mx BMM, G=2, M=9000
+}
 
 
-def kernel_hash():
+def kernel_hash(sources=None):
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in sources or KERNEL_SOURCES:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -183,7 +195,7 @@ def _csvs(d, suffix):
 
 
 def _main_kernel(name):
-    return "tile_kernel" in name or "sk_kernel" in name
+    return "tile_kernel" in name or "sk_kernel" in name or "quant_" in name
 
 
 def summarize(d):
@@ -253,7 +265,9 @@ def traffic(name, fdir, wdir, cfdir, cwdir):
     wv, _ = largest_main(_counter(wdir, "WRITE_SIZE", main))
     fetch = sum(fv) / len(fv) * 1024 * f_scale
     write = sum(wv) / len(wv) * 1024 * w_scale
-    res = {"config": name, "kernel_hash": kernel_hash(), "grid": grid,
+    res = {"config": name,
+           "kernel_hash": kernel_hash(QUANT_SOURCES if name in QUANT_CONFIGS else None),
+           "grid": grid,
            "dispatches": len(fv), "fetch_bytes_per_launch": fetch,
            "write_bytes_per_launch": write, "hbm_bytes_per_launch": fetch + write,
            "fetch_scale": f_scale, "write_scale": w_scale,
@@ -262,6 +276,115 @@ def traffic(name, fdir, wdir, cfdir, cwdir):
     with open(path, "w") as fh:
         json.dump(res, fh, indent=1)
     print(json.dumps(res))
+
+
+def quant_bytes(kind, rows, K):
+    """Algorithmic HBM bytes of one quantiser call: bf16 input read once,
+    1-byte codes and the scales written once."""
+    scale = rows * 4 if kind == "int8" else rows * (K // 128) * (4 if kind == "fp8" else 1)
+    return rows * K * 2 + rows * K + scale
+
+
+def quant_cpu_baseline(kind, x_rows, budget_s):
+    """The oracle's quantiser on a growing sample of rows (about budget_s)."""
+    from oracle import quant as Q
+    fn = {"int8": Q.quant_int8_rowwise, "fp8": Q.quant_fp8_blockwise,
+          "mx": Q.quant_fp8_mx}[kind]
+    R, K = x_rows.shape
+    rows, t = min(R, 64), 0.0
+    while True:
+        t0 = time.perf_counter()
+        fn(x_rows[:rows])
+        t = time.perf_counter() - t0
+        if rows >= R or t >= budget_s * 0.6:
+            break
+        rows = min(R, int(rows * max(1.5, min(8.0, budget_s * 0.8 / max(t, 1e-3)))))
+    return {"value": quant_bytes(kind, rows, K) / t / 1e9, "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{rows} of {R} rows of K={K} (bf16 values widened to fp32); "
+                      f"{t:.2f} s; numpy fp64, one thread"}
+
+
+def bench_quant(args):
+    import numpy as np
+    import torch
+
+    import block_scaled_precision_gemm_amd as bsmm
+    from synth import activations
+
+    name = args.config
+    kind, shape, dist, seed = QUANT_CONFIGS[name]
+    bsmm.load()
+    t0 = time.time()
+    x32 = activations(shape, seed=seed, dist=dist)
+    xb = torch.from_numpy(x32).to(torch.bfloat16)
+    K = shape[-1]
+    R = int(np.prod(shape[:-1]))
+    nbytes = quant_bytes(kind, R, K)
+    # enough copies that successive calls never find their data in the 256 MB
+    # last-level cache
+    copies = max(2, -(-(1 << 30) // nbytes))
+    xs = [xb.cuda() for _ in range(copies)]
+    fn = {"int8": bsmm.bsmm_quant_int8_rowwise, "fp8": bsmm.bsmm_quant_fp8_blockwise,
+          "mx": bsmm.bsmm_quant_fp8_mx}[kind]
+    outs = [fn(x) for x in xs]
+    torch.cuda.synchronize()
+    print(f"[bench] {name}: inputs ready in {time.time() - t0:.1f}s, {copies} copies",
+          file=sys.stderr, flush=True)
+    calls = [(lambda x=x, o=o: fn(x, q=o[0], scale=o[1])) for x, o in zip(xs, outs)]
+    t_settle = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t_settle < args.settle:
+        for _ in range(8):
+            calls[i % copies]()
+            i += 1
+        torch.cuda.synchronize()
+    for j in range(args.warmup):
+        calls[j % copies]()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()      # the stream the quantiser launches on
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t_wall = time.perf_counter()
+    for j, (s, e) in enumerate(ev):
+        s.record(stream)
+        calls[j % copies]()
+        e.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    kern_ms = sum(s.elapsed_time(e) for s, e in ev) / len(ev)
+    ms_per_step = wall * 1e3 / args.steps
+    roof = {"bound": "hbm", "achieved": nbytes / (kern_ms * 1e-3) / 1e9,
+            "peak": HBM_PEAK / 1e9, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    tf = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+    if os.path.exists(tf):
+        t = json.load(open(tf))
+        if t.get("kernel_hash") == kernel_hash(QUANT_SOURCES):
+            roof["traffic"] = t["hbm_bytes_per_launch"]
+    roof["kernel"] = {"int8": "quant_int8_rows", "fp8": "quant_fp8_blocks<fp32 scale>",
+                      "mx": "quant_fp8_blocks<e8m0 scale>"}[kind]
+    roof["kernel_ms_mean"] = kern_ms
+    roof["kernel_alg_bytes"] = nbytes
+    line = {
+        "metric": "GB/s of dynamic quantisation (algorithmic HBM bytes) and % of 8 TB/s",
+        "value": round(nbytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{kind} quantisation of bf16 activations {list(shape)}",
+                   "name": name, "rows": R, "K": K, "seed": seed, "dist": dist,
+                   "copies": copies},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = quant_cpu_baseline(kind, xb.float().numpy().reshape(R, K),
+                                                  args.cpu_budget)
+    print(json.dumps(line), flush=True)
 
 
 def main():
@@ -290,6 +413,9 @@ def main():
               "shards along M, N or G with no exchange, so per-GPU work is the one-GPU "
               "number", file=sys.stderr)
         sys.exit(2)
+
+    if args.config in QUANT_CONFIGS:
+        return bench_quant(args)
 
     import torch
 

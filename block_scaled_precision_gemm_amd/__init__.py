@@ -16,6 +16,7 @@ import os
 __all__ = [
     "load", "lib_path", "BsmmError",
     "bsmm_int8_rowwise", "bsmm_fp8_blockwise", "bsmm_fp8_mx_bmm",
+    "bsmm_quant_int8_rowwise", "bsmm_quant_fp8_blockwise", "bsmm_quant_fp8_mx",
     "bsmm_workspace_bytes", "bsmm_query_plan", "bsmm_set_override",
     "bsmm_variant_names", "bsmm_version", "bsmm_timing_enable", "bsmm_timing_read",
     "I32", "F32", "BF16", "OP_INT8_ROWWISE", "OP_FP8_BLOCKWISE", "OP_FP8_MX_BMM",
@@ -64,7 +65,11 @@ def load():
                                      vp, i64, st, i64, i64, i64, vp, sz, vp]
     L.bsmm_fp8_mx_bmm.argtypes = [vp, i64, i64, vp, i64, i64, vp, i64, i64, vp, i64,
                                   i64, vp, i64, i64, st, i64, i64, i64, i64, vp, sz, vp]
-    for f in ("bsmm_int8_rowwise", "bsmm_fp8_blockwise", "bsmm_fp8_mx_bmm"):
+    L.bsmm_quant_int8_rowwise.argtypes = [vp, i64, st, vp, i64, vp, i64, i64, i64, vp]
+    L.bsmm_quant_fp8_blockwise.argtypes = [vp, i64, st, vp, i64, vp, i64, i64, i64, i64, vp]
+    L.bsmm_quant_fp8_mx.argtypes = [vp, i64, st, vp, i64, vp, i64, i64, i64, i64, vp]
+    for f in ("bsmm_int8_rowwise", "bsmm_fp8_blockwise", "bsmm_fp8_mx_bmm",
+              "bsmm_quant_int8_rowwise", "bsmm_quant_fp8_blockwise", "bsmm_quant_fp8_mx"):
         getattr(L, f).restype = st
     L.bsmm_workspace_bytes.argtypes = [st, i64, i64, i64, i64, st]
     L.bsmm_workspace_bytes.restype = sz
@@ -308,6 +313,111 @@ def bsmm_fp8_mx_bmm(x, w, x_scale, w_scale, *, layout="m_major", out_dtype="bf16
         xs8.data_ptr(), xs_sg, xs_sm, ws8.data_ptr(), ws8.stride(0), ws8.stride(1),
         o.data_ptr(), o_sg, o_sm, code, G, M, N, K, wsp, wsn, _stream(stream)))
     return o
+
+
+def _quant_input(x, name="x"):
+    """A bf16 / fp32 tensor as rows of K: (rows view, input dtype code)."""
+    torch = _torch()
+    if x.dtype == torch.bfloat16:
+        code = BF16
+    elif x.dtype == torch.float32:
+        code = F32
+    else:
+        raise ValueError(f"{name}: expected bf16 or fp32, got {x.dtype}")
+    if x.dim() < 2:
+        raise ValueError(f"{name} must have at least 2 dimensions")
+    K = x.shape[-1]
+    if K and x.stride(-1) != 1:
+        raise ValueError(f"{name} must be contiguous along its last dimension")
+    if x.dim() == 2:
+        return x, code
+    if K == 0:
+        n = 1
+        for d in x.shape[:-1]:
+            n *= d
+        return x.new_empty((n, 0)), code
+    try:
+        rows = x.view(-1, K)
+    except RuntimeError as e:
+        raise ValueError(f"{name}: leading dimensions do not form rows of one stride") from e
+    return rows, code
+
+
+def _quant_out(t, shape, dtype, name, device):
+    torch = _torch()
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name} must be {tuple(shape)} {dtype}, got {tuple(t.shape)} {t.dtype}")
+    return t
+
+
+def bsmm_quant_int8_rowwise(x, *, q=None, scale=None, stream=None):
+    """Per-row symmetric int8 quantisation of x [M, K] (bf16 or fp32).
+
+    Returns (q int8 [M, K], scale fp32 [M, 1]) with x ~ q * scale: the
+    operand and scale_a of bsmm_int8_rowwise.
+    """
+    torch = _torch()
+    x2, code = _quant_input(x)
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M, K]")
+    M, K = x2.shape
+    q = _quant_out(q, (M, K), torch.int8, "q", x.device)
+    scale = _quant_out(scale, (M, 1), torch.float32, "scale", x.device)
+    if K and q.stride(1) != 1:
+        raise ValueError("q must be row-major")
+    _check(load().bsmm_quant_int8_rowwise(
+        x2.data_ptr(), x2.stride(0), code, q.data_ptr(), q.stride(0),
+        scale.data_ptr(), scale.stride(0), M, K, _stream(stream)))
+    return q, scale
+
+
+def bsmm_quant_fp8_blockwise(x, *, q=None, scale=None, stream=None):
+    """fp8 E4M3 quantisation of x [M, K] with one fp32 scale per 1 x 128 block.
+
+    Returns (q float8_e4m3fn [M, K], scale fp32 [M, K/128]); a given
+    ``scale`` may have any strides (e.g. the column-major transpose).
+    """
+    torch = _torch()
+    x2, code = _quant_input(x)
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M, K]")
+    M, K = x2.shape
+    KB = K // 128
+    q = _quant_out(q, (M, K), torch.float8_e4m3fn, "q", x.device)
+    scale = _quant_out(scale, (M, KB), torch.float32, "scale", x.device)
+    if K and q.stride(1) != 1:
+        raise ValueError("q must be row-major")
+    q8 = q.view(torch.uint8)
+    _check(load().bsmm_quant_fp8_blockwise(
+        x2.data_ptr(), x2.stride(0), code, q8.data_ptr(), q8.stride(0),
+        scale.data_ptr(), scale.stride(0), scale.stride(1), M, K, _stream(stream)))
+    return q, scale
+
+
+def bsmm_quant_fp8_mx(x, *, q=None, scale=None, stream=None):
+    """fp8 E4M3 quantisation with an e8m0 scale per 1 x 128 block along the
+    last dimension of x [..., K] (bf16 or fp32), e.g. the BMM's x [M, G, K]
+    or [G, M, K].
+
+    Returns (q float8_e4m3fn [..., K], scale uint8 e8m0 bytes [..., K/128]),
+    the x and x_scale of bsmm_fp8_mx_bmm.
+    """
+    torch = _torch()
+    x2, code = _quant_input(x)
+    K = x.shape[-1]
+    lead = tuple(x.shape[:-1])
+    q = _quant_out(q, lead + (K,), torch.float8_e4m3fn, "q", x.device)
+    scale = _quant_out(scale, lead + (K // 128,), torch.uint8, "scale", x.device)
+    if not q.is_contiguous() or not scale.is_contiguous():
+        raise ValueError("q and scale must be contiguous")
+    q8 = q.view(torch.uint8).view(-1, K) if K else q.view(torch.uint8)
+    M = x2.shape[0]
+    _check(load().bsmm_quant_fp8_mx(
+        x2.data_ptr(), x2.stride(0), code, q8.data_ptr(), K,
+        scale.data_ptr(), K // 128, 1, M, K, _stream(stream)))
+    return q, scale
 
 
 def bsmm_workspace_bytes(op, G, M, N, K, out_dtype):

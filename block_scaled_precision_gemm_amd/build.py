@@ -62,9 +62,10 @@ def build(verbose: bool = False) -> str:
         jobs.append([hipcc, *COMMON, *HIP_FLAGS, f"-DBSMM_TU_OP={op}",
                      f"-DBSMM_TU_OUT={out}", "-x", "hip", "-c",
                      os.path.join(CSRC, HIP_SOURCE), "-o", o])
-    o = os.path.join(OBJDIR, "bsmm_pack.o")
-    jobs.append([hipcc, *COMMON, *HIP_FLAGS, "-x", "hip", "-c",
-                 os.path.join(CSRC, "bsmm_pack.hip"), "-o", o])
+    for src in ("bsmm_pack.hip", "bsmm_quant.hip"):
+        o = os.path.join(OBJDIR, src.replace(".hip", ".o"))
+        jobs.append([hipcc, *COMMON, *HIP_FLAGS, "-x", "hip", "-c",
+                     os.path.join(CSRC, src), "-o", o])
     workers = min(len(jobs), max(1, min(8, os.cpu_count() or 1)))
     with ThreadPoolExecutor(workers) as ex:
         list(ex.map(_run, jobs))

@@ -518,6 +518,98 @@ const char* bsmm_variant_names(void) {
   return names.c_str();
 }
 
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the three quantisers; `block` is 8 (int8 rows) or 128.
+bsmm_status quant_common(const void* x, int64_t ldx, bsmm_dtype x_dtype, const void* q,
+                         int64_t ldq, const void* scale, int64_t s_m, int64_t s_kb,
+                         int64_t M, int64_t K, int block, size_t scale_align) {
+  CHECK(x_dtype == BSMM_F32 || x_dtype == BSMM_BF16, BSMM_ERR_DTYPE,
+        "quantiser input must be fp32 or bf16 (got %d)", (int)x_dtype);
+  CHECK(M >= 0 && K >= 0, BSMM_ERR_SHAPE, "negative size M=%lld K=%lld", (long long)M,
+        (long long)K);
+  CHECK(M < kMaxDim && K < kMaxDim, BSMM_ERR_UNSUPPORTED, "size beyond 2^31");
+  CHECK(K % block == 0, BSMM_ERR_UNSUPPORTED, "K=%lld is not a multiple of %d", (long long)K,
+        block);
+  if (M == 0) return BSMM_OK;
+  if (K == 0 && block != 8) return BSMM_OK;   // no blocks: nothing is written
+  CHECK(scale != nullptr, BSMM_ERR_NULL, "scale is NULL");
+  CHECK(aligned(scale, scale_align), BSMM_ERR_ALIGN, "scale not %d-byte aligned",
+        (int)scale_align);
+  CHECK(s_m >= 0 && s_kb >= 0, BSMM_ERR_SCALE_SHAPE, "scale strides must be >= 0");
+  // every (row, block) must own its scale: the strides may not alias
+  const int64_t KB = block == 8 ? 1 : K / block;
+  if (KB > 0) {
+    const bool rows_ok = M == 1 || s_m >= 1;
+    const bool cols_ok = KB == 1 || s_kb >= 1;
+    const bool disjoint = M == 1 || KB == 1 || s_m >= KB * s_kb || s_kb >= M * s_m;
+    CHECK(rows_ok && cols_ok && disjoint, BSMM_ERR_SCALE_SHAPE,
+          "scale strides s_m=%lld s_kb=%lld make two blocks share a scale", (long long)s_m,
+          (long long)s_kb);
+  }
+  if (K == 0) return BSMM_OK;
+  CHECK(x != nullptr && q != nullptr, BSMM_ERR_NULL, "x or q is NULL");
+  CHECK(ldx >= K && ldq >= K, BSMM_ERR_SHAPE, "leading dimensions ldx=%lld ldq=%lld below K",
+        (long long)ldx, (long long)ldq);
+  CHECK(ldx % 8 == 0, BSMM_ERR_ALIGN, "ldx=%lld is not a multiple of 8 elements",
+        (long long)ldx);
+  CHECK(ldq % 8 == 0, BSMM_ERR_ALIGN, "ldq=%lld is not a multiple of 8 bytes",
+        (long long)ldq);
+  CHECK(aligned(x, 16), BSMM_ERR_ALIGN, "x not 16-byte aligned");
+  CHECK(aligned(q, 8), BSMM_ERR_ALIGN, "q not 8-byte aligned");
+  return BSMM_OK;
+}
+
+bsmm_status quant_run(QuantArgs::Kind kind, const void* x, int64_t ldx, bsmm_dtype x_dtype,
+                      void* q, int64_t ldq, void* scale, int64_t s_m, int64_t s_kb, int64_t M,
+                      int64_t K, void* stream) {
+  QuantArgs a{};
+  a.kind = kind;
+  a.x = x; a.ldx = ldx; a.x_dtype = x_dtype;
+  a.q = q; a.ldq = ldq;
+  a.scale = scale; a.s_m = s_m; a.s_kb = s_kb;
+  a.M = M; a.K = K;
+  if (launch_quant(a, stream) != 0) return fail(BSMM_ERR_HIP, "quantiser launch failed");
+  return BSMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+bsmm_status bsmm_quant_int8_rowwise(const void* x, int64_t ldx, bsmm_dtype x_dtype,
+                                    int8_t* q, int64_t ldq, float* scale, int64_t s_m,
+                                    int64_t M, int64_t K, void* stream) {
+  bsmm_status st = quant_common(x, ldx, x_dtype, q, ldq, scale, s_m, 0, M, K, 8, 4);
+  if (st != BSMM_OK || M == 0) return st;
+  CHECK(M <= ((int64_t)1 << 26), BSMM_ERR_UNSUPPORTED, "M=%lld beyond 2^26 rows",
+        (long long)M);
+  return quant_run(QuantArgs::kInt8Rows, x, ldx, x_dtype, q, ldq, scale, s_m, 0, M, K, stream);
+}
+
+bsmm_status bsmm_quant_fp8_blockwise(const void* x, int64_t ldx, bsmm_dtype x_dtype,
+                                     uint8_t* q, int64_t ldq, float* scale, int64_t s_m,
+                                     int64_t s_kb, int64_t M, int64_t K, void* stream) {
+  bsmm_status st = quant_common(x, ldx, x_dtype, q, ldq, scale, s_m, s_kb, M, K, 128, 4);
+  if (st != BSMM_OK || M == 0 || K == 0) return st;
+  CHECK(M * (K / 128) < ((int64_t)1 << 30), BSMM_ERR_UNSUPPORTED,
+        "M * K / 128 = %lld blocks beyond 2^30", (long long)(M * (K / 128)));
+  return quant_run(QuantArgs::kFp8Blocks, x, ldx, x_dtype, q, ldq, scale, s_m, s_kb, M, K,
+                   stream);
+}
+
+bsmm_status bsmm_quant_fp8_mx(const void* x, int64_t ldx, bsmm_dtype x_dtype, uint8_t* q,
+                              int64_t ldq, uint8_t* scale, int64_t s_m, int64_t s_kb,
+                              int64_t M, int64_t K, void* stream) {
+  bsmm_status st = quant_common(x, ldx, x_dtype, q, ldq, scale, s_m, s_kb, M, K, 128, 1);
+  if (st != BSMM_OK || M == 0 || K == 0) return st;
+  CHECK(M * (K / 128) < ((int64_t)1 << 30), BSMM_ERR_UNSUPPORTED,
+        "M * K / 128 = %lld blocks beyond 2^30", (long long)(M * (K / 128)));
+  return quant_run(QuantArgs::kFp8Mx, x, ldx, x_dtype, q, ldq, scale, s_m, s_kb, M, K, stream);
+}
+
 const char* bsmm_status_string(bsmm_status s) {
   switch (s) {
     case BSMM_OK: return "BSMM_OK";

@@ -107,6 +107,22 @@ size_t splitk_workspace(const Problem& p, int rows, int split);
 bool timing_on();
 void timing_mark(void* stream, const char* name, bool begin);
 
+// Dynamic quantisation of bf16 / fp32 rows (bsmm_quant.hip).  Arguments are
+// validated by the entry points before this is called.
+struct QuantArgs {
+  enum Kind { kInt8Rows = 0, kFp8Blocks = 1, kFp8Mx = 2 };
+  Kind kind;
+  const void* x;        // [M, K] bf16 or fp32, row stride ldx elements
+  int64_t ldx;
+  bsmm_dtype x_dtype;   // BSMM_BF16 or BSMM_F32
+  void* q;              // [M, K] 1-byte codes, row stride ldq
+  int64_t ldq;
+  void* scale;          // fp32 (kInt8Rows, kFp8Blocks) or e8m0 bytes (kFp8Mx)
+  int64_t s_m, s_kb;    // scale strides in elements (s_kb unused for kInt8Rows)
+  int64_t M, K;
+};
+int launch_quant(const QuantArgs& a, void* stream);
+
 // Plan selection (host only).
 Plan make_plan(bsmm_op op, int G, int M, int N, int K, bsmm_dtype dt,
                size_t workspace_bytes);

@@ -1,0 +1,322 @@
+// Dynamic quantisation of bf16 / fp32 activations into the codes and scales
+// the scaled matmuls consume (gfx950).
+//
+//   int8, one scale per row: scale = amax / 127, code = clamp(rne(x / scale),
+//     +-127) -- the symmetric per-row activation quantisation of the torchao
+//     issue "Unify scaled INT8 matmul";
+//   fp8 E4M3FN, one fp32 scale per 1 x 128 block: scale = amax / 448, code =
+//     rne_e4m3(x / scale) -- the [M, K/128] activation scales of the PyTorch
+//     issue "torch._scaled_mm with blockwise scaling doesn't work with
+//     torch.compile";
+//   fp8 E4M3FN, one e8m0 scale per 1 x 128 block: scale = 2^e with
+//     e = ceil(log2(amax / 448)), code = rne_e4m3(x * 2^-e) -- the mxscale
+//     activations of the ROCm aiter PR "Add opus fp8 mxscale BMM kernels for
+//     gfx950" (Motivation).
+//
+// Every quotient is the correctly rounded binary32 quotient; rounding is to
+// nearest, ties to even; e4m3 saturates at +-448.  A row or block whose
+// fp32 scale is 0 (amax 0, or amax so small that amax / 127 or amax / 448
+// underflows) stores scale 1 (e8m0: byte 127, amax 0) and +0 codes.  The
+// e8m0 exponent is clamped below at -127.
+//
+// All three kernels move each input byte once and each output byte once, so
+// they are bound by HBM bandwidth: loads are 16 bytes per lane and
+// coalesced, the arithmetic per element is a handful of VALU operations.
+//
+// Division: x / s with one correctly rounded reciprocal r = 1 / s per row or
+// block and, per element, q0 = x * r, e = fma(-q0, s, x), q = fma(e, r, q0).
+// With r within half an ulp of 1/s and q0 within one ulp of x/s, e is exact
+// and q is the correctly rounded quotient as long as nothing underflows
+// (Markstein, "Computation of elementary functions on the IBM RISC
+// System/6000 processor", 1990).  That holds for every element whose
+// quotient can reach a rounding boundary of the int8 or e4m3 grid when
+// s >= 2^-80; below that the kernels divide each element with the IEEE
+// division instead.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "bsmm.h"
+#include "bsmm_internal.h"
+
+namespace bsmm {
+namespace {
+
+constexpr float kFastDivMin = 0x1p-80f;
+constexpr int kRowsPerWg = 4;          // int8: one wave per row
+constexpr int kBlocksPerIter = 16;     // fp8: 16 lanes per 128-element block
+constexpr int kIters = 4;              // blocks per lane group per workgroup
+constexpr int kBlocksPerWg = kBlocksPerIter * kIters;
+
+// ---- 8 consecutive input elements -------------------------------------------
+
+template <typename T> struct Raw8;
+template <> struct Raw8<uint16_t> { uint4 v; };            // bf16 bits
+template <> struct Raw8<float> { uint4 lo, hi; };          // fp32 bits
+
+__device__ inline void load8(Raw8<uint16_t>& r, const uint16_t* p) {
+  r.v = *reinterpret_cast<const uint4*>(p);
+}
+__device__ inline void load8(Raw8<float>& r, const float* p) {
+  r.lo = reinterpret_cast<const uint4*>(p)[0];
+  r.hi = reinterpret_cast<const uint4*>(p)[1];
+}
+
+// Widen to fp32 (bf16 -> fp32 is exact: the bf16 bits are the top half).
+__device__ inline void widen(const Raw8<uint16_t>& r, float f[8]) {
+  const uint32_t w[4] = {r.v.x, r.v.y, r.v.z, r.v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+__device__ inline void widen(const Raw8<float>& r, float f[8]) {
+  const uint32_t w[8] = {r.lo.x, r.lo.y, r.lo.z, r.lo.w, r.hi.x, r.hi.y, r.hi.z, r.hi.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = __uint_as_float(w[i]);
+}
+
+// max |x| of the 8 elements, as the bits of a non-negative float (integer
+// order equals float order for non-negative finite values)
+template <typename T>
+__device__ inline uint32_t absmax_bits(const Raw8<T>& r) {
+  float f[8];
+  widen(r, f);
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = max(m, __float_as_uint(f[i]) & 0x7FFFFFFFu);
+  return m;
+}
+
+// ---- cross-lane maxima -------------------------------------------------------
+
+// DPP row operations act on 16-lane rows: xor 1 and xor 2 inside each quad,
+// then rotations by 4 and 8 inside the row.
+__device__ inline uint32_t row16_max(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false));
+  return v;
+}
+__device__ inline uint32_t wave_max(uint32_t v) {
+  v = row16_max(v);
+  v = max(v, (uint32_t)__shfl_xor((int)v, 16));
+  v = max(v, (uint32_t)__shfl_xor((int)v, 32));
+  return v;
+}
+
+// ---- division and rounding ---------------------------------------------------
+
+// s > 0, so the quotient has the sign of x; the correction step alone would
+// turn x = -0 into +0 (fma(+0, r, -0) = +0).
+__device__ inline float div_fast(float x, float s, float r) {
+  const float q0 = __fmul_rn(x, r);
+  const float e = __builtin_fmaf(-q0, s, x);
+  return __builtin_copysignf(__builtin_fmaf(e, r, q0), x);
+}
+
+// Four e4m3 codes (nearest, ties to even) of values already within +-448,
+// packed little-endian.  The gfx950 conversion writes OCP E4M3FN in the
+// current rounding mode (round to nearest even).
+__device__ inline uint32_t e4m3x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
+__device__ inline float clamp448(float t) {
+  return __builtin_amdgcn_fmed3f(t, -448.0f, 448.0f);
+}
+
+// int8 codes of four values already rounded to integers in [-127, 127]
+__device__ inline uint32_t i8x4(float a, float b, float c, float d) {
+  const uint32_t lo = __builtin_amdgcn_perm((uint32_t)(int)b, (uint32_t)(int)a, 0x0C0C0400u);
+  const uint32_t hi = __builtin_amdgcn_perm((uint32_t)(int)d, (uint32_t)(int)c, 0x0C0C0400u);
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
+
+__device__ inline float round_i8(float t) {
+  return __builtin_amdgcn_fmed3f(__builtin_rintf(t), -127.0f, 127.0f);
+}
+
+// ---- int8, one scale per row ---------------------------------------------------
+
+// One wave per row.  A pass covers 64 * 8 * NV elements, held in registers;
+// a row longer than that is read twice (amax, then codes).
+template <typename T, int NV>
+__global__ void __launch_bounds__(256)
+quant_int8_rows(const T* __restrict__ x, int64_t ldx, int8_t* __restrict__ q, int64_t ldq,
+                float* __restrict__ scale, int64_t s_m, int M, int K) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kRowsPerWg + (threadIdx.x >> 6);
+  if (row >= M) return;   // whole waves only
+  const T* xr = x + (int64_t)row * ldx;
+  int8_t* qr = q + (int64_t)row * ldq;
+  constexpr int kPass = 64 * 8 * NV;
+  Raw8<T> buf[NV];
+  uint32_t amax = 0;
+  // Lanes past the end of the row load the row's last 8 elements (always in
+  // bounds, K >= 8 here) and leave them out of the maximum; loads are never
+  // branched around, so the buffers stay in registers.
+  for (int base = 0; base < K; base += kPass) {
+#pragma unroll
+    for (int v = 0; v < NV; ++v) load8(buf[v], xr + min(base + (v * 64 + lane) * 8, K - 8));
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const uint32_t m = absmax_bits(buf[v]);
+      amax = max(amax, base + (v * 64 + lane) * 8 < K ? m : 0u);
+    }
+  }
+  amax = wave_max(amax);
+  float s = __uint_as_float(amax) / 127.0f;
+  if (!(s > 0.0f)) s = 1.0f;   // amax 0 or an underflowing scale: codes are 0 anyway
+  if (lane == 0) scale[(int64_t)row * s_m] = s;
+  const bool fast = s >= kFastDivMin;
+  const float r = 1.0f / s;
+  for (int base = 0; base < K; base += kPass) {
+    if (K > kPass) {
+#pragma unroll
+      for (int v = 0; v < NV; ++v) load8(buf[v], xr + min(base + (v * 64 + lane) * 8, K - 8));
+    }
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int k = base + (v * 64 + lane) * 8;
+      if (k >= K) continue;
+      float f[8];
+      widen(buf[v], f);
+      if (fast) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = round_i8(div_fast(f[i], s, r));
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = round_i8(f[i] / s);
+      }
+      uint2 w;
+      w.x = i8x4(f[0], f[1], f[2], f[3]);
+      w.y = i8x4(f[4], f[5], f[6], f[7]);
+      *reinterpret_cast<uint2*>(qr + k) = w;
+    }
+  }
+}
+
+// ---- fp8, one scale per 1 x 128 block ------------------------------------------
+
+// e8m0 exponent ceil(log2(amax / 448)) from the bits of amax, clamped to
+// [-127, 127].  448 = 1.75 * 2^8: for amax = m * 2^E (m in [1, 2)) the
+// exponent is E - 8 when m <= 1.75, else E - 7.  A subnormal amax is below
+// 448 * 2^-127 and takes the clamp; amax 0 gives 0.
+__device__ inline int e8m0_exponent(uint32_t amax_bits) {
+  if (amax_bits == 0) return 0;
+  const int field = (int)(amax_bits >> 23);
+  if (field == 0) return -127;
+  const int e = field - 127 - 8 + ((amax_bits & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  return max(e, -127);
+}
+
+// MX = false: fp32 scale amax / 448; MX = true: e8m0 scale.
+template <typename T, bool MX>
+__global__ void __launch_bounds__(256)
+quant_fp8_blocks(const T* __restrict__ x, int64_t ldx, uint8_t* __restrict__ q, int64_t ldq,
+                 void* __restrict__ scale, int64_t s_m, int64_t s_kb, uint32_t nblocks,
+                 uint32_t KB) {
+  const int l = threadIdx.x & 15;
+  const uint32_t b0 = blockIdx.x * kBlocksPerWg + (threadIdx.x >> 4);
+  Raw8<T> buf[kIters];
+  uint32_t row[kIters], kb[kIters];
+  // a block past the end loads the last block (in bounds, nblocks >= 1) and
+  // stores nothing
+#pragma unroll
+  for (int u = 0; u < kIters; ++u) {
+    const uint32_t b = min(b0 + u * kBlocksPerIter, nblocks - 1);
+    row[u] = b / KB;
+    kb[u] = b - row[u] * KB;
+    load8(buf[u], x + (int64_t)row[u] * ldx + (int64_t)kb[u] * 128 + l * 8);
+  }
+#pragma unroll
+  for (int u = 0; u < kIters; ++u) {
+    // the 16 lanes of a block share a DPP row, and a row is live or dead as a whole
+    const uint32_t amax = row16_max(absmax_bits(buf[u]));
+    if (b0 + u * kBlocksPerIter >= nblocks) continue;
+    float f[8];
+    widen(buf[u], f);
+    uint2 w;
+    if (MX) {
+      const int e = e8m0_exponent(amax);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) f[i] = __builtin_amdgcn_ldexpf(f[i], -e);
+      w.x = e4m3x4(f[0], f[1], f[2], f[3]);
+      w.y = e4m3x4(f[4], f[5], f[6], f[7]);
+      if (amax == 0) w = make_uint2(0, 0);
+      if (l == 0)
+        static_cast<uint8_t*>(scale)[(int64_t)row[u] * s_m + (int64_t)kb[u] * s_kb] =
+            (uint8_t)(e + 127);
+    } else {
+      float s = __uint_as_float(amax) / 448.0f;
+      const bool zero = !(s > 0.0f);
+      if (zero) s = 1.0f;
+      if (s >= kFastDivMin) {
+        const float r = 1.0f / s;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = clamp448(div_fast(f[i], s, r));
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = clamp448(f[i] / s);
+      }
+      w.x = e4m3x4(f[0], f[1], f[2], f[3]);
+      w.y = e4m3x4(f[4], f[5], f[6], f[7]);
+      if (zero) w = make_uint2(0, 0);
+      if (l == 0)
+        static_cast<float*>(scale)[(int64_t)row[u] * s_m + (int64_t)kb[u] * s_kb] = s;
+    }
+    *reinterpret_cast<uint2*>(q + (int64_t)row[u] * ldq + (int64_t)kb[u] * 128 + l * 8) = w;
+  }
+}
+
+template <typename T, int NV>
+void launch_rows(const QuantArgs& a, hipStream_t st) {
+  const unsigned grid = (unsigned)((a.M + kRowsPerWg - 1) / kRowsPerWg);
+  hipLaunchKernelGGL((quant_int8_rows<T, NV>), dim3(grid), dim3(256), 0, st,
+                     static_cast<const T*>(a.x), a.ldx, static_cast<int8_t*>(a.q), a.ldq,
+                     static_cast<float*>(a.scale), a.s_m, (int)a.M, (int)a.K);
+}
+
+template <typename T>
+void launch_rows_nv(const QuantArgs& a, hipStream_t st) {
+  if (a.K <= 512) launch_rows<T, 1>(a, st);
+  else if (a.K <= 1024) launch_rows<T, 2>(a, st);
+  else if (a.K <= 2048) launch_rows<T, 4>(a, st);
+  else launch_rows<T, 8>(a, st);
+}
+
+template <typename T, bool MX>
+void launch_blocks(const QuantArgs& a, hipStream_t st) {
+  const uint32_t KB = (uint32_t)(a.K / 128);
+  const uint32_t nblocks = (uint32_t)(a.M * KB);
+  const unsigned grid = (nblocks + kBlocksPerWg - 1) / kBlocksPerWg;
+  hipLaunchKernelGGL((quant_fp8_blocks<T, MX>), dim3(grid), dim3(256), 0, st,
+                     static_cast<const T*>(a.x), a.ldx, static_cast<uint8_t*>(a.q), a.ldq,
+                     a.scale, a.s_m, a.s_kb, nblocks, KB);
+}
+
+}  // namespace
+
+int launch_quant(const QuantArgs& a, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool bf = a.x_dtype == BSMM_BF16;
+  switch (a.kind) {
+    case QuantArgs::kInt8Rows:
+      if (bf) launch_rows_nv<uint16_t>(a, st); else launch_rows_nv<float>(a, st);
+      break;
+    case QuantArgs::kFp8Blocks:
+      if (bf) launch_blocks<uint16_t, false>(a, st); else launch_blocks<float, false>(a, st);
+      break;
+    default:
+      if (bf) launch_blocks<uint16_t, true>(a, st); else launch_blocks<float, true>(a, st);
+      break;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+}  // namespace bsmm

@@ -158,6 +158,61 @@ bsmm_status bsmm_fp8_mx_bmm(const uint8_t* x, int64_t x_sg, int64_t x_sm,
                             void* workspace, size_t workspace_bytes,
                             void* stream);
 
+/*
+ * Dynamic quantisation: bf16 / fp32 activations -> the 1-byte codes and the
+ * scales the three matmuls above consume.  x is [M, K] row-major with row
+ * stride ldx elements (x_dtype BSMM_BF16 or BSMM_F32); q is [M, K] with row
+ * stride ldq bytes.  A scale is a dequantisation multiplier (x ~ code *
+ * scale).  Quotients are correctly rounded binary32, codes are the nearest
+ * ones (ties to even); e4m3 saturates at +-448.  A row or block whose fp32
+ * scale is 0 -- amax 0, or amax below about 2^-141 so that the division
+ * underflows -- stores scale 1 and +0 codes (the e8m0 quantiser: byte 127
+ * and +0 codes when amax is 0).  NaN / infinite inputs are unsupported.
+ *
+ * Pointers are device pointers owned by the caller; x, q and scale must not
+ * overlap.  Needs ldx % 8 == 0, ldq % 8 == 0, x 16-byte and q 8-byte
+ * aligned, fp32 scales 4-byte aligned; scale strides >= 0 that give every row (block) its
+ * own scale (BSMM_ERR_SCALE_SHAPE otherwise).  M == 0 does nothing; K == 0
+ * writes only the int8 row scales (1.0).  Asynchronous on `stream`, as the
+ * matmuls; errors from the arguments are returned before anything runs.
+ *
+ * int8, one scale per row (the symmetric per-row activation quantisation of
+ * the torchao issue "Unify scaled INT8 matmul"):
+ *   scale[m*s_m] = amax_m / 127,  q[m*ldq + k] = clamp(rne(x / scale), -127, 127)
+ * K % 8 == 0, M <= 2^26.
+ */
+bsmm_status bsmm_quant_int8_rowwise(const void* x, int64_t ldx, bsmm_dtype x_dtype,
+                                    int8_t* q, int64_t ldq,
+                                    float* scale, int64_t s_m,
+                                    int64_t M, int64_t K, void* stream);
+
+/*
+ * fp8 E4M3FN, one fp32 scale per 1 x 128 block of a row (the scale_a
+ * (M, K/128) of the PyTorch issue "torch._scaled_mm with blockwise scaling
+ * doesn't work with torch.compile"):
+ *   scale[m*s_m + kb*s_kb] = amax_{m,kb} / 448,  q = rne_e4m3(x / scale)
+ * K % 128 == 0, M * K / 128 < 2^30.  s_m = K/128, s_kb = 1 is the row-major
+ * scale tensor; s_m = 1, s_kb = M its column-major transpose.
+ */
+bsmm_status bsmm_quant_fp8_blockwise(const void* x, int64_t ldx, bsmm_dtype x_dtype,
+                                     uint8_t* q, int64_t ldq,
+                                     float* scale, int64_t s_m, int64_t s_kb,
+                                     int64_t M, int64_t K, void* stream);
+
+/*
+ * fp8 E4M3FN with an e8m0 scale per 1 x 128 block (the mxscale activations
+ * of the ROCm aiter PR "Add opus fp8 mxscale BMM kernels for gfx950",
+ * Motivation):  e = ceil(log2(amax / 448)) clamped to >= -127,
+ *   scale[m*s_m + kb*s_kb] = e + 127 (byte),  q = rne_e4m3(x * 2^-e)
+ * K % 128 == 0, M * K / 128 < 2^30.  The BMM's x [M, G, K] (m-major) or
+ * [G, M, K] (batch-first) is M*G rows of K, its x_scale the matching
+ * M*G rows of K/128 bytes (s_m = K/128, s_kb = 1).
+ */
+bsmm_status bsmm_quant_fp8_mx(const void* x, int64_t ldx, bsmm_dtype x_dtype,
+                              uint8_t* q, int64_t ldq,
+                              uint8_t* scale, int64_t s_m, int64_t s_kb,
+                              int64_t M, int64_t K, void* stream);
+
 /* Workspace bytes the fastest plan for this problem wants (0 if none). */
 size_t bsmm_workspace_bytes(bsmm_op op, int64_t G, int64_t M, int64_t N,
                             int64_t K, bsmm_dtype out_dtype);

@@ -45,6 +45,7 @@ __all__ = [
     "fp8_blockwise_inputs",
     "fp8_mx_bmm_inputs",
     "config_inputs",
+    "activations",
     "CONFIGS",
 ]
 
@@ -164,6 +165,22 @@ def quant_fp8_blocks_e8m0(x: np.ndarray, br: int, bc: int):
         q = np.ldexp(xb[i0:i1].astype(np.float64), -ex[i0:i1, None, :, None])
         cb[i0:i1] = e4m3_encode(q)
     return codes, (ex + 127).astype(np.uint8)
+
+
+def activations(shape, seed, *, dist="normal", row_scale_log2=None):
+    """Unquantised fp32 activations for the dynamic quantisers: ``normal(0,1)``
+    or ``standard_t(3)`` (``dist="t"``) drawn as above.  ``row_scale_log2``
+    (lo, hi) multiplies each row (all but the last axis) by ``2**u``, u
+    uniform in [lo, hi), drawn after the values, so rows span many binades.
+    """
+    rng = np.random.default_rng(seed)
+    x = _draw(rng, dist, shape)
+    if row_scale_log2 is not None:
+        lo, hi = row_scale_log2
+        rows = x.reshape(-1, x.shape[-1])
+        f = np.exp2(rng.uniform(lo, hi, rows.shape[0])).astype(np.float32)
+        rows *= f[:, None]
+    return x
 
 
 # ---------------------------------------------------------------------------

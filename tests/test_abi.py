@@ -113,6 +113,56 @@ def test_mx_noops():
     assert mx(G=0) == OK and mx(M=0) == OK and mx(N=0) == OK
 
 
+def qi8(*, x=P, ldx=256, xdt=bsmm.BF16, q=P, ldq=256, sc=P, s_m=1, M=64, K=256):
+    return bsmm.load().bsmm_quant_int8_rowwise(x, ldx, xdt, q, ldq, sc, s_m, M, K, None)
+
+
+def qbw(*, fn="bsmm_quant_fp8_blockwise", x=P, ldx=256, xdt=bsmm.F32, q=P, ldq=256, sc=P,
+        s_m=2, s_kb=1, M=64, K=256):
+    return getattr(bsmm.load(), fn)(x, ldx, xdt, q, ldq, sc, s_m, s_kb, M, K, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(xdt=bsmm.I32), DTYPE), (dict(M=-1), SHAPE), (dict(K=-8), SHAPE),
+    (dict(K=100), UNSUP), (dict(M=(1 << 26) + 1), UNSUP), (dict(K=2**31), UNSUP),
+    (dict(sc=None), NULL), (dict(x=None), NULL), (dict(q=None), NULL),
+    (dict(s_m=-1), SCALE), (dict(s_m=0), SCALE),
+    (dict(ldx=128), SHAPE), (dict(ldq=128), SHAPE), (dict(ldx=260), ALIGN),
+    (dict(ldq=260), ALIGN), (dict(x=P + 8), ALIGN), (dict(q=P + 4), ALIGN),
+    (dict(sc=P + 2), ALIGN),
+])
+def test_quant_int8_rejects(kw, status):
+    assert qi8(**kw) == status
+    assert bsmm.load().bsmm_last_error().decode()
+
+
+@pytest.mark.parametrize("fn", ["bsmm_quant_fp8_blockwise", "bsmm_quant_fp8_mx"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(xdt=7), DTYPE), (dict(K=200), UNSUP), (dict(M=1 << 23, K=1 << 14, ldx=1 << 14,
+                                                          ldq=1 << 14, s_m=128), UNSUP),
+    (dict(sc=None), NULL), (dict(x=None), NULL),
+    (dict(s_kb=-1), SCALE), (dict(s_m=1, s_kb=1), SCALE), (dict(s_m=0), SCALE),
+    (dict(s_kb=0), SCALE), (dict(s_m=1, s_kb=63), SCALE),
+    (dict(ldq=255), SHAPE), (dict(ldx=260), ALIGN), (dict(q=P + 4), ALIGN),
+    (dict(ldq=260), ALIGN),
+])
+def test_quant_fp8_rejects(fn, kw, status):
+    assert qbw(fn=fn, **kw) == status
+
+
+def test_quant_noops_and_scale_layouts():
+    assert qi8(M=0, x=None, q=None, sc=None) == OK
+    # fp8 with K == 0 has no blocks: nothing is read or written
+    for fn in ("bsmm_quant_fp8_blockwise", "bsmm_quant_fp8_mx"):
+        assert qbw(fn=fn, K=0, x=None, q=None, sc=None) == OK
+        assert qbw(fn=fn, M=0) == OK
+        # the column-major scale layout (s_m = 1, s_kb = M) passes validation;
+        # M = 0 keeps the call from launching
+        assert qbw(fn=fn, M=0, s_m=1, s_kb=64) == OK
+    assert bsmm.load().bsmm_quant_fp8_mx(P, 256, bsmm.F32, P, 256, P + 1, 2, 1, 0, 256,
+                                         None) == OK   # byte scales need no alignment
+
+
 # ----------------------------------------------------------------- binding --
 
 def test_binding_scale_shape_rules_follow_the_page():
