@@ -66,7 +66,7 @@ def assert_same(kind, got, want, where=""):
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 @pytest.mark.parametrize("M,K", [(37, 8), (37, 520), (5, 4096), (6, 4104), (3, 12288),
-                                 (129, 1024)])
+                                 (129, 1024), (7, 1536), (9, 2048), (4, 8200)])
 def test_int8_rows_parity(gpu_lib, dt, M, K):
     x = activations((M, K), seed=M * 7 + K, dist="t", row_scale_log2=(-40, 40))
     xd, xv = device_input(x, dt)
