@@ -224,6 +224,99 @@ def fp8_mx_bmm(x, w, x_scale, w_scale, layout="m_major", out_dtype="bf16",
 
 
 # ---------------------------------------------------------------------------
+# fp8 E4M3 _scaled_mm with tensorwise or rowwise fp32 scales (Inductor
+# mm.py: tuned_scaled_mm and the Triton template's load_scales /
+# apply_scaling; the PyTorch blockwise issue states the shape rules: both
+# scales scalar, or scale_a (M, 1) and scale_b (1, N)).  The fp8 product is
+# accumulated over all of K, then multiplied by a_scales[:, None] *
+# b_scales[None, :] (or the scalar product); the optional bias [N] is added
+# to the result (tuned_scaled_mm's docstring).  scale_result is only named
+# there; the reading taken here: it multiplies the final value (after the
+# bias) before the conversion to the output type.  Outputs: fp32, bf16, or
+# E4M3 codes (nearest, ties to even, saturating at +-448).
+#   C[m, n] = (sum_k A[m,k] B[k,n] * (sa[m] * sb[n]) + bias[n]) * sr
+# ---------------------------------------------------------------------------
+
+def fp8_scaled_mm(a, b_kn, scale_a, scale_b, bias=None, scale_result=None,
+                  out_dtype="bf16", rows=None, cols=None) -> Result:
+    a = np.asarray(a, dtype=np.uint8)
+    b_kn = np.asarray(b_kn, dtype=np.uint8)
+    M, K = a.shape
+    K2, N = b_kn.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ")
+    sa = np.asarray(scale_a, dtype=np.float32)
+    sb = np.asarray(scale_b, dtype=np.float32)
+    if sa.size == 1 and sb.size == 1 and sa.ndim in (0, 2) and sb.ndim in (0, 2):
+        sa_v = np.full(M, sa.reshape(-1)[0], np.float32)        # tensorwise
+        sb_v = np.full(N, sb.reshape(-1)[0], np.float32)
+    elif sa.shape == (M, 1) and sb.shape == (1, N):
+        sa_v, sb_v = sa[:, 0], sb[0, :]                         # rowwise
+    else:
+        raise ValueError(f"scale shapes {sa.shape}, {sb.shape}: tensorwise needs two "
+                         f"scalars, rowwise ({M}, 1) and (1, {N})")
+    # every partial sum of the integer numerators is below K * 229376**2
+    if K * 229376 ** 2 >= 2 ** 53:
+        raise ValueError("K too large for the exact fp64 route")
+    r = _idx(M, rows)
+    c = _idx(N, cols)
+    nA, nanA = e4m3_numerator(a[r])
+    nB, nanB = e4m3_numerator(b_kn[:, c])
+    if nanA.any() or nanB.any():
+        raise ValueError("NaN codes in the operands")
+    nA = nA.astype(np.float64)
+    nB = nB.astype(np.float64)
+    P = nA @ nB                                           # exact integers
+    Pabs = np.abs(nA) @ np.abs(nB)
+    s = sa_v[r].astype(np.float64)[:, None] * sb_v[c].astype(np.float64)[None, :]   # exact
+    C = s * P * TWO_M18
+    Bd = np.abs(s) * Pabs * TWO_M18
+    if bias is not None:
+        bv = np.asarray(bias, dtype=np.float64).reshape(-1)
+        if bv.shape != (N,):
+            raise ValueError(f"bias must have N = {N} elements")
+        C = C + bv[c][None, :]
+        Bd = Bd + np.abs(bv[c])[None, :]
+    if scale_result is not None:
+        sr = float(np.float32(scale_result))
+        C = C * sr
+        Bd = Bd * abs(sr)
+    if out_dtype == "e4m3":
+        from .quant import e4m3_encode_rne
+        return Result(exact=C, out=e4m3_encode_rne(C), bound=Bd)
+    return _finish_fp(C, Bd, out_dtype)
+
+
+def compare_e4m3(codes, res: Result, gamma: float) -> dict:
+    """E4M3 outputs.  If the GPU's binary32 value before the conversion is
+    within tol = gamma * Bd of the exact value C, its nearest code q obeys
+    |dec(q) - C| <= |dec(RNE(C)) - C| + 2 tol (both are nearest codes to
+    points tol apart), and equals RNE(C) wherever C is farther than tol from
+    every rounding boundary.  gamma: the fp32 accumulation error bound
+    relative to Bd; with gamma = 0 (an exactly representable result) the
+    codes must be identical."""
+    from .formats import e4m3_value
+    codes = np.asarray(codes, dtype=np.uint8)
+    if codes.shape != res.out.shape:
+        return {"ok": False, "why": f"shape {codes.shape} vs {res.out.shape}"}
+    C = res.exact
+    tol = gamma * res.bound
+    dq = e4m3_value(codes)
+    if np.isnan(dq).any():
+        return {"ok": False, "why": "NaN code"}
+    dref = e4m3_value(res.out)
+    lim = np.abs(dref - np.clip(C, -448.0, 448.0)) + 2 * tol
+    bad = np.abs(dq - np.clip(C, -448.0, 448.0)) > lim
+    # identical sign bit where the exact value has a sign (zero codes aside)
+    bad |= (codes != res.out) & (tol == 0)
+    rep = {"ok": not bad.any(), "violations": int(bad.sum()),
+           "identical": float((codes == res.out).mean()) if codes.size else 1.0}
+    if bad.any():
+        rep["first"] = tuple(int(i) for i in np.argwhere(bad)[0])
+    return rep
+
+
+# ---------------------------------------------------------------------------
 # Comparison rule.
 #   integer accumulators and the int8 path's fp32/bf16 outputs: exact equality
 #   (the GPU performs the same binary32 operations in the same order);

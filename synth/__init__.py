@@ -44,6 +44,7 @@ __all__ = [
     "int8_rowwise_inputs",
     "fp8_blockwise_inputs",
     "fp8_mx_bmm_inputs",
+    "fp8_scaled_mm_inputs",
     "config_inputs",
     "activations",
     "CONFIGS",
@@ -233,6 +234,35 @@ def fp8_blockwise_inputs(M, N, K, seed, *, dist="normal"):
     del b_kn
     b_nk = np.ascontiguousarray(b_q.T)
     return dict(a=a, b_nk=b_nk, scale_a=sa, scale_b=sb)
+
+
+def fp8_scaled_mm_inputs(M, N, K, seed, *, scaling="rowwise", bias=None, dist="normal"):
+    """fp8 _scaled_mm problem with tensorwise or rowwise fp32 scales: A [M,K]
+    quantised per row (rowwise) or as a whole (tensorwise) with scale
+    amax/448, B logical [K,N] per output column or as a whole.  ``bias``:
+    None, "f32" (N(0,1) values) or "bf16" (the same, cut to bf16-exact
+    values).
+
+    Returns dict(a uint8 [M,K], b_nk uint8 [N,K], scale_a fp32 (M,1) or (),
+    scale_b fp32 (1,N) or (), bias fp32 [N] or None)."""
+    rng = np.random.default_rng(seed)
+    a_f = _draw(rng, dist, (M, K))
+    b_kn = _draw(rng, dist, (K, N))
+    if scaling == "rowwise":
+        a, sa = quant_fp8_blocks_fp32(a_f, 1, K)            # sa [M, 1]
+        b_q, sb = quant_fp8_blocks_fp32(b_kn, K, 1)         # sb [1, N]
+    elif scaling == "tensorwise":
+        a, sa = quant_fp8_blocks_fp32(a_f, M, K)
+        b_q, sb = quant_fp8_blocks_fp32(b_kn, K, N)
+        sa, sb = sa.reshape(()), sb.reshape(())
+    else:
+        raise ValueError(scaling)
+    bv = None
+    if bias is not None:
+        bv = _draw(rng, "normal", (N,))
+        if bias == "bf16":
+            bv = (bv.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32)
+    return dict(a=a, b_nk=np.ascontiguousarray(b_q.T), scale_a=sa, scale_b=sb, bias=bv)
 
 
 def fp8_mx_bmm_inputs(G, M, N, K, seed, *, layout="m_major", dist="normal"):

@@ -1,0 +1,226 @@
+"""Pins for the oracle's fp8 ``_scaled_mm`` with tensorwise / rowwise scales,
+bias and scale_result (CPU).
+
+* brute force in exact rationals on tiny shapes (every term of the
+  definition: products, both scales, bias, scale_result);
+* PyTorch's fp64 dequantise-then-matmul (its own float8 decode and BLAS);
+* special cases: unit scales give the integer GEMM of the E4M3 numerators;
+  tensorwise equals rowwise with constant scales;
+* invariants: a power-of-two row or column scale scales exactly that row or
+  column; a bias shifts each column exactly;
+* output formats: hand-worked E4M3 results (round to nearest even, ties,
+  saturation) and the comparison rule for E4M3 outputs;
+* the tensorwise and rowwise shape rules of the PyTorch blockwise issue
+  (``tests/golden/blockwise_scale_shapes.txt``).
+"""
+
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import scaled_mm as S
+from oracle.formats import bf16_bits_to_f64, e4m3_numerator, e4m3_value, round_f32
+from synth import fp8_scaled_mm_inputs
+from tests.exact import e4m3_exact, rne_f32
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _brute(a, b_kn, sa, sb, bias, sr, rows, cols):
+    """Exact values, and the magnitude (|acc s| + |bias|) |sr| that bounds the
+    oracle's fp64 rounding (one product, one sum)."""
+    K = a.shape[1]
+    out, mag = [], []
+    for m in rows:
+        row, mrow = [], []
+        for n in cols:
+            acc = sum(e4m3_exact(int(a[m, k])) * e4m3_exact(int(b_kn[k, n])) for k in range(K))
+            v = acc * (Fraction(float(sa[m])) * Fraction(float(sb[n])))
+            g = abs(v)
+            if bias is not None:
+                v += Fraction(float(bias[n]))
+                g += abs(Fraction(float(bias[n])))
+            if sr is not None:
+                v *= Fraction(float(np.float32(sr)))
+                g *= abs(Fraction(float(np.float32(sr))))
+            row.append(v)
+            mrow.append(g)
+        out.append(row)
+        mag.append(mrow)
+    return out, mag
+
+
+def _close(x, w, g):
+    return abs(Fraction(float(x)) - w) <= g * Fraction(1, 2**50) + Fraction(1, 2**80)
+
+
+def _vectors(p, M, N):
+    sa = np.broadcast_to(np.asarray(p["scale_a"], np.float32).reshape(-1), (M,)) \
+        if np.asarray(p["scale_a"]).size == 1 else p["scale_a"][:, 0]
+    sb = np.broadcast_to(np.asarray(p["scale_b"], np.float32).reshape(-1), (N,)) \
+        if np.asarray(p["scale_b"]).size == 1 else p["scale_b"][0, :]
+    return sa, sb
+
+
+@pytest.mark.parametrize("scaling,bias,sr", [("rowwise", None, None), ("rowwise", "f32", 0.375),
+                                             ("tensorwise", "bf16", None),
+                                             ("tensorwise", None, 3.0)])
+def test_brute_force_exact_rationals(scaling, bias, sr):
+    M, N, K = 3, 5, 40
+    p = fp8_scaled_mm_inputs(M, N, K, 7, scaling=scaling, bias=bias)
+    b_kn = p["b_nk"].T
+    res = S.fp8_scaled_mm(p["a"], b_kn, p["scale_a"], p["scale_b"], bias=p["bias"],
+                          scale_result=sr, out_dtype="f32")
+    sa, sb = _vectors(p, M, N)
+    want, mag = _brute(p["a"], b_kn, sa, sb, p["bias"], sr, range(M), range(N))
+    for m in range(M):
+        for n in range(N):
+            w = want[m][n]
+            assert _close(res.exact[m, n], w, mag[m][n])
+            # the fp32 output is the exact value rounded once (the fp64 error
+            # is far below half an fp32 ulp of these values)
+            assert Fraction(float(res.out[m, n])) == rne_f32(w)
+
+
+def test_vs_torch_dequant_matmul():
+    M, N, K = 40, 256, 384
+    p = fp8_scaled_mm_inputs(M, N, K, 3, bias="f32")
+    b_kn = p["b_nk"].T
+    res = S.fp8_scaled_mm(p["a"], b_kn, p["scale_a"], p["scale_b"], bias=p["bias"],
+                          scale_result=0.5, out_dtype="bf16")
+    A = torch.from_numpy(p["a"].copy()).view(torch.float8_e4m3fn).to(torch.float64)
+    B = torch.from_numpy(np.ascontiguousarray(b_kn)).view(torch.float8_e4m3fn).to(torch.float64)
+    sa = torch.from_numpy(p["scale_a"]).to(torch.float64)
+    sb = torch.from_numpy(p["scale_b"]).to(torch.float64)
+    ref = ((A @ B) * (sa * sb) + torch.from_numpy(p["bias"]).to(torch.float64)) * 0.5
+    assert np.allclose(res.exact, ref.numpy(), rtol=1e-12, atol=1e-12)
+    # the bf16 output is the exact value rounded once
+    got = bf16_bits_to_f64(res.out)
+    assert np.allclose(got, ref.numpy(), rtol=2.0**-8, atol=0)
+
+
+def test_unit_scales_give_integer_gemm_and_tensorwise_is_constant_rowwise():
+    M, N, K = 6, 128, 256
+    rng = np.random.default_rng(2)
+    a = rng.integers(0, 0x7F, (M, K), dtype=np.uint8)
+    b = rng.integers(0, 0x7F, (K, N), dtype=np.uint8)
+    one = np.float32(1.0)
+    res = S.fp8_scaled_mm(a, b, one, one, out_dtype="f32")
+    nA, _ = e4m3_numerator(a)
+    nB, _ = e4m3_numerator(b)
+    P = nA.astype(object) @ nB.astype(object)
+    assert all(Fraction(float(res.exact[m, n])) == Fraction(int(P[m, n]), 2**18)
+               for m in range(M) for n in range(N))
+    c_a, c_b = np.float32(0.3), np.float32(-1.7)
+    t = S.fp8_scaled_mm(a, b, c_a, c_b, out_dtype="f32")
+    r = S.fp8_scaled_mm(a, b, np.full((M, 1), c_a), np.full((1, N), c_b), out_dtype="f32")
+    assert np.array_equal(t.exact, r.exact) and np.array_equal(t.out, r.out)
+
+
+def test_row_and_column_homogeneity_and_bias_shift():
+    M, N, K = 9, 256, 256
+    p = fp8_scaled_mm_inputs(M, N, K, 5)
+    b_kn = p["b_nk"].T
+    base = S.fp8_scaled_mm(p["a"], b_kn, p["scale_a"], p["scale_b"], out_dtype="f32").exact
+    sa = p["scale_a"].copy()
+    sa[4, 0] *= 8
+    sb = p["scale_b"].copy()
+    sb[0, 100] *= 0.25
+    got = S.fp8_scaled_mm(p["a"], b_kn, sa, sb, out_dtype="f32").exact
+    want = base.copy()
+    want[4, :] *= 8
+    want[:, 100] *= 0.25
+    assert np.array_equal(got, want)
+    bias = np.linspace(-3, 3, N).astype(np.float32)
+    shifted = S.fp8_scaled_mm(p["a"], b_kn, p["scale_a"], p["scale_b"], bias=bias,
+                              out_dtype="f32").exact
+    # shifted by the bias, up to the one fp64 rounding of the sum
+    diff = shifted - base - bias.astype(np.float64)[None, :]
+    assert np.all(np.abs(diff) <= 2.0**-50 * (np.abs(base) + np.abs(bias)[None, :]))
+
+
+def test_e4m3_output_hand_values():
+    a = np.full((1, 128), 0x38, np.uint8)             # 1.0
+    b = np.full((128, 1), 0x38, np.uint8)
+    one = np.float32(1)
+    cases = [(2.0, None, 0x70),     # 130 -> 128 (nearest)
+             (8.0, None, 0x70),     # 136: halfway 128 / 144, the even mantissa (128)
+             (9.0, None, 0x71),     # 137 -> 144
+             (2.0, 2.0, 0x78),      # 260 -> 256
+             (2.0, 1e4, 0x7E),      # saturates at 448
+             (2.0, -1e4, 0xFE)]
+    for bias, sr, code in cases:
+        r = S.fp8_scaled_mm(a, b, one, one, bias=np.array([bias], np.float32),
+                            scale_result=sr, out_dtype="e4m3")
+        assert r.out[0, 0] == code, (bias, sr, hex(r.out[0, 0]))
+
+
+def test_compare_e4m3_rule():
+    p = fp8_scaled_mm_inputs(16, 128, 256, 9, bias="f32")
+    res = S.fp8_scaled_mm(p["a"], p["b_nk"].T, p["scale_a"], p["scale_b"], bias=p["bias"],
+                          out_dtype="e4m3")
+    assert S.compare_e4m3(res.out, res, 2.0**-20)["ok"]
+    bad = res.out.copy()
+    # two code steps away (same sign, away from zero) is never within the rule
+    i = np.argwhere((bad & 0x7F) < 0x70)[0]
+    bad[tuple(i)] += 2
+    rep = S.compare_e4m3(bad, res, 2.0**-20)
+    assert not rep["ok"] and rep["violations"] == 1
+    # an exactly representable result: any other code is rejected, even an
+    # equally near neighbour of a tie
+    a = np.full((1, 128), 0x38, np.uint8)
+    b = np.full((128, 1), 0x38, np.uint8)
+    r = S.fp8_scaled_mm(a, b, np.float32(1), np.float32(1), bias=np.array([8.0], np.float32),
+                        out_dtype="e4m3")
+    assert S.compare_e4m3(np.array([[0x70]], np.uint8), r, 0.0)["ok"]
+    assert not S.compare_e4m3(np.array([[0x71]], np.uint8), r, 0.0)["ok"]
+
+
+def test_scale_shape_rules_from_golden():
+    lines = [l.split() for l in open(os.path.join(GOLDEN, "blockwise_scale_shapes.txt"))
+             if l.strip() and not l.startswith("#")]
+    dims = {l[0]: int(l[1]) for l in lines if len(l) == 2}
+    M, N, K = dims["M"], dims["N"], dims["K"]
+    rules = {l[0]: (eval(l[1]), eval(l[2])) for l in lines if len(l) == 4}
+    a = np.zeros((M, K), np.uint8)
+    b = np.zeros((K, N), np.uint8)
+    for kind in ("rowwise", "tensorwise"):
+        sa = np.ones(rules[kind][0], np.float32)
+        sb = np.ones(rules[kind][1], np.float32)
+        r = S.fp8_scaled_mm(a, b, sa, sb, rows=[0, M - 1], cols=[0, N - 1], out_dtype="f32")
+        assert (r.exact == 0).all()
+    with pytest.raises(ValueError):
+        S.fp8_scaled_mm(a, b, np.ones(rules["blockwise"][0], np.float32),
+                        np.ones(rules["blockwise"][1], np.float32), rows=[0], cols=[0])
+
+
+def test_planted_mistakes_are_caught(monkeypatch):
+    M, N, K = 2, 3, 24
+    p = fp8_scaled_mm_inputs(M, N, K, 11, bias="f32")
+    b_kn = p["b_nk"].T
+    sa, sb = _vectors(p, M, N)
+    want, mag = _brute(p["a"], b_kn, sa, sb, p["bias"], 0.75, range(M), range(N))
+
+    def ok(res):
+        return all(_close(res.exact[m, n], want[m][n], mag[m][n])
+                   for m in range(M) for n in range(N))
+
+    call = lambda: S.fp8_scaled_mm(p["a"], b_kn, p["scale_a"], p["scale_b"], bias=p["bias"],
+                                   scale_result=0.75, out_dtype="f32")
+    assert ok(call())
+    plain = S.fp8_scaled_mm(p["a"], b_kn, p["scale_a"], p["scale_b"], out_dtype="f32").exact
+    s = sa[:, None].astype(np.float64) * sb[None, :]
+    # the bias scaled by the operand scales (added before the scaling)
+    assert not ok(S.Result(exact=(plain + p["bias"][None, :] * s) * 0.75, out=None))
+    # scale_result ignored
+    assert not ok(S.fp8_scaled_mm(p["a"], b_kn, p["scale_a"], p["scale_b"], bias=p["bias"],
+                                  out_dtype="f32"))
+    # column scale indexed by row
+    assert not ok(S.Result(exact=(plain / sb[None, :] * sb[:M, None] + p["bias"][None, :])
+                           * 0.75, out=None))
+    # wrong exponent bias in the decode
+    monkeypatch.setattr(S, "TWO_M18", 2.0**-16)
+    assert not ok(call())
