@@ -15,19 +15,20 @@ import os
 
 __all__ = [
     "load", "lib_path", "BsmmError",
-    "bsmm_int8_rowwise", "bsmm_fp8_blockwise", "bsmm_fp8_mx_bmm",
+    "bsmm_int8_rowwise", "bsmm_fp8_blockwise", "bsmm_fp8_mx_bmm", "bsmm_fp8_scaled_mm",
     "bsmm_quant_int8_rowwise", "bsmm_quant_fp8_blockwise", "bsmm_quant_fp8_mx",
     "bsmm_workspace_bytes", "bsmm_query_plan", "bsmm_set_override",
     "bsmm_variant_names", "bsmm_version", "bsmm_timing_enable", "bsmm_timing_read",
-    "I32", "F32", "BF16", "OP_INT8_ROWWISE", "OP_FP8_BLOCKWISE", "OP_FP8_MX_BMM",
+    "I32", "F32", "BF16", "E4M3", "OP_INT8_ROWWISE", "OP_FP8_BLOCKWISE", "OP_FP8_MX_BMM",
+    "OP_FP8_SCALED_MM",
     "STATUS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_PKG, "libbsmm.so")
 
-I32, F32, BF16 = 0, 1, 2
-OP_INT8_ROWWISE, OP_FP8_BLOCKWISE, OP_FP8_MX_BMM = 0, 1, 2
+I32, F32, BF16, E4M3 = 0, 1, 2, 3
+OP_INT8_ROWWISE, OP_FP8_BLOCKWISE, OP_FP8_MX_BMM, OP_FP8_SCALED_MM = 0, 1, 2, 3
 STATUS = {0: "BSMM_OK", 1: "BSMM_ERR_NULL", 2: "BSMM_ERR_SHAPE",
           3: "BSMM_ERR_SCALE_SHAPE", 4: "BSMM_ERR_LAYOUT", 5: "BSMM_ERR_ALIGN",
           6: "BSMM_ERR_DTYPE", 7: "BSMM_ERR_UNSUPPORTED", 8: "BSMM_ERR_HIP",
@@ -65,10 +66,12 @@ def load():
                                      vp, i64, st, i64, i64, i64, vp, sz, vp]
     L.bsmm_fp8_mx_bmm.argtypes = [vp, i64, i64, vp, i64, i64, vp, i64, i64, vp, i64,
                                   i64, vp, i64, i64, st, i64, i64, i64, i64, vp, sz, vp]
+    L.bsmm_fp8_scaled_mm.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, vp, st, vp,
+                                     vp, i64, st, i64, i64, i64, vp, sz, vp]
     L.bsmm_quant_int8_rowwise.argtypes = [vp, i64, st, vp, i64, vp, i64, i64, i64, vp]
     L.bsmm_quant_fp8_blockwise.argtypes = [vp, i64, st, vp, i64, vp, i64, i64, i64, i64, vp]
     L.bsmm_quant_fp8_mx.argtypes = [vp, i64, st, vp, i64, vp, i64, i64, i64, i64, vp]
-    for f in ("bsmm_int8_rowwise", "bsmm_fp8_blockwise", "bsmm_fp8_mx_bmm",
+    for f in ("bsmm_int8_rowwise", "bsmm_fp8_blockwise", "bsmm_fp8_mx_bmm", "bsmm_fp8_scaled_mm",
               "bsmm_quant_int8_rowwise", "bsmm_quant_fp8_blockwise", "bsmm_quant_fp8_mx"):
         getattr(L, f).restype = st
     L.bsmm_workspace_bytes.argtypes = [st, i64, i64, i64, i64, st]
@@ -127,18 +130,23 @@ def _workspace(op, G, M, N, K, out_dtype, device):
 
 def _dtype_code(dt):
     torch = _torch()
+    if isinstance(dt, int) and not isinstance(dt, bool) and dt in (I32, F32, BF16, E4M3):
+        return dt
     if dt in (torch.int32, "i32"):
         return I32
     if dt in (torch.float32, "f32"):
         return F32
     if dt in (torch.bfloat16, "bf16"):
         return BF16
+    if dt in (torch.float8_e4m3fn, "e4m3"):
+        return E4M3
     raise ValueError(f"unsupported output dtype {dt}")
 
 
 def _torch_dtype(code):
     torch = _torch()
-    return {I32: torch.int32, F32: torch.float32, BF16: torch.bfloat16}[code]
+    return {I32: torch.int32, F32: torch.float32, BF16: torch.bfloat16,
+            E4M3: torch.float8_e4m3fn}[code]
 
 
 def _bytes_view(t, name):
@@ -312,6 +320,63 @@ def bsmm_fp8_mx_bmm(x, w, x_scale, w_scale, *, layout="m_major", out_dtype="bf16
         x8.data_ptr(), x_sg, x_sm, w8.data_ptr(), w8.stride(0), w8.stride(1),
         xs8.data_ptr(), xs_sg, xs_sm, ws8.data_ptr(), ws8.stride(0), ws8.stride(1),
         o.data_ptr(), o_sg, o_sm, code, G, M, N, K, wsp, wsn, _stream(stream)))
+    return o
+
+
+def bsmm_fp8_scaled_mm(a, b, scale_a, scale_b, *, bias=None, scale_result=None,
+                       out_dtype="bf16", out=None, workspace=None, stream=None):
+    """fp8 E4M3 scaled matmul with tensorwise or rowwise fp32 scales.
+
+    a: [M, K] E4M3 codes, row-major; b: [K, N] column-major.  Tensorwise:
+    scale_a and scale_b one element each (shape () or (1, 1)); rowwise:
+    scale_a (M, 1), scale_b (1, N).  bias: optional [N] fp32 or bf16.
+    scale_result: optional one-element fp32 tensor (or a float).  out_dtype:
+    "f32", "bf16" or "e4m3" (torch.float8_e4m3fn).
+    """
+    torch = _torch()
+    code = _dtype_code(out_dtype)
+    if code == I32:
+        raise ValueError("fp8 scaled_mm writes f32, bf16 or e4m3")
+    a8, b8 = _bytes_view(a, "a"), _bytes_view(b, "b")
+    M, K = a8.shape
+    K2, N = b8.shape
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    if K and a8.stride(1) != 1:
+        raise ValueError(f"a must be row-major, got stride {a8.stride()}")
+    if K and b8.stride(0) != 1:
+        raise ValueError(f"b must be column-major, got stride {b8.stride()}")
+    if scale_a.dtype != torch.float32 or scale_b.dtype != torch.float32:
+        raise ValueError("scale_a and scale_b must be fp32")
+    if scale_a.numel() == 1 and scale_b.numel() == 1:      # tensorwise: one value each
+        sa_m, sb_n = 0, 0
+    elif tuple(scale_a.shape) == (M, 1) and tuple(scale_b.shape) == (1, N):
+        sa_m, sb_n = scale_a.stride(0), scale_b.stride(1)
+    else:
+        raise ValueError(
+            f"scale shapes: tensorwise takes two scalars, rowwise scale_a ({M}, 1) and "
+            f"scale_b (1, {N}); got {tuple(scale_a.shape)} and {tuple(scale_b.shape)}")
+    bias_ptr, bias_code = None, F32
+    if bias is not None:
+        if bias.dtype not in (torch.float32, torch.bfloat16) or bias.dim() != 1 or \
+                bias.shape[0] != N or (N and bias.stride(0) != 1):
+            raise ValueError(f"bias must be a contiguous [N={N}] fp32 or bf16 tensor")
+        bias_ptr, bias_code = bias.data_ptr(), _dtype_code(bias.dtype)
+    sr_ptr = None
+    if scale_result is not None:
+        if not isinstance(scale_result, torch.Tensor):
+            scale_result = torch.tensor([float(scale_result)], dtype=torch.float32,
+                                        device=a8.device)
+        if scale_result.dtype != torch.float32 or scale_result.numel() != 1:
+            raise ValueError("scale_result must be one fp32 value")
+        sr_ptr = scale_result.data_ptr()
+    o = _out(out, (M, N), code, a8.device)
+    o8 = o.view(torch.uint8) if code == E4M3 else o
+    wsp, wsn = _ws_args(workspace, OP_FP8_SCALED_MM, 1, M, N, K, code, a8.device)
+    _check(load().bsmm_fp8_scaled_mm(
+        a8.data_ptr(), a8.stride(0), b8.data_ptr(), b8.stride(1),
+        scale_a.data_ptr(), sa_m, scale_b.data_ptr(), sb_n, bias_ptr, bias_code, sr_ptr,
+        o8.data_ptr(), o.stride(0), code, M, N, K, wsp, wsn, _stream(stream)))
     return o
 
 

@@ -62,6 +62,7 @@ const char* op_name(bsmm_op op) {
   switch (op) {
     case BSMM_OP_INT8_ROWWISE: return "int8_rowwise";
     case BSMM_OP_FP8_BLOCKWISE: return "fp8_blockwise";
+    case BSMM_OP_FP8_SCALED_MM: return "fp8_scaled_mm";
     default: return "fp8_mx_bmm";
   }
 }
@@ -92,7 +93,7 @@ size_t persistent_workspace(const Variant* v, bsmm_op op) {
 }
 
 static bool plan_packed(const Plan& pl, bsmm_op op) {
-  return op != BSMM_OP_INT8_ROWWISE &&
+  return kloop_scales(op) &&
          (pl.v->packed_scales || (pl.tail && pl.tail->packed_scales));
 }
 
@@ -213,7 +214,7 @@ Plan make_plan_heuristic(bsmm_op op, int G, int M, int N, int K, bsmm_dtype dt) 
   Plan pl;
   // fp8 with enough rows: the K loop reads scale_a repacked once per call
   // (one small load per wave and K block instead of one per row group)
-  const bool pack = op != BSMM_OP_INT8_ROWWISE && M > 128 && (int64_t)G * M >= 1024;
+  const bool pack = kloop_scales(op) && M > 128 && (int64_t)G * M >= 1024;
   const char* name;
   if (M <= 16) {
     // decode-sized: one pass over B with K split inside each workgroup
@@ -472,7 +473,8 @@ bsmm_status bsmm_query_plan(bsmm_op op, int64_t G, int64_t M, int64_t N, int64_t
                             bsmm_dtype out_dtype, size_t workspace_bytes,
                             bsmm_plan_info* info) {
   CHECK(info != nullptr, BSMM_ERR_NULL, "info is NULL");
-  CHECK(op == BSMM_OP_INT8_ROWWISE || op == BSMM_OP_FP8_BLOCKWISE || op == BSMM_OP_FP8_MX_BMM,
+  CHECK(op == BSMM_OP_INT8_ROWWISE || op == BSMM_OP_FP8_BLOCKWISE || op == BSMM_OP_FP8_MX_BMM ||
+            op == BSMM_OP_FP8_SCALED_MM,
         BSMM_ERR_ARG, "unknown op %d", (int)op);
   CHECK(G > 0 && M > 0 && N > 0 && K >= 0, BSMM_ERR_SHAPE, "sizes must be positive");
   CHECK(G < kMaxDim && M < kMaxDim && N < kMaxDim && K < kMaxDim, BSMM_ERR_UNSUPPORTED,
@@ -516,6 +518,59 @@ const char* bsmm_variant_names(void) {
     return s;
   }();
   return names.c_str();
+}
+
+bsmm_status bsmm_fp8_scaled_mm(const uint8_t* a, int64_t lda, const uint8_t* b, int64_t ldb,
+                               const float* scale_a, int64_t sa_m, const float* scale_b,
+                               int64_t sb_n, const void* bias, bsmm_dtype bias_dtype,
+                               const float* scale_result, void* out, int64_t ldo,
+                               bsmm_dtype out_dtype, int64_t M, int64_t N, int64_t K,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  CHECK(M >= 0 && N >= 0 && K >= 0, BSMM_ERR_SHAPE, "negative size M=%lld N=%lld K=%lld",
+        (long long)M, (long long)N, (long long)K);
+  CHECK(M < kMaxDim && N < kMaxDim && K < kMaxDim, BSMM_ERR_UNSUPPORTED, "size beyond 2^31");
+  CHECK(out_dtype == BSMM_F32 || out_dtype == BSMM_BF16 || out_dtype == BSMM_E4M3,
+        BSMM_ERR_DTYPE, "fp8 scaled_mm writes fp32, bf16 or e4m3 (got %d)", (int)out_dtype);
+  if (M == 0 || N == 0) return BSMM_OK;
+  CHECK(K % kBlockK == 0, BSMM_ERR_UNSUPPORTED, "K=%lld is not a multiple of 128", (long long)K);
+  CHECK(out != nullptr, BSMM_ERR_NULL, "out is NULL");
+  CHECK(scale_a != nullptr && scale_b != nullptr, BSMM_ERR_NULL, "scale_a / scale_b is NULL");
+  CHECK(sa_m >= 0 && sb_n >= 0, BSMM_ERR_SCALE_SHAPE,
+        "scale strides must be >= 0 (0: tensorwise, one scalar)");
+  CHECK((M - 1) * sa_m < ((int64_t)1 << 30) && (N - 1) * sb_n < ((int64_t)1 << 30),
+        BSMM_ERR_UNSUPPORTED, "scale index range beyond 2^30");
+  CHECK(aligned(scale_a, 4) && aligned(scale_b, 4), BSMM_ERR_ALIGN, "scales not 4-byte aligned");
+  if (bias) {
+    CHECK(bias_dtype == BSMM_F32 || bias_dtype == BSMM_BF16, BSMM_ERR_DTYPE,
+          "bias must be fp32 or bf16 (got %d)", (int)bias_dtype);
+    CHECK(aligned(bias, bias_dtype == BSMM_F32 ? 4 : 2), BSMM_ERR_ALIGN, "bias misaligned");
+  }
+  CHECK(scale_result == nullptr || aligned(scale_result, 4), BSMM_ERR_ALIGN,
+        "scale_result not 4-byte aligned");
+  CHECK(ldo >= N, BSMM_ERR_SHAPE, "ldo=%lld below N", (long long)ldo);
+  if (K > 0) {   // operands are not read when K == 0
+    CHECK(a != nullptr && b != nullptr, BSMM_ERR_NULL, "a or b is NULL");
+    CHECK(lda >= K && ldb >= K, BSMM_ERR_SHAPE, "leading dimensions lda=%lld ldb=%lld below K",
+          (long long)lda, (long long)ldb);
+    CHECK(lda % 16 == 0 && ldb % 16 == 0, BSMM_ERR_ALIGN, "lda / ldb not multiples of 16 bytes");
+    CHECK(lda <= kMaxLd && ldb <= kMaxLd, BSMM_ERR_UNSUPPORTED, "leading dimension beyond 2^23");
+    CHECK(aligned(a, 16) && aligned(b, 16), BSMM_ERR_ALIGN, "a / b not 16-byte aligned");
+  }
+  const uintptr_t osz = out_dtype == BSMM_F32 ? 4 : out_dtype == BSMM_BF16 ? 2 : 1;
+  CHECK(aligned(out, osz), BSMM_ERR_ALIGN, "out not %d-byte aligned", (int)osz);
+  Problem p{};
+  p.op = BSMM_OP_FP8_SCALED_MM;
+  p.out_dtype = out_dtype;
+  p.G = 1; p.M = (int)M; p.N = (int)N; p.K = (int)K;
+  p.a = a; p.lda = lda;
+  p.b = b; p.ldb = ldb;
+  p.sa = scale_a; p.sa_m = sa_m;
+  p.sb = scale_b; p.sb_n = sb_n;
+  p.out = out; p.ldo = ldo;
+  p.bias = bias;
+  p.bias_bf16 = bias && bias_dtype == BSMM_BF16;
+  p.sr = scale_result;
+  return run(p, workspace ? workspace_bytes : 0, workspace, stream);
 }
 
 }  // extern "C"

@@ -28,7 +28,16 @@ struct Problem {
   const void* sa; int64_t sa_sg, sa_m, sa_kb;
   const void* sb; int64_t sb_sg, sb_n, sb_kb;
   void* out; int64_t o_sg, ldo;
+  // fp8 scaled_mm epilogue: bias [N] (fp32, or bf16 when bias_bf16), result
+  // scale (one fp32); null when absent
+  const void* bias; int bias_bf16;
+  const float* sr;
 };
+
+// Operations whose K loop reads scales (and can use packed scale_a).
+inline bool kloop_scales(bsmm_op op) {
+  return op == BSMM_OP_FP8_BLOCKWISE || op == BSMM_OP_FP8_MX_BMM;
+}
 
 struct Variant;
 
@@ -74,7 +83,7 @@ struct Variant {
 // f, f+16, f+32, f+48.  Layout [G][KB][Mp] (G = 1 for blockwise).
 inline int packed_rows(int M) { return (M + 255) / 256 * 256; }
 inline size_t packed_scale_bytes(bsmm_op op, int G, int M, int K) {
-  if (op == BSMM_OP_INT8_ROWWISE) return 0;
+  if (!kloop_scales(op)) return 0;
   const size_t elem = op == BSMM_OP_FP8_BLOCKWISE ? 4u : 1u;
   const size_t n = (size_t)(op == BSMM_OP_FP8_MX_BMM ? G : 1) * (size_t)(K / kBlockK) *
                    (size_t)packed_rows(M) * elem;

@@ -106,6 +106,27 @@ template <int OP> struct OpT;
 template <> struct OpT<BSMM_OP_INT8_ROWWISE> { typedef i32x4 acc_t; typedef int elem_t; };
 template <> struct OpT<BSMM_OP_FP8_BLOCKWISE> { typedef f32x4 acc_t; typedef float elem_t; };
 template <> struct OpT<BSMM_OP_FP8_MX_BMM> { typedef f32x4 acc_t; typedef float elem_t; };
+template <> struct OpT<BSMM_OP_FP8_SCALED_MM> { typedef f32x4 acc_t; typedef float elem_t; };
+
+// fp8 scaled_mm epilogue: Inductor's apply_scaling (acc * (sa * sb)), then
+// the bias, then the result scale; each step one binary32 rounding.
+struct ScaledEpi {
+  float sr;
+  bool has_bias, bias_bf16;
+  const void* bias;
+  __device__ __forceinline__ explicit ScaledEpi(const Problem& p)
+      : sr(p.sr ? *p.sr : 1.0f), has_bias(p.bias != nullptr), bias_bf16(p.bias_bf16 != 0),
+        bias(p.bias) {}
+  __device__ __forceinline__ float bias_at(int n) const {
+    return bias_bf16 ? __uint_as_float((uint32_t)((const uint16_t*)bias)[n] << 16)
+                     : ((const float*)bias)[n];
+  }
+  __device__ __forceinline__ float operator()(float acc, float sa, float sb, int n) const {
+    float y = __fmul_rn(acc, __fmul_rn(sa, sb));
+    if (has_bias) y = __fadd_rn(y, bias_at(n));   // absent: no +0, which would turn -0 into +0
+    return __fmul_rn(y, sr);
+  }
+};
 
 // Map a work unit (flat workgroup id) to (split, group, tile_m, tile_n).
 //  1. XCD-aware remap: consecutive hardware ids land on different XCDs
@@ -249,10 +270,26 @@ __device__ __forceinline__ void wait_vmcnt() {
 // Store 4 consecutive output values of one row.  The vector stores are
 // non-temporal: a round of tile epilogues writes as much as an XCD's L2
 // holds, and would otherwise evict the A and B slices the next tiles read.
+// E4M3 codes of values clamped to +-448 (the gfx950 conversion rounds to
+// nearest even in the default mode); a NaN input is unsupported.
+__device__ __forceinline__ uint32_t e4m3x4(const float* y) {
+  float c[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) c[r] = __builtin_amdgcn_fmed3f(y[r], -448.0f, 448.0f);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], w, true);
+  return (uint32_t)w;
+}
+
 template <int OUT>
 __device__ __forceinline__ void store4(uint8_t* base, int64_t e, const float* y,
                                        const int* yi, bool vec, int nvalid) {
-  if (OUT == BSMM_BF16) {
+  if (OUT == BSMM_E4M3) {
+    uint8_t* o = base + e;
+    const uint32_t w = e4m3x4(y);
+    if (vec && nvalid == 4) __builtin_nontemporal_store(w, (uint32_t*)o);
+    else for (int r = 0; r < nvalid; ++r) o[r] = (uint8_t)(w >> (8 * r));
+  } else if (OUT == BSMM_BF16) {
     uint16_t* o = (uint16_t*)base + e;
     if (vec && nvalid == 4) {
       u32x2 v;
@@ -346,7 +383,7 @@ struct Mainloop {
     // (blockwise) position of each K block's row
     const int64_t pk_lane = (int64_t)(row0 + wm * T::WTM) + 4 * fr;
     const int64_t pk_g = PK && OP == BSMM_OP_FP8_MX_BMM ? (int64_t)g * (p.K / kBlockK) : 0;
-    if constexpr (OP != BSMM_OP_INT8_ROWWISE) {
+    if constexpr (OP == BSMM_OP_FP8_BLOCKWISE || OP == BSMM_OP_FP8_MX_BMM) {
       const int nb = min((col0 + wn * T::WTN) / kBlockK, p.N / kBlockK - 1);
       if constexpr (!PK) {
   #pragma unroll
@@ -711,9 +748,11 @@ skinny_kernel(const KArgs k) {
           w, x, f32x4{0, 0, 0, 0}, 0, 0, 0, 127, 0, 127);
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(s_blk[slot], pp[r], acc[r]);
-    } else {
+    } else if constexpr (OP == BSMM_OP_FP8_MX_BMM) {
       acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w, x, acc, 0, 0, 0, ws_blk[slot], 0,
                                                              xs_blk[slot]);
+    } else {   // scaled_mm: unit hardware scales, the scales come in the epilogue
+      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w, x, acc, 0, 0, 0, 127, 0, 127);
     }
   };
 #pragma unroll
@@ -753,6 +792,11 @@ skinny_kernel(const KArgs k) {
       if constexpr (OUT != BSMM_I32)
         y[r] = __fmul_rn(__fmul_rn((float)sum[r], ((const float*)p.sa)[(int64_t)m * p.sa_m]),
                          ((const float*)p.sb)[(int64_t)min(n + r, p.N - 1) * p.sb_n]);
+    } else if constexpr (OP == BSMM_OP_FP8_SCALED_MM) {
+      const ScaledEpi epi(p);
+      const int nc = min(n + r, p.N - 1);
+      y[r] = epi(sum[r], ((const float*)p.sa)[(int64_t)m * p.sa_m],
+                 ((const float*)p.sb)[(int64_t)nc * p.sb_n], nc);
     } else {
       y[r] = sum[r];
     }
@@ -827,7 +871,11 @@ __device__ __forceinline__ void store_staged(const KArgs& k, int s, int g, int r
   // slot adds (kOutAdd)
   constexpr bool SCALE = OP == BSMM_OP_INT8_ROWWISE && OUT != BSMM_I32 && !PARTIAL;
   constexpr bool SCALE_A_STAGED = SCALE && MODE == kOut;
-  const bool sb_vec = SCALE && p.sb_n == 1 && (((uintptr_t)p.sb) & 15u) == 0;
+  // fp8 scaled_mm: both scales, the bias and the result scale after the
+  // (stream-K) adds
+  constexpr bool SCALED = OP == BSMM_OP_FP8_SCALED_MM && !PARTIAL;
+  const bool sb_vec = (SCALE || SCALED) && p.sb_n == 1 && (((uintptr_t)p.sb) & 15u) == 0;
+  [[maybe_unused]] const ScaledEpi epi(p);
   lds_barrier();     // every wave's K-loop reads of LDS are done
 #pragma unroll
   for (int pass = 0; pass < TI / 2; ++pass) {
@@ -877,7 +925,20 @@ __device__ __forceinline__ void store_staged(const KArgs& k, int s, int g, int r
       }
       float y[4];
       int yi[4];
-      if constexpr (SCALE) {
+      if constexpr (SCALED) {
+        float sb[4];
+        if (sb_vec && nvalid == 4) {
+          const f32x4 t = *(const f32x4*)((const float*)p.sb + n);
+          sb[0] = t[0]; sb[1] = t[1]; sb[2] = t[2]; sb[3] = t[3];
+        } else {
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            sb[c] = ((const float*)p.sb)[(int64_t)min(n + c, p.N - 1) * p.sb_n];
+        }
+        const float sa_m = ((const float*)p.sa)[(int64_t)m * p.sa_m];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) y[c] = epi(__int_as_float(v[c]), sa_m, sb[c], min(n + c, p.N - 1));
+      } else if constexpr (SCALE) {
         float sb[4];
         if (sb_vec && nvalid == 4) {
           const f32x4 t = *(const f32x4*)((const float*)p.sb + n);
@@ -1310,8 +1371,9 @@ splitk_reduce(const KArgs k) {
     const int m = k.row_begin + mr;
     const E* src = ws + r * p.N;
     float sa_m = 1.f;
-    if constexpr (OP == BSMM_OP_INT8_ROWWISE && OUT != BSMM_I32)
+    if constexpr ((OP == BSMM_OP_INT8_ROWWISE && OUT != BSMM_I32) || OP == BSMM_OP_FP8_SCALED_MM)
       sa_m = ((const float*)p.sa)[(int64_t)m * p.sa_m];
+    [[maybe_unused]] const ScaledEpi epi(p);
     uint8_t* obase = (uint8_t*)p.out;
     const int64_t orow = (int64_t)g * p.o_sg + (int64_t)m * p.ldo;
     for (int n = n0 + 4 * (int)threadIdx.x; n < min(p.N, n0 + 1024); n += 4 * (int)blockDim.x) {
@@ -1336,6 +1398,9 @@ splitk_reduce(const KArgs k) {
           if constexpr (OUT != BSMM_I32)
             y[c] = __fmul_rn(__fmul_rn((float)s[c], sa_m),
                              ((const float*)p.sb)[(int64_t)min(n + c, p.N - 1) * p.sb_n]);
+        } else if constexpr (OP == BSMM_OP_FP8_SCALED_MM) {
+          const int nc = min(n + c, p.N - 1);
+          y[c] = epi((float)s[c], sa_m, ((const float*)p.sb)[(int64_t)nc * p.sb_n], nc);
         } else {
           y[c] = (float)s[c];
         }
@@ -1345,12 +1410,14 @@ splitk_reduce(const KArgs k) {
   }
 }
 
-// Output for K == 0: zeros.
+// Output for K == 0: zeros; for scaled_mm the epilogue of the empty sum
+// ((0 * (sa * sb) + bias) * sr).
+template <int OP, int OUT>
 __global__ void zero_out(const KArgs k) {
   const Problem& p = k.p;
   const int64_t per_g = (int64_t)p.M * p.N;
   const int64_t total = per_g * p.G;
-  const int osz = p.out_dtype == BSMM_BF16 ? 2 : 4;
+  [[maybe_unused]] const ScaledEpi epi(p);
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
        e += (int64_t)gridDim.x * blockDim.x) {
     const int g = (int)(e / per_g);
@@ -1358,8 +1425,12 @@ __global__ void zero_out(const KArgs k) {
     const int m = (int)(rem / p.N);
     const int n = (int)(rem - (int64_t)m * p.N);
     const int64_t o = (int64_t)g * p.o_sg + (int64_t)m * p.ldo + n;
-    if (osz == 2) ((uint16_t*)p.out)[o] = 0;
-    else ((uint32_t*)p.out)[o] = 0;
+    float y[4] = {0.f, 0.f, 0.f, 0.f};
+    const int yi[4] = {0, 0, 0, 0};
+    if constexpr (OP == BSMM_OP_FP8_SCALED_MM)
+      y[0] = epi(0.f, ((const float*)p.sa)[(int64_t)m * p.sa_m],
+                 ((const float*)p.sb)[(int64_t)n * p.sb_n], n);
+    store4<OUT>((uint8_t*)p.out, o, y, yi, false, 1);
   }
 }
 
@@ -1375,7 +1446,7 @@ bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 // Output rows allow 8-byte (bf16) / 16-byte (fp32, int32) vector stores.
 template <int OUT>
 bool out_vec_ok(const Problem& p) {
-  const int osz = OUT == BSMM_BF16 ? 2 : 4;
+  const int osz = OUT == BSMM_E4M3 ? 1 : OUT == BSMM_BF16 ? 2 : 4;
   const int vbytes = 4 * osz;
   return ((uintptr_t)p.out % vbytes == 0) && (p.ldo * osz) % vbytes == 0 &&
          (p.o_sg * osz) % vbytes == 0;
@@ -1436,7 +1507,7 @@ int launch_tile(const Problem& p, const Launch& l) {
     k.splits = 1;
     k.kb_per_split = 0;
     k.vec_out = 0;
-    hipLaunchKernelGGL(zero_out, dim3(1024), dim3(256), 0, s, k);
+    hipLaunchKernelGGL((zero_out<OP, OUT>), dim3(1024), dim3(256), 0, s, k);
     return check_launch();
   }
   k.ws = ws;
@@ -1488,7 +1559,7 @@ int launch_tile4(const Problem& p, const Launch& l) {
     k.splits = 1;
     k.kb_per_split = 0;
     k.vec_out = 0;
-    hipLaunchKernelGGL(zero_out, dim3(1024), dim3(256), 0, s, k);
+    hipLaunchKernelGGL((zero_out<OP, OUT>), dim3(1024), dim3(256), 0, s, k);
     return check_launch();
   }
   k.ws = ws;
@@ -1595,7 +1666,7 @@ int launch_skinny(const Problem& p, const Launch& l) {
   k.vec_out = out_vec_ok<OUT>(p);
   hipStream_t s = (hipStream_t)l.stream;
   if (p.K / kBlockK == 0) {
-    hipLaunchKernelGGL(zero_out, dim3(1024), dim3(256), 0, s, k);
+    hipLaunchKernelGGL((zero_out<OP, OUT>), dim3(1024), dim3(256), 0, s, k);
     return check_launch();
   }
   const int64_t grid = (int64_t)k.tiles_n * p.G;
@@ -1605,8 +1676,9 @@ int launch_skinny(const Problem& p, const Launch& l) {
 
 template <int OP, int OUT, int WM, int WN, int RING, bool SK, bool PK, int KIND>
 int launch_kernel(const Problem& p, const Launch& l) {
-  // the int8 K loop reads no scales: packed variants run the plain kernel
-  constexpr bool PKX = PK && OP != BSMM_OP_INT8_ROWWISE;
+  // the int8 and scaled_mm K loops read no scales: packed variants run the
+  // plain kernel
+  constexpr bool PKX = PK && (OP == BSMM_OP_FP8_BLOCKWISE || OP == BSMM_OP_FP8_MX_BMM);
   if constexpr (KIND == 2) {
     return launch_skinny<OP, OUT, RING>(p, l);
   } else if constexpr (KIND == 1) {

@@ -19,14 +19,20 @@ int launch_variant(const Problem& p, const Launch& l) {
       if (p.out_dtype == BSMM_F32)
         return launch_kernel<BSMM_OP_FP8_BLOCKWISE, BSMM_F32, WM, WN, RING, SK, PK, KIND>(p, l);
       return launch_kernel<BSMM_OP_FP8_BLOCKWISE, BSMM_BF16, WM, WN, RING, SK, PK, KIND>(p, l);
-    default:
+    case BSMM_OP_FP8_MX_BMM:
       if (p.out_dtype == BSMM_F32)
         return launch_kernel<BSMM_OP_FP8_MX_BMM, BSMM_F32, WM, WN, RING, SK, PK, KIND>(p, l);
       return launch_kernel<BSMM_OP_FP8_MX_BMM, BSMM_BF16, WM, WN, RING, SK, PK, KIND>(p, l);
+    default:
+      if (p.out_dtype == BSMM_F32)
+        return launch_kernel<BSMM_OP_FP8_SCALED_MM, BSMM_F32, WM, WN, RING, SK, PK, KIND>(p, l);
+      if (p.out_dtype == BSMM_E4M3)
+        return launch_kernel<BSMM_OP_FP8_SCALED_MM, BSMM_E4M3, WM, WN, RING, SK, PK, KIND>(p, l);
+      return launch_kernel<BSMM_OP_FP8_SCALED_MM, BSMM_BF16, WM, WN, RING, SK, PK, KIND>(p, l);
   }
 }
 
-constexpr unsigned kAllOps = 7u;
+constexpr unsigned kAllOps = 15u;
 
 // name, tile_m, tile_n, ops, masked tail, persistent, packed scales,
 // workgroups per CU, unpacked sibling, largest M (the skinny kernel: 16),

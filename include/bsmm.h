@@ -66,13 +66,16 @@ typedef enum {
 typedef enum {
   BSMM_I32 = 0,  /* raw int32 accumulators (int8 entry point only)  */
   BSMM_F32 = 1,  /* IEEE binary32                                   */
-  BSMM_BF16 = 2  /* bfloat16, round-to-nearest-even from binary32   */
+  BSMM_BF16 = 2, /* bfloat16, round-to-nearest-even from binary32   */
+  BSMM_E4M3 = 3  /* OCP E4M3FN codes, nearest even from binary32,   */
+                 /* saturating at +-448 (bsmm_fp8_scaled_mm only)   */
 } bsmm_dtype;
 
 typedef enum {
   BSMM_OP_INT8_ROWWISE = 0,
   BSMM_OP_FP8_BLOCKWISE = 1,
-  BSMM_OP_FP8_MX_BMM = 2
+  BSMM_OP_FP8_MX_BMM = 2,
+  BSMM_OP_FP8_SCALED_MM = 3
 } bsmm_op;
 
 /*
@@ -157,6 +160,39 @@ bsmm_status bsmm_fp8_mx_bmm(const uint8_t* x, int64_t x_sg, int64_t x_sm,
                             int64_t G, int64_t M, int64_t N, int64_t K,
                             void* workspace, size_t workspace_bytes,
                             void* stream);
+
+/*
+ * fp8 E4M3FN x E4M3FN with tensorwise or rowwise fp32 scales, an optional
+ * bias and an optional result scale: the fp8 _scaled_mm of Inductor's
+ * mm.py (tuned_scaled_mm; the Triton template's load_scales /
+ * apply_scaling), with the shape rules the PyTorch blockwise issue prints
+ * (tensorwise: both scales scalar; rowwise: scale_a (M, 1), scale_b (1, N)).
+ *
+ *   acc = sum_k a[m*lda + k] * b[n*ldb + k]        (fp32 accumulation)
+ *   y   = acc * (scale_a[m*sa_m] * scale_b[n*sb_n])  (sa_m = sb_n = 0: tensorwise)
+ *   y   = y + bias[n]                           (bias != NULL)
+ *   y   = y * scale_result[0]                   (scale_result != NULL)
+ *   out[m*ldo + n] = y as fp32, bf16 (RNE) or E4M3 (RNE, saturating)
+ * Each step is one binary32 operation (no fused multiply-add).  scale_result
+ * is named, not defined, by tuned_scaled_mm; here it scales the final value
+ * before the conversion to the output type, for every output type.
+ * a, b: E4M3FN bytes (NaN codes unsupported).  scale_a, scale_b: fp32 device
+ * pointers.  bias: NULL or N values of bias_dtype (BSMM_F32 or BSMM_BF16;
+ * ignored without a bias).  scale_result: NULL or a device pointer to one
+ * fp32.  out_dtype: BSMM_F32, BSMM_BF16 or BSMM_E4M3.  Any N; K % 128 == 0;
+ * otherwise the conventions above.  K == 0 writes (bias) * scale_result, the
+ * value of an empty sum.
+ */
+bsmm_status bsmm_fp8_scaled_mm(const uint8_t* a, int64_t lda,
+                               const uint8_t* b, int64_t ldb,
+                               const float* scale_a, int64_t sa_m,
+                               const float* scale_b, int64_t sb_n,
+                               const void* bias, bsmm_dtype bias_dtype,
+                               const float* scale_result,
+                               void* out, int64_t ldo, bsmm_dtype out_dtype,
+                               int64_t M, int64_t N, int64_t K,
+                               void* workspace, size_t workspace_bytes,
+                               void* stream);
 
 /*
  * Dynamic quantisation: bf16 / fp32 activations -> the 1-byte codes and the

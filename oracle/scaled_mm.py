@@ -247,7 +247,7 @@ def fp8_scaled_mm(a, b_kn, scale_a, scale_b, bias=None, scale_result=None,
         raise ValueError("inner dimensions differ")
     sa = np.asarray(scale_a, dtype=np.float32)
     sb = np.asarray(scale_b, dtype=np.float32)
-    if sa.size == 1 and sb.size == 1 and sa.ndim in (0, 2) and sb.ndim in (0, 2):
+    if sa.size == 1 and sb.size == 1:
         sa_v = np.full(M, sa.reshape(-1)[0], np.float32)        # tensorwise
         sb_v = np.full(N, sb.reshape(-1)[0], np.float32)
     elif sa.shape == (M, 1) and sb.shape == (1, N):

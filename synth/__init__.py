@@ -309,6 +309,10 @@ CONFIGS = {
                      layout="m_major", dist="normal", out="bf16"),
     "c5": dict(op="mx", G=2, M=9000, N=2048, K=7168, seed=5,
                layout="batch_first", dist="t", out="f32"),
+    # the blockwise issue's shape under the rowwise scaling it names, with a
+    # bf16 bias (the fp8 scaled_mm epilogue)
+    "c3r": dict(op="fp8_scaled_mm", M=16640, N=5120, K=8192, seed=3,
+                scaling="rowwise", bias="bf16", out="bf16"),
 }
 
 
@@ -319,5 +323,8 @@ def config_inputs(name: str):
                                    kind=c["kind"])
     if c["op"] == "fp8_blockwise":
         return fp8_blockwise_inputs(c["M"], c["N"], c["K"], c["seed"])
+    if c["op"] == "fp8_scaled_mm":
+        return fp8_scaled_mm_inputs(c["M"], c["N"], c["K"], c["seed"],
+                                    scaling=c["scaling"], bias=c["bias"])
     return fp8_mx_bmm_inputs(c["G"], c["M"], c["N"], c["K"], c["seed"],
                              layout=c["layout"], dist=c["dist"])

@@ -113,6 +113,40 @@ def test_mx_noops():
     assert mx(G=0) == OK and mx(M=0) == OK and mx(N=0) == OK
 
 
+def smm(*, a=P, lda=256, b=P, ldb=256, sa=P, sa_m=1, sb=P, sb_n=1, bias=None,
+        bdt=bsmm.F32, sr=None, out=P, ldo=128, dt=bsmm.BF16, M=64, N=128, K=256):
+    return bsmm.load().bsmm_fp8_scaled_mm(a, lda, b, ldb, sa, sa_m, sb, sb_n, bias, bdt, sr,
+                                          out, ldo, dt, M, N, K, None, 0, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=-1), SHAPE), (dict(dt=bsmm.I32), DTYPE), (dict(dt=9), DTYPE), (dict(K=200), UNSUP),
+    (dict(out=None), NULL), (dict(sa=None), NULL), (dict(sb=None), NULL), (dict(a=None), NULL),
+    (dict(sa_m=-1), SCALE), (dict(sb_n=-1), SCALE), (dict(ldo=100), SHAPE),
+    (dict(lda=128), SHAPE), (dict(ldb=264), ALIGN), (dict(b=P + 4), ALIGN),
+    (dict(sa=P + 2), ALIGN), (dict(bias=P, bdt=bsmm.I32), DTYPE),
+    (dict(bias=P + 2, bdt=bsmm.F32), ALIGN), (dict(sr=P + 1), ALIGN),
+    (dict(out=P + 1, dt=bsmm.BF16), ALIGN), (dict(sa_m=1 << 30), UNSUP),
+])
+def test_scaled_mm_rejects(kw, status):
+    assert smm(**kw) == status
+    assert bsmm.load().bsmm_last_error().decode()
+
+
+def test_scaled_mm_noops_and_plans():
+    assert smm(M=0) == OK and smm(N=0, a=None, b=None, out=None) == OK
+    # an odd byte address is fine for e4m3 output and a bf16 bias; M=0 keeps
+    # the call from launching
+    assert smm(M=0, out=P + 1, dt=bsmm.E4M3, bias=P + 2, bdt=bsmm.BF16) == OK
+    # no scales in the K loop: never a packed-scale plan, no packing workspace
+    p = bsmm.bsmm_query_plan(bsmm.OP_FP8_SCALED_MM, 1, 16640, 5120, 8192, "bf16")
+    assert not p["variant"].endswith("p") and p["tail_split_k"] >= 2
+    assert bsmm.bsmm_query_plan(bsmm.OP_FP8_SCALED_MM, 1, 8, 300, 1024, "e4m3")["variant"] == \
+        "s16x16"
+    p = bsmm.bsmm_query_plan(bsmm.OP_FP8_SCALED_MM, 1, 4096, 4096, 4096, "f32")
+    assert p["workspace"] == 0 and not p["variant"].endswith("p")
+
+
 def qi8(*, x=P, ldx=256, xdt=bsmm.BF16, q=P, ldq=256, sc=P, s_m=1, M=64, K=256):
     return bsmm.load().bsmm_quant_int8_rowwise(x, ldx, xdt, q, ldq, sc, s_m, M, K, None)
 
