@@ -317,6 +317,53 @@ def compare_e4m3(codes, res: Result, gamma: float) -> dict:
 
 
 # ---------------------------------------------------------------------------
+# fp8 E4M3 with MX block scales of 32 elements along K (the "MX variants" of
+# _scaled_mm that Inductor's tuned_scaled_mm routes away from its Triton
+# templates; 32 is the block of the OCP microscaling formats -- the reading
+# taken for the block size, which the pages do not print): one e8m0 scale per
+# row of A per 32-long K chunk, a_scale [M, K/32], and one per column of B
+# per chunk, b_scale [N, K/32].
+#   C[m, n] = sum_c 2**(a_scale[m,c]-127) * 2**(b_scale[n,c]-127)
+#                   * sum_{k in chunk c} A[m,k] B[k,n]
+# ---------------------------------------------------------------------------
+MX_BLOCK = 32
+
+
+def fp8_mx32_mm(a, b_kn, a_scale, b_scale, out_dtype="bf16", rows=None, cols=None) -> Result:
+    a = np.asarray(a, dtype=np.uint8)
+    b_kn = np.asarray(b_kn, dtype=np.uint8)
+    M, K = a.shape
+    K2, N = b_kn.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ")
+    KC = -(-K // MX_BLOCK)
+    sa = np.asarray(a_scale, dtype=np.uint8)
+    sb = np.asarray(b_scale, dtype=np.uint8)
+    if sa.shape != (M, KC) or sb.shape != (N, KC):
+        raise ValueError(f"scale shapes {sa.shape}, {sb.shape}; expected ({M}, {KC}) and "
+                         f"({N}, {KC})")
+    if (sa == 255).any() or (sb == 255).any():
+        raise ValueError("NaN e8m0 scale")
+    r = _idx(M, rows)
+    c = _idx(N, cols)
+    nA, nanA = e4m3_numerator(a[r])
+    nB, nanB = e4m3_numerator(b_kn[:, c])
+    if nanA.any() or nanB.any():
+        raise ValueError("NaN codes in the operands")
+    nA = nA.astype(np.float64)
+    nB = nB.astype(np.float64)
+    C = np.zeros((len(r), len(c)))
+    Bd = np.zeros((len(r), len(c)))
+    for ci, (k0, k1) in enumerate(_blocks(K, MX_BLOCK)):
+        P = nA[:, k0:k1] @ nB[k0:k1, :]                 # exact integers
+        Pabs = np.abs(nA[:, k0:k1]) @ np.abs(nB[k0:k1, :])
+        s = e8m0_value(sa[r, ci])[:, None] * e8m0_value(sb[c, ci])[None, :]   # exact 2**e
+        C += s * P * TWO_M18
+        Bd += s * Pabs * TWO_M18
+    return _finish_fp(C, Bd, out_dtype)
+
+
+# ---------------------------------------------------------------------------
 # Comparison rule.
 #   integer accumulators and the int8 path's fp32/bf16 outputs: exact equality
 #   (the GPU performs the same binary32 operations in the same order);

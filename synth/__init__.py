@@ -45,6 +45,7 @@ __all__ = [
     "fp8_blockwise_inputs",
     "fp8_mx_bmm_inputs",
     "fp8_scaled_mm_inputs",
+    "fp8_mx32_inputs",
     "config_inputs",
     "activations",
     "CONFIGS",
@@ -263,6 +264,24 @@ def fp8_scaled_mm_inputs(M, N, K, seed, *, scaling="rowwise", bias=None, dist="n
         if bias == "bf16":
             bv = (bv.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32)
     return dict(a=a, b_nk=np.ascontiguousarray(b_q.T), scale_a=sa, scale_b=sb, bias=bv)
+
+
+def fp8_mx32_inputs(M, N, K, seed, *, dist="normal"):
+    """fp8 MX problem with 32-element K blocks: A [M,K] quantised per row per
+    32-long K chunk, B logical [K,N] per column per chunk, e8m0 scales
+    ``2**ceil(log2(amax/448))``.
+
+    Returns dict(a uint8 [M,K], b_nk uint8 [N,K], a_scale uint8 [M,K/32],
+    b_scale uint8 [N,K/32])."""
+    rng = np.random.default_rng(seed)
+    a_f = _draw(rng, dist, (M, K))
+    a, sa = quant_fp8_blocks_e8m0(a_f, 1, 32)
+    del a_f
+    b_kn = _draw(rng, dist, (K, N))
+    b_q, sb = quant_fp8_blocks_e8m0(b_kn, 32, 1)          # sb [K/32, N]
+    del b_kn
+    return dict(a=a, b_nk=np.ascontiguousarray(b_q.T), a_scale=sa,
+                b_scale=np.ascontiguousarray(sb.T))
 
 
 def fp8_mx_bmm_inputs(G, M, N, K, seed, *, layout="m_major", dist="normal"):

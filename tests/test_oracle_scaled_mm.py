@@ -224,3 +224,79 @@ def test_planted_mistakes_are_caught(monkeypatch):
     # wrong exponent bias in the decode
     monkeypatch.setattr(S, "TWO_M18", 2.0**-16)
     assert not ok(call())
+
+
+# ------------------------------------------------------------- MX, 32 blocks --
+
+def _mx32_random(M, N, K, seed):
+    rng = np.random.default_rng(seed)
+    a = rng.integers(0, 256, (M, K)).astype(np.uint8) & 0xF7          # no NaN codes
+    b = rng.integers(0, 256, (K, N)).astype(np.uint8) & 0xF7
+    sa = rng.integers(110, 140, (M, K // 32)).astype(np.uint8)
+    sb = rng.integers(110, 140, (N, K // 32)).astype(np.uint8)
+    return a, b, sa, sb
+
+
+def test_mx32_brute_force_exact_rationals():
+    M, N, K = 3, 4, 96
+    a, b, sa, sb = _mx32_random(M, N, K, 1)
+    res = S.fp8_mx32_mm(a, b, sa, sb, "f32")
+    for m in range(M):
+        for n in range(N):
+            w = sum(e4m3_exact(int(a[m, k])) * e4m3_exact(int(b[k, n]))
+                    * Fraction(2) ** (int(sa[m, k // 32]) - 127)
+                    * Fraction(2) ** (int(sb[n, k // 32]) - 127) for k in range(K))
+            g = sum(abs(e4m3_exact(int(a[m, k])) * e4m3_exact(int(b[k, n])))
+                    * Fraction(2) ** (int(sa[m, k // 32]) + int(sb[n, k // 32]) - 254)
+                    for k in range(K))
+            assert _close(res.exact[m, n], w, g)
+            assert Fraction(float(res.out[m, n])) == rne_f32(w)
+
+
+def test_mx32_vs_torch_dequant_matmul():
+    M, N, K = 24, 64, 256
+    a, b, sa, sb = _mx32_random(M, N, K, 2)
+    res = S.fp8_mx32_mm(a, b, sa, sb, "f32")
+    A = torch.from_numpy(a.copy()).view(torch.float8_e4m3fn).to(torch.float64)
+    B = torch.from_numpy(b.copy()).view(torch.float8_e4m3fn).to(torch.float64)
+    A = A * torch.from_numpy(np.exp2(sa.astype(np.float64) - 127)).repeat_interleave(32, 1)
+    B = B * torch.from_numpy(np.exp2(sb.astype(np.float64) - 127)).T.repeat_interleave(32, 0)
+    ref = (A @ B).numpy()
+    assert np.allclose(res.exact, ref, rtol=1e-12, atol=1e-300)
+
+
+def test_mx32_equals_mx128_when_scales_are_constant_per_128_block():
+    G, M, N, K = 1, 7, 256, 384
+    rng = np.random.default_rng(3)
+    a, b, _, _ = _mx32_random(M, N, K, 3)
+    xs = rng.integers(115, 135, (M, K // 128)).astype(np.uint8)
+    ws = rng.integers(115, 135, (N // 128, K // 128)).astype(np.uint8)
+    sa = np.repeat(xs, 4, axis=1)                       # each 128-block's 4 chunks alike
+    sb = np.repeat(np.repeat(ws, 128, axis=0), 4, axis=1)
+    r32 = S.fp8_mx32_mm(a, b, sa, sb, "f32")
+    r128 = S.fp8_mx_bmm(a[None], np.ascontiguousarray(b.T)[None], xs[None], ws[None],
+                        layout="batch_first", out_dtype="f32")
+    assert np.allclose(r32.exact, r128.exact[0], rtol=1e-13, atol=0)
+
+
+def test_mx32_unit_scales_and_chunk_homogeneity():
+    M, N, K = 4, 32, 128
+    a, b, _, _ = _mx32_random(M, N, K, 4)
+    one_a = np.full((M, K // 32), 127, np.uint8)
+    one_b = np.full((N, K // 32), 127, np.uint8)
+    res = S.fp8_mx32_mm(a, b, one_a, one_b, "f32")
+    nA, _ = e4m3_numerator(a)
+    nB, _ = e4m3_numerator(b)
+    P = nA.astype(object) @ nB.astype(object)
+    assert all(Fraction(float(res.exact[m, n])) == Fraction(int(P[m, n]), 2**18)
+               for m in range(M) for n in range(N))
+    # raising one chunk's scale by one doubles that chunk's share of its row only
+    sa = one_a.copy()
+    sa[2, 1] += 1
+    got = S.fp8_mx32_mm(a, b, sa, one_b, "f32").exact
+    part = nA[2, 32:64].astype(np.float64) @ nB[32:64, :].astype(np.float64) * 2.0**-18
+    want = res.exact.copy()
+    want[2] += part
+    assert np.allclose(got, want, rtol=1e-14, atol=0)
+    with pytest.raises(ValueError):
+        S.fp8_mx32_mm(a, b, one_a[:, :2], one_b, "f32")
