@@ -16,6 +16,7 @@ import os
 __all__ = [
     "load", "lib_path", "BsmmError",
     "bsmm_int8_rowwise", "bsmm_fp8_blockwise", "bsmm_fp8_mx_bmm", "bsmm_fp8_scaled_mm",
+    "bsmm_fp8_mx32_mm", "OP_FP8_MX32_MM",
     "bsmm_quant_int8_rowwise", "bsmm_quant_fp8_blockwise", "bsmm_quant_fp8_mx",
     "bsmm_workspace_bytes", "bsmm_query_plan", "bsmm_set_override",
     "bsmm_variant_names", "bsmm_version", "bsmm_timing_enable", "bsmm_timing_read",
@@ -28,7 +29,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_PKG, "libbsmm.so")
 
 I32, F32, BF16, E4M3 = 0, 1, 2, 3
-OP_INT8_ROWWISE, OP_FP8_BLOCKWISE, OP_FP8_MX_BMM, OP_FP8_SCALED_MM = 0, 1, 2, 3
+OP_INT8_ROWWISE, OP_FP8_BLOCKWISE, OP_FP8_MX_BMM, OP_FP8_SCALED_MM, OP_FP8_MX32_MM = 0, 1, 2, 3, 4
 STATUS = {0: "BSMM_OK", 1: "BSMM_ERR_NULL", 2: "BSMM_ERR_SHAPE",
           3: "BSMM_ERR_SCALE_SHAPE", 4: "BSMM_ERR_LAYOUT", 5: "BSMM_ERR_ALIGN",
           6: "BSMM_ERR_DTYPE", 7: "BSMM_ERR_UNSUPPORTED", 8: "BSMM_ERR_HIP",
@@ -68,10 +69,13 @@ def load():
                                   i64, vp, i64, i64, st, i64, i64, i64, i64, vp, sz, vp]
     L.bsmm_fp8_scaled_mm.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, vp, st, vp,
                                      vp, i64, st, i64, i64, i64, vp, sz, vp]
+    L.bsmm_fp8_mx32_mm.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, st, i64, i64,
+                                   i64, vp, sz, vp]
     L.bsmm_quant_int8_rowwise.argtypes = [vp, i64, st, vp, i64, vp, i64, i64, i64, vp]
     L.bsmm_quant_fp8_blockwise.argtypes = [vp, i64, st, vp, i64, vp, i64, i64, i64, i64, vp]
     L.bsmm_quant_fp8_mx.argtypes = [vp, i64, st, vp, i64, vp, i64, i64, i64, i64, vp]
     for f in ("bsmm_int8_rowwise", "bsmm_fp8_blockwise", "bsmm_fp8_mx_bmm", "bsmm_fp8_scaled_mm",
+              "bsmm_fp8_mx32_mm",
               "bsmm_quant_int8_rowwise", "bsmm_quant_fp8_blockwise", "bsmm_quant_fp8_mx"):
         getattr(L, f).restype = st
     L.bsmm_workspace_bytes.argtypes = [st, i64, i64, i64, i64, st]
@@ -377,6 +381,42 @@ def bsmm_fp8_scaled_mm(a, b, scale_a, scale_b, *, bias=None, scale_result=None,
         a8.data_ptr(), a8.stride(0), b8.data_ptr(), b8.stride(1),
         scale_a.data_ptr(), sa_m, scale_b.data_ptr(), sb_n, bias_ptr, bias_code, sr_ptr,
         o8.data_ptr(), o.stride(0), code, M, N, K, wsp, wsn, _stream(stream)))
+    return o
+
+
+def bsmm_fp8_mx32_mm(a, b, a_scale, b_scale, *, out_dtype="bf16", out=None, workspace=None,
+                     stream=None):
+    """fp8 E4M3 matmul with e8m0 scales on 32-element K blocks (MX).
+
+    a: [M, K] E4M3 codes, row-major; b: [K, N] column-major; a_scale
+    [M, K/32] and b_scale [N, K/32] e8m0 bytes (uint8 or float8_e8m0fnu)
+    with contiguous rows.
+    """
+    code = _dtype_code(out_dtype)
+    if code not in (F32, BF16):
+        raise ValueError("fp8 mx32 writes f32 or bf16")
+    a8, b8 = _bytes_view(a, "a"), _bytes_view(b, "b")
+    sa8, sb8 = _bytes_view(a_scale, "a_scale"), _bytes_view(b_scale, "b_scale")
+    M, K = a8.shape
+    K2, N = b8.shape
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    if K and a8.stride(1) != 1:
+        raise ValueError(f"a must be row-major, got stride {a8.stride()}")
+    if K and b8.stride(0) != 1:
+        raise ValueError(f"b must be column-major, got stride {b8.stride()}")
+    KC = -(-K // 32)
+    if tuple(sa8.shape) != (M, KC) or tuple(sb8.shape) != (N, KC):
+        raise ValueError(f"MX scales: a_scale should be ({M}, {KC}) and b_scale ({N}, {KC}); "
+                         f"got {tuple(sa8.shape)} and {tuple(sb8.shape)}")
+    if KC and (sa8.stride(1) != 1 or sb8.stride(1) != 1):
+        raise ValueError("scale rows must be contiguous")
+    o = _out(out, (M, N), code, a8.device)
+    wsp, wsn = _ws_args(workspace, OP_FP8_MX32_MM, 1, M, N, K, code, a8.device)
+    _check(load().bsmm_fp8_mx32_mm(
+        a8.data_ptr(), a8.stride(0), b8.data_ptr(), b8.stride(1),
+        sa8.data_ptr(), sa8.stride(0), sb8.data_ptr(), sb8.stride(0),
+        o.data_ptr(), o.stride(0), code, M, N, K, wsp, wsn, _stream(stream)))
     return o
 
 

@@ -63,6 +63,7 @@ const char* op_name(bsmm_op op) {
     case BSMM_OP_INT8_ROWWISE: return "int8_rowwise";
     case BSMM_OP_FP8_BLOCKWISE: return "fp8_blockwise";
     case BSMM_OP_FP8_SCALED_MM: return "fp8_scaled_mm";
+    case BSMM_OP_FP8_MX32_MM: return "fp8_mx32_mm";
     default: return "fp8_mx_bmm";
   }
 }
@@ -93,7 +94,7 @@ size_t persistent_workspace(const Variant* v, bsmm_op op) {
 }
 
 static bool plan_packed(const Plan& pl, bsmm_op op) {
-  return kloop_scales(op) &&
+  return packable_scales(op) &&
          (pl.v->packed_scales || (pl.tail && pl.tail->packed_scales));
 }
 
@@ -214,7 +215,7 @@ Plan make_plan_heuristic(bsmm_op op, int G, int M, int N, int K, bsmm_dtype dt) 
   Plan pl;
   // fp8 with enough rows: the K loop reads scale_a repacked once per call
   // (one small load per wave and K block instead of one per row group)
-  const bool pack = kloop_scales(op) && M > 128 && (int64_t)G * M >= 1024;
+  const bool pack = packable_scales(op) && M > 128 && (int64_t)G * M >= 1024;
   const char* name;
   if (M <= 16) {
     // decode-sized: one pass over B with K split inside each workgroup
@@ -474,7 +475,7 @@ bsmm_status bsmm_query_plan(bsmm_op op, int64_t G, int64_t M, int64_t N, int64_t
                             bsmm_plan_info* info) {
   CHECK(info != nullptr, BSMM_ERR_NULL, "info is NULL");
   CHECK(op == BSMM_OP_INT8_ROWWISE || op == BSMM_OP_FP8_BLOCKWISE || op == BSMM_OP_FP8_MX_BMM ||
-            op == BSMM_OP_FP8_SCALED_MM,
+            op == BSMM_OP_FP8_SCALED_MM || op == BSMM_OP_FP8_MX32_MM,
         BSMM_ERR_ARG, "unknown op %d", (int)op);
   CHECK(G > 0 && M > 0 && N > 0 && K >= 0, BSMM_ERR_SHAPE, "sizes must be positive");
   CHECK(G < kMaxDim && M < kMaxDim && N < kMaxDim && K < kMaxDim, BSMM_ERR_UNSUPPORTED,
@@ -570,6 +571,48 @@ bsmm_status bsmm_fp8_scaled_mm(const uint8_t* a, int64_t lda, const uint8_t* b, 
   p.bias = bias;
   p.bias_bf16 = bias && bias_dtype == BSMM_BF16;
   p.sr = scale_result;
+  return run(p, workspace ? workspace_bytes : 0, workspace, stream);
+}
+
+bsmm_status bsmm_fp8_mx32_mm(const uint8_t* a, int64_t lda, const uint8_t* b, int64_t ldb,
+                             const uint8_t* a_scale, int64_t as_m, const uint8_t* b_scale,
+                             int64_t bs_n, void* out, int64_t ldo, bsmm_dtype out_dtype,
+                             int64_t M, int64_t N, int64_t K, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  CHECK(M >= 0 && N >= 0 && K >= 0, BSMM_ERR_SHAPE, "negative size M=%lld N=%lld K=%lld",
+        (long long)M, (long long)N, (long long)K);
+  CHECK(M < kMaxDim && N < kMaxDim && K < kMaxDim, BSMM_ERR_UNSUPPORTED, "size beyond 2^31");
+  CHECK(out_dtype == BSMM_F32 || out_dtype == BSMM_BF16, BSMM_ERR_DTYPE,
+        "fp8 mx32 writes fp32 or bf16 (got %d)", (int)out_dtype);
+  if (M == 0 || N == 0) return BSMM_OK;
+  CHECK(K % kBlockK == 0, BSMM_ERR_UNSUPPORTED, "K=%lld is not a multiple of 128", (long long)K);
+  CHECK(out != nullptr, BSMM_ERR_NULL, "out is NULL");
+  CHECK(ldo >= N, BSMM_ERR_SHAPE, "ldo=%lld below N", (long long)ldo);
+  if (K > 0) {
+    const int64_t KC = K / 32;
+    CHECK(a != nullptr && b != nullptr, BSMM_ERR_NULL, "a or b is NULL");
+    CHECK(a_scale != nullptr && b_scale != nullptr, BSMM_ERR_NULL, "a_scale / b_scale is NULL");
+    CHECK(as_m >= KC && bs_n >= KC, BSMM_ERR_SCALE_SHAPE,
+          "scale rows of K/32 = %lld bytes need strides as_m=%lld bs_n=%lld >= K/32",
+          (long long)KC, (long long)as_m, (long long)bs_n);
+    CHECK((M - 1) * as_m + KC < ((int64_t)1 << 31) && (N - 1) * bs_n + KC < ((int64_t)1 << 31),
+          BSMM_ERR_UNSUPPORTED, "scale index range beyond 2^31");
+    CHECK(lda >= K && ldb >= K, BSMM_ERR_SHAPE, "leading dimensions lda=%lld ldb=%lld below K",
+          (long long)lda, (long long)ldb);
+    CHECK(lda % 16 == 0 && ldb % 16 == 0, BSMM_ERR_ALIGN, "lda / ldb not multiples of 16 bytes");
+    CHECK(lda <= kMaxLd && ldb <= kMaxLd, BSMM_ERR_UNSUPPORTED, "leading dimension beyond 2^23");
+    CHECK(aligned(a, 16) && aligned(b, 16), BSMM_ERR_ALIGN, "a / b not 16-byte aligned");
+  }
+  CHECK(aligned(out, 4), BSMM_ERR_ALIGN, "out not 4-byte aligned");
+  Problem p{};
+  p.op = BSMM_OP_FP8_MX32_MM;
+  p.out_dtype = out_dtype;
+  p.G = 1; p.M = (int)M; p.N = (int)N; p.K = (int)K;
+  p.a = a; p.lda = lda;
+  p.b = b; p.ldb = ldb;
+  p.sa = a_scale; p.sa_m = as_m;
+  p.sb = b_scale; p.sb_n = bs_n;
+  p.out = out; p.ldo = ldo;
   return run(p, workspace ? workspace_bytes : 0, workspace, stream);
 }
 

@@ -25,6 +25,8 @@ struct Problem {
   //   int8:      sa[m*sa_m], sb[n*sb_n]                       (sb_kb unused)
   //   blockwise: sa[m*sa_m + kb*sa_kb], sb[kb*sb_kb + nb*sb_n]
   //   mx:        sa[g*sa_sg + m*sa_m + kb], sb[g*sb_sg + nb*sb_n + kb]
+  //   mx32:      sa[m*sa_m + c], sb[n*sb_n + c] for 32-long K chunk c (bytes)
+  //   scaled_mm: sa[m*sa_m], sb[n*sb_n] (fp32; stride 0 for one scalar)
   const void* sa; int64_t sa_sg, sa_m, sa_kb;
   const void* sb; int64_t sb_sg, sb_n, sb_kb;
   void* out; int64_t o_sg, ldo;
@@ -34,8 +36,9 @@ struct Problem {
   const float* sr;
 };
 
-// Operations whose K loop reads scales (and can use packed scale_a).
-inline bool kloop_scales(bsmm_op op) {
+// Operations whose K loop can read scale_a from the packed layout of the
+// pre-pass (one scale per row per 128-K block).
+inline bool packable_scales(bsmm_op op) {
   return op == BSMM_OP_FP8_BLOCKWISE || op == BSMM_OP_FP8_MX_BMM;
 }
 
@@ -83,7 +86,7 @@ struct Variant {
 // f, f+16, f+32, f+48.  Layout [G][KB][Mp] (G = 1 for blockwise).
 inline int packed_rows(int M) { return (M + 255) / 256 * 256; }
 inline size_t packed_scale_bytes(bsmm_op op, int G, int M, int K) {
-  if (!kloop_scales(op)) return 0;
+  if (!packable_scales(op)) return 0;
   const size_t elem = op == BSMM_OP_FP8_BLOCKWISE ? 4u : 1u;
   const size_t n = (size_t)(op == BSMM_OP_FP8_MX_BMM ? G : 1) * (size_t)(K / kBlockK) *
                    (size_t)packed_rows(M) * elem;

@@ -24,7 +24,8 @@
 //   16x16 operand: lane l holds row (l % 16); its 32 bytes cover K bytes
 //     [32*(l/16), +32) of the 128-byte block (the hardware's internal K order
 //     within those bytes is irrelevant because A and B use the same order and
-//     one scale covers the whole block);
+//     one scale covers the whole block; the 32-element MX blocks need the
+//     instruction's own order -- see kChunk);
 //   16x16 result D = X * Y: lane l, register r -> D[4*(l/16) + r][l % 16].
 // The kernels compute the transposed product (X = B fragment, Y = A
 // fragment), so lane l holds output row (l % 16) and the four consecutive
@@ -107,6 +108,7 @@ template <> struct OpT<BSMM_OP_INT8_ROWWISE> { typedef i32x4 acc_t; typedef int 
 template <> struct OpT<BSMM_OP_FP8_BLOCKWISE> { typedef f32x4 acc_t; typedef float elem_t; };
 template <> struct OpT<BSMM_OP_FP8_MX_BMM> { typedef f32x4 acc_t; typedef float elem_t; };
 template <> struct OpT<BSMM_OP_FP8_SCALED_MM> { typedef f32x4 acc_t; typedef float elem_t; };
+template <> struct OpT<BSMM_OP_FP8_MX32_MM> { typedef f32x4 acc_t; typedef float elem_t; };
 
 // fp8 scaled_mm epilogue: Inductor's apply_scaling (acc * (sa * sb)), then
 // the bias, then the result scale; each step one binary32 rounding.
@@ -240,6 +242,49 @@ __device__ __forceinline__ f32x4 mfma_mx(i32x8 x, i32x8 y, f32x4 c, int sx, int 
   }
 }
 
+// Which 16-byte chunks of a row's 128-byte K block a lane (group g = lane
+// / 16) gives the 16 x 16 x 128 fp8 instruction.  The instruction reads a
+// lane's 32 bytes as K [16 g, 16 g + 16) and then K [64 + 16 g, 64 + 16 g +
+// 16), and multiplies its 32-K block b (K [32 b, 32 b + 32) in that order)
+// by the scale byte of lane group b -- measured on gfx950 by doubling one
+// scale byte at a time against data in one 16-K chunk at a time.  With one
+// scale per 128-K block any assignment used alike for both operands works,
+// and the lane reads chunks 2g and 2g + 1; with 32-element blocks (mx32) it
+// reads chunks g and g + 4, so that the instruction's K order is the true
+// one and scale byte b covers true K [32 b, 32 b + 32).
+template <int OP> struct kChunk {
+  __device__ __forceinline__ static int first(int g) {
+    return OP == BSMM_OP_FP8_MX32_MM ? g : 2 * g;
+  }
+  __device__ __forceinline__ static int second(int g) {
+    return OP == BSMM_OP_FP8_MX32_MM ? g + 4 : 2 * g + 1;
+  }
+};
+
+// MX with 32-element K blocks: every lane brings the e8m0 scale of its own
+// 32 K values (its row or column, K chunk lane / 16), for the B fragment
+// byte `selx` of sx and for the A fragment byte `sely` of sy (both constants
+// after unrolling).
+template <int SY>
+__device__ __forceinline__ f32x4 mfma_mx32_x(i32x8 x, i32x8 y, f32x4 c, uint32_t sx, int selx,
+                                             uint32_t sy) {
+  switch (selx) {
+    case 0: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, c, 0, 0, 0, (int)sx, SY, (int)sy);
+    case 1: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, c, 0, 0, 1, (int)sx, SY, (int)sy);
+    case 2: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, c, 0, 0, 2, (int)sx, SY, (int)sy);
+    default: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, c, 0, 0, 3, (int)sx, SY, (int)sy);
+  }
+}
+__device__ __forceinline__ f32x4 mfma_mx32(i32x8 x, i32x8 y, f32x4 c, uint32_t sx, int selx,
+                                           uint32_t sy, int sely) {
+  switch (sely) {
+    case 0: return mfma_mx32_x<0>(x, y, c, sx, selx, sy);
+    case 1: return mfma_mx32_x<1>(x, y, c, sx, selx, sy);
+    case 2: return mfma_mx32_x<2>(x, y, c, sx, selx, sy);
+    default: return mfma_mx32_x<3>(x, y, c, sx, selx, sy);
+  }
+}
+
 // Lane part of a tile load's offset, (8 wave + l/8) * ld + 16 * chunk, for
 // rows 8q + l/8 with q of parity qpar (see load_row_group); the rest of the
 // offset, 8 t NW ld + the K-block byte offset, is wave-uniform.
@@ -364,11 +409,13 @@ struct Mainloop {
     // Per-lane fragment addresses (bytes within a slot): row / column
     // (lane % 16) of the wave's first 16-row tile, chunks 2*(lane/16) + h.
     const int fr = lane & 15;
-    const int fc = (lane >> 4) * 2;
+    // the lane's two 16-byte chunks of its row's 128 K bytes (mx32: the
+    // matrix instruction's own K order, see kChunk)
+    const int fc0 = kChunk<OP>::first(lane >> 4), fc1 = kChunk<OP>::second(lane >> 4);
     const int a_r = wm * T::WTM + fr;
     const int b_r = wn * T::WTN + fr;
-    const int a_off0 = lds_off(a_r, fc), a_off1 = lds_off(a_r, fc + 1);
-    const int b_off0 = lds_off(b_r, fc), b_off1 = lds_off(b_r, fc + 1);
+    const int a_off0 = lds_off(a_r, fc0), a_off1 = lds_off(a_r, fc1);
+    const int b_off0 = lds_off(b_r, fc0), b_off1 = lds_off(b_r, fc1);
 
     lds_barrier();     // LDS reads of a previous call are finished
     // Scale pointers.  mx: x_scale bytes of this lane's row in each 16-row
@@ -401,6 +448,28 @@ struct Mainloop {
         sb_blk = (const float*)p.sb + (int64_t)nb * p.sb_n;
     }
 
+    // mx32: byte offsets (below 2^31, checked on the host) of the lane's K
+    // chunk (lane / 16) in the scale rows of its A rows and of its column in
+    // each B tile j; rows past M / columns past N read a valid one.  32-bit
+    // offsets from the uniform bases take half the registers of pointers.
+    uint32_t xs_off[TI], ws_off[TJ];
+    if constexpr (OP == BSMM_OP_FP8_MX32_MM) {
+      const int fq = lane >> 4;
+  #pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        const int m = min(row0 + wm * T::WTM + i * 16 + fr, k.row_end - 1);
+        xs_off[i] = (uint32_t)((int64_t)m * p.sa_m + fq);
+      }
+  #pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int n = min(col0 + wn * T::WTN + j * 16 + fr, p.N - 1);
+        ws_off[j] = (uint32_t)((int64_t)n * p.sb_n + fq);
+      }
+    }
+    uint32_t wc_cur[TJ / 4], wc_nxt[TJ / 4];     // mx32: B scale bytes, byte j % 4 of word j / 4
+  #pragma unroll
+    for (int q = 0; q < TJ / 4; ++q) wc_cur[q] = wc_nxt[q] = 0x7F7F7F7Fu;
+
     // Scale registers of the current K block (cur) and the next one (nxt),
     // loaded at least half a K block before they are used.
     // mx: the four row scale bytes of a lane, byte i for 16-row tile i (the
@@ -431,6 +500,20 @@ struct Mainloop {
           for (int i = 0; i < TI; ++i) sa_nxt[i] = sa_row[i][(int64_t)kb * p.sa_kb];
         }
         sb_nxt = sb_blk[(int64_t)kb * p.sb_kb];
+      } else if constexpr (OP == BSMM_OP_FP8_MX32_MM) {
+        const uint8_t* xsb = (const uint8_t*)p.sa + 4 * kb;
+        const uint8_t* wsb = (const uint8_t*)p.sb + 4 * kb;
+        uint32_t v = 0;
+  #pragma unroll
+        for (int i = 0; i < TI; ++i) v |= (uint32_t)xsb[xs_off[i]] << (8 * i);
+        xs_nxt = v;
+  #pragma unroll
+        for (int q = 0; q < TJ / 4; ++q) {
+          uint32_t w = 0;
+  #pragma unroll
+          for (int t = 0; t < 4; ++t) w |= (uint32_t)wsb[ws_off[4 * q + t]] << (8 * t);
+          wc_nxt[q] = w;
+        }
       }
     };
     auto use_scales = [&]() {
@@ -440,6 +523,10 @@ struct Mainloop {
       } else if constexpr (OP == BSMM_OP_FP8_BLOCKWISE) {
   #pragma unroll
         for (int i = 0; i < TI; ++i) sc[i] = sa_nxt[i] * sb_nxt;
+      } else if constexpr (OP == BSMM_OP_FP8_MX32_MM) {
+        xs_cur = xs_nxt;
+  #pragma unroll
+        for (int q = 0; q < TJ / 4; ++q) wc_cur[q] = wc_nxt[q];
       }
     };
 
@@ -500,6 +587,8 @@ struct Mainloop {
           }
           ring[tt % D] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
               bcur, af[i], f32x4{0, 0, 0, 0}, 0, 0, 0, 127, 0, 127);
+        } else if constexpr (OP == BSMM_OP_FP8_MX32_MM) {
+          acc[i][j] = mfma_mx32(bcur, af[i], acc[i][j], wc_cur[j >> 2], j & 3, xs_cur, i);
         } else {
           acc[i][j] = mfma_mx(bcur, af[i], acc[i][j], ws_cur, i, xs_cur);
         }
@@ -704,7 +793,9 @@ skinny_kernel(const KArgs k) {
   const int KB = p.K / kBlockK;
   const int kbA = wave * KB / 4, kbB = (wave + 1) * KB / 4;
   const int r16 = lane & 15;             // B row n0 + r16, A row r16
-  const uint32_t co = (uint32_t)(lane >> 4) * 32;
+  // byte offsets of the lane's two 16-byte chunks within a K block
+  const uint32_t co = (uint32_t)kChunk<OP>::first(lane >> 4) * 16;
+  const uint32_t co2 = (uint32_t)(kChunk<OP>::second(lane >> 4) - kChunk<OP>::first(lane >> 4)) * 16;
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(
       p.b + (int64_t)g * p.b_sg + (int64_t)n0 * p.ldb, (uint64_t)(p.N - n0) * p.ldb);
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(
@@ -721,15 +812,20 @@ skinny_kernel(const KArgs k) {
   auto load = [&](int kb, int slot) {
     const uint32_t kbyte = (uint32_t)kb * kBlockK;
     const i32x4 wl = __builtin_amdgcn_raw_buffer_load_b128(rw, wrow + kbyte, 0, 0);
-    const i32x4 wh = __builtin_amdgcn_raw_buffer_load_b128(rw, wrow + kbyte + 16, 0, 0);
+    const i32x4 wh = __builtin_amdgcn_raw_buffer_load_b128(rw, wrow + kbyte + co2, 0, 0);
     const uint32_t xo = xlive ? xrow + kbyte : kOob;   // rows past M read as zero
     const i32x4 xl = __builtin_amdgcn_raw_buffer_load_b128(rx, xo, 0, 0);
-    const i32x4 xh = __builtin_amdgcn_raw_buffer_load_b128(rx, xlive ? xo + 16 : kOob, 0, 0);
+    const i32x4 xh = __builtin_amdgcn_raw_buffer_load_b128(rx, xlive ? xo + co2 : kOob, 0, 0);
     wf[slot] = i32x8{wl.x, wl.y, wl.z, wl.w, wh.x, wh.y, wh.z, wh.w};
     xf[slot] = i32x8{xl.x, xl.y, xl.z, xl.w, xh.x, xh.y, xh.z, xh.w};
     if constexpr (OP == BSMM_OP_FP8_MX_BMM) {
       xs_blk[slot] = ((const uint8_t*)p.sa)[(int64_t)g * p.sa_sg + (int64_t)m_s * p.sa_m + kb];
       ws_blk[slot] = ((const uint8_t*)p.sb)[(int64_t)g * p.sb_sg + (int64_t)nb * p.sb_n + kb];
+    } else if constexpr (OP == BSMM_OP_FP8_MX32_MM) {
+      // the lane's own K chunk: row / column r16, chunk 4 kb + lane / 16
+      const int c = 4 * kb + (lane >> 4);
+      xs_blk[slot] = ((const uint8_t*)p.sa)[(int64_t)m_s * p.sa_m + c];
+      ws_blk[slot] = ((const uint8_t*)p.sb)[(int64_t)min(n0 + r16, p.N - 1) * p.sb_n + c];
     } else if constexpr (OP == BSMM_OP_FP8_BLOCKWISE) {
       s_blk[slot] = ((const float*)p.sa)[(int64_t)m_s * p.sa_m + (int64_t)kb * p.sa_kb] *
                     ((const float*)p.sb)[(int64_t)kb * p.sb_kb + (int64_t)nb * p.sb_n];
@@ -748,7 +844,7 @@ skinny_kernel(const KArgs k) {
           w, x, f32x4{0, 0, 0, 0}, 0, 0, 0, 127, 0, 127);
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(s_blk[slot], pp[r], acc[r]);
-    } else if constexpr (OP == BSMM_OP_FP8_MX_BMM) {
+    } else if constexpr (OP == BSMM_OP_FP8_MX_BMM || OP == BSMM_OP_FP8_MX32_MM) {
       acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w, x, acc, 0, 0, 0, ws_blk[slot], 0,
                                                              xs_blk[slot]);
     } else {   // scaled_mm: unit hardware scales, the scales come in the epilogue
@@ -1682,8 +1778,9 @@ int launch_kernel(const Problem& p, const Launch& l) {
   if constexpr (KIND == 2) {
     return launch_skinny<OP, OUT, RING>(p, l);
   } else if constexpr (KIND == 1) {
-    // wide waves for int8 / mx; blockwise runs the 256 x 256 eight-wave kernel
-    if constexpr (OP == BSMM_OP_FP8_BLOCKWISE)
+    // wide waves for int8 / mx / scaled_mm; blockwise and mx32 (per-lane
+    // column scales) run the 256 x 256 eight-wave kernel
+    if constexpr (OP == BSMM_OP_FP8_BLOCKWISE || OP == BSMM_OP_FP8_MX32_MM)
       return launch_tile<OP, OUT, 4, 2, 5, PKX>(p, l);
     else
       return launch_tile4<OP, OUT, PKX>(p, l);

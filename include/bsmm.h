@@ -75,7 +75,8 @@ typedef enum {
   BSMM_OP_INT8_ROWWISE = 0,
   BSMM_OP_FP8_BLOCKWISE = 1,
   BSMM_OP_FP8_MX_BMM = 2,
-  BSMM_OP_FP8_SCALED_MM = 3
+  BSMM_OP_FP8_SCALED_MM = 3,
+  BSMM_OP_FP8_MX32_MM = 4
 } bsmm_op;
 
 /*
@@ -193,6 +194,31 @@ bsmm_status bsmm_fp8_scaled_mm(const uint8_t* a, int64_t lda,
                                int64_t M, int64_t N, int64_t K,
                                void* workspace, size_t workspace_bytes,
                                void* stream);
+
+/*
+ * fp8 E4M3FN x E4M3FN with e8m0 scales on 32-element K blocks of both
+ * operands: the MX variants of _scaled_mm that Inductor's tuned_scaled_mm
+ * (mm.py) routes away from its Triton templates, with the 32-element block
+ * of the OCP microscaling formats (a reading: the pages do not print the
+ * block).  One scale byte per row of A and per column of B for each 32-long
+ * K chunk c:
+ *
+ *   out[m*ldo + n] = sum_c 2^(a_scale[m*as_m + c] - 127) * 2^(b_scale[n*bs_n + c] - 127)
+ *                          * sum_{k in chunk c} A[m,k] * B[k,n]
+ * accumulated in fp32 (the chunk scales are the hardware scale operands of
+ * the matrix instruction) and stored as fp32 or bf16 (RNE).  a, b: E4M3FN
+ * bytes, A row-major, B K-contiguous (b[n*ldb + k]).  Scale rows are
+ * K/32 contiguous bytes.  K % 128 == 0, any N; scale byte 255 (NaN)
+ * unsupported; otherwise the conventions above.
+ */
+bsmm_status bsmm_fp8_mx32_mm(const uint8_t* a, int64_t lda,
+                             const uint8_t* b, int64_t ldb,
+                             const uint8_t* a_scale, int64_t as_m,
+                             const uint8_t* b_scale, int64_t bs_n,
+                             void* out, int64_t ldo, bsmm_dtype out_dtype,
+                             int64_t M, int64_t N, int64_t K,
+                             void* workspace, size_t workspace_bytes,
+                             void* stream);
 
 /*
  * Dynamic quantisation: bf16 / fp32 activations -> the 1-byte codes and the

@@ -332,6 +332,8 @@ CONFIGS = {
     # bf16 bias (the fp8 scaled_mm epilogue)
     "c3r": dict(op="fp8_scaled_mm", M=16640, N=5120, K=8192, seed=3,
                 scaling="rowwise", bias="bf16", out="bf16"),
+    # the same shape with 32-element MX (e8m0) block scales
+    "c3x": dict(op="fp8_mx32", M=16640, N=5120, K=8192, seed=3, out="bf16"),
 }
 
 
@@ -342,6 +344,8 @@ def config_inputs(name: str):
                                    kind=c["kind"])
     if c["op"] == "fp8_blockwise":
         return fp8_blockwise_inputs(c["M"], c["N"], c["K"], c["seed"])
+    if c["op"] == "fp8_mx32":
+        return fp8_mx32_inputs(c["M"], c["N"], c["K"], c["seed"])
     if c["op"] == "fp8_scaled_mm":
         return fp8_scaled_mm_inputs(c["M"], c["N"], c["K"], c["seed"],
                                     scaling=c["scaling"], bias=c["bias"])

@@ -147,6 +147,33 @@ def test_scaled_mm_noops_and_plans():
     assert p["workspace"] == 0 and not p["variant"].endswith("p")
 
 
+def mx32(*, a=P, lda=256, b=P, ldb=256, sa=P, as_m=8, sb=P, bs_n=8, out=P, ldo=128,
+         dt=bsmm.BF16, M=64, N=128, K=256):
+    return bsmm.load().bsmm_fp8_mx32_mm(a, lda, b, ldb, sa, as_m, sb, bs_n, out, ldo, dt, M, N,
+                                        K, None, 0, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=-1), SHAPE), (dict(dt=bsmm.I32), DTYPE), (dict(dt=bsmm.E4M3), DTYPE),
+    (dict(K=96), UNSUP), (dict(out=None), NULL), (dict(sa=None), NULL), (dict(b=None), NULL),
+    (dict(as_m=7), SCALE), (dict(bs_n=-1), SCALE), (dict(ldo=100), SHAPE), (dict(lda=128), SHAPE),
+    (dict(ldb=264), ALIGN), (dict(a=P + 4), ALIGN), (dict(out=P + 2), ALIGN),
+    (dict(as_m=1 << 26), UNSUP),
+])
+def test_mx32_rejects(kw, status):
+    assert mx32(**kw) == status
+    assert bsmm.load().bsmm_last_error().decode()
+
+
+def test_mx32_noops_and_plans():
+    assert mx32(M=0) == OK and mx32(N=0) == OK
+    # byte scales need no alignment; no packed-scale plans
+    assert mx32(M=0, sa=P + 1, sb=P + 3) == OK
+    p = bsmm.bsmm_query_plan(bsmm.OP_FP8_MX32_MM, 1, 16640, 5120, 8192, "bf16")
+    assert not p["variant"].endswith("p")
+    assert bsmm.bsmm_query_plan(bsmm.OP_FP8_MX32_MM, 1, 3, 256, 512, "f32")["variant"] == "s16x16"
+
+
 def qi8(*, x=P, ldx=256, xdt=bsmm.BF16, q=P, ldq=256, sc=P, s_m=1, M=64, K=256):
     return bsmm.load().bsmm_quant_int8_rowwise(x, ldx, xdt, q, ldq, sc, s_m, M, K, None)
 
