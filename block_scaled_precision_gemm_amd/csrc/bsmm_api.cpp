@@ -102,7 +102,7 @@ static bool plan_packed(const Plan& pl, bsmm_op op) {
 // split-K partials or stream-K slots of the bulk launch or of the tail
 // launch (they run one after the other on the stream and share the space).
 static size_t plan_ws(const Plan& pl, bsmm_op op, int G, int M, int N, int K) {
-  const size_t pack = plan_packed(pl, op) ? packed_scale_bytes(op, G, M, K) : 0;
+  const size_t pack = plan_packed(pl, op) ? packed_scale_bytes(op, G, M, K, N) : 0;
   const int rows = pl.m_split ? pl.m_split : M;
   size_t main = pl.v->persistent ? persistent_workspace(pl.v, op) : ws_bytes(G, rows, N, pl.split);
   if (pl.tail && pl.m_split) {
@@ -215,7 +215,11 @@ Plan make_plan_heuristic(bsmm_op op, int G, int M, int N, int K, bsmm_dtype dt) 
   Plan pl;
   // fp8 with enough rows: the K loop reads scale_a repacked once per call
   // (one small load per wave and K block instead of one per row group)
-  const bool pack = packable_scales(op) && M > 128 && (int64_t)G * M >= 1024;
+  // mx32 reads twelve scale bytes per lane and K block unpacked, two words
+  // packed: it packs whenever it runs the tile kernel
+  const bool pack = op == BSMM_OP_FP8_MX32_MM
+                        ? M > 16
+                        : packable_scales(op) && M > 128 && (int64_t)G * M >= 1024;
   const char* name;
   if (M <= 16) {
     // decode-sized: one pass over B with K split inside each workgroup
@@ -288,7 +292,7 @@ static bsmm_status run(const Problem& p, size_t workspace_bytes, void* ws,
   l.ws = ws;
   l.ws_bytes = ws ? workspace_bytes : 0;
   if (plan_packed(pl, p.op)) {
-    const size_t pack = packed_scale_bytes(p.op, p.G, p.M, p.K);
+    const size_t pack = packed_scale_bytes(p.op, p.G, p.M, p.K, p.N);
     if (!ws || l.ws_bytes < pack) return fail(BSMM_ERR_ARG, "workspace too small for the plan");
     if (pack_scale_a(p, ws, stream)) return fail(BSMM_ERR_HIP, "scale packing launch failed");
     l.psa = ws;

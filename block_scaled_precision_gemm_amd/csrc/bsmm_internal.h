@@ -36,10 +36,10 @@ struct Problem {
   const float* sr;
 };
 
-// Operations whose K loop can read scale_a from the packed layout of the
-// pre-pass (one scale per row per 128-K block).
+// Operations whose K loop can read its scales from the packed layouts of
+// the pre-pass.
 inline bool packable_scales(bsmm_op op) {
-  return op == BSMM_OP_FP8_BLOCKWISE || op == BSMM_OP_FP8_MX_BMM;
+  return op == BSMM_OP_FP8_BLOCKWISE || op == BSMM_OP_FP8_MX_BMM || op == BSMM_OP_FP8_MX32_MM;
 }
 
 struct Variant;
@@ -84,9 +84,21 @@ struct Variant {
 // 64q + 16i + f stored at position 64q + 4f + i, so that one 16-byte
 // (fp32) or 4-byte (e8m0) load gives a lane the scales of its four rows
 // f, f+16, f+32, f+48.  Layout [G][KB][Mp] (G = 1 for blockwise).
+//
+// mx32 (32-element K chunks, both operands): a_scale packed as above with
+// the chunk c = K/32 index in place of the K block, [KC][Mp] bytes; then
+// (at the next 256-byte boundary) b_scale with column 128g + 16j + f at
+// position 128g + 8f + j, [KC][Np] bytes (Np = N rounded up to 256), so
+// that one 8-byte load gives a lane the scales of its eight columns f,
+// f+16, .., f+112 of a 128-column wave tile.
 inline int packed_rows(int M) { return (M + 255) / 256 * 256; }
-inline size_t packed_scale_bytes(bsmm_op op, int G, int M, int K) {
+inline size_t packed_mx32_a_bytes(int M, int K) {
+  return ((size_t)(K / 32) * (size_t)packed_rows(M) + 255) / 256 * 256;
+}
+inline size_t packed_scale_bytes(bsmm_op op, int G, int M, int K, int N = 0) {
   if (!packable_scales(op)) return 0;
+  if (op == BSMM_OP_FP8_MX32_MM)
+    return packed_mx32_a_bytes(M, K) + ((size_t)(K / 32) * (size_t)packed_rows(N) + 255) / 256 * 256;
   const size_t elem = op == BSMM_OP_FP8_BLOCKWISE ? 4u : 1u;
   const size_t n = (size_t)(op == BSMM_OP_FP8_MX_BMM ? G : 1) * (size_t)(K / kBlockK) *
                    (size_t)packed_rows(M) * elem;

@@ -453,7 +453,19 @@ struct Mainloop {
     // each B tile j; rows past M / columns past N read a valid one.  32-bit
     // offsets from the uniform bases take half the registers of pointers.
     uint32_t xs_off[TI], ws_off[TJ];
-    if constexpr (OP == BSMM_OP_FP8_MX32_MM) {
+    // packed (PK): the lane's A word at chunk c sits at c*Mp + a_lane, its
+    // B word at c*Np + b_lane of the B region
+    const uint8_t* pk_a = (const uint8_t*)k.psa;
+    const uint8_t* pk_b = nullptr;
+    int64_t a_lane = 0, b_lane = 0, mp = 0, np = 0;
+    if constexpr (OP == BSMM_OP_FP8_MX32_MM && PK) {
+      const int fq = lane >> 4;
+      mp = k.psa_ld;
+      np = (p.N + 255) / 256 * 256;    // the pre-pass's column padding
+      pk_b = pk_a + (((int64_t)(p.K / 32) * mp + 255) & ~(int64_t)255);
+      a_lane = fq * mp + (row0 + wm * T::WTM) + 4 * fr;
+      b_lane = fq * np + (col0 + wn * T::WTN) + 8 * fr;
+    } else if constexpr (OP == BSMM_OP_FP8_MX32_MM) {
       const int fq = lane >> 4;
   #pragma unroll
       for (int i = 0; i < TI; ++i) {
@@ -500,6 +512,11 @@ struct Mainloop {
           for (int i = 0; i < TI; ++i) sa_nxt[i] = sa_row[i][(int64_t)kb * p.sa_kb];
         }
         sb_nxt = sb_blk[(int64_t)kb * p.sb_kb];
+      } else if constexpr (OP == BSMM_OP_FP8_MX32_MM && PK) {
+        xs_nxt = *(const uint32_t*)(pk_a + a_lane + 4 * kb * mp);
+        const u32x2 w = *(const u32x2*)(pk_b + b_lane + 4 * kb * np);
+        wc_nxt[0] = w.x;
+        wc_nxt[1] = w.y;
       } else if constexpr (OP == BSMM_OP_FP8_MX32_MM) {
         const uint8_t* xsb = (const uint8_t*)p.sa + 4 * kb;
         const uint8_t* wsb = (const uint8_t*)p.sb + 4 * kb;
@@ -1774,7 +1791,8 @@ template <int OP, int OUT, int WM, int WN, int RING, bool SK, bool PK, int KIND>
 int launch_kernel(const Problem& p, const Launch& l) {
   // the int8 and scaled_mm K loops read no scales: packed variants run the
   // plain kernel
-  constexpr bool PKX = PK && (OP == BSMM_OP_FP8_BLOCKWISE || OP == BSMM_OP_FP8_MX_BMM);
+  constexpr bool PKX = PK && (OP == BSMM_OP_FP8_BLOCKWISE || OP == BSMM_OP_FP8_MX_BMM ||
+                              OP == BSMM_OP_FP8_MX32_MM);
   if constexpr (KIND == 2) {
     return launch_skinny<OP, OUT, RING>(p, l);
   } else if constexpr (KIND == 1) {

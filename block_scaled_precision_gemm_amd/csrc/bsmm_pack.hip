@@ -48,17 +48,60 @@ pack_kernel(const Problem p, void* dst, int64_t ld) {
   }
 }
 
+// mx32: one thread per packed group of one 32-K chunk c.  A: rows 64q + f
+// + 16i, i = 0..3, into one 4-byte word at c*Mp + 64q + 4f.  B: columns
+// 128q + f + 16j, j = 0..7, into one 8-byte word at c*Np + 128q + 8f.  Rows
+// past M / columns past N repeat the last one.  A workgroup covers 16
+// chunks x 16 groups.
+template <bool B_SIDE>
+__global__ void __launch_bounds__(256)
+pack_mx32_kernel(const Problem p, uint8_t* dst, int64_t ld) {
+  const int KC = p.K / 32;
+  const int q = blockIdx.x;
+  const int f = threadIdx.x & 15;
+  const int c = blockIdx.y * 16 + (threadIdx.x >> 4);
+  if (c >= KC) return;
+  if constexpr (!B_SIDE) {
+    const uint8_t* src = (const uint8_t*)p.sa + c;
+    uint32_t v = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      v |= (uint32_t)src[(int64_t)min(q * 64 + 16 * i + f, p.M - 1) * p.sa_m] << (8 * i);
+    *(uint32_t*)(dst + (int64_t)c * ld + (int64_t)q * 64 + 4 * f) = v;
+  } else {
+    const uint8_t* src = (const uint8_t*)p.sb + c;
+    uint32_t v[2] = {0, 0};
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      v[j >> 2] |= (uint32_t)src[(int64_t)min(q * 128 + 16 * j + f, p.N - 1) * p.sb_n]
+                   << (8 * (j & 3));
+    typedef unsigned u2 __attribute__((ext_vector_type(2)));
+    *(u2*)(dst + (int64_t)c * ld + (int64_t)q * 128 + 8 * f) = u2{v[0], v[1]};
+  }
+}
+
 }  // namespace
 
 int pack_scale_a(const Problem& p, void* dst, void* stream) {
-  if (p.op == BSMM_OP_INT8_ROWWISE || dst == nullptr || ((uintptr_t)dst & 15u) || p.M <= 0)
+  if (!packable_scales(p.op) || dst == nullptr || ((uintptr_t)dst & 15u) || p.M <= 0)
     return 1;
+  hipStream_t s = (hipStream_t)stream;
+  if (p.op == BSMM_OP_FP8_MX32_MM) {
+    const int KC = p.K / 32;
+    if (KC == 0) return 0;
+    const int64_t mp = packed_rows(p.M), np = packed_rows(p.N);
+    uint8_t* d = (uint8_t*)dst;
+    hipLaunchKernelGGL(pack_mx32_kernel<false>, dim3((unsigned)(mp / 64), (unsigned)((KC + 15) / 16)),
+                       dim3(256), 0, s, p, d, mp);
+    hipLaunchKernelGGL(pack_mx32_kernel<true>, dim3((unsigned)(np / 128), (unsigned)((KC + 15) / 16)),
+                       dim3(256), 0, s, p, d + packed_mx32_a_bytes(p.M, p.K), np);
+    return hipGetLastError() == hipSuccess ? 0 : 1;
+  }
   const int KB = p.K / kBlockK;
   if (KB == 0) return 0;
   const int64_t ld = packed_rows(p.M);
   const dim3 grid((unsigned)(ld / 64), (unsigned)((KB + 15) / 16),
                   (unsigned)(p.op == BSMM_OP_FP8_MX_BMM ? p.G : 1));
-  hipStream_t s = (hipStream_t)stream;
   if (p.op == BSMM_OP_FP8_MX_BMM)
     hipLaunchKernelGGL(pack_kernel<BSMM_OP_FP8_MX_BMM>, grid, dim3(256), 0, s, p, dst, ld);
   else

@@ -167,10 +167,17 @@ def test_mx32_rejects(kw, status):
 
 def test_mx32_noops_and_plans():
     assert mx32(M=0) == OK and mx32(N=0) == OK
-    # byte scales need no alignment; no packed-scale plans
+    # byte scales need no alignment
     assert mx32(M=0, sa=P + 1, sb=P + 3) == OK
-    p = bsmm.bsmm_query_plan(bsmm.OP_FP8_MX32_MM, 1, 16640, 5120, 8192, "bf16")
-    assert not p["variant"].endswith("p")
+    # the tile kernels read packed scales: A [K/32][M rounded to 256] bytes,
+    # then B [K/32][N rounded to 256] bytes, before the split-K partials
+    M, N, K = 16640, 5120, 8192
+    p = bsmm.bsmm_query_plan(bsmm.OP_FP8_MX32_MM, 1, M, N, K, "bf16")
+    assert p["variant"] == "t256x256p" and p["m_split"] == 16384
+    pack = (K // 32) * 16640 + (K // 32) * 5120
+    assert p["workspace"] == pack + p["tail_split_k"] * 256 * N * 4
+    q = bsmm.bsmm_query_plan(bsmm.OP_FP8_MX32_MM, 1, 200, 384, 512, "bf16", workspace_bytes=0)
+    assert q["variant"] == "t256x128" and q["workspace"] == 0      # no workspace: unpacked
     assert bsmm.bsmm_query_plan(bsmm.OP_FP8_MX32_MM, 1, 3, 256, 512, "f32")["variant"] == "s16x16"
 
 

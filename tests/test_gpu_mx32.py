@@ -5,8 +5,8 @@ The scale bytes vary independently per (row, 32-long K chunk) and per
 values, row or column gives errors far outside the floating-point bar.
 Inputs whose sums are exact in fp32 (small integer codes, scales within a
 few binades) must match bit for bit.  Every kernel path runs: the tile
-kernel, split-K, stream-K, the eight-wave fallback of the wide variant, and
-the skinny kernel.
+kernel with packed and unpacked scales, split-K, stream-K, the eight-wave
+fallback of the wide variant, and the skinny kernel.
 """
 
 import numpy as np
@@ -59,7 +59,8 @@ def test_mx32_parity(gpu_lib, out, M, N, K):
 
 
 @pytest.mark.parametrize("variant,split", [("t128x128", 4), ("t256x256sk", 0), ("w256x256", 0),
-                                           ("t64x256", 3), ("t256x128", 0), ("t128x256p", 2)])
+                                           ("t64x256", 3), ("t256x128", 0), ("t128x256p", 2),
+                                           ("t256x256p", 0), ("t256x256skp", 0)])
 def test_mx32_every_kernel_path(gpu_lib, variant, split):
     M, N, K = 600, 640, 1024
     p = random_problem(M, N, K, 77)
