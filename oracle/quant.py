@@ -87,11 +87,11 @@ def quant_int8_rowwise(x):
     return np.clip(q, -127, 127).astype(np.int8), scale
 
 
-def _blocks(x):
+def _blocks(x, block=BLOCK):
     M, K = x.shape
-    if K % BLOCK:
-        raise ValueError(f"K={K} is not a multiple of {BLOCK}")
-    return x.reshape(M, K // BLOCK, BLOCK)
+    if K % block:
+        raise ValueError(f"K={K} is not a multiple of {block}")
+    return x.reshape(M, K // block, block)
 
 
 def quant_fp8_blockwise(x):
@@ -123,13 +123,13 @@ def e8m0_exponent(amax) -> np.ndarray:
     return np.maximum(ex, -127).astype(np.int64)
 
 
-def quant_fp8_mx(x):
-    """1 x 128 blocks with an e8m0 scale ``2**e``, ``e = ceil(log2(amax/448))``
-    (byte e + 127; 127 where amax is 0), codes ``e4m3_rne(x * 2**-e)`` (a
-    power-of-two scaling, exact in fp64).  Returns (codes uint8 [M, K], scale
-    bytes uint8 [M, K/128])."""
+def quant_fp8_mx(x, block=BLOCK):
+    """1 x ``block`` blocks (128, or 32 for the MX formats' block) with an
+    e8m0 scale ``2**e``, ``e = ceil(log2(amax/448))`` (byte e + 127; 127 where
+    amax is 0), codes ``e4m3_rne(x * 2**-e)`` (a power-of-two scaling, exact
+    in fp64).  Returns (codes uint8 [M, K], scale bytes uint8 [M, K/block])."""
     x = _f32(x)
-    xb = _blocks(x)
+    xb = _blocks(x, block)
     amax = np.abs(xb).max(axis=2)
     ex = e8m0_exponent(amax)
     codes = e4m3_encode_rne(np.ldexp(xb.astype(np.float64), -ex[:, :, None]))

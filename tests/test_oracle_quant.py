@@ -273,3 +273,24 @@ def test_fp8_mx_bottom_clamp_and_zero_block():
     assert not Q.quant_fp8_mx(x)[0][0, 128:].any()
     x[0, 5] = -0.0                                 # in a live block -0 keeps its sign
     assert Q.quant_fp8_mx(x)[0][0, 5] == 0x80
+
+
+def test_fp8_mx_32_element_blocks():
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal((6, 256)) * np.exp2(rng.uniform(-30, 30, (6, 8)).repeat(32, 1))) \
+        .astype(np.float32)
+    codes, e = Q.quant_fp8_mx(x, block=32)
+    assert e.shape == (6, 8)
+    ex = e.astype(np.int64) - 127
+    xb = x.reshape(6, 8, 32).astype(np.float64)
+    r = np.abs(xb).max(axis=2) * np.exp2(-ex.astype(np.float64))
+    assert np.all((r > 224) & (r <= 448))          # the smallest fitting exponent, per 32
+    scaled = np.ldexp(xb, -ex[:, :, None]).astype(np.float32)
+    assert np.array_equal(codes.reshape(6, 8, 32), torch_e4m3(scaled))
+    # four 32-blocks of equal exponent give the 128-block result
+    y = np.tile(np.linspace(-300, 400, 32, dtype=np.float32), (2, 4))
+    c32, e32 = Q.quant_fp8_mx(y, block=32)
+    c128, e128 = Q.quant_fp8_mx(y)
+    assert np.array_equal(c32, c128) and (e32 == e128[:, :1]).all()
+    with pytest.raises(ValueError):
+        Q.quant_fp8_mx(np.ones((2, 48), np.float32), block=32)
