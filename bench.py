@@ -16,7 +16,7 @@ blockwise GEMM whose throughput is the headline target).  Other workloads:
 --config c1 | c2 | c4_m1 | c4_m128 | c4_m8192 | c5 | c3r (the fp8 scaled_mm with
 rowwise scales and a bias on the blockwise workload's shape) | c3x (the same
 shape with 32-element MX scales), and the dynamic
-quantisers of their bf16 activations --config q_int8 | q_fp8 | q_mx | q_mx_t
+quantisers of their bf16 activations --config q_int8 | q_fp8 | q_mx | q_mx_t | q_mx32
 (one quantiser call per step, GB/s against 8 TB/s).
 
 The JSON line also carries
@@ -54,6 +54,7 @@ QUANT_CONFIGS = {
     "q_fp8": ("fp8", (16640, 8192), "normal", 3),         # A of the fp8 16640x5120x8192 GEMM
     "q_mx": ("mx", (8192, 8, 4096), "normal", 43),        # x of the mx BMM, M=8192, G=8
     "q_mx_t": ("mx", (2, 9000, 7168), "t", 5),            # x of the mx BMM, G=2, M=9000
+    "q_mx32": ("mx32", (16640, 8192), "normal", 3),       # A of the MX-32 16640x5120x8192 GEMM
 }
 
 
@@ -317,7 +318,12 @@ def traffic(name, fdir, wdir, cfdir, cwdir):
 def quant_bytes(kind, rows, K):
     """Algorithmic HBM bytes of one quantiser call: bf16 input read once,
     1-byte codes and the scales written once."""
-    scale = rows * 4 if kind == "int8" else rows * (K // 128) * (4 if kind == "fp8" else 1)
+    if kind == "int8":
+        scale = rows * 4
+    elif kind == "mx32":
+        scale = rows * (K // 32)
+    else:
+        scale = rows * (K // 128) * (4 if kind == "fp8" else 1)
     return rows * K * 2 + rows * K + scale
 
 
@@ -325,7 +331,7 @@ def quant_cpu_baseline(kind, x_rows, budget_s):
     """The oracle's quantiser on a growing sample of rows (about budget_s)."""
     from oracle import quant as Q
     fn = {"int8": Q.quant_int8_rowwise, "fp8": Q.quant_fp8_blockwise,
-          "mx": Q.quant_fp8_mx}[kind]
+          "mx": Q.quant_fp8_mx, "mx32": lambda x: Q.quant_fp8_mx(x, block=32)}[kind]
     R, K = x_rows.shape
     rows, t = min(R, 64), 0.0
     while True:
@@ -362,7 +368,8 @@ def bench_quant(args):
     copies = max(2, -(-(1 << 30) // nbytes))
     xs = [xb.cuda() for _ in range(copies)]
     fn = {"int8": bsmm.bsmm_quant_int8_rowwise, "fp8": bsmm.bsmm_quant_fp8_blockwise,
-          "mx": bsmm.bsmm_quant_fp8_mx}[kind]
+          "mx": bsmm.bsmm_quant_fp8_mx,
+          "mx32": lambda x, **kw: bsmm.bsmm_quant_fp8_mx(x, block=32, **kw)}[kind]
     outs = [fn(x) for x in xs]
     torch.cuda.synchronize()
     print(f"[bench] {name}: inputs ready in {time.time() - t0:.1f}s, {copies} copies",
@@ -400,7 +407,8 @@ def bench_quant(args):
         if t.get("kernel_hash") == kernel_hash(QUANT_SOURCES):
             roof["traffic"] = t["hbm_bytes_per_launch"]
     roof["kernel"] = {"int8": "quant_int8_rows", "fp8": "quant_fp8_blocks<fp32 scale>",
-                      "mx": "quant_fp8_blocks<e8m0 scale>"}[kind]
+                      "mx": "quant_fp8_blocks<e8m0 scale>",
+                      "mx32": "quant_fp8_blocks<e8m0 scale, 32-element blocks>"}[kind]
     roof["kernel_ms_mean"] = kern_ms
     roof["kernel_alg_bytes"] = nbytes
     line = {

@@ -74,9 +74,11 @@ def load():
     L.bsmm_quant_int8_rowwise.argtypes = [vp, i64, st, vp, i64, vp, i64, i64, i64, vp]
     L.bsmm_quant_fp8_blockwise.argtypes = [vp, i64, st, vp, i64, vp, i64, i64, i64, i64, vp]
     L.bsmm_quant_fp8_mx.argtypes = [vp, i64, st, vp, i64, vp, i64, i64, i64, i64, vp]
+    L.bsmm_quant_fp8_mx32.argtypes = [vp, i64, st, vp, i64, vp, i64, i64, i64, i64, vp]
     for f in ("bsmm_int8_rowwise", "bsmm_fp8_blockwise", "bsmm_fp8_mx_bmm", "bsmm_fp8_scaled_mm",
               "bsmm_fp8_mx32_mm",
-              "bsmm_quant_int8_rowwise", "bsmm_quant_fp8_blockwise", "bsmm_quant_fp8_mx"):
+              "bsmm_quant_int8_rowwise", "bsmm_quant_fp8_blockwise", "bsmm_quant_fp8_mx",
+              "bsmm_quant_fp8_mx32"):
         getattr(L, f).restype = st
     L.bsmm_workspace_bytes.argtypes = [st, i64, i64, i64, i64, st]
     L.bsmm_workspace_bytes.restype = sz
@@ -501,27 +503,30 @@ def bsmm_quant_fp8_blockwise(x, *, q=None, scale=None, stream=None):
     return q, scale
 
 
-def bsmm_quant_fp8_mx(x, *, q=None, scale=None, stream=None):
-    """fp8 E4M3 quantisation with an e8m0 scale per 1 x 128 block along the
-    last dimension of x [..., K] (bf16 or fp32), e.g. the BMM's x [M, G, K]
-    or [G, M, K].
+def bsmm_quant_fp8_mx(x, *, block=128, q=None, scale=None, stream=None):
+    """fp8 E4M3 quantisation with an e8m0 scale per 1 x ``block`` block
+    (128, or 32 for bsmm_fp8_mx32_mm) along the last dimension of x [..., K]
+    (bf16 or fp32), e.g. the BMM's x [M, G, K] or [G, M, K].
 
-    Returns (q float8_e4m3fn [..., K], scale uint8 e8m0 bytes [..., K/128]),
-    the x and x_scale of bsmm_fp8_mx_bmm.
+    Returns (q float8_e4m3fn [..., K], scale uint8 e8m0 bytes
+    [..., K/block]): the x and x_scale of bsmm_fp8_mx_bmm, or (block 32) an
+    operand and its scales for bsmm_fp8_mx32_mm.
     """
     torch = _torch()
+    if block not in (32, 128):
+        raise ValueError("block must be 32 or 128")
     x2, code = _quant_input(x)
     K = x.shape[-1]
     lead = tuple(x.shape[:-1])
     q = _quant_out(q, lead + (K,), torch.float8_e4m3fn, "q", x.device)
-    scale = _quant_out(scale, lead + (K // 128,), torch.uint8, "scale", x.device)
+    scale = _quant_out(scale, lead + (K // block,), torch.uint8, "scale", x.device)
     if not q.is_contiguous() or not scale.is_contiguous():
         raise ValueError("q and scale must be contiguous")
     q8 = q.view(torch.uint8).view(-1, K) if K else q.view(torch.uint8)
     M = x2.shape[0]
-    _check(load().bsmm_quant_fp8_mx(
-        x2.data_ptr(), x2.stride(0), code, q8.data_ptr(), K,
-        scale.data_ptr(), K // 128, 1, M, K, _stream(stream)))
+    fn = load().bsmm_quant_fp8_mx if block == 128 else load().bsmm_quant_fp8_mx32
+    _check(fn(x2.data_ptr(), x2.stride(0), code, q8.data_ptr(), K,
+              scale.data_ptr(), K // block, 1, M, K, _stream(stream)))
     return q, scale
 
 

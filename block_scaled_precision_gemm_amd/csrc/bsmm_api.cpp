@@ -624,7 +624,7 @@ bsmm_status bsmm_fp8_mx32_mm(const uint8_t* a, int64_t lda, const uint8_t* b, in
 
 namespace {
 
-// Checks shared by the three quantisers; `block` is 8 (int8 rows) or 128.
+// Checks shared by the quantisers; `block` is 8 (int8 rows), 32 or 128.
 bsmm_status quant_common(const void* x, int64_t ldx, bsmm_dtype x_dtype, const void* q,
                          int64_t ldq, const void* scale, int64_t s_m, int64_t s_kb,
                          int64_t M, int64_t K, int block, size_t scale_align) {
@@ -710,6 +710,17 @@ bsmm_status bsmm_quant_fp8_mx(const void* x, int64_t ldx, bsmm_dtype x_dtype, ui
   CHECK(M * (K / 128) < ((int64_t)1 << 30), BSMM_ERR_UNSUPPORTED,
         "M * K / 128 = %lld blocks beyond 2^30", (long long)(M * (K / 128)));
   return quant_run(QuantArgs::kFp8Mx, x, ldx, x_dtype, q, ldq, scale, s_m, s_kb, M, K, stream);
+}
+
+bsmm_status bsmm_quant_fp8_mx32(const void* x, int64_t ldx, bsmm_dtype x_dtype, uint8_t* q,
+                                int64_t ldq, uint8_t* scale, int64_t s_m, int64_t s_kb,
+                                int64_t M, int64_t K, void* stream) {
+  bsmm_status st = quant_common(x, ldx, x_dtype, q, ldq, scale, s_m, s_kb, M, K, 32, 1);
+  if (st != BSMM_OK || M == 0 || K == 0) return st;
+  CHECK(M * (K / 32) < ((int64_t)1 << 30), BSMM_ERR_UNSUPPORTED,
+        "M * K / 32 = %lld blocks beyond 2^30", (long long)(M * (K / 32)));
+  return quant_run(QuantArgs::kFp8Mx32, x, ldx, x_dtype, q, ldq, scale, s_m, s_kb, M, K,
+                   stream);
 }
 
 const char* bsmm_status_string(bsmm_status s) {

@@ -134,7 +134,7 @@ void timing_mark(void* stream, const char* name, bool begin);
 // Dynamic quantisation of bf16 / fp32 rows (bsmm_quant.hip).  Arguments are
 // validated by the entry points before this is called.
 struct QuantArgs {
-  enum Kind { kInt8Rows = 0, kFp8Blocks = 1, kFp8Mx = 2 };
+  enum Kind { kInt8Rows = 0, kFp8Blocks = 1, kFp8Mx = 2, kFp8Mx32 = 3 };
   Kind kind;
   const void* x;        // [M, K] bf16 or fp32, row stride ldx elements
   int64_t ldx;

@@ -700,91 +700,6 @@ struct Mainloop {
   }
 };
 
-// Lane (wave wm, wn; lane l) holds output rows row0 + 16 TI wm + 16 i + l % 16
-// and columns col0 + 16 TJ wn + 16 j + 4 (l / 16) .. +3 of the tile (a wave
-// owns TI x TJ MFMA tiles of 16 x 16).
-struct LanePos { int mrow, ncol; };
-template <int WN, int TI, int TJ>
-__device__ __forceinline__ LanePos lane_pos(int row0, int col0) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int wm = wave / WN, wn = wave % WN;
-  return LanePos{row0 + wm * 16 * TI + (lane & 15), col0 + wn * 16 * TJ + 4 * (lane >> 4)};
-}
-
-// Final epilogue: scale (int8), convert, store the tile to the output.
-template <int OP, int OUT, int WM, int WN, int TI, int TJ, class acc_t>
-__device__ __forceinline__ void store_output(const KArgs& k, int g, int row0, int col0,
-                                             const acc_t (&acc)[TI][TJ]) {
-  const Problem& p = k.p;
-  const LanePos lp = lane_pos<WN, TI, TJ>(row0, col0);
-  const bool vec = k.vec_out != 0;
-  uint8_t* obase = (uint8_t*)p.out;
-  const int64_t og = (int64_t)g * p.o_sg;
-#pragma unroll
-  for (int i = 0; i < TI; ++i) {
-    const int m = lp.mrow + i * 16;
-    if (m >= k.row_end) continue;
-    float sa_m = 1.f;
-    if constexpr (OP == BSMM_OP_INT8_ROWWISE && OUT != BSMM_I32)
-      sa_m = ((const float*)p.sa)[(int64_t)m * p.sa_m];
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-      const int n = lp.ncol + j * 16;
-      const int nvalid = min(4, p.N - n);
-      if (nvalid <= 0) continue;
-      const int64_t e = og + (int64_t)m * p.ldo + n;
-      float y[4];
-      int yi[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if constexpr (OP == BSMM_OP_INT8_ROWWISE) {
-          yi[r] = acc[i][j][r];
-          if constexpr (OUT != BSMM_I32) {
-            // (f32(acc) * sa) * sb, two separately rounded binary32 products
-            const float sb_n = ((const float*)p.sb)[(int64_t)min(n + r, p.N - 1) * p.sb_n];
-            y[r] = __fmul_rn(__fmul_rn((float)acc[i][j][r], sa_m), sb_n);
-          }
-        } else {
-          y[r] = acc[i][j][r];
-        }
-      }
-      store4<OUT>(obase, e, y, yi, vec, nvalid);
-    }
-  }
-}
-
-// Split-K partial: fp32 / int32 values into workspace [splits][G][rows][N].
-template <int OP, int WM, int WN, int TI, int TJ, class acc_t>
-__device__ __forceinline__ void store_splitk(const KArgs& k, int s, int g, int row0,
-                                             int col0, const acc_t (&acc)[TI][TJ]) {
-  const Problem& p = k.p;
-  const LanePos lp = lane_pos<WN, TI, TJ>(row0, col0);
-  const bool vec = k.vec_out != 0;
-  const int rows = k.row_end - k.row_begin;
-  typedef typename OpT<OP>::elem_t E;
-  uint8_t* ws = (uint8_t*)((E*)k.ws + ((int64_t)s * p.G + g) * (int64_t)rows * p.N);
-#pragma unroll
-  for (int i = 0; i < TI; ++i) {
-    const int m = lp.mrow + i * 16;
-    if (m >= k.row_end) continue;
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-      const int n = lp.ncol + j * 16;
-      const int nvalid = min(4, p.N - n);
-      if (nvalid <= 0) continue;
-      const int64_t e = (int64_t)(m - k.row_begin) * p.N + n;
-      if constexpr (OP == BSMM_OP_INT8_ROWWISE) {
-        const int yi[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
-        store4<BSMM_I32>(ws, e, nullptr, yi, vec, nvalid);
-      } else {
-        const float y[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
-        store4<BSMM_F32>(ws, e, y, nullptr, vec, nvalid);
-      }
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Skinny kernel for M <= 16 (decode-sized calls, bound by reading B once).
 // One workgroup per 16 output columns of one batch; its four waves split

@@ -11,7 +11,8 @@
 //   fp8 E4M3FN, one e8m0 scale per 1 x 128 block: scale = 2^e with
 //     e = ceil(log2(amax / 448)), code = rne_e4m3(x * 2^-e) -- the mxscale
 //     activations of the ROCm aiter PR "Add opus fp8 mxscale BMM kernels for
-//     gfx950" (Motivation).
+//     gfx950" (Motivation); the same per 1 x 32 block for the 32-element MX
+//     blocks of the MX matmul.
 //
 // Every quotient is the correctly rounded binary32 quotient; rounding is to
 // nearest, ties to even; e4m3 saturates at +-448.  A row or block whose
@@ -46,9 +47,7 @@ namespace bsmm {
 namespace {
 
 constexpr float kFastDivMin = 0x1p-80f;
-constexpr int kBlocksPerIter = 16;     // fp8: 16 lanes per 128-element block
-constexpr int kIters = 3;              // blocks per lane group per workgroup
-constexpr int kBlocksPerWg = kBlocksPerIter * kIters;
+constexpr int kIters = 3;              // fp8: blocks per lane group per workgroup
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -110,6 +109,14 @@ __device__ inline uint32_t row16_max(uint32_t v) {
   v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
   v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false));
   v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false));
+  return v;
+}
+// the same within groups of LPB = 4 or 16 consecutive lanes
+template <int LPB>
+__device__ inline uint32_t group_max(uint32_t v) {
+  if constexpr (LPB == 16) return row16_max(v);
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
   return v;
 }
 __device__ inline uint32_t wave_max(uint32_t v) {
@@ -239,30 +246,33 @@ __device__ inline int e8m0_exponent(uint32_t amax_bits) {
   return max(e, -127);
 }
 
-// MX = false: fp32 scale amax / 448; MX = true: e8m0 scale.
-template <typename T, bool MX>
+// MX = false: fp32 scale amax / 448; MX = true: e8m0 scale.  LPB lanes of
+// 8 elements per block: 16 (128-element blocks) or 4 (32-element MX blocks).
+template <typename T, bool MX, int LPB>
 __global__ void __launch_bounds__(256)
 quant_fp8_blocks(const T* __restrict__ x, int64_t ldx, uint8_t* __restrict__ q, int64_t ldq,
                  void* __restrict__ scale, int64_t s_m, int64_t s_kb, uint32_t nblocks,
                  uint32_t KB) {
-  const int l = threadIdx.x & 15;
-  const uint32_t b0 = blockIdx.x * kBlocksPerWg + (threadIdx.x >> 4);
+  constexpr int BLOCK = 8 * LPB;
+  constexpr int PER_ITER = 256 / LPB;          // blocks per iteration of the workgroup
+  const int l = threadIdx.x % LPB;
+  const uint32_t b0 = blockIdx.x * (PER_ITER * kIters) + threadIdx.x / LPB;
   Raw8<T> buf[kIters];
   uint32_t row[kIters], kb[kIters];
   // a block past the end loads the last block (in bounds, nblocks >= 1) and
   // stores nothing
 #pragma unroll
   for (int u = 0; u < kIters; ++u) {
-    const uint32_t b = min(b0 + u * kBlocksPerIter, nblocks - 1);
+    const uint32_t b = min(b0 + u * PER_ITER, nblocks - 1);
     row[u] = b / KB;
     kb[u] = b - row[u] * KB;
-    load8(buf[u], x + (int64_t)row[u] * ldx + (int64_t)kb[u] * 128 + l * 8);
+    load8(buf[u], x + (int64_t)row[u] * ldx + (int64_t)kb[u] * BLOCK + l * 8);
   }
 #pragma unroll
   for (int u = 0; u < kIters; ++u) {
-    // the 16 lanes of a block share a DPP row, and a row is live or dead as a whole
-    const uint32_t amax = row16_max(absmax_bits(buf[u]));
-    if (b0 + u * kBlocksPerIter >= nblocks) continue;
+    // the lanes of a block share a DPP row (or quad), which is live or dead as a whole
+    const uint32_t amax = group_max<LPB>(absmax_bits(buf[u]));
+    if (b0 + u * PER_ITER >= nblocks) continue;
     float f[8];
     widen(buf[u], f);
     uint2 w;
@@ -294,7 +304,7 @@ quant_fp8_blocks(const T* __restrict__ x, int64_t ldx, uint8_t* __restrict__ q, 
       if (l == 0)
         static_cast<float*>(scale)[(int64_t)row[u] * s_m + (int64_t)kb[u] * s_kb] = s;
     }
-    store8_nt(q + (int64_t)row[u] * ldq + (int64_t)kb[u] * 128 + l * 8, w);
+    store8_nt(q + (int64_t)row[u] * ldq + (int64_t)kb[u] * BLOCK + l * 8, w);
   }
 }
 
@@ -319,12 +329,13 @@ void launch_rows_nv(const QuantArgs& a, hipStream_t st) {
   else launch_rows<T, 4, 4>(a, st);
 }
 
-template <typename T, bool MX>
+template <typename T, bool MX, int LPB>
 void launch_blocks(const QuantArgs& a, hipStream_t st) {
-  const uint32_t KB = (uint32_t)(a.K / 128);
+  const uint32_t KB = (uint32_t)(a.K / (8 * LPB));
   const uint32_t nblocks = (uint32_t)(a.M * KB);
-  const unsigned grid = (nblocks + kBlocksPerWg - 1) / kBlocksPerWg;
-  hipLaunchKernelGGL((quant_fp8_blocks<T, MX>), dim3(grid), dim3(256), 0, st,
+  const uint32_t per_wg = 256 / LPB * kIters;
+  const unsigned grid = (nblocks + per_wg - 1) / per_wg;
+  hipLaunchKernelGGL((quant_fp8_blocks<T, MX, LPB>), dim3(grid), dim3(256), 0, st,
                      static_cast<const T*>(a.x), a.ldx, static_cast<uint8_t*>(a.q), a.ldq,
                      a.scale, a.s_m, a.s_kb, nblocks, KB);
 }
@@ -339,10 +350,13 @@ int launch_quant(const QuantArgs& a, void* stream) {
       if (bf) launch_rows_nv<uint16_t>(a, st); else launch_rows_nv<float>(a, st);
       break;
     case QuantArgs::kFp8Blocks:
-      if (bf) launch_blocks<uint16_t, false>(a, st); else launch_blocks<float, false>(a, st);
+      if (bf) launch_blocks<uint16_t, false, 16>(a, st); else launch_blocks<float, false, 16>(a, st);
+      break;
+    case QuantArgs::kFp8Mx32:
+      if (bf) launch_blocks<uint16_t, true, 4>(a, st); else launch_blocks<float, true, 4>(a, st);
       break;
     default:
-      if (bf) launch_blocks<uint16_t, true>(a, st); else launch_blocks<float, true>(a, st);
+      if (bf) launch_blocks<uint16_t, true, 16>(a, st); else launch_blocks<float, true, 16>(a, st);
       break;
   }
   return hipGetLastError() == hipSuccess ? 0 : 1;

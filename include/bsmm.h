@@ -275,6 +275,19 @@ bsmm_status bsmm_quant_fp8_mx(const void* x, int64_t ldx, bsmm_dtype x_dtype,
                               uint8_t* scale, int64_t s_m, int64_t s_kb,
                               int64_t M, int64_t K, void* stream);
 
+/*
+ * The e8m0 quantiser on 1 x 32 blocks, for bsmm_fp8_mx32_mm's operands (the
+ * 32-element block of the OCP microscaling formats; the same definition as
+ * bsmm_quant_fp8_mx per 32-element block):  e = ceil(log2(amax / 448))
+ * clamped to >= -127,  scale[m*s_m + c*s_kb] = e + 127,  q = rne_e4m3(x * 2^-e).
+ * K % 32 == 0, M * K / 32 < 2^30.  s_m = K/32, s_kb = 1 is the a_scale row
+ * layout of bsmm_fp8_mx32_mm; for its b_scale, quantise B's rows (N of K).
+ */
+bsmm_status bsmm_quant_fp8_mx32(const void* x, int64_t ldx, bsmm_dtype x_dtype,
+                                uint8_t* q, int64_t ldq,
+                                uint8_t* scale, int64_t s_m, int64_t s_kb,
+                                int64_t M, int64_t K, void* stream);
+
 /* Workspace bytes the fastest plan for this problem wants (0 if none). */
 size_t bsmm_workspace_bytes(bsmm_op op, int64_t G, int64_t M, int64_t N,
                             int64_t K, bsmm_dtype out_dtype);

@@ -204,6 +204,19 @@ def test_quant_int8_rejects(kw, status):
     assert bsmm.load().bsmm_last_error().decode()
 
 
+def test_quant_mx32_rejects_and_noops():
+    L = bsmm.load()
+    call = lambda **kw: L.bsmm_quant_fp8_mx32(
+        kw.get("x", P), kw.get("ldx", 256), kw.get("xdt", bsmm.BF16), kw.get("q", P),
+        kw.get("ldq", 256), kw.get("sc", P), kw.get("s_m", 8), kw.get("s_kb", 1),
+        kw.get("M", 64), kw.get("K", 256), None)
+    assert call(K=48) == UNSUP                    # not a multiple of 32
+    assert call(K=96, s_m=3, M=0) == OK           # 32-element blocks: K = 96 is fine
+    assert call(s_m=7) == SCALE                   # rows of 8 scales overlap
+    assert call(xdt=bsmm.I32) == DTYPE
+    assert call(K=0, x=None, q=None, sc=None) == OK
+
+
 @pytest.mark.parametrize("fn", ["bsmm_quant_fp8_blockwise", "bsmm_quant_fp8_mx"])
 @pytest.mark.parametrize("kw,status", [
     (dict(xdt=7), DTYPE), (dict(K=200), UNSUP), (dict(M=1 << 23, K=1 << 14, ldx=1 << 14,

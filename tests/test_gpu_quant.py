@@ -30,7 +30,8 @@ def device_input(x32, dt):
 
 def run(bsmm, kind, xd):
     fn = {"int8": bsmm.bsmm_quant_int8_rowwise, "fp8": bsmm.bsmm_quant_fp8_blockwise,
-          "mx": bsmm.bsmm_quant_fp8_mx}[kind]
+          "mx": bsmm.bsmm_quant_fp8_mx,
+          "mx32": lambda x: bsmm.bsmm_quant_fp8_mx(x, block=32)}[kind]
     q, s = fn(xd)
     torch.cuda.synchronize()
     q = q.view(torch.uint8).cpu().numpy() if kind != "int8" else q.cpu().numpy()
@@ -44,6 +45,8 @@ def oracle(kind, xv):
         return q, s.reshape(-1, 1)
     if kind == "fp8":
         return Q.quant_fp8_blockwise(rows)
+    if kind == "mx32":
+        return Q.quant_fp8_mx(rows, block=32)
     return Q.quant_fp8_mx(rows)
 
 
@@ -73,15 +76,16 @@ def test_int8_rows_parity(gpu_lib, dt, M, K):
     assert_same("int8", run(gpu_lib, "int8", xd), oracle("int8", xv), f" {dt} {M}x{K}")
 
 
-@pytest.mark.parametrize("kind", ["fp8", "mx"])
+@pytest.mark.parametrize("kind", ["fp8", "mx", "mx32"])
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 @pytest.mark.parametrize("M,K", [(37, 128), (37, 384), (21, 7168), (1, 128), (64, 1024)])
 def test_fp8_blocks_parity(gpu_lib, kind, dt, M, K):
     x = activations((M, K), seed=M * 11 + K, dist="normal", row_scale_log2=(-60, 60))
     # vary the magnitude per block as well, so neighbouring blocks differ
     rng = np.random.default_rng(M + K)
-    x = (x.reshape(M, K // 128, 128) *
-         np.exp2(rng.integers(-20, 20, (M, K // 128, 1))).astype(np.float32)).reshape(M, K)
+    bl = 32 if kind == "mx32" else 128
+    x = (x.reshape(M, K // bl, bl) *
+         np.exp2(rng.integers(-20, 20, (M, K // bl, 1))).astype(np.float32)).reshape(M, K)
     xd, xv = device_input(x, dt)
     assert_same(kind, run(gpu_lib, kind, xd), oracle(kind, xv), f" {dt} {M}x{K}")
 
@@ -129,7 +133,7 @@ def edge_blocks():
     return np.stack(b)
 
 
-@pytest.mark.parametrize("kind", ["fp8", "mx"])
+@pytest.mark.parametrize("kind", ["fp8", "mx", "mx32"])
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 def test_fp8_ties_and_edges(gpu_lib, kind, dt):
     x = np.concatenate([e4m3_tie_blocks(), edge_blocks()])
@@ -197,6 +201,33 @@ def test_mx_3d_activation_layouts(gpu_lib, layout):
     assert np.array_equal(s.cpu().numpy().reshape(-1, K // 128), sw)
 
 
+@pytest.mark.parametrize("M,K", [(37, 96), (5, 224), (130, 32)])
+def test_mx32_quant_short_rows(gpu_lib, M, K):
+    """K a multiple of 32 but not of 128; ragged block counts per workgroup."""
+    x = activations((M, K), seed=K, dist="t", row_scale_log2=(-20, 20))
+    xd, xv = device_input(x, "bf16")
+    assert_same("mx32", run(gpu_lib, "mx32", xd), oracle("mx32", xv), f" {M}x{K}")
+
+
+def test_mx32_quantise_then_matmul(gpu_lib):
+    """bf16 activations and weights quantised on the GPU feed the MX matmul;
+    the oracle quantises the same bf16 values itself and multiplies."""
+    from oracle import scaled_mm as S
+    from oracle.formats import bf16_bits_to_f64
+    M, N, K = 200, 384, 1024
+    xd, xv = device_input(activations((M, K), seed=1), "bf16")
+    wd, wv = device_input(activations((N, K), seed=2, dist="t"), "bf16")
+    qx, sx = gpu_lib.bsmm_quant_fp8_mx(xd, block=32)
+    qw, sw = gpu_lib.bsmm_quant_fp8_mx(wd, block=32)
+    y = gpu_lib.bsmm_fp8_mx32_mm(qx, qw.t(), sx, sw, out_dtype="bf16")
+    torch.cuda.synchronize()
+    got = bf16_bits_to_f64(y.view(torch.int16).cpu().numpy().view(np.uint16))
+    ax, ex = Q.quant_fp8_mx(xv, block=32)
+    aw, ew = Q.quant_fp8_mx(wv, block=32)
+    rep = S.compare(got, S.fp8_mx32_mm(ax, aw.T, ex, ew, "bf16"))
+    assert rep["ok"], rep
+
+
 def test_degenerate_sizes(gpu_lib):
     x = torch.zeros((0, 256), dtype=torch.bfloat16, device="cuda")
     q, s = gpu_lib.bsmm_quant_fp8_blockwise(x)
@@ -214,6 +245,7 @@ def test_degenerate_sizes(gpu_lib):
 # ------------------------------------------------ workload sizes, sampled rows --
 
 WORKLOADS = {
+    "mx32_a_16640x8192": ("mx32", (16640, 8192), "normal", 3),
     # the activations of the matmul workloads, bf16 as a model holds them
     "int8_x_8192x4096": ("int8", (8192, 4096), "normal", 2),
     "fp8_a_16640x8192": ("fp8", (16640, 8192), "normal", 3),
@@ -241,7 +273,8 @@ def test_workload_size_sampled_rows(gpu_lib, name):
     if kind == "int8":
         assert np.all(s > 0) and np.all(np.abs(q.astype(np.int16)).max(axis=1) == 127)
     else:
-        top = (q.reshape(R, K // 128, 128) & 0x7F).max(axis=2)
+        bl = 32 if kind == "mx32" else 128
+        top = (q.reshape(R, K // bl, bl) & 0x7F).max(axis=2)
         if kind == "fp8":
             assert np.all(top == 0x7E)
         else:   # amax * 2**-e lies in (224, 448]: codes 0x76 (224) to 0x7E (448)
