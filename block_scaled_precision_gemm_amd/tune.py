@@ -19,13 +19,15 @@ import re
 
 import torch
 
-from . import (BF16, F32, I32, OP_FP8_BLOCKWISE, OP_FP8_MX_BMM, OP_INT8_ROWWISE,
-               bsmm_fp8_blockwise, bsmm_fp8_mx_bmm, bsmm_int8_rowwise, bsmm_query_plan,
+from . import (BF16, E4M3, F32, I32, OP_FP8_BLOCKWISE, OP_FP8_MX32_MM, OP_FP8_MX_BMM,
+               OP_FP8_SCALED_MM, OP_INT8_ROWWISE, bsmm_fp8_blockwise, bsmm_fp8_mx32_mm,
+               bsmm_fp8_mx_bmm, bsmm_fp8_scaled_mm, bsmm_int8_rowwise, bsmm_query_plan,
                bsmm_set_override, bsmm_variant_names, load)
 
 TABLE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc", "bsmm_tuned_table.inc")
-OPS = {"int8": OP_INT8_ROWWISE, "fp8_blockwise": OP_FP8_BLOCKWISE, "mx": OP_FP8_MX_BMM}
-DTYPES = {"i32": I32, "f32": F32, "bf16": BF16}
+OPS = {"int8": OP_INT8_ROWWISE, "fp8_blockwise": OP_FP8_BLOCKWISE, "mx": OP_FP8_MX_BMM,
+       "scaled_mm": OP_FP8_SCALED_MM, "mx32": OP_FP8_MX32_MM}
+DTYPES = {"i32": I32, "f32": F32, "bf16": BF16, "e4m3": E4M3}
 SPLITS = (1, 2, 3, 4, 6, 8, 12)
 
 
@@ -44,7 +46,8 @@ def make_call(sh, dev="cuda:0"):
     the E4M3 NaN patterns masked out, scales random)."""
     G, M, N, K, out = sh["G"], sh["M"], sh["N"], sh["K"], sh["out"]
     g = torch.Generator(device=dev).manual_seed(0)
-    odt = {"i32": torch.int32, "f32": torch.float32, "bf16": torch.bfloat16}[out]
+    odt = {"i32": torch.int32, "f32": torch.float32, "bf16": torch.bfloat16,
+           "e4m3": torch.float8_e4m3fn}[out]
     if sh["op"] == "int8":
         a = torch.randint(-127, 128, (M, K), dtype=torch.int8, device=dev, generator=g)
         b = torch.randint(-127, 128, (N, K), dtype=torch.int8, device=dev, generator=g)
@@ -53,13 +56,25 @@ def make_call(sh, dev="cuda:0"):
         o = torch.empty((M, N), dtype=odt, device=dev)
         return lambda: bsmm_int8_rowwise(a, b.t(), sa, sb, out_dtype=out, out=o)
     codes = lambda *s: torch.randint(0, 256, s, dtype=torch.uint8, device=dev, generator=g) & 0x77
+    if sh["op"] == "scaled_mm":
+        a, b = codes(M, K), codes(N, K)
+        sa = torch.rand((M, 1), device=dev, generator=g)
+        sb = torch.rand((1, N), device=dev, generator=g)
+        bias = torch.rand((N,), device=dev, generator=g).to(torch.bfloat16)
+        o = torch.empty((M, N), dtype=odt, device=dev)
+        return lambda: bsmm_fp8_scaled_mm(a, b.t(), sa, sb, bias=bias, out_dtype=out, out=o)
+    e8 = lambda *s: torch.randint(120, 135, s, dtype=torch.uint8, device=dev, generator=g)
+    if sh["op"] == "mx32":
+        a, b = codes(M, K), codes(N, K)
+        o = torch.empty((M, N), dtype=odt, device=dev)
+        sa, sb = e8(M, K // 32), e8(N, K // 32)
+        return lambda: bsmm_fp8_mx32_mm(a, b.t(), sa, sb, out_dtype=out, out=o)
     if sh["op"] == "fp8_blockwise":
         a, b = codes(M, K), codes(N, K)
         sa = torch.rand((M, K // 128), device=dev, generator=g)
         sb = torch.rand((K // 128, N // 128), device=dev, generator=g)
         o = torch.empty((M, N), dtype=odt, device=dev)
         return lambda: bsmm_fp8_blockwise(a, b.t(), sa, sb, out_dtype=out, out=o)
-    e8 = lambda *s: torch.randint(120, 135, s, dtype=torch.uint8, device=dev, generator=g)
     if sh["layout"] == "m_major":
         x, xs = codes(M, G, K), e8(M, G, K // 128)
         o = torch.empty((M, G, N), dtype=odt, device=dev)
@@ -125,7 +140,7 @@ def write_table(rows, path=None):
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--shape", action="append", required=True,
-                    help="op,out,G,M,N,K[,layout]  (op: int8 | fp8_blockwise | mx)")
+                    help="op,out,G,M,N,K[,layout]  (op: int8 | fp8_blockwise | mx | scaled_mm | mx32)")
     ap.add_argument("--margin", type=float, default=0.03,
                     help="required gain over the dispatcher's own plan")
     ap.add_argument("--dry-run", action="store_true", help="print, do not write the table")
