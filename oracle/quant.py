@@ -14,7 +14,13 @@ consume.  The recipe is the one the pages state for their workloads:
   blockwise scaling doesn't work with torch.compile" ([M, K/128]);
 * fp8 e4m3, 1 x 128 blocks with an e8m0 (power-of-two) scale, the
   mxscale activations of the ROCm aiter PR "Add opus fp8 mxscale BMM
-  kernels for gfx950" (Motivation): ``2**ceil(log2(amax / 448))``.
+  kernels for gfx950" (Motivation): ``2**ceil(log2(amax / 448))``;
+* for the backward pass of the blockwise fp8 linear layer that the PyTorch
+  issue benchmarks: the weight's 128 x 128 blocks (the blockwise scale_b
+  [K/128, N/128] of that issue, read as a weight's own blocks) with an
+  fp32 scale ``amax / 448``, and 1 x 128 groups taken down the columns of
+  an activation or gradient (128 consecutive tokens of one feature), the
+  operands of the weight-gradient GEMM, whose contraction runs over tokens.
 
 Readings (also listed in the design doc): the quotient ``x / scale`` is the
 binary32 quotient (correctly rounded); it is then rounded to the nearest
@@ -135,3 +141,33 @@ def quant_fp8_mx(x, block=BLOCK):
     codes = e4m3_encode_rne(np.ldexp(xb.astype(np.float64), -ex[:, :, None]))
     codes = np.where((amax == 0)[:, :, None], np.uint8(0), codes).astype(np.uint8)
     return codes.reshape(x.shape), (ex + 127).astype(np.uint8)
+
+
+def quant_fp8_weight_blocks(w):
+    """128 x 128 blocks, fp32 scale ``fl32(amax / 448)`` per block (1 where
+    amax is 0), codes ``e4m3_rne(fl32(w / scale))``.  Returns (codes uint8
+    [R, C], scale fp32 [R/128, C/128])."""
+    w = _f32(w)
+    R, C = w.shape
+    if R % BLOCK or C % BLOCK:
+        raise ValueError(f"shape {w.shape} is not a multiple of {BLOCK} x {BLOCK}")
+    wb = w.reshape(R // BLOCK, BLOCK, C // BLOCK, BLOCK)
+    amax = np.abs(wb).max(axis=(1, 3))
+    scale = _div_f32(amax, np.float32(E4M3_MAX))
+    zero = scale == 0
+    scale = np.where(zero, np.float32(1.0), scale).astype(np.float32)
+    s4 = scale[:, None, :, None]
+    t = np.where(zero[:, None, :, None], 0.0, _div_f32(wb, s4))
+    codes = e4m3_encode_rne(t)
+    return codes.reshape(R, C), scale
+
+
+def quant_fp8_columns(x):
+    """1 x 128 groups down the columns: for each column c and each run of
+    128 rows, fp32 scale ``fl32(amax / 448)`` (1 where amax is 0), codes
+    ``e4m3_rne(fl32(x / scale))``.  The codes are returned transposed, one
+    row per column of x with its rows contiguous (the layout a GEMM whose
+    contraction runs over x's rows reads).  Returns (codes uint8 [C, R],
+    scale fp32 [R/128, C])."""
+    codes_t, scale_t = quant_fp8_blockwise(_f32(x).T)
+    return codes_t, np.ascontiguousarray(scale_t.T)

@@ -157,6 +157,52 @@ def fp8_blockwise(a, b_kn, scale_a, scale_b, out_dtype="bf16", rows=None,
 
 
 # ---------------------------------------------------------------------------
+# fp8 E4M3, 1 x 128 groups on both operands (the backward pass's weight
+# gradient; PyTorch issue "torch._scaled_mm with blockwise scaling doesn't
+# work with torch.compile", whose benchmark is a blockwise fp8 linear layer,
+# forward and backward).  The pages give no layout for the backward GEMMs;
+# reading: each operand's scale must be constant over each 128-long block of
+# the contraction for the per-block dequantisation to factor out of the
+# block's partial sum, and the finest such scale is one per (row of A or
+# column of B, K block).  scale_a [M, K/128], scale_b [K/128, N]:
+#   C[m, n] = sum_kb sa[m, kb] * sb[kb, n] * sum_{k in kb} A[m, k] B[k, n]
+# ---------------------------------------------------------------------------
+
+def fp8_groupwise(a, b_kn, scale_a, scale_b, out_dtype="bf16", rows=None,
+                  cols=None) -> Result:
+    a = np.asarray(a, dtype=np.uint8)
+    b_kn = np.asarray(b_kn, dtype=np.uint8)
+    M, K = a.shape
+    K2, N = b_kn.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ")
+    sa = np.asarray(scale_a, dtype=np.float32)
+    sb = np.asarray(scale_b, dtype=np.float32)
+    KB = -(-K // BLOCK)
+    if sa.shape != (M, KB) or sb.shape != (KB, N):
+        raise ValueError(f"scale shapes {sa.shape}, {sb.shape}; expected "
+                         f"({M}, {KB}) and ({KB}, {N})")
+    r = _idx(M, rows)
+    c = _idx(N, cols)
+    nA, nanA = e4m3_numerator(a[r])
+    nB, nanB = e4m3_numerator(b_kn[:, c])
+    if nanA.any() or nanB.any():
+        raise ValueError("NaN codes in the operands")
+    nA = nA.astype(np.float64)
+    nB = nB.astype(np.float64)
+    C = np.zeros((len(r), len(c)))
+    Bd = np.zeros((len(r), len(c)))
+    for kb, (k0, k1) in enumerate(_blocks(K)):
+        P = nA[:, k0:k1] @ nB[k0:k1, :]                 # exact integers
+        Pabs = np.abs(nA[:, k0:k1]) @ np.abs(nB[k0:k1, :])
+        s = (sa[r, kb].astype(np.float64)[:, None]
+             * sb[kb, c].astype(np.float64)[None, :])   # exact
+        C += s * P * TWO_M18
+        Bd += np.abs(s) * Pabs * TWO_M18
+    return _finish_fp(C, Bd, out_dtype)
+
+
+# ---------------------------------------------------------------------------
 # fp8 E4M3 with e8m0 "mxscale" per-128-K-block scales, batched over G
 # (ROCm aiter PR, Motivation): m-major layout x [M, G, K],
 # x_scale [M, G, K/128]; batch-first layout x [G, M, K], x_scale [G, M, K/128];

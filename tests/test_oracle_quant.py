@@ -294,3 +294,105 @@ def test_fp8_mx_32_element_blocks():
     assert np.array_equal(c32, c128) and (e32 == e128[:, :1]).all()
     with pytest.raises(ValueError):
         Q.quant_fp8_mx(np.ones((2, 48), np.float32), block=32)
+
+
+# ---------------------------------------------------------------------------
+# fp8, 128 x 128 weight blocks, fp32 scale
+# ---------------------------------------------------------------------------
+
+def test_weight_blocks_hand_values():
+    w = np.zeros((256, 256), np.float32)
+    w[3, 100], w[77, 5] = -896.0, 3.0          # block (0,0): scale 2
+    w[200, 10] = 0.5                           # block (1,0): 0.5 / 448
+    w[130, 250] = 448.0                        # block (1,1): scale 1
+    codes, s = Q.quant_fp8_weight_blocks(w)
+    assert s.tolist() == [[2.0, 1.0], [np.float32(0.5 / 448), 1.0]]
+    assert codes[3, 100] == 0xFE and codes[77, 5] == 0x3C     # 3/2 = 1.5
+    assert codes[200, 10] == 0x7E and codes[130, 250] == 0x7E
+    assert not codes[:128, 128:].any()                       # block (0,1) all zero
+
+
+def test_weight_blocks_brute_force():
+    rng = np.random.default_rng(21)
+    w = (rng.standard_normal((256, 384)) * np.exp2(rng.uniform(-8, 8, (256, 384)))) \
+        .astype(np.float32)
+    w[5, 300] = -0.0
+    codes, s = Q.quant_fp8_weight_blocks(w)
+    for bi in range(2):
+        for bj in range(3):
+            blk = w[bi * 128:(bi + 1) * 128, bj * 128:(bj + 1) * 128]
+            amax = max(abs(Fraction(float(v))) for v in blk.ravel())
+            scale = rne_f32(amax / 448)
+            assert Fraction(float(s[bi, bj])) == scale
+            for r in range(0, 128, 29):
+                for c in range(0, 128, 31):
+                    t = rne_f32(Fraction(float(blk[r, c])) / scale)
+                    assert codes[bi * 128 + r, bj * 128 + c] == \
+                        brute_e4m3(t, bool(np.signbit(blk[r, c])))
+    assert codes[5, 300] == 0x80
+
+
+def test_weight_blocks_invariants():
+    rng = np.random.default_rng(22)
+    w = (rng.standard_t(3, (384, 512)) * np.exp2(rng.uniform(-20, 20, (3, 1, 4, 1)))
+         .repeat(128, 1).repeat(128, 3).reshape(384, 512)).astype(np.float32)
+    codes, s = Q.quant_fp8_weight_blocks(w)
+    wb = w.reshape(3, 128, 4, 128).transpose(0, 2, 1, 3).reshape(3, 4, -1)
+    cb = codes.reshape(3, 128, 4, 128).transpose(0, 2, 1, 3).reshape(3, 4, -1)
+    arg = np.abs(wb).argmax(axis=2)
+    top = np.take_along_axis(cb, arg[:, :, None], 2)[:, :, 0]
+    assert np.all((top & 0x7F) == 0x7E)
+    dq = F.e4m3_value(cb) * s[:, :, None]
+    bound = np.maximum(np.abs(wb) * 2.0**-4, 2.0**-10 * s[:, :, None]) * (1 + 1e-6)
+    assert np.all(np.abs(dq - wb) <= bound)
+
+
+def test_weight_blocks_reject_ragged_shapes():
+    with pytest.raises(ValueError):
+        Q.quant_fp8_weight_blocks(np.ones((128, 200), np.float32))
+
+
+# ---------------------------------------------------------------------------
+# fp8, 1 x 128 groups down the columns, transposed codes
+# ---------------------------------------------------------------------------
+
+def test_columns_hand_values():
+    x = np.zeros((256, 3), np.float32)
+    x[0, 0], x[127, 0], x[128, 0] = 448.0, -1.0625, 0.25      # column 0, groups 0 and 1
+    x[40, 2] = -896.0                                        # column 2, group 0: scale 2
+    codes_t, s = Q.quant_fp8_columns(x)
+    assert codes_t.shape == (3, 256) and s.shape == (2, 3)
+    assert s.tolist() == [[1.0, 1.0, 2.0], [np.float32(0.25 / 448), 1.0, 1.0]]
+    assert codes_t[0, 0] == 0x7E and codes_t[0, 127] == 0xB8 and codes_t[0, 128] == 0x7E
+    assert codes_t[2, 40] == 0xFE and not codes_t[1].any()
+
+
+def test_columns_brute_force():
+    rng = np.random.default_rng(23)
+    x = (rng.standard_normal((384, 40)) * np.exp2(rng.uniform(-10, 10, (384, 40)))) \
+        .astype(np.float32)
+    codes_t, s = Q.quant_fp8_columns(x)
+    for c in (0, 13, 39):
+        for g in range(3):
+            col = x[g * 128:(g + 1) * 128, c]
+            amax = max(abs(Fraction(float(v))) for v in col)
+            scale = rne_f32(amax / 448)
+            assert Fraction(float(s[g, c])) == scale
+            for r in range(0, 128, 7):
+                t = rne_f32(Fraction(float(col[r])) / scale)
+                assert codes_t[c, g * 128 + r] == brute_e4m3(t, bool(np.signbit(col[r])))
+
+
+def test_columns_invariants():
+    rng = np.random.default_rng(24)
+    x = (rng.standard_t(3, (512, 96)) * np.exp2(rng.uniform(-20, 20, (4, 1, 96)))
+         .repeat(128, 1).reshape(512, 96)).astype(np.float32)
+    codes_t, s = Q.quant_fp8_columns(x)
+    xg = x.T.reshape(96, 4, 128)
+    cg = codes_t.reshape(96, 4, 128)
+    arg = np.abs(xg).argmax(axis=2)
+    top = np.take_along_axis(cg, arg[:, :, None], 2)[:, :, 0]
+    assert np.all((top & 0x7F) == 0x7E)
+    dq = F.e4m3_value(cg) * s.T[:, :, None]
+    bound = np.maximum(np.abs(xg) * 2.0**-4, 2.0**-10 * s.T[:, :, None]) * (1 + 1e-6)
+    assert np.all(np.abs(dq - xg) <= bound)

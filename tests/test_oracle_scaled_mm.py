@@ -300,3 +300,84 @@ def test_mx32_unit_scales_and_chunk_homogeneity():
     assert np.allclose(got, want, rtol=1e-14, atol=0)
     with pytest.raises(ValueError):
         S.fp8_mx32_mm(a, b, one_a[:, :2], one_b, "f32")
+
+
+# ------------------------------------------- groupwise (1 x 128 on both sides) --
+
+def _gw_random(M, N, K, seed):
+    rng = np.random.default_rng(seed)
+    a = rng.integers(0, 256, (M, K)).astype(np.uint8) & 0xF7          # no NaN codes
+    b = rng.integers(0, 256, (K, N)).astype(np.uint8) & 0xF7
+    sa = (rng.uniform(0.5, 2, (M, K // 128)) * np.exp2(rng.integers(-12, 12, (M, K // 128)))) \
+        .astype(np.float32)
+    sb = (rng.uniform(0.5, 2, (K // 128, N)) * np.exp2(rng.integers(-12, 12, (K // 128, N)))) \
+        .astype(np.float32)
+    sb[0, 1] *= -1
+    return a, b, sa, sb
+
+
+def test_groupwise_brute_force_exact_rationals():
+    M, N, K = 3, 5, 384
+    a, b, sa, sb = _gw_random(M, N, K, 11)
+    res = S.fp8_groupwise(a, b, sa, sb, "f32")
+    for m in range(M):
+        for n in range(N):
+            w = g = Fraction(0)
+            for k in range(K):
+                t = (e4m3_exact(int(a[m, k])) * e4m3_exact(int(b[k, n]))
+                     * Fraction(float(sa[m, k // 128])) * Fraction(float(sb[k // 128, n])))
+                w += t
+                g += abs(t)
+            assert _close(res.exact[m, n], w, g)
+            assert Fraction(float(res.out[m, n])) == rne_f32(w)
+
+
+def test_groupwise_vs_torch_dequant_matmul():
+    M, N, K = 20, 72, 512
+    a, b, sa, sb = _gw_random(M, N, K, 12)
+    res = S.fp8_groupwise(a, b, sa, sb, "f32")
+    A = torch.from_numpy(a.copy()).view(torch.float8_e4m3fn).to(torch.float64)
+    B = torch.from_numpy(b.copy()).view(torch.float8_e4m3fn).to(torch.float64)
+    A = A * torch.from_numpy(sa.astype(np.float64)).repeat_interleave(128, 1)
+    B = B * torch.from_numpy(sb.astype(np.float64)).repeat_interleave(128, 0)
+    assert np.allclose(res.exact, (A @ B).numpy(), rtol=1e-12, atol=1e-300)
+
+
+def test_groupwise_equals_blockwise_when_column_scales_are_constant_per_128_columns():
+    M, N, K = 9, 256, 384
+    a, b, sa, _ = _gw_random(M, N, K, 13)
+    rng = np.random.default_rng(14)
+    sbb = rng.uniform(0.25, 4, (K // 128, N // 128)).astype(np.float32)
+    gw = S.fp8_groupwise(a, b, sa, np.repeat(sbb, 128, axis=1), "f32")
+    bw = S.fp8_blockwise(a, b, sa, sbb, "f32")
+    assert np.array_equal(gw.exact, bw.exact)
+
+
+def test_groupwise_column_scale_multiplies_its_own_column_and_block():
+    M, N, K = 4, 32, 384
+    a, b, _, _ = _gw_random(M, N, K, 15)
+    one_a = np.ones((M, K // 128), np.float32)
+    one_b = np.ones((K // 128, N), np.float32)
+    base = S.fp8_groupwise(a, b, one_a, one_b, "f32").exact
+    sb = one_b.copy()
+    sb[2, 7] = 3.0                              # K block 2 of column 7 only
+    got = S.fp8_groupwise(a, b, one_a, sb, "f32").exact
+    nA, _ = e4m3_numerator(a)
+    nB, _ = e4m3_numerator(b)
+    part = nA[:, 256:384].astype(np.float64) @ nB[256:384, 7].astype(np.float64) * 2.0**-18
+    want = base.copy()
+    want[:, 7] += 2 * part
+    assert np.allclose(got, want, rtol=1e-14, atol=0)
+    sa = one_a.copy()
+    sa[1, 0] = 0.5                              # K block 0 of row 1 only
+    got = S.fp8_groupwise(a, b, sa, one_b, "f32").exact
+    part = nA[1, :128].astype(np.float64) @ nB[:128].astype(np.float64) * 2.0**-18
+    want = base.copy()
+    want[1] -= 0.5 * part
+    assert np.allclose(got, want, rtol=1e-14, atol=0)
+
+
+def test_groupwise_rejects_blockwise_scale_shapes():
+    a, b, sa, _ = _gw_random(4, 256, 256, 16)
+    with pytest.raises(ValueError):
+        S.fp8_groupwise(a, b, sa, np.ones((2, 2), np.float32))
