@@ -15,7 +15,9 @@ Default workload: the fp8 E4M3 blockwise GEMM M=16640, N=5120, K=8192 with
 blockwise GEMM whose throughput is the headline target).  Other workloads:
 --config c1 | c2 | c4_m1 | c4_m128 | c4_m8192 | c5 | c3r (the fp8 scaled_mm with
 rowwise scales and a bias on the blockwise workload's shape) | c3x (the same
-shape with 32-element MX scales), and the dynamic
+shape with 32-element MX scales) | c3d, c3w (that layer's backward pass: the
+input gradient, a blockwise GEMM 16640x8192x5120, and the weight gradient, a
+groupwise GEMM 5120x8192 over 16640 tokens), and the dynamic
 quantisers of their bf16 activations --config q_int8 | q_fp8 | q_mx | q_mx_t | q_mx32
 (one quantiser call per step, GB/s against 8 TB/s).
 
@@ -76,6 +78,9 @@ def describe(name, c):
     if c["op"] == "fp8_mx32":
         return (f"fp8 e4m3 MX GEMM M={c['M']} N={c['N']} K={c['K']}, e8m0 scales per 32-long "
                 f"K block of every row and column, {c['out']} out")
+    if c["op"] == "fp8_groupwise":
+        return (f"fp8 e4m3 groupwise GEMM M={c['M']} N={c['N']} K={c['K']}, fp32 scales per "
+                f"128-long K block of every row and column, {c['out']} out")
     if c["op"] == "fp8_scaled_mm":
         return (f"fp8 e4m3 scaled_mm M={c['M']} N={c['N']} K={c['K']}, {c['scaling']} fp32 "
                 f"scales, {c['bias']} bias, {c['out']} out")
@@ -95,6 +100,8 @@ def alg_bytes(c):
         sc = 4 * (M + N) + 2 * N          # row and column scales, bf16 bias
     elif c["op"] == "fp8_mx32":
         sc = (M + N) * (K // 32)
+    elif c["op"] == "fp8_groupwise":
+        sc = 4 * (M + N) * (K // 128)
     elif c["op"] == "fp8_blockwise":
         sc = 4 * (M * (K // 128) + (K // 128) * (N // 128))
     else:
@@ -114,6 +121,8 @@ def launch_bytes(c, rows):
         sa, sb = 4 * rows, 4 * N + 2 * N
     elif c["op"] == "fp8_mx32":
         sa, sb = rows * (K // 32), N * (K // 32)
+    elif c["op"] == "fp8_groupwise":
+        sa, sb = 4 * rows * (K // 128), 4 * N * (K // 128)
     elif c["op"] == "fp8_blockwise":
         sa, sb = 4 * rows * (K // 128), 4 * (K // 128) * (N // 128)
     else:
@@ -145,6 +154,12 @@ def make_call(name, c, p, torch, bsmm):
         out = torch.empty((c["M"], c["N"]), dtype=torch.bfloat16 if c["out"] == "bf16"
                           else torch.float32, device=dev)
         return lambda: bsmm.bsmm_fp8_mx32_mm(a, b, sa, sb, out_dtype=c["out"], out=out)
+    if c["op"] == "fp8_groupwise":
+        a, b = d(p["a"]), d(p["b_nk"]).t()
+        sa, sb = d(p["scale_a"]), d(p["scale_b"])
+        out = torch.empty((c["M"], c["N"]), dtype=torch.bfloat16 if c["out"] == "bf16"
+                          else torch.float32, device=dev)
+        return lambda: bsmm.bsmm_fp8_groupwise(a, b, sa, sb, out_dtype=c["out"], out=out)
     if c["op"] == "fp8_scaled_mm":
         a, b = d(p["a"]), d(p["b_nk"]).t()
         sa, sb = d(p["scale_a"]), d(p["scale_b"])
@@ -180,6 +195,8 @@ def cpu_baseline(name, c, p, budget_s=15.0):
             S.fp8_blockwise(p["a"], p["b_nk"].T, p["scale_a"], p["scale_b"], c["out"], rows=r)
         elif c["op"] == "fp8_mx32":
             S.fp8_mx32_mm(p["a"], p["b_nk"].T, p["a_scale"], p["b_scale"], c["out"], rows=r)
+        elif c["op"] == "fp8_groupwise":
+            S.fp8_groupwise(p["a"], p["b_nk"].T, p["scale_a"], p["scale_b"], c["out"], rows=r)
         elif c["op"] == "fp8_scaled_mm":
             S.fp8_scaled_mm(p["a"], p["b_nk"].T, p["scale_a"], p["scale_b"], bias=p["bias"],
                             out_dtype=c["out"], rows=r)
@@ -509,7 +526,8 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     value = flops / (ms_per_step * 1e-3) / 1e12
 
-    op = {"int8": 0, "fp8_blockwise": 1, "mx": 2, "fp8_scaled_mm": 3, "fp8_mx32": 4}[c["op"]]
+    op = {"int8": 0, "fp8_blockwise": 1, "mx": 2, "fp8_scaled_mm": 3, "fp8_mx32": 4,
+          "fp8_groupwise": 5}[c["op"]]
     plan = bsmm.bsmm_query_plan(op, G, M, N, K, c["out"])
     # dominant kernel: the main launch of the plan (all rows, or the bulk rows
     # of an M-split plan); its algorithmic work is its share of the rows

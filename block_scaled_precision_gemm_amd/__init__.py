@@ -16,7 +16,7 @@ import os
 __all__ = [
     "load", "lib_path", "BsmmError",
     "bsmm_int8_rowwise", "bsmm_fp8_blockwise", "bsmm_fp8_mx_bmm", "bsmm_fp8_scaled_mm",
-    "bsmm_fp8_mx32_mm", "OP_FP8_MX32_MM",
+    "bsmm_fp8_mx32_mm", "OP_FP8_MX32_MM", "bsmm_fp8_groupwise", "OP_FP8_GROUPWISE",
     "bsmm_quant_int8_rowwise", "bsmm_quant_fp8_blockwise", "bsmm_quant_fp8_mx",
     "bsmm_workspace_bytes", "bsmm_query_plan", "bsmm_set_override",
     "bsmm_variant_names", "bsmm_version", "bsmm_timing_enable", "bsmm_timing_read",
@@ -30,6 +30,7 @@ lib_path = os.path.join(_PKG, "libbsmm.so")
 
 I32, F32, BF16, E4M3 = 0, 1, 2, 3
 OP_INT8_ROWWISE, OP_FP8_BLOCKWISE, OP_FP8_MX_BMM, OP_FP8_SCALED_MM, OP_FP8_MX32_MM = 0, 1, 2, 3, 4
+OP_FP8_GROUPWISE = 5
 STATUS = {0: "BSMM_OK", 1: "BSMM_ERR_NULL", 2: "BSMM_ERR_SHAPE",
           3: "BSMM_ERR_SCALE_SHAPE", 4: "BSMM_ERR_LAYOUT", 5: "BSMM_ERR_ALIGN",
           6: "BSMM_ERR_DTYPE", 7: "BSMM_ERR_UNSUPPORTED", 8: "BSMM_ERR_HIP",
@@ -64,6 +65,8 @@ def load():
     L.bsmm_int8_rowwise.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, st,
                                     i64, i64, i64, vp, sz, vp]
     L.bsmm_fp8_blockwise.argtypes = [vp, i64, vp, i64, vp, i64, i64, vp, i64, i64,
+                                     vp, i64, st, i64, i64, i64, vp, sz, vp]
+    L.bsmm_fp8_groupwise.argtypes = [vp, i64, vp, i64, vp, i64, i64, vp, i64, i64,
                                      vp, i64, st, i64, i64, i64, vp, sz, vp]
     L.bsmm_fp8_mx_bmm.argtypes = [vp, i64, i64, vp, i64, i64, vp, i64, i64, vp, i64,
                                   i64, vp, i64, i64, st, i64, i64, i64, i64, vp, sz, vp]
@@ -265,6 +268,45 @@ def bsmm_fp8_blockwise(a, b, scale_a, scale_b, *, out_dtype="bf16", out=None,
     o = _out(out, (M, N), code, a8.device)
     wsp, wsn = _ws_args(workspace, OP_FP8_BLOCKWISE, 1, M, N, K, code, a8.device)
     _check(load().bsmm_fp8_blockwise(
+        a8.data_ptr(), a8.stride(0), b8.data_ptr(), b8.stride(1),
+        scale_a.data_ptr(), scale_a.stride(0), scale_a.stride(1),
+        scale_b.data_ptr(), scale_b.stride(0), scale_b.stride(1),
+        o.data_ptr(), o.stride(0), code, M, N, K, wsp, wsn, _stream(stream)))
+    return o
+
+
+def bsmm_fp8_groupwise(a, b, scale_a, scale_b, *, out_dtype="bf16", out=None,
+                       workspace=None, stream=None):
+    """fp8 E4M3 matmul with 1 x 128 groups on both operands (the weight
+    gradient of a blockwise fp8 linear layer).
+
+    a: [M, K] E4M3 codes, row-major.  b: [K, N] column-major.  scale_a: fp32
+    [M, K/128] (per row of a and K block); scale_b: fp32 [K/128, N] (per K
+    block and column of b); any strides.  The call needs a workspace (the
+    default allocates one); ``workspace=False`` is rejected by the library.
+    """
+    torch = _torch()
+    code = _dtype_code(out_dtype)
+    a8, b8 = _bytes_view(a, "a"), _bytes_view(b, "b")
+    M, K = a8.shape
+    K2, N = b8.shape
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    if K and a8.stride(1) != 1:
+        raise ValueError(f"a must be row-major, got stride {a8.stride()}")
+    if K and b8.stride(0) != 1:
+        raise ValueError(f"b must be column-major, got stride {b8.stride()}")
+    KB = -(-K // 128)
+    if scale_a.dtype != torch.float32 or scale_b.dtype != torch.float32:
+        raise ValueError("groupwise scales must be fp32")
+    if tuple(scale_a.shape) != (M, KB) or tuple(scale_b.shape) != (KB, N):
+        raise ValueError(
+            "Invalid scaling configuration. For groupwise (1x128 x 128x1) scaling, scale_a "
+            f"should be ({M}, {KB}) and scale_b should be ({KB}, {N}). Got "
+            f"scale_a.size()={tuple(scale_a.shape)} and scale_b.size()={tuple(scale_b.shape)}")
+    o = _out(out, (M, N), code, a8.device)
+    wsp, wsn = _ws_args(workspace, OP_FP8_GROUPWISE, 1, M, N, K, code, a8.device)
+    _check(load().bsmm_fp8_groupwise(
         a8.data_ptr(), a8.stride(0), b8.data_ptr(), b8.stride(1),
         scale_a.data_ptr(), scale_a.stride(0), scale_a.stride(1),
         scale_b.data_ptr(), scale_b.stride(0), scale_b.stride(1),

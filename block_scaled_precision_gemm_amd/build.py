@@ -25,10 +25,11 @@ HOST_SOURCES = ["bsmm_api.cpp", "bsmm_tuned.cpp", "bsmm_variants.cpp", "bsmm_tim
 HIP_SOURCE = "bsmm_kernels.hip"
 # The kernel source is compiled once per (operation, output type) pair, in
 # parallel; each object holds that pair's kernels for every configuration.
-#   ops: 0 int8 rowwise, 1 fp8 blockwise, 2 fp8 mx, 3 fp8 scaled_mm, 4 fp8 mx32;
+#   ops: 0 int8 rowwise, 1 fp8 blockwise, 2 fp8 mx, 3 fp8 scaled_mm, 4 fp8 mx32,
+#        5 fp8 groupwise;
 #   outputs: 0 i32, 1 f32, 2 bf16, 3 e4m3
 KERNEL_UNITS = [(0, 0), (0, 1), (0, 2), (1, 1), (1, 2), (2, 1), (2, 2), (3, 1), (3, 2), (3, 3),
-                (4, 1), (4, 2)]
+                (4, 1), (4, 2), (5, 1), (5, 2)]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-I" + INCLUDE, "-I" + CSRC, "-Wall",
           "-Wno-unused-function"]

@@ -64,6 +64,7 @@ const char* op_name(bsmm_op op) {
     case BSMM_OP_FP8_BLOCKWISE: return "fp8_blockwise";
     case BSMM_OP_FP8_SCALED_MM: return "fp8_scaled_mm";
     case BSMM_OP_FP8_MX32_MM: return "fp8_mx32_mm";
+    case BSMM_OP_FP8_GROUPWISE: return "fp8_groupwise";
     default: return "fp8_mx_bmm";
   }
 }
@@ -216,18 +217,21 @@ Plan make_plan_heuristic(bsmm_op op, int G, int M, int N, int K, bsmm_dtype dt) 
   // fp8 with enough rows: the K loop reads scale_a repacked once per call
   // (one small load per wave and K block instead of one per row group)
   // mx32 reads twelve scale bytes per lane and K block unpacked, two words
-  // packed: it packs whenever it runs the tile kernel
-  const bool pack = op == BSMM_OP_FP8_MX32_MM
-                        ? M > 16
-                        : packable_scales(op) && M > 128 && (int64_t)G * M >= 1024;
+  // packed: it packs whenever it runs the tile kernel.  groupwise has only
+  // packed kernels (its K loop stages the packed scales through LDS).
+  const bool gw = op == BSMM_OP_FP8_GROUPWISE;
+  const bool pack = gw || (op == BSMM_OP_FP8_MX32_MM
+                               ? M > 16
+                               : packable_scales(op) && M > 128 && (int64_t)G * M >= 1024);
   const char* name;
-  if (M <= 16) {
+  if (M <= 16 && !gw) {
     // decode-sized: one pass over B with K split inside each workgroup
     pl.v = find_variant("s16x16");
     return pl;
   }
-  if (M <= 64) name = N % 256 == 0 ? "t64x256" : "t64x128";
-  else if (M <= 128) name = N % 256 == 0 ? (pack ? "t128x256p" : "t128x256") : "t128x128";
+  if (M <= 64 && !gw) name = N % 256 == 0 ? "t64x256" : "t64x128";
+  else if (M <= 128)
+    name = N % 256 == 0 ? (pack ? "t128x256p" : "t128x256") : (gw ? "t256x128p" : "t128x128");
   else if (N % 256 == 0) name = pack ? "t256x256p" : "t256x256";
   else name = pack ? "t256x128p" : "t256x128";
   pl.v = find_variant(name);
@@ -270,7 +274,7 @@ Plan make_plan_heuristic(bsmm_op op, int G, int M, int N, int K, bsmm_dtype dt) 
   // M-split: aligned bulk on the big tile plus a narrow tail launch.
   const int bulk = (M / bm) * bm;
   const int tail = M - bulk;
-  if (bm == 256 && tail > 0 && tail <= 64 && (int64_t)G * bulk >= 8192) {
+  if (bm == 256 && tail > 0 && tail <= 64 && (int64_t)G * bulk >= 8192 && !gw) {
     pl.m_split = bulk;
     pl.tail = find_variant(N % 256 == 0 ? "t64x256" : "t64x128");
   }
@@ -286,12 +290,18 @@ static bsmm_status run(const Problem& p, size_t workspace_bytes, void* ws,
             pl.m_split, pl.tail ? pl.tail->name : "-", pl.tail_split, pl.source);
   // packed scale_a first (shared by both launches), then the launches, which
   // share the rest of the workspace
+  if (p.op == BSMM_OP_FP8_GROUPWISE &&
+      (!pl.v->packed_scales || (pl.m_split && pl.tail && !pl.tail->packed_scales)))
+    return fail(BSMM_ERR_ARG,
+                "fp8 groupwise runs packed-scale kernels only: it needs a workspace of %zu bytes "
+                "(variant %s)",
+                bsmm_workspace_bytes(p.op, p.G, p.M, p.N, p.K, p.out_dtype), pl.v->name);
   Launch l;
   l.psa = nullptr;
   l.stream = stream;
   l.ws = ws;
   l.ws_bytes = ws ? workspace_bytes : 0;
-  if (plan_packed(pl, p.op)) {
+  if (plan_packed(pl, p.op) && p.K >= kBlockK) {
     const size_t pack = packed_scale_bytes(p.op, p.G, p.M, p.K, p.N);
     if (!ws || l.ws_bytes < pack) return fail(BSMM_ERR_ARG, "workspace too small for the plan");
     if (pack_scale_a(p, ws, stream)) return fail(BSMM_ERR_HIP, "scale packing launch failed");
@@ -419,6 +429,54 @@ bsmm_status bsmm_fp8_blockwise(const uint8_t* a, int64_t lda, const uint8_t* b,
   return run(p, workspace ? workspace_bytes : 0, workspace, stream);
 }
 
+bsmm_status bsmm_fp8_groupwise(const uint8_t* a, int64_t lda, const uint8_t* b,
+                               int64_t ldb, const float* scale_a, int64_t sa_m,
+                               int64_t sa_kb, const float* scale_b, int64_t sb_kb,
+                               int64_t sb_n, void* out, int64_t ldo,
+                               bsmm_dtype out_dtype, int64_t M, int64_t N, int64_t K,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  CHECK(M >= 0 && N >= 0 && K >= 0, BSMM_ERR_SHAPE, "negative size M=%lld N=%lld K=%lld",
+        (long long)M, (long long)N, (long long)K);
+  CHECK(M < kMaxDim && N < kMaxDim && K < kMaxDim, BSMM_ERR_UNSUPPORTED, "size beyond 2^31");
+  CHECK(out_dtype == BSMM_F32 || out_dtype == BSMM_BF16, BSMM_ERR_DTYPE,
+        "fp8 groupwise writes fp32 or bf16 (got %d)", (int)out_dtype);
+  if (M == 0 || N == 0) return BSMM_OK;
+  CHECK(K % kBlockK == 0, BSMM_ERR_UNSUPPORTED, "K=%lld is not a multiple of 128", (long long)K);
+  CHECK(out != nullptr, BSMM_ERR_NULL, "out is NULL");
+  if (K > 0) {
+    CHECK(a != nullptr && b != nullptr, BSMM_ERR_NULL, "a or b is NULL");
+    CHECK(scale_a != nullptr && scale_b != nullptr, BSMM_ERR_NULL, "scale_a / scale_b is NULL");
+    CHECK(sa_m >= 0 && sa_kb >= 0 && sb_kb >= 0 && sb_n >= 0, BSMM_ERR_SCALE_SHAPE,
+          "scale strides must be >= 0 (0 broadcasts)");
+    const int64_t KB = K / kBlockK;
+    CHECK(((M - 1) * sa_m + (KB - 1) * sa_kb) < ((int64_t)1 << 30) &&
+              ((KB - 1) * sb_kb + (N - 1) * sb_n) < ((int64_t)1 << 30),
+          BSMM_ERR_UNSUPPORTED, "scale index range beyond 2^30");
+    // the K loop addresses the packed scales with 32-bit byte offsets
+    CHECK(KB <= 65535 && packed_scale_bytes(BSMM_OP_FP8_GROUPWISE, 1, (int)M, (int)K, (int)N) <
+                             ((size_t)1 << 31),
+          BSMM_ERR_UNSUPPORTED, "packed scales beyond 2^31 bytes");
+    CHECK(aligned(scale_a, 4) && aligned(scale_b, 4), BSMM_ERR_ALIGN, "scales not 4-byte aligned");
+    CHECK(aligned(a, 16) && aligned(b, 16), BSMM_ERR_ALIGN, "a / b not 16-byte aligned");
+    CHECK(lda >= K && ldb >= K, BSMM_ERR_SHAPE, "leading dimensions lda=%lld ldb=%lld below K",
+          (long long)lda, (long long)ldb);
+    CHECK(lda % 16 == 0 && ldb % 16 == 0, BSMM_ERR_ALIGN, "lda / ldb not multiples of 16 bytes");
+    CHECK(lda <= kMaxLd && ldb <= kMaxLd, BSMM_ERR_UNSUPPORTED, "leading dimension beyond 2^23");
+  }
+  CHECK(ldo >= N, BSMM_ERR_SHAPE, "ldo=%lld below N", (long long)ldo);
+  CHECK(aligned(out, 4), BSMM_ERR_ALIGN, "out not 4-byte aligned");
+  Problem p{};
+  p.op = BSMM_OP_FP8_GROUPWISE;
+  p.out_dtype = out_dtype;
+  p.G = 1; p.M = (int)M; p.N = (int)N; p.K = (int)K;
+  p.a = a; p.lda = lda;
+  p.b = b; p.ldb = ldb;
+  p.sa = scale_a; p.sa_m = sa_m; p.sa_kb = sa_kb;
+  p.sb = scale_b; p.sb_kb = sb_kb; p.sb_n = sb_n;
+  p.out = out; p.ldo = ldo;
+  return run(p, workspace ? workspace_bytes : 0, workspace, stream);
+}
+
 bsmm_status bsmm_fp8_mx_bmm(const uint8_t* x, int64_t x_sg, int64_t x_sm,
                             const uint8_t* w, int64_t w_sg, int64_t w_sn,
                             const uint8_t* x_scale, int64_t xs_sg, int64_t xs_sm,
@@ -479,7 +537,8 @@ bsmm_status bsmm_query_plan(bsmm_op op, int64_t G, int64_t M, int64_t N, int64_t
                             bsmm_plan_info* info) {
   CHECK(info != nullptr, BSMM_ERR_NULL, "info is NULL");
   CHECK(op == BSMM_OP_INT8_ROWWISE || op == BSMM_OP_FP8_BLOCKWISE || op == BSMM_OP_FP8_MX_BMM ||
-            op == BSMM_OP_FP8_SCALED_MM || op == BSMM_OP_FP8_MX32_MM,
+            op == BSMM_OP_FP8_SCALED_MM || op == BSMM_OP_FP8_MX32_MM ||
+            op == BSMM_OP_FP8_GROUPWISE,
         BSMM_ERR_ARG, "unknown op %d", (int)op);
   CHECK(G > 0 && M > 0 && N > 0 && K >= 0, BSMM_ERR_SHAPE, "sizes must be positive");
   CHECK(G < kMaxDim && M < kMaxDim && N < kMaxDim && K < kMaxDim, BSMM_ERR_UNSUPPORTED,

@@ -27,6 +27,7 @@ struct Problem {
   //   mx:        sa[g*sa_sg + m*sa_m + kb], sb[g*sb_sg + nb*sb_n + kb]
   //   mx32:      sa[m*sa_m + c], sb[n*sb_n + c] for 32-long K chunk c (bytes)
   //   scaled_mm: sa[m*sa_m], sb[n*sb_n] (fp32; stride 0 for one scalar)
+  //   groupwise: sa[m*sa_m + kb*sa_kb], sb[kb*sb_kb + n*sb_n]
   const void* sa; int64_t sa_sg, sa_m, sa_kb;
   const void* sb; int64_t sb_sg, sb_n, sb_kb;
   void* out; int64_t o_sg, ldo;
@@ -39,7 +40,8 @@ struct Problem {
 // Operations whose K loop can read its scales from the packed layouts of
 // the pre-pass.
 inline bool packable_scales(bsmm_op op) {
-  return op == BSMM_OP_FP8_BLOCKWISE || op == BSMM_OP_FP8_MX_BMM || op == BSMM_OP_FP8_MX32_MM;
+  return op == BSMM_OP_FP8_BLOCKWISE || op == BSMM_OP_FP8_MX_BMM || op == BSMM_OP_FP8_MX32_MM ||
+         op == BSMM_OP_FP8_GROUPWISE;
 }
 
 struct Variant;
@@ -91,7 +93,15 @@ struct Variant {
 // position 128g + 8f + j, [KC][Np] bytes (Np = N rounded up to 256), so
 // that one 8-byte load gives a lane the scales of its eight columns f,
 // f+16, .., f+112 of a 128-column wave tile.
+//
+// groupwise (1 x 128 groups on both operands): scale_a packed as for
+// blockwise, [KB][Mp] fp32; then (at the next 256-byte boundary) scale_b
+// in plain column order, [KB][Np] fp32, columns past N repeating column
+// N-1.  The K loop stages each K block's slices of both through LDS.
 inline int packed_rows(int M) { return (M + 255) / 256 * 256; }
+inline size_t packed_gw_a_bytes(int M, int K) {
+  return ((size_t)(K / kBlockK) * (size_t)packed_rows(M) * 4u + 255) / 256 * 256;
+}
 inline size_t packed_mx32_a_bytes(int M, int K) {
   return ((size_t)(K / 32) * (size_t)packed_rows(M) + 255) / 256 * 256;
 }
@@ -99,6 +109,8 @@ inline size_t packed_scale_bytes(bsmm_op op, int G, int M, int K, int N = 0) {
   if (!packable_scales(op)) return 0;
   if (op == BSMM_OP_FP8_MX32_MM)
     return packed_mx32_a_bytes(M, K) + ((size_t)(K / 32) * (size_t)packed_rows(N) + 255) / 256 * 256;
+  if (op == BSMM_OP_FP8_GROUPWISE)
+    return packed_gw_a_bytes(M, K) + packed_gw_a_bytes(N, K);
   const size_t elem = op == BSMM_OP_FP8_BLOCKWISE ? 4u : 1u;
   const size_t n = (size_t)(op == BSMM_OP_FP8_MX_BMM ? G : 1) * (size_t)(K / kBlockK) *
                    (size_t)packed_rows(M) * elem;

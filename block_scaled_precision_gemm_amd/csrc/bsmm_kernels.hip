@@ -109,6 +109,7 @@ template <> struct OpT<BSMM_OP_FP8_BLOCKWISE> { typedef f32x4 acc_t; typedef flo
 template <> struct OpT<BSMM_OP_FP8_MX_BMM> { typedef f32x4 acc_t; typedef float elem_t; };
 template <> struct OpT<BSMM_OP_FP8_SCALED_MM> { typedef f32x4 acc_t; typedef float elem_t; };
 template <> struct OpT<BSMM_OP_FP8_MX32_MM> { typedef f32x4 acc_t; typedef float elem_t; };
+template <> struct OpT<BSMM_OP_FP8_GROUPWISE> { typedef f32x4 acc_t; typedef float elem_t; };
 
 // fp8 scaled_mm epilogue: Inductor's apply_scaling (acc * (sa * sb)), then
 // the bias, then the result scale; each step one binary32 rounding.
@@ -177,8 +178,14 @@ __device__ __forceinline__ TileId decode_tile(const KArgs& k, int pid) {
 // the whole 160 KB, so 1.5 K blocks stay in flight).  The two slots of block
 // c - 1 are refilled with half-stages 2c + NSLOT - 2 and 2c + NSLOT - 1 as
 // soon as every wave has passed the barrier at the top of block c.  Scales
-// do not go through LDS: each lane loads the ones it needs into registers one
-// K block ahead.
+// do not go through LDS (groupwise aside): each lane loads the ones it needs
+// into registers one K block ahead.
+//
+// Groupwise (a column scale per lane column, 32 per lane and K block, more
+// than the registers hold): each K block's packed scale_a slice (BM rows)
+// and scale_b slice (BN columns) ride with its A half-stage into a 1 KB
+// region each beside the slot, and the K loop reads them from LDS when it
+// folds.  The ring then has four slots (the regions take the fifth's room).
 // ---------------------------------------------------------------------------
 template <int OP, int WM, int WN, int RING>
 struct Tile {
@@ -190,8 +197,8 @@ struct Tile {
   static constexpr int A_BYTES = BM * kBlockK;
   static constexpr int B_BYTES = BN * kBlockK;
   static constexpr int SLOT = A_BYTES > B_BYTES ? A_BYTES : B_BYTES;
-  static constexpr int NSLOT = RING;
-  static constexpr int LDS = NSLOT * SLOT;
+  static constexpr bool GW = OP == BSMM_OP_FP8_GROUPWISE;
+  static constexpr int NSLOT = GW ? 4 : RING;
 #ifndef BSMM_LOADER_SPLIT
 #define BSMM_LOADER_SPLIT 1
 #endif
@@ -199,8 +206,16 @@ struct Tile {
   // while a loading wave waits to issue a load its SIMD sibling keeps the
   // matrix core busy.
   static constexpr int NLD = BSMM_LOADER_SPLIT && NW >= 8 ? NW / 2 : NW;
-  // direct-to-LDS loads per loading wave for one A / one B half-stage
-  static constexpr int LA = BM / 8 / NLD, LB = BN / 8 / NLD;
+  // groupwise: scale loads per loading wave and A half-stage (instruction
+  // q = t * NLD + wave moves 1 KB: q = 0 scale_a, q = 1 scale_b, others no
+  // memory), and the LDS bytes of one slot's scale regions
+  static constexpr int SCL_LOADS = GW ? (NLD >= 2 ? 1 : 2) : 0;
+  static constexpr int SCL = NLD * SCL_LOADS * 1024;
+  static constexpr int LDS = NSLOT * (SLOT + SCL);
+  // direct-to-LDS loads per loading wave for one A (tile rows, then the
+  // scale loads) / one B half-stage
+  static constexpr int LA_ROWS = BM / 8 / NLD;
+  static constexpr int LA = LA_ROWS + SCL_LOADS, LB = BN / 8 / NLD;
   // loads of the half-stages after block c's pair that may still be in
   // flight when block c starts: h = 2c+2 .. 2c+NSLOT-3 (A, B, A, ...)
   static constexpr int WAIT = ((NSLOT - 3) / 2) * LA + ((NSLOT - 4) / 2) * LB;
@@ -208,6 +223,7 @@ struct Tile {
   static_assert((BM / 8) % NLD == 0 && (BN / 8) % NLD == 0, "loader split");
   static_assert(WAIT < 64, "vmcnt range");
   static_assert(TI == 4, "packed scales hold four rows per lane");
+  static_assert(!GW || (BM * 4 <= 1024 && BN * 4 <= 1024), "one scale load per slice");
 };
 
 // R rows x 128 bytes; one wave instruction moves 8 rows (64 x 16 bytes) to
@@ -392,14 +408,53 @@ struct Mainloop {
         p.b + (int64_t)g * p.b_sg + (int64_t)col0 * p.ldb,
         (uint64_t)(p.N - col0) * p.ldb);
 
+    // Groupwise scale loads (see Tile): per scale load t of this wave, the
+    // lane's byte offset into the packed scales at K block 0, the per-block
+    // step, and a floor that sends lanes past the slice (and waves with
+    // nothing to load) out of range.  Offsets fit 32 bits (checked on the
+    // host).
+    __amdgpu_buffer_rsrc_t rsc = make_rsrc(k.psa, 0);
+    uint32_t gw_base[2] = {0, 0}, gw_step[2] = {0, 0}, gw_floor[2] = {kOob, kOob};
+    if constexpr (T::GW) {
+      const int KBt = p.K / kBlockK;
+      const uint32_t mp = (uint32_t)k.psa_ld, np = (uint32_t)((p.N + 255) / 256 * 256);
+      const uint32_t b_region = ((uint32_t)KBt * mp * 4u + 255u) & ~255u;
+      rsc = make_rsrc(k.psa, (uint64_t)b_region + (uint64_t)KBt * np * 4u);
+  #pragma unroll
+      for (int t = 0; t < T::SCL_LOADS; ++t) {
+        const int q = t * T::NLD + wave;
+        if (q == 0) {
+          gw_base[t] = (uint32_t)row0 * 4u + 16u * lane;
+          gw_step[t] = mp * 4u;
+          gw_floor[t] = lane < T::BM / 4 ? 0u : kOob;
+        } else if (q == 1) {
+          gw_base[t] = b_region + (uint32_t)col0 * 4u + 16u * lane;
+          gw_step[t] = np * 4u;
+          gw_floor[t] = lane < T::BN / 4 ? 0u : kOob;
+        }
+      }
+    }
+    uint8_t* const scl_base = smem + T::NSLOT * SLOT;
+
     // Load t of half-stage h (relative to kb0): its K block's A tile (h
-    // even, LA loads per wave) or B tile (h odd, LB loads), into `slot`.
+    // even, LA loads per wave, the groupwise scale loads last) or B tile (h
+    // odd, LB loads), into `slot`.
     auto issue_load = [&](int h, int slot, int t) {
       uint8_t* dst = smem + slot * SLOT;
       const bool live = h < 2 * nkb;
       const uint32_t kbyte = (uint32_t)(kb0 + (h >> 1)) * kBlockK;
-      if (h & 1) load_row_group<T::NLD>(rb, dst, ldb, kbyte, wave, lane, live, t);
-      else load_row_group<T::NLD>(ra, dst, lda, kbyte, wave, lane, live, t);
+      if (h & 1) {
+        load_row_group<T::NLD>(rb, dst, ldb, kbyte, wave, lane, live, t);
+      } else if (T::GW && t >= T::LA_ROWS) {
+        const int ts = t - T::LA_ROWS;
+        const uint32_t floor = live ? gw_floor[ts] : kOob;
+        const uint32_t vo = max(gw_base[ts] + (uint32_t)(kb0 + (h >> 1)) * gw_step[ts], floor);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsc, (lds_ptr_t)(scl_base + slot * T::SCL + (ts * T::NLD + wave) * 1024), 16, vo, 0,
+            0, 0);
+      } else {
+        load_row_group<T::NLD>(ra, dst, lda, kbyte, wave, lane, live, t);
+      }
     };
     auto issue_half = [&](int h, int slot) {
       const int n = (h & 1) ? T::LB : T::LA;
@@ -490,7 +545,8 @@ struct Mainloop {
     int ws_cur = 127, ws_nxt = 127;
     float sa_nxt[TI];
     float sb_nxt = 1.f;
-    float sc[TI];     // blockwise: scale product of this lane's row in each 16-row tile
+    float sc[TI];     // blockwise: scale product of this lane's row in each 16-row tile;
+                      // groupwise: that row's scale
     auto load_scales = [&](int kb) {
       if constexpr (OP == BSMM_OP_FP8_MX_BMM) {
         if constexpr (PK) {
@@ -559,9 +615,21 @@ struct Mainloop {
       const i32x4 hi = *(const i32x4*)(SB + b_off1 + j * 2048);
       return i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
     };
+    // groupwise: the current K block's staged scales; this lane's four row
+    // scales (packed, one 16-byte read) and the four columns it holds in
+    // 16-column tile j (16 bytes at 64 j of the scale_b region)
+    const uint8_t* scl = scl_base;
+    const int gw_sa = (wm * T::WTM + 4 * fr) * 4;
+    const int gw_sb = 1024 + (wn * T::WTN + 4 * (lane >> 4)) * 4;
     auto read_frags = [&](int slot_a, int slot_b) {
       SA = smem + slot_a * SLOT;
       SB = smem + slot_b * SLOT;
+      if constexpr (T::GW) {
+        scl = scl_base + slot_a * T::SCL;
+        const f32x4 v = *(const f32x4*)(scl + gw_sa);
+  #pragma unroll
+        for (int i = 0; i < TI; ++i) sc[i] = v[i];
+      }
       bcur = read_b(0);
   #pragma unroll
       for (int i = 0; i < TI; ++i) {
@@ -576,10 +644,14 @@ struct Mainloop {
     // multiply-adds never wait on the MFMA that was just issued; the ring is
     // drained at the end of the block.
     constexpr int D = 4;
+    static_assert(!T::GW || D == TI, "groupwise folds the previous column's tiles");
     f32x4 ring[D];
     auto columns = [&](auto refill, auto is_loader) {
       constexpr bool LOADER = decltype(is_loader)::value;
       (void)LOADER;
+      // groupwise: column scales of the column whose tiles are being folded
+      // (the previous one) and of the current one
+      f32x4 sbp = f32x4{0, 0, 0, 0}, sbn = sbp;
       // The order is fixed by hard scheduling fences: per column j, its first
       // MFMA, then the reads of B tile j+1 and the column's refill loads, then
       // its other MFMAs, each preceded (blockwise) by the four multiply-adds
@@ -604,6 +676,16 @@ struct Mainloop {
           }
           ring[tt % D] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
               bcur, af[i], f32x4{0, 0, 0, 0}, 0, 0, 0, 127, 0, 127);
+        } else if constexpr (OP == BSMM_OP_FP8_GROUPWISE) {
+          if (tt >= D) {
+            const int u = tt - D, ui = u % TI, uj = u / TI;   // uj = j - 1
+  #pragma unroll
+            for (int r = 0; r < 4; ++r)
+              acc[ui][uj][r] = __builtin_fmaf(__fmul_rn(sc[ui], sbp[r]), ring[u % D][r],
+                                              acc[ui][uj][r]);
+          }
+          ring[tt % D] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              bcur, af[i], f32x4{0, 0, 0, 0}, 0, 0, 0, 127, 0, 127);
         } else if constexpr (OP == BSMM_OP_FP8_MX32_MM) {
           acc[i][j] = mfma_mx32(bcur, af[i], acc[i][j], wc_cur[j >> 2], j & 3, xs_cur, i);
         } else {
@@ -619,6 +701,7 @@ struct Mainloop {
         // texture unit and hold up the issuing wave)
         i32x8 bnext = bcur;
         if (j + 1 < TJ) bnext = read_b(j + 1);
+        if constexpr (T::GW) sbn = *(const f32x4*)(scl + gw_sb + 64 * j);
         refill(j * TI);
         __builtin_amdgcn_sched_barrier(0);
   #pragma unroll
@@ -628,6 +711,7 @@ struct Mainloop {
           __builtin_amdgcn_sched_barrier(0);
         }
         bcur = bnext;
+        sbp = sbn;
       }
       if constexpr (OP == BSMM_OP_FP8_BLOCKWISE) {
   #pragma unroll
@@ -636,6 +720,15 @@ struct Mainloop {
   #pragma unroll
           for (int r = 0; r < 4; ++r)
             acc[ui][uj][r] = __builtin_fmaf(sc[ui], ring[u % D][r], acc[ui][uj][r]);
+        }
+      } else if constexpr (OP == BSMM_OP_FP8_GROUPWISE) {
+  #pragma unroll
+        for (int u = TI * TJ - D; u < TI * TJ; ++u) {
+          const int ui = u % TI, uj = u / TI;
+  #pragma unroll
+          for (int r = 0; r < 4; ++r)
+            acc[ui][uj][r] = __builtin_fmaf(__fmul_rn(sc[ui], sbp[r]), ring[u % D][r],
+                                            acc[ui][uj][r]);
         }
       }
     };
@@ -1486,7 +1579,8 @@ template <bool PK>
 bool set_packed(KArgs& k, const Launch& l) {
   k.psa = l.psa;
   k.psa_ld = packed_rows(k.p.M);
-  return !PK || (l.psa != nullptr && l.row_begin % 64 == 0);
+  // an empty K sum reads no scales (the output is zeroed)
+  return !PK || k.p.K < kBlockK || (l.psa != nullptr && l.row_begin % 64 == 0);
 }
 
 // Workgroups of a kernel the current device holds at once (0 on error),
@@ -1707,13 +1801,19 @@ int launch_kernel(const Problem& p, const Launch& l) {
   // the int8 and scaled_mm K loops read no scales: packed variants run the
   // plain kernel
   constexpr bool PKX = PK && (OP == BSMM_OP_FP8_BLOCKWISE || OP == BSMM_OP_FP8_MX_BMM ||
-                              OP == BSMM_OP_FP8_MX32_MM);
-  if constexpr (KIND == 2) {
+                              OP == BSMM_OP_FP8_MX32_MM || OP == BSMM_OP_FP8_GROUPWISE);
+  if constexpr (OP == BSMM_OP_FP8_GROUPWISE && (!PK || KIND == 2)) {
+    // groupwise reads its scales packed; no unpacked or skinny kernel
+    (void)p;
+    (void)l;
+    return 1;
+  } else if constexpr (KIND == 2) {
     return launch_skinny<OP, OUT, RING>(p, l);
   } else if constexpr (KIND == 1) {
     // wide waves for int8 / mx / scaled_mm; blockwise and mx32 (per-lane
     // column scales) run the 256 x 256 eight-wave kernel
-    if constexpr (OP == BSMM_OP_FP8_BLOCKWISE || OP == BSMM_OP_FP8_MX32_MM)
+    if constexpr (OP == BSMM_OP_FP8_BLOCKWISE || OP == BSMM_OP_FP8_MX32_MM ||
+                  OP == BSMM_OP_FP8_GROUPWISE)
       return launch_tile<OP, OUT, 4, 2, 5, PKX>(p, l);
     else
       return launch_tile4<OP, OUT, PKX>(p, l);

@@ -80,6 +80,17 @@ pack_mx32_kernel(const Problem p, uint8_t* dst, int64_t ld) {
   }
 }
 
+// groupwise scale_b: one thread per packed column n of K block kb, plain
+// column order, columns past N repeating column N-1.
+__global__ void __launch_bounds__(256)
+pack_cols_kernel(const Problem p, float* dst, int64_t ld) {
+  const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int kb = blockIdx.y;
+  if (n >= ld) return;
+  const float* src = (const float*)p.sb + (int64_t)kb * p.sb_kb;
+  dst[(int64_t)kb * ld + n] = src[(int64_t)min((int)n, p.N - 1) * p.sb_n];
+}
+
 }  // namespace
 
 int pack_scale_a(const Problem& p, void* dst, void* stream) {
@@ -99,6 +110,15 @@ int pack_scale_a(const Problem& p, void* dst, void* stream) {
   }
   const int KB = p.K / kBlockK;
   if (KB == 0) return 0;
+  if (p.op == BSMM_OP_FP8_GROUPWISE) {
+    const int64_t mp = packed_rows(p.M), np = packed_rows(p.N);
+    hipLaunchKernelGGL(pack_kernel<BSMM_OP_FP8_BLOCKWISE>,
+                       dim3((unsigned)(mp / 64), (unsigned)((KB + 15) / 16), 1u), dim3(256), 0, s,
+                       p, dst, mp);
+    hipLaunchKernelGGL(pack_cols_kernel, dim3((unsigned)(np / 256), (unsigned)KB), dim3(256), 0, s,
+                       p, (float*)((uint8_t*)dst + packed_gw_a_bytes(p.M, p.K)), np);
+    return hipGetLastError() == hipSuccess ? 0 : 1;
+  }
   const int64_t ld = packed_rows(p.M);
   const dim3 grid((unsigned)(ld / 64), (unsigned)((KB + 15) / 16),
                   (unsigned)(p.op == BSMM_OP_FP8_MX_BMM ? p.G : 1));

@@ -27,6 +27,10 @@ int launch_variant(const Problem& p, const Launch& l) {
       if (p.out_dtype == BSMM_F32)
         return launch_kernel<BSMM_OP_FP8_MX32_MM, BSMM_F32, WM, WN, RING, SK, PK, KIND>(p, l);
       return launch_kernel<BSMM_OP_FP8_MX32_MM, BSMM_BF16, WM, WN, RING, SK, PK, KIND>(p, l);
+    case BSMM_OP_FP8_GROUPWISE:
+      if (p.out_dtype == BSMM_F32)
+        return launch_kernel<BSMM_OP_FP8_GROUPWISE, BSMM_F32, WM, WN, RING, SK, PK, KIND>(p, l);
+      return launch_kernel<BSMM_OP_FP8_GROUPWISE, BSMM_BF16, WM, WN, RING, SK, PK, KIND>(p, l);
     default:
       if (p.out_dtype == BSMM_F32)
         return launch_kernel<BSMM_OP_FP8_SCALED_MM, BSMM_F32, WM, WN, RING, SK, PK, KIND>(p, l);
@@ -36,7 +40,7 @@ int launch_variant(const Problem& p, const Launch& l) {
   }
 }
 
-constexpr unsigned kAllOps = 31u;
+constexpr unsigned kAllOps = 63u;
 
 // name, tile_m, tile_n, ops, masked tail, persistent, packed scales,
 // workgroups per CU, unpacked sibling, largest M (the skinny kernel: 16),

@@ -30,7 +30,8 @@
  *   returned as BSMM_ERR_HIP.  No call synchronises the stream or the host.
  * Workspace: optional device scratch for split-K partial sums.  Pass the size
  *   from bsmm_workspace_bytes for the fastest plan; with less (or NULL) the
- *   call still succeeds with a plan that needs none.  Results do not depend on
+ *   call still succeeds with a plan that needs none (except
+ *   bsmm_fp8_groupwise, whose kernels read repacked scales from it).  Results do not depend on
  *   the split: int32 accumulators are identical for every split, fp32 sums of
  *   the split partials are added in ascending split order.
  * Threads: the library keeps no mutable state across calls except a
@@ -76,7 +77,8 @@ typedef enum {
   BSMM_OP_FP8_BLOCKWISE = 1,
   BSMM_OP_FP8_MX_BMM = 2,
   BSMM_OP_FP8_SCALED_MM = 3,
-  BSMM_OP_FP8_MX32_MM = 4
+  BSMM_OP_FP8_MX32_MM = 4,
+  BSMM_OP_FP8_GROUPWISE = 5
 } bsmm_op;
 
 /*
@@ -127,6 +129,48 @@ bsmm_status bsmm_fp8_blockwise(const uint8_t* a, int64_t lda,
                                const uint8_t* b, int64_t ldb,
                                const float* scale_a, int64_t sa_m, int64_t sa_kb,
                                const float* scale_b, int64_t sb_kb, int64_t sb_nb,
+                               void* out, int64_t ldo, bsmm_dtype out_dtype,
+                               int64_t M, int64_t N, int64_t K,
+                               void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
+ * fp8 E4M3FN x E4M3FN with fp32 scales per (row of A, 128-long K block) and
+ * per (column of B, 128-long K block): 1 x 128 groups on both operands.
+ *
+ * The backward pass of the blockwise fp8 linear layer whose benchmark the
+ * PyTorch issue "torch._scaled_mm with blockwise scaling doesn't work with
+ * torch.compile" runs (forward and backward).  Its weight gradient
+ * dW = dY^T X contracts over tokens, so both operands are quantised in
+ * groups of 128 tokens: A = dY^T with scale_a [N_out, tokens/128], B = X
+ * with scale_b [tokens/128, K_in].  (The input gradient dX = dY W is a
+ * bsmm_fp8_blockwise call: the weight's 128 x 128 block scales serve the
+ * transposed product unchanged.)
+ *
+ *   a        (m, k)   at a[m*lda + k]           E4M3FN codes, K-contiguous
+ *   b        (k, n)   at b[n*ldb + k]           E4M3FN codes, K-contiguous
+ *   scale_a  (m, kb)  at scale_a[m*sa_m + kb*sa_kb]    fp32
+ *   scale_b  (kb, n)  at scale_b[kb*sb_kb + n*sb_n]    fp32
+ *   out      (m, n)   at out[m*ldo + n]                fp32 or bf16
+ *
+ *   out(m,n) = sum_kb scale_a(m,kb) * scale_b(kb,n)
+ *                     * sum_{k in block kb} a(m,k) * b(k,n)
+ * accumulated in fp32 (each block's partial by the matrix core, then one
+ * multiply by the binary32 scale product and one fused multiply-add per
+ * element and block) and stored as bf16 (RNE) or fp32.
+ *
+ * Requirements: K a multiple of 128; a, b and lda, ldb 16-byte aligned;
+ * scale strides >= 0.  N and M need not be multiples of anything.  The
+ * kernel reads the scales repacked per K block, which the call writes to
+ * the start of the workspace first: the workspace is required and must hold
+ * at least bsmm_workspace_bytes(BSMM_OP_FP8_GROUPWISE, 1, M, N, K, out)
+ * bytes (BSMM_ERR_ARG otherwise).  Returns the bsmm_status of the first
+ * failed check, nothing written.
+ */
+bsmm_status bsmm_fp8_groupwise(const uint8_t* a, int64_t lda,
+                               const uint8_t* b, int64_t ldb,
+                               const float* scale_a, int64_t sa_m, int64_t sa_kb,
+                               const float* scale_b, int64_t sb_kb, int64_t sb_n,
                                void* out, int64_t ldo, bsmm_dtype out_dtype,
                                int64_t M, int64_t N, int64_t K,
                                void* workspace, size_t workspace_bytes,

@@ -46,6 +46,7 @@ __all__ = [
     "fp8_mx_bmm_inputs",
     "fp8_scaled_mm_inputs",
     "fp8_mx32_inputs",
+    "fp8_groupwise_inputs",
     "config_inputs",
     "activations",
     "CONFIGS",
@@ -284,6 +285,24 @@ def fp8_mx32_inputs(M, N, K, seed, *, dist="normal"):
                 b_scale=np.ascontiguousarray(sb.T))
 
 
+def fp8_groupwise_inputs(M, N, K, seed, *, dist="normal"):
+    """fp8 problem with 1x128 fp32 scales on both operands: A [M,K] quantised
+    per row per 128-long K block (scale_a [M, K/128]), B logical [K,N] per
+    column per 128-long K block (scale_b [K/128, N]).  This is the shape of a
+    weight-gradient GEMM, whose contraction runs over tokens.
+
+    Returns dict(a uint8 [M,K], b_nk uint8 [N,K], scale_a fp32 [M,K/128],
+    scale_b fp32 [K/128,N])."""
+    rng = np.random.default_rng(seed)
+    a_f = _draw(rng, dist, (M, K))
+    a, sa = quant_fp8_blocks_fp32(a_f, 1, BLOCK)
+    del a_f
+    b_kn = _draw(rng, dist, (K, N))
+    b_q, sb = quant_fp8_blocks_fp32(b_kn, BLOCK, 1)
+    del b_kn
+    return dict(a=a, b_nk=np.ascontiguousarray(b_q.T), scale_a=sa, scale_b=sb)
+
+
 def fp8_mx_bmm_inputs(G, M, N, K, seed, *, layout="m_major", dist="normal"):
     """fp8 mx BMM problem with e8m0 per-128-K-block scales.
 
@@ -334,6 +353,12 @@ CONFIGS = {
                 scaling="rowwise", bias="bf16", out="bf16"),
     # the same shape with 32-element MX (e8m0) block scales
     "c3x": dict(op="fp8_mx32", M=16640, N=5120, K=8192, seed=3, out="bf16"),
+    # the backward pass of that layer (y = x w^T with x [16640, 8192] and
+    # w [5120, 8192]): the input gradient dx = dy w, a blockwise GEMM over
+    # the 5120 output features, and the weight gradient dw = dy^T x, a
+    # groupwise GEMM over the 16640 tokens
+    "c3d": dict(op="fp8_blockwise", M=16640, N=8192, K=5120, seed=31, out="bf16"),
+    "c3w": dict(op="fp8_groupwise", M=5120, N=8192, K=16640, seed=32, out="bf16"),
 }
 
 
@@ -346,6 +371,8 @@ def config_inputs(name: str):
         return fp8_blockwise_inputs(c["M"], c["N"], c["K"], c["seed"])
     if c["op"] == "fp8_mx32":
         return fp8_mx32_inputs(c["M"], c["N"], c["K"], c["seed"])
+    if c["op"] == "fp8_groupwise":
+        return fp8_groupwise_inputs(c["M"], c["N"], c["K"], c["seed"])
     if c["op"] == "fp8_scaled_mm":
         return fp8_scaled_mm_inputs(c["M"], c["N"], c["K"], c["seed"],
                                     scaling=c["scaling"], bias=c["bias"])

@@ -181,6 +181,51 @@ def test_mx32_noops_and_plans():
     assert bsmm.bsmm_query_plan(bsmm.OP_FP8_MX32_MM, 1, 3, 256, 512, "f32")["variant"] == "s16x16"
 
 
+def gw(*, a=P, lda=256, b=P, ldb=256, sa=P, sa_m=2, sa_kb=1, sb=P, sb_kb=200, sb_n=1, out=P,
+       ldo=200, dt=bsmm.BF16, M=64, N=200, K=256, ws=None, wsn=0):
+    return bsmm.load().bsmm_fp8_groupwise(a, lda, b, ldb, sa, sa_m, sa_kb, sb, sb_kb, sb_n, out,
+                                          ldo, dt, M, N, K, ws, wsn, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=-1), SHAPE), (dict(dt=bsmm.I32), DTYPE), (dict(dt=bsmm.E4M3), DTYPE),
+    (dict(K=200), UNSUP), (dict(out=None), NULL), (dict(sa=None), NULL), (dict(sb=None), NULL),
+    (dict(a=None), NULL), (dict(sa_kb=-1), SCALE), (dict(sb_n=-1), SCALE),
+    (dict(ldo=100), SHAPE), (dict(lda=128), SHAPE), (dict(ldb=264), ALIGN),
+    (dict(b=P + 4), ALIGN), (dict(sa=P + 2), ALIGN), (dict(out=P + 2), ALIGN),
+    (dict(sb_n=1 << 30), UNSUP), (dict(K=128 * 70000, lda=128 * 70000, ldb=128 * 70000), UNSUP),
+])
+def test_groupwise_rejects(kw, status):
+    assert gw(**kw) == status
+    assert bsmm.load().bsmm_last_error().decode()
+
+
+def test_groupwise_noops_and_needs_a_workspace():
+    assert gw(M=0) == OK and gw(N=0) == OK
+    # N need not be a multiple of 128 (one scale per column); without a
+    # workspace for the packed scales the call is refused before any launch
+    assert gw() == 9
+    assert "workspace" in bsmm.load().bsmm_last_error().decode()
+    need = bsmm.bsmm_workspace_bytes(bsmm.OP_FP8_GROUPWISE, 1, 64, 200, 256, "bf16")
+    assert need == 2 * (2 * 256 * 4)       # K/128 blocks x rows / columns padded to 256
+    assert gw(ws=P, wsn=need - 256) == 9
+
+
+def test_groupwise_plans():
+    # the weight gradient of the 16640 x 8192 -> 5120 layer: dW [5120, 8192]
+    # over 16640 tokens; two whole rounds of 256 x 256 tiles, the last 1024
+    # rows split K two ways
+    M, N, K = 5120, 8192, 16640
+    p = bsmm.bsmm_query_plan(bsmm.OP_FP8_GROUPWISE, 1, M, N, K, "bf16")
+    assert p["variant"] == "t256x256p" and p["m_split"] == 4096 and p["tail_split_k"] == 2
+    pack = (K // 128) * M * 4 + (K // 128) * N * 4
+    assert p["workspace"] == pack + 2 * 1024 * N * 4
+    # only packed-scale kernels, at every M (no skinny or 64-row kernel)
+    for m, n in ((1, 256), (16, 384), (64, 200), (128, 512), (300, 640)):
+        v = bsmm.bsmm_query_plan(bsmm.OP_FP8_GROUPWISE, 1, m, n, 1024, "f32")["variant"]
+        assert v.endswith("p"), (m, n, v)
+
+
 def qi8(*, x=P, ldx=256, xdt=bsmm.BF16, q=P, ldq=256, sc=P, s_m=1, M=64, K=256):
     return bsmm.load().bsmm_quant_int8_rowwise(x, ldx, xdt, q, ldq, sc, s_m, M, K, None)
 
