@@ -20,13 +20,14 @@ import re
 import torch
 
 from . import (BF16, E4M3, F32, I32, OP_FP8_BLOCKWISE, OP_FP8_MX32_MM, OP_FP8_MX_BMM,
-               OP_FP8_SCALED_MM, OP_INT8_ROWWISE, bsmm_fp8_blockwise, bsmm_fp8_mx32_mm,
+               OP_FP8_SCALED_MM, OP_INT8_ROWWISE, OP_FP8_GROUPWISE, bsmm_fp8_blockwise,
+               bsmm_fp8_groupwise, bsmm_fp8_mx32_mm,
                bsmm_fp8_mx_bmm, bsmm_fp8_scaled_mm, bsmm_int8_rowwise, bsmm_query_plan,
                bsmm_set_override, bsmm_variant_names, load)
 
 TABLE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc", "bsmm_tuned_table.inc")
 OPS = {"int8": OP_INT8_ROWWISE, "fp8_blockwise": OP_FP8_BLOCKWISE, "mx": OP_FP8_MX_BMM,
-       "scaled_mm": OP_FP8_SCALED_MM, "mx32": OP_FP8_MX32_MM}
+       "scaled_mm": OP_FP8_SCALED_MM, "mx32": OP_FP8_MX32_MM, "groupwise": OP_FP8_GROUPWISE}
 DTYPES = {"i32": I32, "f32": F32, "bf16": BF16, "e4m3": E4M3}
 SPLITS = (1, 2, 3, 4, 6, 8, 12)
 
@@ -69,6 +70,12 @@ def make_call(sh, dev="cuda:0"):
         o = torch.empty((M, N), dtype=odt, device=dev)
         sa, sb = e8(M, K // 32), e8(N, K // 32)
         return lambda: bsmm_fp8_mx32_mm(a, b.t(), sa, sb, out_dtype=out, out=o)
+    if sh["op"] == "groupwise":
+        a, b = codes(M, K), codes(N, K)
+        sa = torch.rand((M, K // 128), device=dev, generator=g)
+        sb = torch.rand((K // 128, N), device=dev, generator=g)
+        o = torch.empty((M, N), dtype=odt, device=dev)
+        return lambda: bsmm_fp8_groupwise(a, b.t(), sa, sb, out_dtype=out, out=o)
     if sh["op"] == "fp8_blockwise":
         a, b = codes(M, K), codes(N, K)
         sa = torch.rand((M, K // 128), device=dev, generator=g)
@@ -102,11 +109,14 @@ def time_call(call, reps=3, n=20):
 
 
 def candidates(sh):
-    """Distinct (variant, split) plans the override produces for the shape."""
+    """Distinct (variant, split) plans the override produces for the shape
+    (groupwise: packed-scale variants only, the kernels it has)."""
     op, dt = OPS[sh["op"]], sh["out"]
     seen = {}
     try:
         for v in bsmm_variant_names():
+            if sh["op"] == "groupwise" and not v.endswith("p"):
+                continue
             for sp in SPLITS:
                 bsmm_set_override(v, sp)
                 p = bsmm_query_plan(op, sh["G"], sh["M"], sh["N"], sh["K"], dt)
@@ -140,7 +150,8 @@ def write_table(rows, path=None):
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--shape", action="append", required=True,
-                    help="op,out,G,M,N,K[,layout]  (op: int8 | fp8_blockwise | mx | scaled_mm | mx32)")
+                    help="op,out,G,M,N,K[,layout]  "
+                         "(op: int8 | fp8_blockwise | mx | scaled_mm | mx32 | groupwise)")
     ap.add_argument("--margin", type=float, default=0.03,
                     help="required gain over the dispatcher's own plan")
     ap.add_argument("--dry-run", action="store_true", help="print, do not write the table")
