@@ -60,6 +60,10 @@ QUANT_CONFIGS = {
 }
 
 
+OP_CODES = {"int8": 0, "fp8_blockwise": 1, "mx": 2, "fp8_scaled_mm": 3, "fp8_mx32": 4,
+            "fp8_groupwise": 5}
+
+
 def kernel_hash(sources=None):
     h = hashlib.sha256()
     for f in sources or KERNEL_SOURCES:
@@ -252,11 +256,26 @@ def _main_kernel(name):
     return "tile_kernel" in name or "sk_kernel" in name or "quant_" in name
 
 
-def summarize(d):
+def launches_per_call(name):
+    """Main-kernel launches of one call of a workload: two for an M-split
+    plan (the bulk launch first, then the tail), else one."""
+    if name in QUANT_CONFIGS:
+        return 1
+    import block_scaled_precision_gemm_amd as bsmm
+    from synth import CONFIGS
+    c = CONFIGS[name]
+    plan = bsmm.bsmm_query_plan(OP_CODES[c["op"]], c.get("G", 1), c["M"], c["N"], c["K"],
+                                c["out"])
+    return 2 if plan["m_split"] else 1
+
+
+def summarize(d, name=None):
     """Kernel statistics of a rocprofv3 run plus the main kernel's dispatches
-    grouped by grid size (the bulk and the tail launch of an M-split plan run
-    the same kernel with different grids)."""
+    grouped by grid size and, for an M-split plan of workload `name`, by
+    launch (the bulk and the tail launch run the same kernel, often with the
+    same persistent grid)."""
     import csv
+    per_call = launches_per_call(name) if name else 1
     out = []
     for f in _csvs(d, "kernel_stats.csv"):
         rows = list(csv.DictReader(open(f)))
@@ -267,21 +286,22 @@ def summarize(d):
                        f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} "
                        f"{float(r['Percentage']):8.2f}  {r['Name'][:110]}")
     for f in _csvs(d, "kernel_trace.csv"):
-        rows = list(csv.DictReader(open(f)))
+        rows = [r for r in csv.DictReader(open(f)) if _main_kernel(r["Kernel_Name"])]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
         groups = {}
-        for r in rows:
-            if not _main_kernel(r["Kernel_Name"]):
-                continue
+        for i, r in enumerate(rows):
             grid = int(r.get("Grid_Size_X") or r.get("Grid_Size") or 0)
-            key = (r["Kernel_Name"][:110], grid)
+            launch = ("bulk" if i % per_call == 0 else "tail") if per_call > 1 else "-"
+            key = (r["Kernel_Name"][:110], grid, launch)
             groups.setdefault(key, []).append(
                 (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
         out.append("")
-        out.append("main-kernel dispatches by grid size (rocprofv3 --kernel-trace)")
-        out.append(f"{'grid':>9} {'calls':>6} {'avg us':>10} {'min us':>10} {'max us':>10}  kernel")
-        for (k, grid), v in sorted(groups.items(), key=lambda kv: -kv[0][1]):
-            out.append(f"{grid:9d} {len(v):6d} {sum(v) / len(v):10.2f} {min(v):10.2f} "
-                       f"{max(v):10.2f}  {k}")
+        out.append("main-kernel dispatches by grid size and launch (rocprofv3 --kernel-trace)")
+        out.append(f"{'grid':>9} {'launch':>6} {'calls':>6} {'avg us':>10} {'min us':>10} "
+                   f"{'max us':>10}  kernel")
+        for (k, grid, launch), v in sorted(groups.items(), key=lambda kv: (-kv[0][1], kv[0][2])):
+            out.append(f"{grid:9d} {launch:>6} {len(v):6d} {sum(v) / len(v):10.2f} "
+                       f"{min(v):10.2f} {max(v):10.2f}  {k}")
     print("\n".join(out))
 
 
@@ -305,10 +325,13 @@ def traffic(name, fdir, wdir, cfdir, cwdir):
     """HBM bytes per launch of the main kernel from FETCH_SIZE / WRITE_SIZE
     (KiB per dispatch), each scaled by what the counter reads for the plain
     copy of COPY_BYTES."""
+    per_call = launches_per_call(name)
+
     def largest_main(per):
-        # the bulk launch is the main kernel's largest grid
-        grid = max(g for (_, g) in per.values())
-        return [v for (v, g) in per.values() if g == grid], grid
+        # the bulk launch: the first main-kernel dispatch of every call
+        keys = sorted(per, key=lambda k: (k[0], int(k[1])))
+        picked = [per[k] for i, k in enumerate(keys) if i % per_call == 0]
+        return [v for v, _ in picked], picked[0][1]
     copy = lambda r: "copy" in r["Kernel_Name"].lower()
     cf = [v for v, _ in _counter(cfdir, "FETCH_SIZE", copy).values()]
     cw = [v for v, _ in _counter(cwdir, "WRITE_SIZE", copy).values()]
@@ -464,7 +487,7 @@ def main():
                                                    "COPY_WRITE_DIR"))
     args = ap.parse_args()
     if args.summarize:
-        return summarize(args.summarize)
+        return summarize(args.summarize, args.config)
     if args.traffic:
         return traffic(args.config, *args.traffic)
     if args.copy_kernel:
@@ -526,8 +549,7 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     value = flops / (ms_per_step * 1e-3) / 1e12
 
-    op = {"int8": 0, "fp8_blockwise": 1, "mx": 2, "fp8_scaled_mm": 3, "fp8_mx32": 4,
-          "fp8_groupwise": 5}[c["op"]]
+    op = OP_CODES[c["op"]]
     plan = bsmm.bsmm_query_plan(op, G, M, N, K, c["out"])
     # dominant kernel: the main launch of the plan (all rows, or the bulk rows
     # of an M-split plan); its algorithmic work is its share of the rows
