@@ -18,8 +18,9 @@ rowwise scales and a bias on the blockwise workload's shape) | c3x (the same
 shape with 32-element MX scales) | c3d, c3w (that layer's backward pass: the
 input gradient, a blockwise GEMM 16640x8192x5120, and the weight gradient, a
 groupwise GEMM 5120x8192 over 16640 tokens), and the dynamic
-quantisers of their bf16 activations --config q_int8 | q_fp8 | q_mx | q_mx_t | q_mx32
-(one quantiser call per step, GB/s against 8 TB/s).
+quantisers of their bf16 activations --config q_int8 | q_fp8 | q_mx | q_mx_t | q_mx32,
+and of the backward pass q_cols_x | q_cols_dy | q_w (one quantiser call per step,
+GB/s against 8 TB/s).
 
 The JSON line also carries
   roofline      achieved / peak for the dominant kernel (MFMA-bound shapes
@@ -57,6 +58,12 @@ QUANT_CONFIGS = {
     "q_mx": ("mx", (8192, 8, 4096), "normal", 43),        # x of the mx BMM, M=8192, G=8
     "q_mx_t": ("mx", (2, 9000, 7168), "t", 5),            # x of the mx BMM, G=2, M=9000
     "q_mx32": ("mx32", (16640, 8192), "normal", 3),       # A of the MX-32 16640x5120x8192 GEMM
+    # the backward pass of the 16640-token layer: X and dY in groups of 128
+    # tokens down their columns (codes transposed), W in 128 x 128 blocks
+    # (plain and transposed codes)
+    "q_cols_x": ("columns", (16640, 8192), "normal", 31),
+    "q_cols_dy": ("columns", (16640, 5120), "normal", 32),
+    "q_w": ("weight", (5120, 8192), "normal", 33),
 }
 
 
@@ -362,6 +369,10 @@ def quant_bytes(kind, rows, K):
         scale = rows * 4
     elif kind == "mx32":
         scale = rows * (K // 32)
+    elif kind == "columns":
+        scale = (rows // 128) * K * 4
+    elif kind == "weight":               # plain and transposed codes
+        return rows * K * 2 + 2 * rows * K + (rows // 128) * (K // 128) * 4
     else:
         scale = rows * (K // 128) * (4 if kind == "fp8" else 1)
     return rows * K * 2 + rows * K + scale
@@ -371,9 +382,11 @@ def quant_cpu_baseline(kind, x_rows, budget_s):
     """The oracle's quantiser on a growing sample of rows (about budget_s)."""
     from oracle import quant as Q
     fn = {"int8": Q.quant_int8_rowwise, "fp8": Q.quant_fp8_blockwise,
-          "mx": Q.quant_fp8_mx, "mx32": lambda x: Q.quant_fp8_mx(x, block=32)}[kind]
+          "mx": Q.quant_fp8_mx, "mx32": lambda x: Q.quant_fp8_mx(x, block=32),
+          "columns": Q.quant_fp8_columns, "weight": Q.quant_fp8_weight_blocks}[kind]
     R, K = x_rows.shape
-    rows, t = min(R, 64), 0.0
+    step = 128 if kind in ("columns", "weight") else 1      # whole groups of 128 rows
+    rows, t = min(R, max(64, step)), 0.0
     while True:
         t0 = time.perf_counter()
         fn(x_rows[:rows])
@@ -381,6 +394,7 @@ def quant_cpu_baseline(kind, x_rows, budget_s):
         if rows >= R or t >= budget_s * 0.6:
             break
         rows = min(R, int(rows * max(1.5, min(8.0, budget_s * 0.8 / max(t, 1e-3)))))
+        rows = max(step, rows // step * step)
     return {"value": quant_bytes(kind, rows, K) / t / 1e9, "unit": "GB/s", "cores": 1,
             "kind": "oracle",
             "sample": f"{rows} of {R} rows of K={K} (bf16 values widened to fp32); "
@@ -409,12 +423,19 @@ def bench_quant(args):
     xs = [xb.cuda() for _ in range(copies)]
     fn = {"int8": bsmm.bsmm_quant_int8_rowwise, "fp8": bsmm.bsmm_quant_fp8_blockwise,
           "mx": bsmm.bsmm_quant_fp8_mx,
-          "mx32": lambda x, **kw: bsmm.bsmm_quant_fp8_mx(x, block=32, **kw)}[kind]
+          "mx32": lambda x, **kw: bsmm.bsmm_quant_fp8_mx(x, block=32, **kw),
+          "columns": bsmm.bsmm_quant_fp8_columns, "weight": bsmm.bsmm_quant_fp8_weight}[kind]
     outs = [fn(x) for x in xs]
     torch.cuda.synchronize()
     print(f"[bench] {name}: inputs ready in {time.time() - t0:.1f}s, {copies} copies",
           file=sys.stderr, flush=True)
-    calls = [(lambda x=x, o=o: fn(x, q=o[0], scale=o[1])) for x, o in zip(xs, outs)]
+    if kind == "columns":
+        calls = [(lambda x=x, o=o: fn(x, q_t=o[0], scale=o[1])) for x, o in zip(xs, outs)]
+    elif kind == "weight":
+        calls = [(lambda x=x, o=o: fn(x, q=o[0], q_t=o[1], scale=o[2]))
+                 for x, o in zip(xs, outs)]
+    else:
+        calls = [(lambda x=x, o=o: fn(x, q=o[0], scale=o[1])) for x, o in zip(xs, outs)]
     t_settle = time.perf_counter()
     i = 0
     while time.perf_counter() - t_settle < args.settle:
@@ -448,7 +469,9 @@ def bench_quant(args):
             roof["traffic"] = t["hbm_bytes_per_launch"]
     roof["kernel"] = {"int8": "quant_int8_rows", "fp8": "quant_fp8_blocks<fp32 scale>",
                       "mx": "quant_fp8_blocks<e8m0 scale>",
-                      "mx32": "quant_fp8_blocks<e8m0 scale, 32-element blocks>"}[kind]
+                      "mx32": "quant_fp8_blocks<e8m0 scale, 32-element blocks>",
+                      "columns": "quant_fp8_tiles<groups of 128 rows down the columns>",
+                      "weight": "quant_fp8_tiles<128 x 128 blocks, plain and transposed>"}[kind]
     roof["kernel_ms_mean"] = kern_ms
     roof["kernel_alg_bytes"] = nbytes
     line = {
@@ -460,7 +483,8 @@ def bench_quant(args):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": f"{kind} quantisation of bf16 activations {list(shape)}",
+        "config": {"workload": f"{kind} quantisation of bf16 "
+                               f"{'weights' if kind == 'weight' else 'activations'} {list(shape)}",
                    "name": name, "rows": R, "K": K, "seed": seed, "dist": dist,
                    "copies": copies},
         "roofline": roof,

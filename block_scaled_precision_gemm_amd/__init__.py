@@ -18,6 +18,7 @@ __all__ = [
     "bsmm_int8_rowwise", "bsmm_fp8_blockwise", "bsmm_fp8_mx_bmm", "bsmm_fp8_scaled_mm",
     "bsmm_fp8_mx32_mm", "OP_FP8_MX32_MM", "bsmm_fp8_groupwise", "OP_FP8_GROUPWISE",
     "bsmm_quant_int8_rowwise", "bsmm_quant_fp8_blockwise", "bsmm_quant_fp8_mx",
+    "bsmm_quant_fp8_columns", "bsmm_quant_fp8_weight",
     "bsmm_workspace_bytes", "bsmm_query_plan", "bsmm_set_override",
     "bsmm_variant_names", "bsmm_version", "bsmm_timing_enable", "bsmm_timing_read",
     "I32", "F32", "BF16", "E4M3", "OP_INT8_ROWWISE", "OP_FP8_BLOCKWISE", "OP_FP8_MX_BMM",
@@ -78,10 +79,13 @@ def load():
     L.bsmm_quant_fp8_blockwise.argtypes = [vp, i64, st, vp, i64, vp, i64, i64, i64, i64, vp]
     L.bsmm_quant_fp8_mx.argtypes = [vp, i64, st, vp, i64, vp, i64, i64, i64, i64, vp]
     L.bsmm_quant_fp8_mx32.argtypes = [vp, i64, st, vp, i64, vp, i64, i64, i64, i64, vp]
+    L.bsmm_quant_fp8_columns.argtypes = [vp, i64, st, vp, i64, vp, i64, i64, i64, i64, vp]
+    L.bsmm_quant_fp8_weight.argtypes = [vp, i64, st, vp, i64, vp, i64, vp, i64, i64, i64, i64,
+                                        vp]
     for f in ("bsmm_int8_rowwise", "bsmm_fp8_blockwise", "bsmm_fp8_mx_bmm", "bsmm_fp8_scaled_mm",
               "bsmm_fp8_mx32_mm",
               "bsmm_quant_int8_rowwise", "bsmm_quant_fp8_blockwise", "bsmm_quant_fp8_mx",
-              "bsmm_quant_fp8_mx32"):
+              "bsmm_quant_fp8_mx32", "bsmm_quant_fp8_columns", "bsmm_quant_fp8_weight"):
         getattr(L, f).restype = st
     L.bsmm_workspace_bytes.argtypes = [st, i64, i64, i64, i64, st]
     L.bsmm_workspace_bytes.restype = sz
@@ -543,6 +547,65 @@ def bsmm_quant_fp8_blockwise(x, *, q=None, scale=None, stream=None):
         x2.data_ptr(), x2.stride(0), code, q8.data_ptr(), q8.stride(0),
         scale.data_ptr(), scale.stride(0), scale.stride(1), M, K, _stream(stream)))
     return q, scale
+
+
+def bsmm_quant_fp8_columns(x, *, q_t=None, scale=None, stream=None):
+    """fp8 E4M3 quantisation of x [R, C] (bf16 or fp32; R a multiple of 128,
+    C of 8) in groups of 128 consecutive rows of one column, one fp32 scale
+    each: the operands of the weight-gradient GEMM bsmm_fp8_groupwise, which
+    contracts over the R tokens.
+
+    Returns (q_t float8_e4m3fn [C, R], the codes transposed, and scale fp32
+    [R/128, C]).  With dY [R, N] and X [R, K] quantised this way,
+    ``bsmm_fp8_groupwise(dYq_t, Xq_t.t(), s_dy.t(), s_x)`` is dW [N, K].
+    """
+    torch = _torch()
+    x2, code = _quant_input(x)
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [R, C]")
+    R, C = x2.shape
+    q_t = _quant_out(q_t, (C, R), torch.float8_e4m3fn, "q_t", x.device)
+    scale = _quant_out(scale, (R // 128, C), torch.float32, "scale", x.device)
+    if R and q_t.stride(1) != 1:
+        raise ValueError("q_t must be row-major")
+    q8 = q_t.view(torch.uint8)
+    _check(load().bsmm_quant_fp8_columns(
+        x2.data_ptr(), x2.stride(0), code, q8.data_ptr(), q8.stride(0),
+        scale.data_ptr(), scale.stride(0), scale.stride(1), R, C, _stream(stream)))
+    return q_t, scale
+
+
+def bsmm_quant_fp8_weight(w, *, plain=True, transposed=True, q=None, q_t=None, scale=None,
+                          stream=None):
+    """fp8 E4M3 quantisation of a weight w [R, C] (bf16 or fp32; R and C
+    multiples of 128) in 128 x 128 blocks, one fp32 scale each.
+
+    Returns (q [R, C] or None, q_t [C, R] or None, scale fp32 [R/128, C/128]):
+    the codes as they are (the forward GEMM's B = ``q.t()`` with scale_b
+    ``scale.t()``) and transposed (the input gradient's B = ``q_t.t()`` with
+    scale_b ``scale``).
+    """
+    torch = _torch()
+    if not (plain or transposed):
+        raise ValueError("ask for the plain or the transposed codes (or both)")
+    w2, code = _quant_input(w, "w")
+    if w.dim() != 2:
+        raise ValueError("w must be 2-D [R, C]")
+    R, C = w2.shape
+    q = _quant_out(q, (R, C), torch.float8_e4m3fn, "q", w.device) if plain else None
+    q_t = _quant_out(q_t, (C, R), torch.float8_e4m3fn, "q_t", w.device) if transposed else None
+    scale = _quant_out(scale, (R // 128, C // 128), torch.float32, "scale", w.device)
+    for t, n in ((q, "q"), (q_t, "q_t")):
+        if t is not None and t.numel() and t.stride(1) != 1:
+            raise ValueError(f"{n} must be row-major")
+    qv = q.view(torch.uint8) if q is not None else None
+    qtv = q_t.view(torch.uint8) if q_t is not None else None
+    _check(load().bsmm_quant_fp8_weight(
+        w2.data_ptr(), w2.stride(0), code,
+        qv.data_ptr() if qv is not None else None, qv.stride(0) if qv is not None else 0,
+        qtv.data_ptr() if qtv is not None else None, qtv.stride(0) if qtv is not None else 0,
+        scale.data_ptr(), scale.stride(0), scale.stride(1), R, C, _stream(stream)))
+    return q, q_t, scale
 
 
 def bsmm_quant_fp8_mx(x, *, block=128, q=None, scale=None, stream=None):

@@ -723,6 +723,46 @@ bsmm_status quant_common(const void* x, int64_t ldx, bsmm_dtype x_dtype, const v
   return BSMM_OK;
 }
 
+// Checks shared by the transposing quantisers of x [R, C]: R a multiple of
+// 128, C of `cmult` (8 for the column groups, 128 for the weight blocks);
+// one scale per (128-row group, column or 128-column block).
+bsmm_status quant_t_common(const void* x, int64_t ldx, bsmm_dtype x_dtype, const void* scale,
+                           int64_t s_g, int64_t s_c, int64_t R, int64_t C, int cmult) {
+  CHECK(x_dtype == BSMM_F32 || x_dtype == BSMM_BF16, BSMM_ERR_DTYPE,
+        "quantiser input must be fp32 or bf16 (got %d)", (int)x_dtype);
+  CHECK(R >= 0 && C >= 0, BSMM_ERR_SHAPE, "negative size R=%lld C=%lld", (long long)R,
+        (long long)C);
+  CHECK(R < kMaxDim && C < kMaxDim, BSMM_ERR_UNSUPPORTED, "size beyond 2^31");
+  CHECK(R % 128 == 0, BSMM_ERR_UNSUPPORTED, "R=%lld is not a multiple of 128", (long long)R);
+  CHECK(C % cmult == 0, BSMM_ERR_UNSUPPORTED, "C=%lld is not a multiple of %d", (long long)C,
+        cmult);
+  if (R == 0 || C == 0) return BSMM_OK;
+  CHECK(R / 128 <= 65535, BSMM_ERR_UNSUPPORTED, "R=%lld beyond 65535 groups of 128 rows",
+        (long long)R);
+  CHECK(scale != nullptr, BSMM_ERR_NULL, "scale is NULL");
+  CHECK(aligned(scale, 4), BSMM_ERR_ALIGN, "scale not 4-byte aligned");
+  CHECK(s_g >= 0 && s_c >= 0, BSMM_ERR_SCALE_SHAPE, "scale strides must be >= 0");
+  const int64_t G = R / 128, NC = cmult == 128 ? C / 128 : C;
+  const bool rows_ok = G == 1 || s_g >= 1;
+  const bool cols_ok = NC == 1 || s_c >= 1;
+  const bool disjoint = G == 1 || NC == 1 || s_g >= NC * s_c || s_c >= G * s_g;
+  CHECK(rows_ok && cols_ok && disjoint, BSMM_ERR_SCALE_SHAPE,
+        "scale strides s_g=%lld s_c=%lld make two groups share a scale", (long long)s_g,
+        (long long)s_c);
+  CHECK(x != nullptr, BSMM_ERR_NULL, "x is NULL");
+  CHECK(ldx >= C, BSMM_ERR_SHAPE, "ldx=%lld below C", (long long)ldx);
+  CHECK(ldx % 8 == 0 && aligned(x, 16), BSMM_ERR_ALIGN,
+        "x not 16-byte aligned or ldx=%lld not a multiple of 8 elements", (long long)ldx);
+  return BSMM_OK;
+}
+
+// transposed codes [C, R]: 16-byte row segments
+bsmm_status check_qt(const void* q_t, int64_t ldqt, int64_t R) {
+  CHECK(ldqt >= R, BSMM_ERR_SHAPE, "ldqt=%lld below R", (long long)ldqt);
+  CHECK(ldqt % 16 == 0 && aligned(q_t, 16), BSMM_ERR_ALIGN, "q_t or ldqt not 16-byte aligned");
+  return BSMM_OK;
+}
+
 bsmm_status quant_run(QuantArgs::Kind kind, const void* x, int64_t ldx, bsmm_dtype x_dtype,
                       void* q, int64_t ldq, void* scale, int64_t s_m, int64_t s_kb, int64_t M,
                       int64_t K, void* stream) {
@@ -780,6 +820,50 @@ bsmm_status bsmm_quant_fp8_mx32(const void* x, int64_t ldx, bsmm_dtype x_dtype, 
         "M * K / 32 = %lld blocks beyond 2^30", (long long)(M * (K / 32)));
   return quant_run(QuantArgs::kFp8Mx32, x, ldx, x_dtype, q, ldq, scale, s_m, s_kb, M, K,
                    stream);
+}
+
+bsmm_status bsmm_quant_fp8_columns(const void* x, int64_t ldx, bsmm_dtype x_dtype,
+                                   uint8_t* q_t, int64_t ldqt, float* scale, int64_t s_g,
+                                   int64_t s_c, int64_t R, int64_t C, void* stream) {
+  bsmm_status st = quant_t_common(x, ldx, x_dtype, scale, s_g, s_c, R, C, 8);
+  if (st != BSMM_OK || R == 0 || C == 0) return st;
+  CHECK(q_t != nullptr, BSMM_ERR_NULL, "q_t is NULL");
+  st = check_qt(q_t, ldqt, R);
+  if (st != BSMM_OK) return st;
+  QuantArgs a{};
+  a.kind = QuantArgs::kFp8Columns;
+  a.x = x; a.ldx = ldx; a.x_dtype = x_dtype;
+  a.q = nullptr; a.ldq = 0;
+  a.qt = q_t; a.ldqt = ldqt;
+  a.scale = scale; a.s_m = s_g; a.s_kb = s_c;
+  a.M = R; a.K = C;
+  if (launch_quant(a, stream) != 0) return fail(BSMM_ERR_HIP, "quantiser launch failed");
+  return BSMM_OK;
+}
+
+bsmm_status bsmm_quant_fp8_weight(const void* w, int64_t ldw, bsmm_dtype w_dtype, uint8_t* q,
+                                  int64_t ldq, uint8_t* q_t, int64_t ldqt, float* scale,
+                                  int64_t s_r, int64_t s_c, int64_t R, int64_t C, void* stream) {
+  bsmm_status st = quant_t_common(w, ldw, w_dtype, scale, s_r, s_c, R, C, 128);
+  if (st != BSMM_OK || R == 0 || C == 0) return st;
+  CHECK(q != nullptr || q_t != nullptr, BSMM_ERR_NULL, "q and q_t are both NULL");
+  if (q != nullptr) {
+    CHECK(ldq >= C, BSMM_ERR_SHAPE, "ldq=%lld below C", (long long)ldq);
+    CHECK(ldq % 8 == 0 && aligned(q, 8), BSMM_ERR_ALIGN, "q or ldq not 8-byte aligned");
+  }
+  if (q_t != nullptr) {
+    st = check_qt(q_t, ldqt, R);
+    if (st != BSMM_OK) return st;
+  }
+  QuantArgs a{};
+  a.kind = QuantArgs::kFp8Weight;
+  a.x = w; a.ldx = ldw; a.x_dtype = w_dtype;
+  a.q = q; a.ldq = ldq;
+  a.qt = q_t; a.ldqt = ldqt;
+  a.scale = scale; a.s_m = s_r; a.s_kb = s_c;
+  a.M = R; a.K = C;
+  if (launch_quant(a, stream) != 0) return fail(BSMM_ERR_HIP, "quantiser launch failed");
+  return BSMM_OK;
 }
 
 const char* bsmm_status_string(bsmm_status s) {

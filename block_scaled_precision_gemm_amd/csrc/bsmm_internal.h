@@ -145,8 +145,15 @@ void timing_mark(void* stream, const char* name, bool begin);
 
 // Dynamic quantisation of bf16 / fp32 rows (bsmm_quant.hip).  Arguments are
 // validated by the entry points before this is called.
+//
+// kFp8Columns: groups of 128 rows down each column of x [M, K]; codes only
+// transposed, qt [K, M] (row stride ldqt); scale (g, c) at scale[g*s_m +
+// c*s_kb] for g < M/128.  kFp8Weight: 128 x 128 blocks; codes in q [M, K]
+// and / or qt [K, M] (either may be null); scale (g, cb) at scale[g*s_m +
+// cb*s_kb].
 struct QuantArgs {
-  enum Kind { kInt8Rows = 0, kFp8Blocks = 1, kFp8Mx = 2, kFp8Mx32 = 3 };
+  enum Kind { kInt8Rows = 0, kFp8Blocks = 1, kFp8Mx = 2, kFp8Mx32 = 3, kFp8Columns = 4,
+              kFp8Weight = 5 };
   Kind kind;
   const void* x;        // [M, K] bf16 or fp32, row stride ldx elements
   int64_t ldx;
@@ -156,6 +163,8 @@ struct QuantArgs {
   void* scale;          // fp32 (kInt8Rows, kFp8Blocks) or e8m0 bytes (kFp8Mx)
   int64_t s_m, s_kb;    // scale strides in elements (s_kb unused for kInt8Rows)
   int64_t M, K;
+  void* qt = nullptr;   // transposed codes [K, M] (kFp8Columns, kFp8Weight)
+  int64_t ldqt = 0;
 };
 int launch_quant(const QuantArgs& a, void* stream);
 

@@ -12,7 +12,13 @@
 //     e = ceil(log2(amax / 448)), code = rne_e4m3(x * 2^-e) -- the mxscale
 //     activations of the ROCm aiter PR "Add opus fp8 mxscale BMM kernels for
 //     gfx950" (Motivation); the same per 1 x 32 block for the 32-element MX
-//     blocks of the MX matmul.
+//     blocks of the MX matmul;
+//   for the backward pass of the blockwise fp8 linear layer the PyTorch issue
+//     benchmarks: fp8 E4M3FN with one fp32 scale amax / 448 per group of 128
+//     consecutive rows of one column (the weight gradient contracts over
+//     tokens), and per 128 x 128 block of a weight; both write the codes
+//     transposed (the layout in which the GEMM that consumes them reads its
+//     contraction contiguously), the weight optionally also as it is.
 //
 // Every quotient is the correctly rounded binary32 quotient; rounding is to
 // nearest, ties to even; e4m3 saturates at +-448.  A row or block whose
@@ -308,6 +314,140 @@ quant_fp8_blocks(const T* __restrict__ x, int64_t ldx, uint8_t* __restrict__ q, 
   }
 }
 
+// ---- fp8 down the columns / 128 x 128 blocks, transposed codes ---------------
+
+// A workgroup quantises a tile of 128 rows x CW columns: CW = 64, one scale
+// per column (groups of 128 rows down the columns), or CW = 128 with
+// BLOCK2D, one scale for the 128 x 128 block.  Work item it = threadIdx.x +
+// 256 * ii holds rows 4a .. 4a + 3 of the 8 columns 8c .. 8c + 7 of the tile
+// (c = it % (CW / 8), a = it / (CW / 8)), so 8 consecutive items read one
+// 128-byte row segment (bf16).  Column chunks past C (C a multiple of 8) load
+// the last chunk and store nothing.  The codes of one column's four rows
+// make a dword, written to LDS at byte (8c + j) * kPitch + 4a (row pitch 132:
+// at most two lanes of a wave per bank); each column's 128 codes then leave
+// as 16-byte segments of row c0 + 8c + j of the transposed output.  BLOCK2D
+// also stores the codes untransposed when q is not null.
+template <typename T, int CW, bool BLOCK2D>
+__global__ void __launch_bounds__(256)
+quant_fp8_tiles(const T* __restrict__ x, int64_t ldx, uint8_t* __restrict__ q, int64_t ldq,
+                uint8_t* __restrict__ qt, int64_t ldqt, float* __restrict__ scale, int64_t s_g,
+                int64_t s_c, int C) {
+  constexpr int NI = CW / 64;          // work items per thread
+  constexpr int QW = CW / 8;           // 8-column chunks per tile row
+  constexpr int kPitch = 132;
+  constexpr int NS = BLOCK2D ? 1 : CW; // scales per tile
+  __shared__ uint32_t part[4][NS];
+  __shared__ float sc[NS];
+  __shared__ __attribute__((aligned(16))) uint8_t tt[CW * kPitch];
+  const int g = blockIdx.y;
+  const int c0 = blockIdx.x * CW;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t row0 = (int64_t)g * 128;
+  Raw8<T> buf[NI][4];
+#pragma unroll
+  for (int ii = 0; ii < NI; ++ii) {
+    const int it = threadIdx.x + 256 * ii;
+    const int col = min(c0 + 8 * (it % QW), C - 8);
+    const int a = it / QW;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) load8(buf[ii][i], x + (row0 + 4 * a + i) * ldx + col);
+  }
+  // maxima: per column (groups down the columns) or over the tile (blocks)
+  if constexpr (BLOCK2D) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int ii = 0; ii < NI; ++ii)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m = max(m, absmax_bits(buf[ii][i]));
+    m = wave_max(m);
+    if (lane == 0) part[wave][0] = m;
+  } else {
+    // lanes 8k + c of a wave hold column chunk c (NI = 1): reduce over k
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      uint32_t m = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float f[8];
+        widen(buf[0][i], f);
+        m = max(m, __float_as_uint(f[j]) & 0x7FFFFFFFu);
+      }
+      m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x128, 0xF, 0xF, false));
+      m = max(m, (uint32_t)__shfl_xor((int)m, 16));
+      m = max(m, (uint32_t)__shfl_xor((int)m, 32));
+      if (lane < 8) part[wave][8 * lane + j] = m;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < NS) {
+    const int t = threadIdx.x;
+    const uint32_t amax = max(max(part[0][t], part[1][t]), max(part[2][t], part[3][t]));
+    float sv = __uint_as_float(amax) / 448.0f;
+    if (!(sv > 0.0f)) sv = 0.0f;       // marks a zero group: scale 1, codes +0
+    sc[t] = sv;
+    const int cs = BLOCK2D ? blockIdx.x : c0 + t;
+    if (BLOCK2D || cs < C) scale[(int64_t)g * s_g + (int64_t)cs * s_c] = sv > 0.0f ? sv : 1.0f;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int ii = 0; ii < NI; ++ii) {
+    const int it = threadIdx.x + 256 * ii;
+    const int cc = it % QW, a = it / QW;
+    float f[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) widen(buf[ii][i], f[i]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float sv = sc[BLOCK2D ? 0 : 8 * cc + j];
+      const float s = sv > 0.0f ? sv : 1.0f;
+      if (s >= kFastDivMin) {
+        const float r = 1.0f / s;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f[i][j] = clamp448(div_fast(f[i][j], s, r));
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f[i][j] = clamp448(f[i][j] / s);
+      }
+      if (!(sv > 0.0f))
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f[i][j] = 0.0f;
+      *reinterpret_cast<uint32_t*>(tt + (8 * cc + j) * kPitch + 4 * a) =
+          e4m3x4(f[0][j], f[1][j], f[2][j], f[3][j]);
+    }
+    if (BLOCK2D && q != nullptr) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint2 w;
+        w.x = e4m3x4(f[i][0], f[i][1], f[i][2], f[i][3]);
+        w.y = e4m3x4(f[i][4], f[i][5], f[i][6], f[i][7]);
+        store8_nt(q + (row0 + 4 * a + i) * ldq + c0 + 8 * cc, w);
+      }
+    }
+  }
+  if (qt == nullptr) return;
+  __syncthreads();
+  // row c of the tile's transposed codes: 8 segments of 16 bytes
+#pragma unroll
+  for (int n = 0; n < CW * 8 / 256; ++n) {
+    const int ci = threadIdx.x + 256 * n;
+    const int c = ci >> 3, k = ci & 7;
+    if (c0 + c >= C) continue;
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(tt + c * kPitch + 16 * k);
+    const u32x4 v = {src[0], src[1], src[2], src[3]};
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(qt + (int64_t)(c0 + c) * ldqt +
+                                                            row0 + 16 * k));
+  }
+}
+
+template <typename T, int CW, bool BLOCK2D>
+void launch_tiles(const QuantArgs& a, hipStream_t st) {
+  const dim3 grid((unsigned)((a.K + CW - 1) / CW), (unsigned)(a.M / 128));
+  hipLaunchKernelGGL((quant_fp8_tiles<T, CW, BLOCK2D>), grid, dim3(256), 0, st,
+                     static_cast<const T*>(a.x), a.ldx, static_cast<uint8_t*>(a.q), a.ldq,
+                     static_cast<uint8_t*>(a.qt), a.ldqt, static_cast<float*>(a.scale), a.s_m,
+                     a.s_kb, (int)a.K);
+}
+
 template <typename T, int WPR, int NV>
 void launch_rows(const QuantArgs& a, hipStream_t st) {
   const unsigned grid = (unsigned)(WPR == 1 ? (a.M + 3) / 4 : a.M);
@@ -354,6 +494,12 @@ int launch_quant(const QuantArgs& a, void* stream) {
       break;
     case QuantArgs::kFp8Mx32:
       if (bf) launch_blocks<uint16_t, true, 4>(a, st); else launch_blocks<float, true, 4>(a, st);
+      break;
+    case QuantArgs::kFp8Columns:
+      if (bf) launch_tiles<uint16_t, 64, false>(a, st); else launch_tiles<float, 64, false>(a, st);
+      break;
+    case QuantArgs::kFp8Weight:
+      if (bf) launch_tiles<uint16_t, 128, true>(a, st); else launch_tiles<float, 128, true>(a, st);
       break;
     default:
       if (bf) launch_blocks<uint16_t, true, 16>(a, st); else launch_blocks<float, true, 16>(a, st);

@@ -332,6 +332,46 @@ bsmm_status bsmm_quant_fp8_mx32(const void* x, int64_t ldx, bsmm_dtype x_dtype,
                                 uint8_t* scale, int64_t s_m, int64_t s_kb,
                                 int64_t M, int64_t K, void* stream);
 
+/*
+ * Quantisers for the backward pass of the blockwise fp8 linear layer that
+ * the PyTorch issue "torch._scaled_mm with blockwise scaling doesn't work
+ * with torch.compile" benchmarks (forward and backward).  Same rounding as
+ * bsmm_quant_fp8_blockwise: scale = fl32(amax / 448), code =
+ * e4m3_rne(fl32(x / scale)) saturating at +-448; a group whose scale is 0
+ * stores scale 1 and +0 codes.
+ *
+ * bsmm_quant_fp8_columns: x [R, C] (bf16 or fp32, row stride ldx elements)
+ * in groups of 128 consecutive rows of one column -- an activation or
+ * output gradient with tokens along R, for the weight-gradient GEMM
+ * bsmm_fp8_groupwise, which contracts over tokens.  Writes the codes
+ * transposed, q_t [C, R] (row stride ldqt bytes), so that each row of q_t
+ * is one operand row of that GEMM with its contraction contiguous; scale
+ * (g, c) for group g < R/128 of column c at scale[g*s_g + c*s_c] (s_g = C,
+ * s_c = 1 is the [R/128, C] array that GEMM takes as scale_b, its
+ * transpose as scale_a).
+ *   Requirements: R a multiple of 128 (at most 65535 groups), C of 8; x and
+ *   ldx 16-byte aligned (ldx a multiple of 8 elements); q_t and ldqt 16-byte
+ *   aligned; scale 4-byte aligned with strides that give every (g, c) its
+ *   own element.
+ *
+ * bsmm_quant_fp8_weight: w [R, C] in 128 x 128 blocks (the weight blocks of
+ * bsmm_fp8_blockwise's scale_b).  Writes the codes as they are, q [R, C]
+ * (row stride ldq), and / or transposed, q_t [C, R] (row stride ldqt);
+ * either may be NULL, not both.  scale (rb, cb) at scale[rb*s_r + cb*s_c].
+ * The forward GEMM reads W [N, K] as B through q (scale_b = the transpose
+ * of the [N/128, K/128] scales); the input gradient dX = dY W reads it as B
+ * through q_t with the same scales as [K_contraction/128, N_out/128].
+ *   Requirements: R and C multiples of 128; q and ldq 8-byte aligned; q_t
+ *   and ldqt 16-byte aligned; as above otherwise.
+ */
+bsmm_status bsmm_quant_fp8_columns(const void* x, int64_t ldx, bsmm_dtype x_dtype,
+                                   uint8_t* q_t, int64_t ldqt, float* scale, int64_t s_g,
+                                   int64_t s_c, int64_t R, int64_t C, void* stream);
+bsmm_status bsmm_quant_fp8_weight(const void* w, int64_t ldw, bsmm_dtype w_dtype, uint8_t* q,
+                                  int64_t ldq, uint8_t* q_t, int64_t ldqt, float* scale,
+                                  int64_t s_r, int64_t s_c, int64_t R, int64_t C,
+                                  void* stream);
+
 /* Workspace bytes the fastest plan for this problem wants (0 if none). */
 size_t bsmm_workspace_bytes(bsmm_op op, int64_t G, int64_t M, int64_t N,
                             int64_t K, bsmm_dtype out_dtype);

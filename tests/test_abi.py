@@ -291,6 +291,47 @@ def test_quant_noops_and_scale_layouts():
 
 # ----------------------------------------------------------------- binding --
 
+def qcol(*, x=P, ldx=256, xdt=bsmm.BF16, qt=P, ldqt=256, sc=P, s_g=256, s_c=1, R=256, C=256):
+    return bsmm.load().bsmm_quant_fp8_columns(x, ldx, xdt, qt, ldqt, sc, s_g, s_c, R, C, None)
+
+
+def qw(*, w=P, ldw=256, wdt=bsmm.F32, q=P, ldq=256, qt=P, ldqt=256, sc=P, s_r=2, s_c=1, R=256,
+       C=256):
+    return bsmm.load().bsmm_quant_fp8_weight(w, ldw, wdt, q, ldq, qt, ldqt, sc, s_r, s_c, R, C,
+                                             None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(xdt=bsmm.I32), DTYPE), (dict(R=-128), SHAPE), (dict(R=200), UNSUP), (dict(C=100), UNSUP),
+    (dict(R=128 * 65536, ldqt=128 * 65536), UNSUP), (dict(sc=None), NULL), (dict(x=None), NULL),
+    (dict(qt=None), NULL), (dict(s_g=-1), SCALE), (dict(s_g=100), SCALE), (dict(s_c=0), SCALE),
+    (dict(ldx=128), SHAPE), (dict(ldqt=128), SHAPE), (dict(ldx=260), ALIGN),
+    (dict(ldqt=264), ALIGN), (dict(x=P + 8), ALIGN), (dict(qt=P + 8), ALIGN), (dict(sc=P + 2), ALIGN),
+])
+def test_quant_columns_rejects(kw, status):
+    assert qcol(**kw) == status
+    assert bsmm.load().bsmm_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(wdt=bsmm.BF16 + 5), DTYPE), (dict(C=200, ldw=256, ldq=256), UNSUP), (dict(R=192), UNSUP),
+    (dict(q=None, qt=None), NULL), (dict(sc=None), NULL), (dict(w=None), NULL),
+    (dict(s_r=1, s_c=1), SCALE), (dict(ldq=128), SHAPE), (dict(ldq=260), ALIGN),
+    (dict(q=P + 4), ALIGN), (dict(ldqt=255), SHAPE), (dict(qt=P + 8), ALIGN),
+])
+def test_quant_weight_rejects(kw, status):
+    assert qw(**kw) == status
+    assert bsmm.load().bsmm_last_error().decode()
+
+
+def test_quant_backward_noops_and_single_outputs():
+    assert qcol(R=0) == OK and qcol(C=0) == OK and qw(R=0) == OK and qw(C=0) == OK
+    # C need only be a multiple of 8 for the column groups; either output
+    # of the weight quantiser alone is fine (M = 0 rows keeps it from launching)
+    assert qcol(C=200, ldx=200 + 8, R=0) == OK
+    assert qw(q=None, R=0) == OK and qw(qt=None, R=0) == OK
+
+
 def test_binding_scale_shape_rules_follow_the_page():
     """The rowwise/tensorwise message and the blockwise shapes of the PyTorch
     blockwise _scaled_mm issue: (16640, 64) / (64, 40) for M=16640, K=8192,
