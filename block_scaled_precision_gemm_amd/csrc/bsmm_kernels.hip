@@ -229,21 +229,28 @@ struct Tile {
 // R rows x 128 bytes; one wave instruction moves 8 rows (64 x 16 bytes) to
 // LDS bytes [q*1024, q*1024+1024) of the slot, lane l -> slot byte 16 l.
 // Wave `wave` of NW issues instructions t = 0 .. R/8/NW - 1, q = t*NW + wave.
-// A dead half-stage (past the last K block) is issued with out-of-range
-// offsets: it keeps the per-wave load count uniform and touches no memory.
+// The lane's part of the offset (its row and swizzled chunk) is the same for
+// every K block, so it stays in a register; the block's byte offset goes in
+// the instruction's scalar offset, and the load costs no VALU work.  A dead
+// half-stage (past the last K block) is issued through `dead`, a resource
+// of zero bytes: it keeps the per-wave load count uniform and touches no
+// memory.  Rows past the end of the matrix are out of range through their
+// lane offset alone, and a valid row's access stays inside that row, so the
+// result does not depend on whether the range check counts the scalar
+// offset.
 template <int NW>
-__device__ __forceinline__ void load_row_group(__amdgpu_buffer_rsrc_t rs, uint8_t* dst,
+__device__ __forceinline__ void load_row_group(__amdgpu_buffer_rsrc_t rs,
+                                               __amdgpu_buffer_rsrc_t dead, uint8_t* dst,
                                                uint32_t ld, uint32_t kbyte, int wave,
                                                int lane, bool live, int t) {
   const int q = t * NW + wave;
   const int r = q * 8 + (lane >> 3);
   const int c = (lane & 7) ^ swz(r);
-  // dead: an offset past any range, as a max with a uniform floor rather
-  // than a per-lane select (which the compiler may turn into a branch that
-  // splits the K loop's scheduling region)
-  const uint32_t floor = live ? 0u : kOob;
-  const uint32_t vo = max((uint32_t)r * ld + kbyte + ((uint32_t)c << 4), floor);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + q * 1024), 16, vo, 0, 0, 0);
+  const uint32_t vo = (uint32_t)r * ld + ((uint32_t)c << 4);
+  // the LDS address is the low word of the generic one; formed as an
+  // integer it needs no null check of the generic pointer
+  const lds_ptr_t l = (lds_ptr_t)(uintptr_t)(uint32_t)(uintptr_t)(dst + q * 1024);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? rs : dead, l, 16, vo, (int)kbyte, 0, 0);
 }
 
 // mx MFMA: scale byte-select `sel` (0..3, a constant after unrolling) picks the
@@ -407,6 +414,7 @@ struct Mainloop {
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(
         p.b + (int64_t)g * p.b_sg + (int64_t)col0 * p.ldb,
         (uint64_t)(p.N - col0) * p.ldb);
+    const __amdgpu_buffer_rsrc_t rdead = make_rsrc(p.b, 0);    // every access out of range
 
     // Groupwise scale loads (see Tile): per scale load t of this wave, the
     // lane's byte offset into the packed scales at K block 0, the per-block
@@ -444,7 +452,7 @@ struct Mainloop {
       const bool live = h < 2 * nkb;
       const uint32_t kbyte = (uint32_t)(kb0 + (h >> 1)) * kBlockK;
       if (h & 1) {
-        load_row_group<T::NLD>(rb, dst, ldb, kbyte, wave, lane, live, t);
+        load_row_group<T::NLD>(rb, rdead, dst, ldb, kbyte, wave, lane, live, t);
       } else if (T::GW && t >= T::LA_ROWS) {
         const int ts = t - T::LA_ROWS;
         const uint32_t floor = live ? gw_floor[ts] : kOob;
@@ -453,7 +461,7 @@ struct Mainloop {
             rsc, (lds_ptr_t)(scl_base + slot * T::SCL + (ts * T::NLD + wave) * 1024), 16, vo, 0,
             0, 0);
       } else {
-        load_row_group<T::NLD>(ra, dst, lda, kbyte, wave, lane, live, t);
+        load_row_group<T::NLD>(ra, rdead, dst, lda, kbyte, wave, lane, live, t);
       }
     };
     auto issue_half = [&](int h, int slot) {
