@@ -316,9 +316,9 @@ quant_fp8_blocks(const T* __restrict__ x, int64_t ldx, uint8_t* __restrict__ q, 
 
 // ---- fp8 down the columns / 128 x 128 blocks, transposed codes ---------------
 
-// A workgroup quantises a tile of 128 rows x CW columns: CW = 64, one scale
-// per column (groups of 128 rows down the columns), or CW = 128 with
-// BLOCK2D, one scale for the 128 x 128 block.  Work item it = threadIdx.x +
+// A workgroup quantises a tile of 128 rows x CW columns: one scale per
+// column (groups of 128 rows down the columns; CW = 64 or 128), or, with
+// BLOCK2D and CW = 128, one scale for the 128 x 128 block.  Work item it = threadIdx.x +
 // 256 * ii holds rows 4a .. 4a + 3 of the 8 columns 8c .. 8c + 7 of the tile
 // (c = it % (CW / 8), a = it / (CW / 8)), so 8 consecutive items read one
 // 128-byte row segment (bf16).  Column chunks past C (C a multiple of 8) load
@@ -362,20 +362,25 @@ quant_fp8_tiles(const T* __restrict__ x, int64_t ldx, uint8_t* __restrict__ q, i
     m = wave_max(m);
     if (lane == 0) part[wave][0] = m;
   } else {
-    // lanes 8k + c of a wave hold column chunk c (NI = 1): reduce over k
+    // lanes QW k + c of a wave hold column chunk c in every item (256 is a
+    // multiple of QW): reduce over the items, then over k
+    static_assert(QW == 8 || QW == 16, "column chunks per tile row");
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       uint32_t m = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float f[8];
-        widen(buf[0][i], f);
-        m = max(m, __float_as_uint(f[j]) & 0x7FFFFFFFu);
-      }
-      m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x128, 0xF, 0xF, false));
+      for (int ii = 0; ii < NI; ++ii)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float f[8];
+          widen(buf[ii][i], f);
+          m = max(m, __float_as_uint(f[j]) & 0x7FFFFFFFu);
+        }
+      if (QW == 8)
+        m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x128, 0xF, 0xF, false));
       m = max(m, (uint32_t)__shfl_xor((int)m, 16));
       m = max(m, (uint32_t)__shfl_xor((int)m, 32));
-      if (lane < 8) part[wave][8 * lane + j] = m;
+      if (lane < QW) part[wave][8 * lane + j] = m;
     }
   }
   __syncthreads();
@@ -439,6 +444,10 @@ quant_fp8_tiles(const T* __restrict__ x, int64_t ldx, uint8_t* __restrict__ q, i
   }
 }
 
+// columns per workgroup tile of the column-group quantiser: 128 (eight
+// 16-byte loads in flight per lane) measured 4-6% faster than 64 on MI355X
+constexpr int kColTile = 128;
+
 template <typename T, int CW, bool BLOCK2D>
 void launch_tiles(const QuantArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)((a.K + CW - 1) / CW), (unsigned)(a.M / 128));
@@ -496,7 +505,8 @@ int launch_quant(const QuantArgs& a, void* stream) {
       if (bf) launch_blocks<uint16_t, true, 4>(a, st); else launch_blocks<float, true, 4>(a, st);
       break;
     case QuantArgs::kFp8Columns:
-      if (bf) launch_tiles<uint16_t, 64, false>(a, st); else launch_tiles<float, 64, false>(a, st);
+      if (bf) launch_tiles<uint16_t, kColTile, false>(a, st);
+      else launch_tiles<float, kColTile, false>(a, st);
       break;
     case QuantArgs::kFp8Weight:
       if (bf) launch_tiles<uint16_t, 128, true>(a, st); else launch_tiles<float, 128, true>(a, st);
