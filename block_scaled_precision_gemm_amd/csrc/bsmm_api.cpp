@@ -264,6 +264,19 @@ Plan make_plan_heuristic(bsmm_op op, int G, int M, int N, int K, bsmm_dtype dt) 
       if (s >= 2) {
         pl.m_split = m_split;
         pl.tail = pl.v;
+        // A short tail (at most 32 bulk tiles) runs on narrower tiles with
+        // fewer K slices, so fewer partial planes are reduced: 128 x 128
+        // tiles with at most 4 slices, or for mx32 (whose unpacked K loop
+        // is slow) the packed 256 x 128 tile with at most 6 (MI355X, the
+        // 256-row tails of 16640 x 5120 x 8192 and 16640 x 8192 x 5120:
+        // 1.2-2.5% per call).  Groupwise keeps its packed bulk tile.
+        if (tail_tiles <= 32 && !gw) {
+          const bool mx32 = op == BSMM_OP_FP8_MX32_MM;
+          if (const Variant* tv = find_variant(mx32 ? "t256x128p" : "t128x128")) {
+            pl.tail = tv;
+            if (s > (mx32 ? 6 : 4)) s = mx32 ? 6 : 4;
+          }
+        }
         if (!ovr().tail_variant.empty())
           if (const Variant* tv = find_variant(ovr().tail_variant.c_str())) pl.tail = tv;
         pl.tail_split = s;
