@@ -55,12 +55,19 @@ class PlanInfo(ctypes.Structure):
 
 
 def load():
-    """Load the in-tree libbsmm.so (once) and declare its prototypes."""
+    """Load the in-tree libbsmm.so (once) and declare its prototypes.
+
+    PyTorch is imported first: its HIP runtime must be the one in the
+    process before the library's own dependency on a HIP runtime is
+    resolved, or the library would bring in a second runtime whose launches
+    and allocations do not mix with torch's.
+    """
     global _lib
     if _lib is not None:
         return _lib
     if not os.path.exists(lib_path):
         raise RuntimeError(f"{lib_path} is not built; run __graft_entry__.build()")
+    import torch  # noqa: F401  (see above)
     L = ctypes.CDLL(lib_path)
     i64, vp, sz, st = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
     L.bsmm_int8_rowwise.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, st,
@@ -119,19 +126,35 @@ def _torch():
     return torch
 
 
+_RAW_STREAM = []
+
+
 def _stream(stream):
+    """The HIP stream handle of ``stream``, or of the current stream of the
+    current device (read without building a Stream object: the per-call
+    host cost matters for decode-sized calls)."""
     torch = _torch()
-    if stream is None:
-        stream = torch.cuda.current_stream()
-    return ctypes.c_void_p(stream.cuda_stream)
+    if stream is not None:
+        return stream.cuda_stream
+    if not _RAW_STREAM:
+        _RAW_STREAM.append(getattr(torch._C, "_cuda_getCurrentRawStream", None))
+    raw = _RAW_STREAM[0]
+    if raw is not None:
+        return raw(torch.cuda.current_device())
+    return torch.cuda.current_stream().cuda_stream
 
 
 _WS = {}
+_WS_NEED = {}     # workspace bytes per (op, G, M, N, K, out dtype); cleared by the override
 
 
 def _workspace(op, G, M, N, K, out_dtype, device):
     """Workspace for the fastest plan, cached per device (grow-only)."""
-    need = load().bsmm_workspace_bytes(op, G, M, N, K, out_dtype)
+    key = (op, G, M, N, K, out_dtype)
+    need = _WS_NEED.get(key)
+    if need is None:
+        need = load().bsmm_workspace_bytes(op, G, M, N, K, out_dtype)
+        _WS_NEED[key] = need
     if need == 0:
         return None, 0
     buf = _WS.get(device)
@@ -650,6 +673,7 @@ def bsmm_query_plan(op, G, M, N, K, out_dtype, workspace_bytes=2**62):
 
 
 def bsmm_set_override(variant=None, split_k=0):
+    _WS_NEED.clear()              # the plans, and so their workspace, change
     _check(load().bsmm_set_override(variant.encode() if variant else None, split_k))
 
 
