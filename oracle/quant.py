@@ -22,7 +22,7 @@ consume.  The recipe is the one the pages state for their workloads:
   an activation or gradient (128 consecutive tokens of one feature), the
   operands of the weight-gradient GEMM, whose contraction runs over tokens.
 
-Readings (also listed in the design doc): the quotient ``x / scale`` is the
+Readings: the quotient ``x / scale`` is the
 binary32 quotient (correctly rounded); it is then rounded to the nearest
 code, ties to even (to an even integer for int8, to the even mantissa for
 e4m3), and e4m3 saturates at +-448.  A row or block whose amax is 0, or
