@@ -19,7 +19,7 @@ shape with 32-element MX scales) | c3d, c3w (that layer's backward pass: the
 input gradient, a blockwise GEMM 16640x8192x5120, and the weight gradient, a
 groupwise GEMM 5120x8192 over 16640 tokens), and the dynamic
 quantisers of their bf16 activations --config q_int8 | q_fp8 | q_mx | q_mx_t | q_mx32,
-and of the backward pass q_cols_x | q_cols_dy | q_w (one quantiser call per step,
+and of the backward pass q_cols_x | q_cols_dy | q_w | q_rows_cols_x (one quantiser call per step,
 GB/s against 8 TB/s).
 
 The JSON line also carries
@@ -64,6 +64,8 @@ QUANT_CONFIGS = {
     "q_cols_x": ("columns", (16640, 8192), "normal", 31),
     "q_cols_dy": ("columns", (16640, 5120), "normal", 32),
     "q_w": ("weight", (5120, 8192), "normal", 33),
+    # X once for both: the forward's 1 x 128 row blocks and the column groups
+    "q_rows_cols_x": ("rows_cols", (16640, 8192), "normal", 31),
 }
 
 
@@ -373,6 +375,8 @@ def quant_bytes(kind, rows, K):
         scale = (rows // 128) * K * 4
     elif kind == "weight":               # plain and transposed codes
         return rows * K * 2 + 2 * rows * K + (rows // 128) * (K // 128) * 4
+    elif kind == "rows_cols":            # both layouts, row-block and column-group scales
+        return rows * K * 2 + 2 * rows * K + rows * (K // 128) * 4 + (rows // 128) * K * 4
     else:
         scale = rows * (K // 128) * (4 if kind == "fp8" else 1)
     return rows * K * 2 + rows * K + scale
@@ -383,9 +387,10 @@ def quant_cpu_baseline(kind, x_rows, budget_s):
     from oracle import quant as Q
     fn = {"int8": Q.quant_int8_rowwise, "fp8": Q.quant_fp8_blockwise,
           "mx": Q.quant_fp8_mx, "mx32": lambda x: Q.quant_fp8_mx(x, block=32),
-          "columns": Q.quant_fp8_columns, "weight": Q.quant_fp8_weight_blocks}[kind]
+          "columns": Q.quant_fp8_columns, "weight": Q.quant_fp8_weight_blocks,
+          "rows_cols": lambda x: (Q.quant_fp8_blockwise(x), Q.quant_fp8_columns(x))}[kind]
     R, K = x_rows.shape
-    step = 128 if kind in ("columns", "weight") else 1      # whole groups of 128 rows
+    step = 128 if kind in ("columns", "weight", "rows_cols") else 1    # whole groups of 128 rows
     rows, t = min(R, max(64, step)), 0.0
     while True:
         t0 = time.perf_counter()
@@ -424,7 +429,8 @@ def bench_quant(args):
     fn = {"int8": bsmm.bsmm_quant_int8_rowwise, "fp8": bsmm.bsmm_quant_fp8_blockwise,
           "mx": bsmm.bsmm_quant_fp8_mx,
           "mx32": lambda x, **kw: bsmm.bsmm_quant_fp8_mx(x, block=32, **kw),
-          "columns": bsmm.bsmm_quant_fp8_columns, "weight": bsmm.bsmm_quant_fp8_weight}[kind]
+          "columns": bsmm.bsmm_quant_fp8_columns, "weight": bsmm.bsmm_quant_fp8_weight,
+          "rows_cols": bsmm.bsmm_quant_fp8_blockwise_columns}[kind]
     outs = [fn(x) for x in xs]
     torch.cuda.synchronize()
     print(f"[bench] {name}: inputs ready in {time.time() - t0:.1f}s, {copies} copies",
@@ -433,6 +439,9 @@ def bench_quant(args):
         calls = [(lambda x=x, o=o: fn(x, q_t=o[0], scale=o[1])) for x, o in zip(xs, outs)]
     elif kind == "weight":
         calls = [(lambda x=x, o=o: fn(x, q=o[0], q_t=o[1], scale=o[2]))
+                 for x, o in zip(xs, outs)]
+    elif kind == "rows_cols":
+        calls = [(lambda x=x, o=o: fn(x, q=o[0], scale=o[1], q_t=o[2], scale_t=o[3]))
                  for x, o in zip(xs, outs)]
     else:
         calls = [(lambda x=x, o=o: fn(x, q=o[0], scale=o[1])) for x, o in zip(xs, outs)]
@@ -471,7 +480,8 @@ def bench_quant(args):
                       "mx": "quant_fp8_blocks<e8m0 scale>",
                       "mx32": "quant_fp8_blocks<e8m0 scale, 32-element blocks>",
                       "columns": "quant_fp8_tiles<groups of 128 rows down the columns>",
-                      "weight": "quant_fp8_tiles<128 x 128 blocks, plain and transposed>"}[kind]
+                      "weight": "quant_fp8_tiles<128 x 128 blocks, plain and transposed>",
+                      "rows_cols": "quant_fp8_tiles<1 x 128 row blocks and column groups>"}[kind]
     roof["kernel_ms_mean"] = kern_ms
     roof["kernel_alg_bytes"] = nbytes
     line = {

@@ -18,7 +18,7 @@ __all__ = [
     "bsmm_int8_rowwise", "bsmm_fp8_blockwise", "bsmm_fp8_mx_bmm", "bsmm_fp8_scaled_mm",
     "bsmm_fp8_mx32_mm", "OP_FP8_MX32_MM", "bsmm_fp8_groupwise", "OP_FP8_GROUPWISE",
     "bsmm_quant_int8_rowwise", "bsmm_quant_fp8_blockwise", "bsmm_quant_fp8_mx",
-    "bsmm_quant_fp8_columns", "bsmm_quant_fp8_weight",
+    "bsmm_quant_fp8_columns", "bsmm_quant_fp8_weight", "bsmm_quant_fp8_blockwise_columns",
     "bsmm_workspace_bytes", "bsmm_query_plan", "bsmm_set_override",
     "bsmm_variant_names", "bsmm_version", "bsmm_timing_enable", "bsmm_timing_read",
     "I32", "F32", "BF16", "E4M3", "OP_INT8_ROWWISE", "OP_FP8_BLOCKWISE", "OP_FP8_MX_BMM",
@@ -89,10 +89,13 @@ def load():
     L.bsmm_quant_fp8_columns.argtypes = [vp, i64, st, vp, i64, vp, i64, i64, i64, i64, vp]
     L.bsmm_quant_fp8_weight.argtypes = [vp, i64, st, vp, i64, vp, i64, vp, i64, i64, i64, i64,
                                         vp]
+    L.bsmm_quant_fp8_blockwise_columns.argtypes = [vp, i64, st, vp, i64, vp, i64, i64, vp, i64,
+                                                   vp, i64, i64, i64, i64, vp]
     for f in ("bsmm_int8_rowwise", "bsmm_fp8_blockwise", "bsmm_fp8_mx_bmm", "bsmm_fp8_scaled_mm",
               "bsmm_fp8_mx32_mm",
               "bsmm_quant_int8_rowwise", "bsmm_quant_fp8_blockwise", "bsmm_quant_fp8_mx",
-              "bsmm_quant_fp8_mx32", "bsmm_quant_fp8_columns", "bsmm_quant_fp8_weight"):
+              "bsmm_quant_fp8_mx32", "bsmm_quant_fp8_columns", "bsmm_quant_fp8_weight",
+              "bsmm_quant_fp8_blockwise_columns"):
         getattr(L, f).restype = st
     L.bsmm_workspace_bytes.argtypes = [st, i64, i64, i64, i64, st]
     L.bsmm_workspace_bytes.restype = sz
@@ -596,6 +599,42 @@ def bsmm_quant_fp8_columns(x, *, q_t=None, scale=None, stream=None):
         x2.data_ptr(), x2.stride(0), code, q8.data_ptr(), q8.stride(0),
         scale.data_ptr(), scale.stride(0), scale.stride(1), R, C, _stream(stream)))
     return q_t, scale
+
+
+def bsmm_quant_fp8_blockwise_columns(x, *, q=None, scale=None, q_t=None, scale_t=None,
+                                     stream=None):
+    """Both fp8 quantisations of a layer input x [R, C] (bf16 or fp32; R and C
+    multiples of 128) from one read of x: the 1 x 128 row blocks of
+    bsmm_quant_fp8_blockwise (the forward GEMM's A) and the groups of 128
+    rows down the columns of bsmm_quant_fp8_columns (the weight gradient's
+    operand).  Bit-identical to the two separate calls.
+
+    Returns (q float8_e4m3fn [R, C], scale fp32 [R, C/128], q_t
+    float8_e4m3fn [C, R], scale_t fp32 [R/128, C]).  Unless given, ``scale``
+    is allocated column-major (strides (1, R)): the kernel writes one
+    128-column block of every row per tile, which is then one contiguous
+    run; bsmm_fp8_blockwise takes scale_a with any strides.
+    """
+    torch = _torch()
+    x2, code = _quant_input(x)
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [R, C]")
+    R, C = x2.shape
+    q = _quant_out(q, (R, C), torch.float8_e4m3fn, "q", x.device)
+    if scale is None:
+        scale = torch.empty((C // 128, R), dtype=torch.float32, device=x.device).t()
+    scale = _quant_out(scale, (R, C // 128), torch.float32, "scale", x.device)
+    q_t = _quant_out(q_t, (C, R), torch.float8_e4m3fn, "q_t", x.device)
+    scale_t = _quant_out(scale_t, (R // 128, C), torch.float32, "scale_t", x.device)
+    for t, n in ((q, "q"), (q_t, "q_t")):
+        if t.numel() and t.stride(1) != 1:
+            raise ValueError(f"{n} must be row-major")
+    qv, qtv = q.view(torch.uint8), q_t.view(torch.uint8)
+    _check(load().bsmm_quant_fp8_blockwise_columns(
+        x2.data_ptr(), x2.stride(0), code, qv.data_ptr(), qv.stride(0),
+        scale.data_ptr(), scale.stride(0), scale.stride(1), qtv.data_ptr(), qtv.stride(0),
+        scale_t.data_ptr(), scale_t.stride(0), scale_t.stride(1), R, C, _stream(stream)))
+    return q, scale, q_t, scale_t
 
 
 def bsmm_quant_fp8_weight(w, *, plain=True, transposed=True, q=None, q_t=None, scale=None,

@@ -737,10 +737,12 @@ bsmm_status quant_common(const void* x, int64_t ldx, bsmm_dtype x_dtype, const v
 }
 
 // Checks shared by the transposing quantisers of x [R, C]: R a multiple of
-// 128, C of `cmult` (8 for the column groups, 128 for the weight blocks);
-// one scale per (128-row group, column or 128-column block).
+// 128, C of `cmult` (8 for the column groups, 128 with row or weight
+// blocks); one scale per (128-row group, column) or, with `blocks`, per
+// (128-row group, 128-column block).
 bsmm_status quant_t_common(const void* x, int64_t ldx, bsmm_dtype x_dtype, const void* scale,
-                           int64_t s_g, int64_t s_c, int64_t R, int64_t C, int cmult) {
+                           int64_t s_g, int64_t s_c, int64_t R, int64_t C, int cmult,
+                           bool blocks) {
   CHECK(x_dtype == BSMM_F32 || x_dtype == BSMM_BF16, BSMM_ERR_DTYPE,
         "quantiser input must be fp32 or bf16 (got %d)", (int)x_dtype);
   CHECK(R >= 0 && C >= 0, BSMM_ERR_SHAPE, "negative size R=%lld C=%lld", (long long)R,
@@ -755,7 +757,7 @@ bsmm_status quant_t_common(const void* x, int64_t ldx, bsmm_dtype x_dtype, const
   CHECK(scale != nullptr, BSMM_ERR_NULL, "scale is NULL");
   CHECK(aligned(scale, 4), BSMM_ERR_ALIGN, "scale not 4-byte aligned");
   CHECK(s_g >= 0 && s_c >= 0, BSMM_ERR_SCALE_SHAPE, "scale strides must be >= 0");
-  const int64_t G = R / 128, NC = cmult == 128 ? C / 128 : C;
+  const int64_t G = R / 128, NC = blocks ? C / 128 : C;
   const bool rows_ok = G == 1 || s_g >= 1;
   const bool cols_ok = NC == 1 || s_c >= 1;
   const bool disjoint = G == 1 || NC == 1 || s_g >= NC * s_c || s_c >= G * s_g;
@@ -838,7 +840,7 @@ bsmm_status bsmm_quant_fp8_mx32(const void* x, int64_t ldx, bsmm_dtype x_dtype, 
 bsmm_status bsmm_quant_fp8_columns(const void* x, int64_t ldx, bsmm_dtype x_dtype,
                                    uint8_t* q_t, int64_t ldqt, float* scale, int64_t s_g,
                                    int64_t s_c, int64_t R, int64_t C, void* stream) {
-  bsmm_status st = quant_t_common(x, ldx, x_dtype, scale, s_g, s_c, R, C, 8);
+  bsmm_status st = quant_t_common(x, ldx, x_dtype, scale, s_g, s_c, R, C, 8, false);
   if (st != BSMM_OK || R == 0 || C == 0) return st;
   CHECK(q_t != nullptr, BSMM_ERR_NULL, "q_t is NULL");
   st = check_qt(q_t, ldqt, R);
@@ -857,7 +859,7 @@ bsmm_status bsmm_quant_fp8_columns(const void* x, int64_t ldx, bsmm_dtype x_dtyp
 bsmm_status bsmm_quant_fp8_weight(const void* w, int64_t ldw, bsmm_dtype w_dtype, uint8_t* q,
                                   int64_t ldq, uint8_t* q_t, int64_t ldqt, float* scale,
                                   int64_t s_r, int64_t s_c, int64_t R, int64_t C, void* stream) {
-  bsmm_status st = quant_t_common(w, ldw, w_dtype, scale, s_r, s_c, R, C, 128);
+  bsmm_status st = quant_t_common(w, ldw, w_dtype, scale, s_r, s_c, R, C, 128, true);
   if (st != BSMM_OK || R == 0 || C == 0) return st;
   CHECK(q != nullptr || q_t != nullptr, BSMM_ERR_NULL, "q and q_t are both NULL");
   if (q != nullptr) {
@@ -874,6 +876,42 @@ bsmm_status bsmm_quant_fp8_weight(const void* w, int64_t ldw, bsmm_dtype w_dtype
   a.q = q; a.ldq = ldq;
   a.qt = q_t; a.ldqt = ldqt;
   a.scale = scale; a.s_m = s_r; a.s_kb = s_c;
+  a.M = R; a.K = C;
+  if (launch_quant(a, stream) != 0) return fail(BSMM_ERR_HIP, "quantiser launch failed");
+  return BSMM_OK;
+}
+
+bsmm_status bsmm_quant_fp8_blockwise_columns(const void* x, int64_t ldx, bsmm_dtype x_dtype,
+                                             uint8_t* q, int64_t ldq, float* s_rows,
+                                             int64_t sr_m, int64_t sr_kb, uint8_t* q_t,
+                                             int64_t ldqt, float* s_cols, int64_t sc_g,
+                                             int64_t sc_c, int64_t R, int64_t C, void* stream) {
+  bsmm_status st = quant_t_common(x, ldx, x_dtype, s_cols, sc_g, sc_c, R, C, 128, false);
+  if (st != BSMM_OK || R == 0 || C == 0) return st;
+  CHECK(q != nullptr && q_t != nullptr && s_rows != nullptr, BSMM_ERR_NULL,
+        "q, q_t or s_rows is NULL");
+  CHECK(ldq >= C, BSMM_ERR_SHAPE, "ldq=%lld below C", (long long)ldq);
+  CHECK(ldq % 8 == 0 && aligned(q, 8), BSMM_ERR_ALIGN, "q or ldq not 8-byte aligned");
+  st = check_qt(q_t, ldqt, R);
+  if (st != BSMM_OK) return st;
+  CHECK(aligned(s_rows, 4), BSMM_ERR_ALIGN, "s_rows not 4-byte aligned");
+  CHECK(sr_m >= 0 && sr_kb >= 0, BSMM_ERR_SCALE_SHAPE, "scale strides must be >= 0");
+  {
+    const int64_t KB = C / 128;
+    const bool rows_ok = R == 1 || sr_m >= 1;
+    const bool cols_ok = KB == 1 || sr_kb >= 1;
+    const bool disjoint = R == 1 || KB == 1 || sr_m >= KB * sr_kb || sr_kb >= R * sr_m;
+    CHECK(rows_ok && cols_ok && disjoint, BSMM_ERR_SCALE_SHAPE,
+          "row-scale strides sr_m=%lld sr_kb=%lld make two blocks share a scale",
+          (long long)sr_m, (long long)sr_kb);
+  }
+  QuantArgs a{};
+  a.kind = QuantArgs::kFp8RowsColumns;
+  a.x = x; a.ldx = ldx; a.x_dtype = x_dtype;
+  a.q = q; a.ldq = ldq;
+  a.qt = q_t; a.ldqt = ldqt;
+  a.scale = s_cols; a.s_m = sc_g; a.s_kb = sc_c;
+  a.scale2 = s_rows; a.s2_m = sr_m; a.s2_kb = sr_kb;
   a.M = R; a.K = C;
   if (launch_quant(a, stream) != 0) return fail(BSMM_ERR_HIP, "quantiser launch failed");
   return BSMM_OK;

@@ -150,10 +150,11 @@ void timing_mark(void* stream, const char* name, bool begin);
 // transposed, qt [K, M] (row stride ldqt); scale (g, c) at scale[g*s_m +
 // c*s_kb] for g < M/128.  kFp8Weight: 128 x 128 blocks; codes in q [M, K]
 // and / or qt [K, M] (either may be null); scale (g, cb) at scale[g*s_m +
-// cb*s_kb].
+// cb*s_kb].  kFp8RowsColumns: kFp8Columns plus the 1 x 128 row blocks of the
+// same input, codes in q [M, K], scale (m, kb) at scale2[m*s2_m + kb*s2_kb].
 struct QuantArgs {
   enum Kind { kInt8Rows = 0, kFp8Blocks = 1, kFp8Mx = 2, kFp8Mx32 = 3, kFp8Columns = 4,
-              kFp8Weight = 5 };
+              kFp8Weight = 5, kFp8RowsColumns = 6 };
   Kind kind;
   const void* x;        // [M, K] bf16 or fp32, row stride ldx elements
   int64_t ldx;
@@ -165,6 +166,8 @@ struct QuantArgs {
   int64_t M, K;
   void* qt = nullptr;   // transposed codes [K, M] (kFp8Columns, kFp8Weight)
   int64_t ldqt = 0;
+  void* scale2 = nullptr;   // row-block scales (kFp8RowsColumns)
+  int64_t s2_m = 0, s2_kb = 0;
 };
 int launch_quant(const QuantArgs& a, void* stream);
 

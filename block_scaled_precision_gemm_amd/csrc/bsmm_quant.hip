@@ -326,12 +326,18 @@ quant_fp8_blocks(const T* __restrict__ x, int64_t ldx, uint8_t* __restrict__ q, 
 // make a dword, written to LDS at byte (8c + j) * kPitch + 4a (row pitch 132:
 // at most two lanes of a wave per bank); each column's 128 codes then leave
 // as 16-byte segments of row c0 + 8c + j of the transposed output.  BLOCK2D
-// also stores the codes untransposed when q is not null.
-template <typename T, int CW, bool BLOCK2D>
+// also stores the codes untransposed when q is not null.  ROWQ (column
+// groups, CW = 128) also quantises each row's 128 columns of the tile as a
+// 1 x 128 block, the forward quantisation of the same input: the 16 lanes
+// that hold one row form a DPP row, so the block maximum is a row16_max;
+// codes go to q untransposed and the row scale to srow.
+template <typename T, int CW, bool BLOCK2D, bool ROWQ = false>
 __global__ void __launch_bounds__(256)
 quant_fp8_tiles(const T* __restrict__ x, int64_t ldx, uint8_t* __restrict__ q, int64_t ldq,
                 uint8_t* __restrict__ qt, int64_t ldqt, float* __restrict__ scale, int64_t s_g,
-                int64_t s_c, int C) {
+                int64_t s_c, int C, float* __restrict__ srow = nullptr, int64_t sr_m = 0,
+                int64_t sr_kb = 0) {
+  static_assert(!ROWQ || (CW == 128 && !BLOCK2D), "row blocks span the 128-column tile");
   constexpr int NI = CW / 64;          // work items per thread
   constexpr int QW = CW / 8;           // 8-column chunks per tile row
   constexpr int kPitch = 132;
@@ -401,6 +407,33 @@ quant_fp8_tiles(const T* __restrict__ x, int64_t ldx, uint8_t* __restrict__ q, i
     float f[4][8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) widen(buf[ii][i], f[i]);
+    if constexpr (ROWQ) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) m = max(m, __float_as_uint(f[i][j]) & 0x7FFFFFFFu);
+        m = row16_max(m);
+        float sv = __uint_as_float(m) / 448.0f;
+        const bool zero = !(sv > 0.0f);
+        if (zero) sv = 1.0f;
+        float g[8];
+        if (sv >= kFastDivMin) {
+          const float r = 1.0f / sv;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) g[j] = clamp448(div_fast(f[i][j], sv, r));
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) g[j] = clamp448(f[i][j] / sv);
+        }
+        uint2 w;
+        w.x = e4m3x4(g[0], g[1], g[2], g[3]);
+        w.y = e4m3x4(g[4], g[5], g[6], g[7]);
+        if (zero) w = make_uint2(0, 0);
+        store8_nt(q + (row0 + 4 * a + i) * ldq + c0 + 8 * cc, w);
+        if (cc == 0) srow[(row0 + 4 * a + i) * sr_m + (int64_t)blockIdx.x * sr_kb] = sv;
+      }
+    }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const float sv = sc[BLOCK2D ? 0 : 8 * cc + j];
@@ -448,13 +481,13 @@ quant_fp8_tiles(const T* __restrict__ x, int64_t ldx, uint8_t* __restrict__ q, i
 // 16-byte loads in flight per lane) measured 4-6% faster than 64 on MI355X
 constexpr int kColTile = 128;
 
-template <typename T, int CW, bool BLOCK2D>
+template <typename T, int CW, bool BLOCK2D, bool ROWQ = false>
 void launch_tiles(const QuantArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)((a.K + CW - 1) / CW), (unsigned)(a.M / 128));
-  hipLaunchKernelGGL((quant_fp8_tiles<T, CW, BLOCK2D>), grid, dim3(256), 0, st,
+  hipLaunchKernelGGL((quant_fp8_tiles<T, CW, BLOCK2D, ROWQ>), grid, dim3(256), 0, st,
                      static_cast<const T*>(a.x), a.ldx, static_cast<uint8_t*>(a.q), a.ldq,
                      static_cast<uint8_t*>(a.qt), a.ldqt, static_cast<float*>(a.scale), a.s_m,
-                     a.s_kb, (int)a.K);
+                     a.s_kb, (int)a.K, static_cast<float*>(a.scale2), a.s2_m, a.s2_kb);
 }
 
 template <typename T, int WPR, int NV>
@@ -510,6 +543,10 @@ int launch_quant(const QuantArgs& a, void* stream) {
       break;
     case QuantArgs::kFp8Weight:
       if (bf) launch_tiles<uint16_t, 128, true>(a, st); else launch_tiles<float, 128, true>(a, st);
+      break;
+    case QuantArgs::kFp8RowsColumns:
+      if (bf) launch_tiles<uint16_t, 128, false, true>(a, st);
+      else launch_tiles<float, 128, false, true>(a, st);
       break;
     default:
       if (bf) launch_blocks<uint16_t, true, 16>(a, st); else launch_blocks<float, true, 16>(a, st);

@@ -372,6 +372,26 @@ bsmm_status bsmm_quant_fp8_weight(const void* w, int64_t ldw, bsmm_dtype w_dtype
                                   int64_t s_r, int64_t s_c, int64_t R, int64_t C,
                                   void* stream);
 
+/*
+ * bsmm_quant_fp8_blockwise_columns: both quantisations of one layer input
+ * x [R, C] (tokens along R) from a single read of x -- the 1 x 128 row
+ * blocks of bsmm_quant_fp8_blockwise (the forward GEMM's A: codes q [R, C],
+ * scale (r, kb) at s_rows[r*sr_m + kb*sr_kb]) and the groups of 128 rows
+ * down the columns of bsmm_quant_fp8_columns (the weight gradient's
+ * operand: codes q_t [C, R], scale (g, c) at s_cols[g*sc_g + c*sc_c]).
+ * Bit-identical to the two separate calls.
+ *   Requirements: R and C multiples of 128 (at most 65535 groups of rows);
+ *   x as for bsmm_quant_fp8_columns; q and ldq 8-byte aligned; q_t and ldqt
+ *   16-byte aligned; both scale arrays 4-byte aligned with strides that give
+ *   every block its own element.
+ */
+bsmm_status bsmm_quant_fp8_blockwise_columns(const void* x, int64_t ldx, bsmm_dtype x_dtype,
+                                             uint8_t* q, int64_t ldq, float* s_rows,
+                                             int64_t sr_m, int64_t sr_kb, uint8_t* q_t,
+                                             int64_t ldqt, float* s_cols, int64_t sc_g,
+                                             int64_t sc_c, int64_t R, int64_t C,
+                                             void* stream);
+
 /* Workspace bytes the fastest plan for this problem wants (0 if none). */
 size_t bsmm_workspace_bytes(bsmm_op op, int64_t G, int64_t M, int64_t N,
                             int64_t K, bsmm_dtype out_dtype);

@@ -324,8 +324,27 @@ def test_quant_weight_rejects(kw, status):
     assert bsmm.load().bsmm_last_error().decode()
 
 
+def qrc(*, x=P, ldx=256, xdt=bsmm.BF16, q=P, ldq=256, sr=P, sr_m=2, sr_kb=1, qt=P, ldqt=256,
+        sc=P, sc_g=256, sc_c=1, R=256, C=256):
+    return bsmm.load().bsmm_quant_fp8_blockwise_columns(x, ldx, xdt, q, ldq, sr, sr_m, sr_kb, qt,
+                                                        ldqt, sc, sc_g, sc_c, R, C, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(xdt=bsmm.I32), DTYPE), (dict(R=200), UNSUP), (dict(C=200, ldx=256, ldq=256), UNSUP),
+    (dict(q=None), NULL), (dict(qt=None), NULL), (dict(sr=None), NULL), (dict(sc=None), NULL),
+    (dict(sr_m=1, sr_kb=1), SCALE), (dict(sr_m=-1), SCALE), (dict(sc_c=0), SCALE),
+    (dict(ldq=128), SHAPE), (dict(ldq=260), ALIGN), (dict(ldqt=128), SHAPE),
+    (dict(qt=P + 8), ALIGN), (dict(sr=P + 2), ALIGN), (dict(x=P + 8), ALIGN),
+])
+def test_quant_blockwise_columns_rejects(kw, status):
+    assert qrc(**kw) == status
+    assert bsmm.load().bsmm_last_error().decode()
+
+
 def test_quant_backward_noops_and_single_outputs():
     assert qcol(R=0) == OK and qcol(C=0) == OK and qw(R=0) == OK and qw(C=0) == OK
+    assert qrc(R=0) == OK and qrc(C=0) == OK
     # C need only be a multiple of 8 for the column groups; either output
     # of the weight quantiser alone is fine (M = 0 rows keeps it from launching)
     assert qcol(C=200, ldx=200 + 8, R=0) == OK

@@ -181,3 +181,37 @@ def test_layer_activations_full_size_sampled_columns(gpu_lib):
         assert np.array_equal(q[:, 128 * cb:128 * (cb + 1)].view(torch.uint8).cpu().numpy(), qo)
         assert np.array_equal(q_t[128 * cb:128 * (cb + 1)].view(torch.uint8).cpu().numpy(), qo.T)
         assert np.array_equal(s[:, cb].cpu().numpy(), so[:, 0])
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("R,C", [(128, 128), (256, 384), (384, 256), (1280, 640)])
+def test_blockwise_and_columns_from_one_read(gpu_lib, dt, R, C):
+    """The fused quantiser equals the two separate quantisations bit for bit:
+    the row blocks of quant_fp8_blockwise and the column groups of
+    quant_fp8_columns, zero and underflowing rows and columns included."""
+    print(f"quant rows+columns {R}x{C} {dt}", flush=True)
+    x = spread(R, C, 3 * R + C, zero_cols=(0,), tiny_cols=(C - 1,))
+    x[7, :] = 0.0                                       # a zero row (all its blocks)
+    x[9, 128:] *= np.float32(2.0**-150)                 # underflowing row blocks
+    xd, xv = device_input(x, dt)
+    q, s, q_t, s_t = gpu_lib.bsmm_quant_fp8_blockwise_columns(xd)
+    torch.cuda.synchronize()
+    assert_same((u8(q), s.cpu().numpy()), Q.quant_fp8_blockwise(xv), f"rows {R}x{C} {dt}")
+    assert_same((u8(q_t), s_t.cpu().numpy()), Q.quant_fp8_columns(xv), f"columns {R}x{C} {dt}")
+
+
+def test_blockwise_and_columns_full_size_sampled(gpu_lib):
+    """X [16640, 8192] of the 16640-token layer: sampled rows and columns."""
+    print("quant rows+columns full size", flush=True)
+    xd, xv = device_input(activations((16640, 8192), 34, row_scale_log2=(-3, 3)), "bf16")
+    q, s, q_t, s_t = gpu_lib.bsmm_quant_fp8_blockwise_columns(xd)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(6)
+    rows = np.unique(np.concatenate([[0, 16639], rng.choice(16640, 14)]))
+    qo, so = Q.quant_fp8_blockwise(xv[rows])
+    assert_same((q[rows].view(torch.uint8).cpu().numpy(), s[rows].cpu().numpy()), (qo, so),
+                "rows")
+    cols = np.unique(np.concatenate([[0, 8191], rng.choice(8192, 14)]))
+    qo, so = Q.quant_fp8_columns(xv[:, cols])
+    assert_same((q_t[cols].view(torch.uint8).cpu().numpy(), s_t[:, cols].cpu().numpy()),
+                (qo, so), "columns")
