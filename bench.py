@@ -262,7 +262,8 @@ def _csvs(d, suffix):
 
 
 def _main_kernel(name):
-    return "tile_kernel" in name or "sk_kernel" in name or "quant_" in name
+    return any(k in name for k in ("tile_kernel", "tile4_kernel", "sk_kernel", "skinny_kernel",
+                                   "quant_"))
 
 
 def launches_per_call(name):
