@@ -62,3 +62,44 @@ def test_summarize_groups_the_skinny_launches(tmp_path, capsys):
     assert (grid, launch, calls) == ("2048", "-", "3")
     assert (float(avg), float(lo), float(hi)) == (9.0, 8.0, 10.0)
     assert "splitk_reduce" not in section and "pack_kernel" not in section
+
+
+def _counters(d, rows):
+    d.mkdir(parents=True)
+    _write(d / "1_counter_collection.csv",
+           ["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"], rows)
+
+
+def test_traffic_scales_the_counters_by_the_copy_calibration(tmp_path, monkeypatch):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch, summed over the counter's
+    instances) of the main kernel, averaged over its dispatches and scaled
+    by the copy kernel's bytes over what the counter read for the copy; a
+    helper kernel's dispatches do not count."""
+    import json
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_hash", lambda sources=None: "0" * 16)
+    (tmp_path / "profiles").mkdir()
+    copy_kib = bench.COPY_BYTES / 1024
+    cp = "__amd_rocclr_copyBuffer"
+    # the copy reads as half its size (scale 2) and writes as a quarter (scale 4)
+    _counters(tmp_path / "cf", [dict(Dispatch_Id=1, Kernel_Name=cp, Grid_Size=1, Counter_Name="FETCH_SIZE",
+                                     Counter_Value=copy_kib / 4)] * 2)
+    _counters(tmp_path / "cw", [dict(Dispatch_Id=1, Kernel_Name=cp, Grid_Size=1, Counter_Name="WRITE_SIZE",
+                                     Counter_Value=copy_kib / 4)])
+    q = "void bsmm::(anonymous namespace)::quant_fp8_blocks<unsigned short, 128, 0>(...)"
+    fetch = [dict(Dispatch_Id=i + 1, Kernel_Name=q, Grid_Size=4096, Counter_Name="FETCH_SIZE",
+                  Counter_Value=v) for i, v in enumerate((1000, 1100, 1200))]
+    fetch.append(dict(Dispatch_Id=9, Kernel_Name=HELPERS[0], Grid_Size=64, Counter_Name="FETCH_SIZE",
+                      Counter_Value=99999))
+    _counters(tmp_path / "f", fetch)
+    # dispatch 1 in two counter instances (200 + 300), dispatch 2 in one (500)
+    _counters(tmp_path / "w", [dict(Dispatch_Id=i, Kernel_Name=q, Grid_Size=4096,
+                                    Counter_Name="WRITE_SIZE", Counter_Value=v)
+                               for i, v in ((1, 200), (1, 300), (2, 500))])
+    bench.traffic("q_fp8", *(str(tmp_path / n) for n in ("f", "w", "cf", "cw")))
+    res = json.load(open(tmp_path / "profiles" / "traffic_q_fp8.json"))
+    assert res["fetch_scale"] == 2.0 and res["write_scale"] == 4.0
+    assert res["dispatches"] == 3 and res["grid"] == 4096
+    assert res["fetch_bytes_per_launch"] == 1100 * 1024 * 2.0
+    assert res["write_bytes_per_launch"] == 500 * 1024 * 4.0
+    assert res["hbm_bytes_per_launch"] == res["fetch_bytes_per_launch"] + res["write_bytes_per_launch"]
