@@ -464,3 +464,40 @@ def compare(Y, res: Result, *, exact=False) -> dict:
         "worst": tuple(int(i) for i in worst),
     }
     return rep
+
+
+def compare_within(Y, res: Result, gamma: float) -> dict:
+    """A tighter check than ``compare`` for a result computed in binary32:
+    if the GPU's binary32 value Y32 obeys |Y32 - C| <= tol = gamma * Bd (gamma
+    the error bound of its fp32 accumulation, relative to Bd), then
+
+    * fp32 output: |Y - C| <= tol;
+    * bf16 output: Y is the round-to-nearest-even of a value in
+      [C - tol, C + tol], and rounding is monotone, so
+      RNE(C - tol) <= Y <= RNE(C + tol).
+
+    Where Bd = 0 the interval is {0}.  ``Y``: float32 values, or uint16
+    bfloat16 bit patterns (the oracle's bf16 representation)."""
+    from .formats import bf16_bits_to_f64
+    Y = np.asarray(Y)
+    C = res.exact
+    if Y.shape != C.shape:
+        return {"ok": False, "why": f"shape {Y.shape} vs {C.shape}"}
+    # the endpoints C +- tol are formed in fp64: widen by its rounding
+    tol = gamma * res.bound + 2.0 ** -50 * np.abs(C)
+    if Y.dtype == np.uint16:
+        y = bf16_bits_to_f64(Y)
+        lo = bf16_bits_to_f64(bf16_bits_from_f64(C - tol))
+        hi = bf16_bits_to_f64(bf16_bits_from_f64(C + tol))
+        bad = ~((y >= lo) & (y <= hi))
+    else:
+        y = Y.astype(np.float64)
+        bad = ~(np.abs(y - C) <= tol)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(res.bound > 0, np.abs(y - C) / res.bound,
+                         np.where(y != C, np.inf, 0.0))
+    rep = {"ok": not bad.any(), "violations": int(bad.sum()),
+           "max_err_over_bound": float(ratio.max()) if ratio.size else 0.0}
+    if bad.any():
+        rep["first"] = tuple(int(i) for i in np.argwhere(bad)[0])
+    return rep

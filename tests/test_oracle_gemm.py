@@ -330,6 +330,60 @@ def test_compare_accepts_oracle_and_rejects_planted_error():
     assert not S.compare(off, r, exact=True)["ok"]
 
 
+def test_compare_within_fp32_and_bf16_intervals():
+    """The tight rule: a binary32 rounding of the exact value passes with
+    gamma = 2**-24 (its error is at most 2**-24 |C| <= 2**-24 Bd); one ulp
+    further fails once gamma is below that ulp; the bf16 result must lie in
+    [RNE(C - tol), RNE(C + tol)] -- with gamma = 0 exactly RNE(C)."""
+    p = fp8_blockwise_inputs(32, 256, 1024, 18)
+    r32 = S.fp8_blockwise(p["a"], p["b_nk"].T, p["scale_a"], p["scale_b"], "f32")
+    assert S.compare_within(r32.out, r32, 2.0**-24)["ok"]
+    # an error of 4 * 2**-24 Bd (after rounding, at least 3 * 2**-24 Bd) fails
+    off = r32.out.copy()
+    off[5, 9] = np.float32(r32.exact[5, 9] + 4 * 2.0**-24 * r32.bound[5, 9])
+    rep = S.compare_within(off, r32, 2.0**-24)
+    assert not rep["ok"] and rep["first"] == (5, 9) and rep["violations"] == 1
+    rb = S.fp8_blockwise(p["a"], p["b_nk"].T, p["scale_a"], p["scale_b"], "bf16")
+    assert S.compare_within(rb.out, rb, 0.0)["ok"]
+    # one bf16 ulp away from RNE(C), where C is not within tol of a rounding
+    # boundary, is rejected
+    bits = rb.out.copy()
+    C = rb.exact[2, 3]
+    ulp = 2.0 ** (np.floor(np.log2(abs(C))) - 7)
+    bits[2, 3] = bits[2, 3] + 1 if (C > 0) == (bf16_bits_to_f64(bits[2, 3]) >= C) else bits[2, 3] - 1
+    assert abs(bf16_bits_to_f64(bits[2, 3]) - C) > 0.5 * ulp
+    assert not S.compare_within(bits, rb, 2.0**-24)["ok"]
+    # the interval rule agrees with exact rounding at its ends: C - tol and
+    # C + tol rounded by the exact-rational RNE bracket the accepted values
+    tol = 2.0**-12 * rb.bound[2, 3]
+    lo, hi = rne_bf16(Fraction(C) - Fraction(tol)), rne_bf16(Fraction(C) + Fraction(tol))
+    for v in (lo, hi):
+        q = rb.out.copy()
+        q[2, 3] = np.float32(float(v)).view(np.uint32) >> 16
+        assert S.compare_within(q, rb, 2.0**-12)["ok"]
+
+
+def test_compare_within_zero_bound_needs_zero_and_catches_one_misscaled_block():
+    """Where Bd = 0 only 0 passes.  A K block whose scale is off by a factor
+    of two in one row fails the tight rule at the fp32 accumulation bound of
+    the kernels in that row and nowhere else."""
+    p = fp8_blockwise_inputs(16, 256, 8192, 19)
+    a = p["a"].copy()
+    a[4, :] = 0                                      # a zero row: Bd = 0 there
+    res = S.fp8_blockwise(a, p["b_nk"].T, p["scale_a"], p["scale_b"], "f32")
+    assert (res.bound[4] == 0).all()
+    y = res.out.copy()
+    assert S.compare_within(y, res, 2.0**-20)["ok"]
+    y[4, 0] = np.float32(2.0**-140)
+    assert not S.compare_within(y, res, 2.0**-20)["ok"]
+    sa = p["scale_a"].copy()
+    sa[7, 40] *= 2
+    wrong = S.fp8_blockwise(a, p["b_nk"].T, sa, p["scale_b"], "f32")
+    gamma = 2.0**-17 + 72 * 2.0**-24
+    rep = S.compare_within(wrong.out, res, gamma)
+    assert not rep["ok"] and {f[0] for f in np.argwhere(wrong.out != res.out)} == {7}
+
+
 def _brute_check(fn):
     """Run the brute-force blockwise pin against oracle function ``fn``."""
     a, b_kn, sa, sb = _tiny_blockwise(21, M=2, N=256, K=256)
