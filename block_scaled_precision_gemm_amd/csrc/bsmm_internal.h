@@ -64,6 +64,7 @@ struct Launch {
   size_t ws_bytes;
   const void* psa;       // packed scale_a, already written (packed variants)
   void* stream;
+  int sk_grid = 0;       // stream-K grid (0: the device's co-resident capacity)
 };
 
 // Kernel variants compiled into the library.
@@ -117,8 +118,8 @@ inline size_t packed_scale_bytes(bsmm_op op, int G, int M, int K, int N = 0) {
   return (n + 255) / 256 * 256;
 }
 
-// Workspace a persistent (stream-K) variant wants: one partial tile plus a
-// 64-bit flag per workgroup, for a device of kPlanCUs compute units.
+// Workspace a persistent (stream-K) variant wants: two partial tiles and
+// two 64-bit counters per workgroup, for a device of kPlanCUs compute units.
 constexpr int kPlanCUs = 256;
 size_t persistent_workspace(const Variant* v, bsmm_op op);
 

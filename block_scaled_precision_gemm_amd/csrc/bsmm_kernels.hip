@@ -398,8 +398,7 @@ struct Mainloop {
   __device__ __forceinline__ static void run(const KArgs& k, uint8_t* smem, int g,
                                              int row0, int col0, int kb0, int nkb,
                                              acc_t (&acc)[TI][TJ]) {
-    constexpr int BM = T::BM, BN = T::BN;
-    constexpr int NW = T::NW, NSLOT = T::NSLOT, SLOT = T::SLOT;
+    constexpr int NSLOT = T::NSLOT, SLOT = T::SLOT;
     const Problem& p = k.p;
     const int lane = threadIdx.x & 63;
     // wave-uniform values live in scalar registers
@@ -949,15 +948,25 @@ skinny_kernel(const KArgs k) {
 //            [splits][G][rows][N];
 //   kSlot    a stream-K partial: the whole BM x BN tile, row-major, into
 //            the slot `sl.base` (int32 / fp32);
-//   kOutAdd  the output after adding, in K order, the partials of the
-//            tile's later K segments from slots sl.first .. sl.first +
-//            sl.count - 1 (int8: the raw sums are staged and both scales
-//            applied after the adds, so the operations are those of kOut).
+//   kOutAdd  the output of a stream-K tile whose `sl.count` K segments sit
+//            in slots sl.slot(0) .. sl.slot(count - 1), in K order; segment
+//            sl.own is this workgroup's, taken from its registers.  The sum
+//            runs in K order whichever segment this is, so the result does
+//            not depend on which workgroup adds (int8: the raw sums are
+//            staged and both scales applied after the adds, so the
+//            operations are those of kOut).
 enum { kOut = 0, kSplitK = 1, kSlot = 2, kOutAdd = 3 };
 struct SlotRef {
   void* base = nullptr;       // slot 0
-  int first = 0, count = 0;   // kOutAdd: slots to add
   int64_t stride = 0;         // elements per slot
+  // kOutAdd: the tile's segments are those of workgroups first .. first +
+  // count - 1.  A workgroup's slot 2w holds the first segment of its K
+  // range, slot 2w + 1 the segment that starts a tile at the end of its
+  // range; only the tile's first segment can be of the second kind.
+  int first = 0, count = 0, own = 0, first_odd = 0;
+  __device__ __forceinline__ int64_t slot(int j) const {
+    return 2 * (int64_t)(first + j) + (j == 0 ? first_odd : 0);
+  }
 };
 
 template <int OP, int OUT, int NW, int WN, int MODE, int BM, int BN, int TI, int TJ,
@@ -1043,12 +1052,25 @@ __device__ __forceinline__ void store_staged(const KArgs& k, int s, int g, int r
       if constexpr (MODE == kOutAdd) {
         typedef E e4 __attribute__((ext_vector_type(4)));
         const int64_t off = (int64_t)(m - row0) * BN + (n - col0);
+        const i32x4 mine = v;
         for (int q2 = 0; q2 < sl.count; ++q2) {
-          const e4 t = *(const e4*)((const E*)sl.base + (int64_t)(sl.first + q2) * sl.stride + off);
+          i32x4 t = mine;
+          if (q2 != sl.own) {
+            const e4 s = *(const e4*)((const E*)sl.base + sl.slot(q2) * sl.stride + off);
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            if constexpr (OP == BSMM_OP_INT8_ROWWISE) v[c] += t[c];
-            else v[c] = __float_as_int(__int_as_float(v[c]) + t[c]);
+            for (int c = 0; c < 4; ++c) {
+              if constexpr (OP == BSMM_OP_INT8_ROWWISE) t[c] = s[c];
+              else t[c] = __float_as_int(s[c]);
+            }
+          }
+          if (q2 == 0) {
+            v = t;
+          } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              if constexpr (OP == BSMM_OP_INT8_ROWWISE) v[c] += t[c];
+              else v[c] = __float_as_int(__int_as_float(v[c]) + __int_as_float(t[c]));
+            }
           }
         }
       }
@@ -1344,29 +1366,29 @@ tile_kernel(const KArgs k) {
 }
 
 // ---------------------------------------------------------------------------
-// Persistent stream-K kernel.  The grid is exactly the number of workgroups
-// the device holds at once.  The work, tiles x K blocks, is cut into equal
+// Persistent stream-K kernel.  The work, tiles x K blocks, is cut into equal
 // contiguous ranges, one per workgroup, so every CU gets the same number of
 // K blocks however the tile count divides the CU count.  A tile split between
-// consecutive ranges is finished by the workgroup holding its K block 0 (it
-// reaches that segment last, at the end of its range); every other segment
-// of the tile is the *first* segment of a later range, computed first, and is
-// stored as an fp32 / int32 partial with a flag carrying the launch's epoch.
-// The owner waits for the flags (bounded), adds the partials in K order and
-// stores the tile.  With two segments the sum is exactly order-independent;
-// with more, the fixed K order keeps it deterministic.
-// Workspace: one partial slot of BM x BN elements per workgroup, then one
-// 64-bit flag per workgroup.
+// consecutive ranges is finished by whichever of its segments' workgroups
+// arrives last: each segment stores its fp32 / int32 partial in a slot of
+// its own, then counts itself in the tile's counter with a global atomic;
+// the workgroup that brings the count to the number of segments adds all of
+// them in K order (its own from registers) and stores the tile.  No
+// workgroup ever waits for another, so the result does not depend on how
+// many of the grid's workgroups the device holds at once, and the fixed K
+// order makes it deterministic.
+// A counter holds the launch's 40-bit tag above a 24-bit count; a value with
+// another tag (an earlier launch, or whatever the workspace held) counts as
+// zero, so the counters need no clearing between launches.
+// Workspace: two partial slots of BM x BN elements per workgroup (see
+// SlotRef), then one 64-bit counter per stream-K tile (at most 2P of them).
 // ---------------------------------------------------------------------------
 struct SkArgs {
-  int64_t units;       // K-block units of the stream-K phase: sk tiles * KB
-  uint64_t epoch;      // distinct per launch
+  int64_t units;       // K-block units of the stream-K phase: sk tiles * KB (>= P)
+  uint64_t epoch;      // distinct per launch (its low 40 bits tag the counters)
   int tiles_total;     // tiles_m * tiles_n * G
   int dp_tiles;        // whole tiles before the stream-K phase
 };
-
-constexpr int kSpinLimit = 1 << 22;   // ~ seconds of polling; never reached
-                                      // when the grid is co-resident
 
 template <int OP, int OUT, int WM, int WN, int RING, bool PK>
 __global__ void __launch_bounds__(64 * WM * WN)
@@ -1375,9 +1397,12 @@ sk_kernel(const KArgs k, const SkArgs sk) {
   using T = typename M::T;
   using acc_t = typename M::acc_t;
   typedef typename OpT<OP>::elem_t E;
-  constexpr int TI = M::TI, TJ = M::TJ, NT = T::NT;
+  constexpr int TI = M::TI, TJ = M::TJ;
   constexpr int SLOT_ELEMS = T::BM * T::BN;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[M::SMEM];
+  // the last-arrival flag: the ring's first word, idle between a segment's
+  // stores and the next barrier (the ring fills the whole LDS)
+  int* const last_arrival = (int*)smem;
   const int P = gridDim.x;
   // XCD-aware: consecutive ranges run on the same XCD
   const int hw = blockIdx.x;
@@ -1387,8 +1412,12 @@ sk_kernel(const KArgs k, const SkArgs sk) {
                             : rem * (per + 1) + (xcd - rem) * per + local;
   const int KB = k.p.K / kBlockK;
   auto range_start = [&](int wi) { return (int64_t)wi * sk.units / P; };   // units * P < 2^63
+  // the range holding unit u: the last wi with range_start(wi) <= u (every
+  // range is non-empty because units >= P)
+  auto range_of = [&](int64_t u) { return (int)(((u + 1) * P - 1) / sk.units); };
   E* slots = (E*)k.ws;
-  uint64_t* flags = (uint64_t*)((uint8_t*)k.ws + (size_t)P * SLOT_ELEMS * sizeof(E));
+  uint64_t* counters = (uint64_t*)((uint8_t*)k.ws + (size_t)2 * P * SLOT_ELEMS * sizeof(E));
+  const uint64_t tag = sk.epoch & ((1ull << 40) - 1);
   const int tid = threadIdx.x;
 
   // Data-parallel phase: whole tiles dp_tiles in the persistent order
@@ -1431,43 +1460,44 @@ sk_kernel(const KArgs k, const SkArgs sk) {
       for (int j = 0; j < TJ; ++j) acc[i][j] = acc_t{0, 0, 0, 0};
     M::run(k, smem, g, row0, col0, kb_a, kb_b - kb_a, acc);
 
-    SlotRef sl;
-    sl.base = slots;
-    sl.stride = SLOT_ELEMS;
-    if (kb_a > 0) {
-      // a later K segment of a split tile: publish the partial (the staged
-      // tile into this workgroup's slot) and its flag
-      sl.base = slots + (size_t)w * SLOT_ELEMS;
-      store_staged<OP, OUT, WM * WN, WN, kSlot, T::BM, T::BN>(k, 0, g, row0, col0, acc, smem, sl);
-      __threadfence();
-      __syncthreads();
-      if (tid == 0)
-        __hip_atomic_store(&flags[w], sk.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    if (kb_a == 0 && kb_b == KB) {
+      store_staged<OP, OUT, WM * WN, WN, kOut, T::BM, T::BN>(k, 0, g, row0, col0, acc, smem);
     } else {
-      // owner (K blocks from 0): the tile's later K segments are the first
-      // segments of the following ranges, computed first.  A split tile
-      // waits for their flags, then adds their partials, in K order, while
-      // storing the output.
-      int w_end = w + 1;
-      if (kb_b < KB)
-        while (w_end < P && range_start(w_end) < (int64_t)(tile - sk.dp_tiles + 1) * KB) ++w_end;
-      if (w_end > w + 1) {
-        if (tid == 0) {
-          for (int w2 = w + 1; w2 < w_end; ++w2) {
-            int spins = 0;
-            while (__hip_atomic_load(&flags[w2], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) !=
-                       sk.epoch &&
-                   ++spins < kSpinLimit)
-              __builtin_amdgcn_s_sleep(2);
-          }
-        }
-        __syncthreads();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        sl.first = w + 1;
-        sl.count = w_end - (w + 1);
-        store_staged<OP, OUT, WM * WN, WN, kOutAdd, T::BM, T::BN>(k, 0, g, row0, col0, acc, smem, sl);
-      } else {
-        store_staged<OP, OUT, WM * WN, WN, kOut, T::BM, T::BN>(k, 0, g, row0, col0, acc, smem);
+      // a segment of a split tile (tiles of the data-parallel phase are
+      // never split)
+      const int64_t t0 = (int64_t)(tile - sk.dp_tiles) * KB;   // the tile's first unit
+      SlotRef sl;
+      sl.base = slots;
+      sl.stride = SLOT_ELEMS;
+      sl.first = range_of(t0);
+      sl.count = range_of(t0 + KB - 1) - sl.first + 1;
+      sl.first_odd = range_start(sl.first) < t0 ? 1 : 0;
+      sl.own = w - sl.first;
+      // publish this segment's partial, then count it in
+      SlotRef mine;
+      mine.base = slots + sl.slot(sl.own) * SLOT_ELEMS;
+      store_staged<OP, OUT, WM * WN, WN, kSlot, T::BM, T::BN>(k, 0, g, row0, col0, acc, smem,
+                                                              mine);
+      __threadfence();     // the partial is visible device-wide before the count
+      __syncthreads();
+      if (tid == 0) {
+        uint64_t* ctr = counters + (tile - sk.dp_tiles);
+        uint64_t old = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        uint64_t now;
+        // lock-free: a failed exchange means another segment's succeeded,
+        // so at most count attempts
+        do {
+          now = (old >> 24) == tag ? old + 1 : ((tag << 24) | 1u);
+        } while (!__hip_atomic_compare_exchange_strong(ctr, &old, now, __ATOMIC_ACQ_REL,
+                                                       __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT));
+        *last_arrival = (int)(now & 0xFFFFFFu) == sl.count;
+      }
+      __syncthreads();
+      if (*last_arrival) {   // store_staged's first barrier precedes any LDS write
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // the other partials
+        store_staged<OP, OUT, WM * WN, WN, kOutAdd, T::BM, T::BN>(k, 0, g, row0, col0, acc, smem,
+                                                                  sl);
       }
     }
     if (dp < sk.dp_tiles) dp += P;
@@ -1732,13 +1762,18 @@ int launch_sk(const Problem& p, const Launch& l) {
   using T = Tile<OP, WM, WN, RING>;
   const int KB = p.K / kBlockK;
   typedef typename OpT<OP>::elem_t E;
-  const size_t per_wg = (size_t)T::BM * T::BN * sizeof(E) + sizeof(uint64_t);
+  // two partial slots and two counters per workgroup (see sk_kernel)
+  const size_t per_wg = 2 * ((size_t)T::BM * T::BN * sizeof(E) + sizeof(uint64_t));
   if (KB == 0 || !aligned16(l.ws) || l.ws_bytes < per_wg)
     return launch_tile<OP, OUT, WM, WN, RING, PK>(p, l);
-  // co-resident capacity of this kernel on the current device (cached)
+  // the grid: the kernel's co-resident capacity on the current device
+  // (cached), or the caller's choice -- the kernel never waits, so any grid
+  // is correct
   static std::atomic<int> cap_cache[64];
-  const int cap = device_slots(reinterpret_cast<const void*>(&sk_kernel<OP, OUT, WM, WN, RING, PK>),
-                               T::NT, cap_cache);
+  const int cap = l.sk_grid > 0 ? l.sk_grid
+                                : device_slots(reinterpret_cast<const void*>(
+                                                   &sk_kernel<OP, OUT, WM, WN, RING, PK>),
+                                               T::NT, cap_cache);
   if (cap <= 0) return 1;
   KArgs k;
   k.p = p;
