@@ -19,7 +19,7 @@ __all__ = [
     "bsmm_fp8_mx32_mm", "OP_FP8_MX32_MM", "bsmm_fp8_groupwise", "OP_FP8_GROUPWISE",
     "bsmm_quant_int8_rowwise", "bsmm_quant_fp8_blockwise", "bsmm_quant_fp8_mx",
     "bsmm_quant_fp8_columns", "bsmm_quant_fp8_weight", "bsmm_quant_fp8_blockwise_columns",
-    "bsmm_workspace_bytes", "bsmm_query_plan", "bsmm_set_override",
+    "bsmm_workspace_bytes", "bsmm_query_plan", "bsmm_set_override", "bsmm_set_streamk_grid", "bsmm_mfma_probe",
     "bsmm_variant_names", "bsmm_version", "bsmm_timing_enable", "bsmm_timing_read",
     "I32", "F32", "BF16", "E4M3", "OP_INT8_ROWWISE", "OP_FP8_BLOCKWISE", "OP_FP8_MX_BMM",
     "OP_FP8_SCALED_MM",
@@ -103,6 +103,10 @@ def load():
     L.bsmm_query_plan.restype = st
     L.bsmm_set_override.argtypes = [ctypes.c_char_p, st]
     L.bsmm_set_override.restype = st
+    L.bsmm_set_streamk_grid.argtypes = [st]
+    L.bsmm_set_streamk_grid.restype = st
+    L.bsmm_mfma_probe.argtypes = [st, st, st, vp, vp]
+    L.bsmm_mfma_probe.restype = st
     L.bsmm_variant_names.restype = ctypes.c_char_p
     L.bsmm_status_string.argtypes = [st]
     L.bsmm_status_string.restype = ctypes.c_char_p
@@ -147,12 +151,18 @@ def _stream(stream):
     return torch.cuda.current_stream().cuda_stream
 
 
-_WS = {}
+_WS = {}          # workspace buffer per (device, stream handle)
 _WS_NEED = {}     # workspace bytes per (op, G, M, N, K, out dtype); cleared by the override
 
 
-def _workspace(op, G, M, N, K, out_dtype, device):
-    """Workspace for the fastest plan, cached per device (grow-only)."""
+def _workspace(op, G, M, N, K, out_dtype, device, stream, handle):
+    """Workspace for the fastest plan, cached per (device, stream) and grown
+    when a call needs more.  Calls on one stream run in order, so they may
+    share a buffer; calls on different streams get different buffers.  A
+    buffer is allocated while its stream is current, so the caching
+    allocator hands its memory to no other stream before the work queued on
+    that stream has finished, even once the buffer is replaced by a larger
+    one."""
     key = (op, G, M, N, K, out_dtype)
     need = _WS_NEED.get(key)
     if need is None:
@@ -160,10 +170,16 @@ def _workspace(op, G, M, N, K, out_dtype, device):
         _WS_NEED[key] = need
     if need == 0:
         return None, 0
-    buf = _WS.get(device)
+    wkey = (device, handle)
+    buf = _WS.get(wkey)
     if buf is None or buf.numel() < need:
-        buf = _torch().empty(need, dtype=_torch().uint8, device=device)
-        _WS[device] = buf
+        torch = _torch()
+        if stream is None:
+            buf = torch.empty(need, dtype=torch.uint8, device=device)
+        else:
+            with torch.cuda.stream(stream):
+                buf = torch.empty(need, dtype=torch.uint8, device=device)
+        _WS[wkey] = buf
     return buf, buf.numel()
 
 
@@ -207,11 +223,11 @@ def _out(out, shape, code, device):
     return out
 
 
-def _ws_args(workspace, op, G, M, N, K, code, device):
+def _ws_args(workspace, op, G, M, N, K, code, device, stream, handle):
     if workspace is False:
         return None, 0
     if workspace is None:
-        buf, n = _workspace(op, G, M, N, K, code, device)
+        buf, n = _workspace(op, G, M, N, K, code, device, stream, handle)
         return (buf.data_ptr() if buf is not None else None), n
     return workspace.data_ptr(), workspace.numel() * workspace.element_size()
 
@@ -259,12 +275,13 @@ def bsmm_int8_rowwise(a, b, scale_a=None, scale_b=None, *, out_dtype="bf16",
                 f"scale_b should be (1, {N}). Got scale_a.size()={tuple(scale_a.shape)} "
                 f"and scale_b.size()={tuple(scale_b.shape)}")
     o = _out(out, (M, N), code, a.device)
-    wsp, wsn = _ws_args(workspace, OP_INT8_ROWWISE, 1, M, N, K, code, a.device)
+    hs = _stream(stream)
+    wsp, wsn = _ws_args(workspace, OP_INT8_ROWWISE, 1, M, N, K, code, a.device, stream, hs)
     _check(load().bsmm_int8_rowwise(
         a.data_ptr(), a.stride(0), b.data_ptr(), b.stride(1),
         scale_a.data_ptr() if scale_a is not None else None, sa_m,
         scale_b.data_ptr() if scale_b is not None else None, sb_n,
-        o.data_ptr(), o.stride(0), code, M, N, K, wsp, wsn, _stream(stream)))
+        o.data_ptr(), o.stride(0), code, M, N, K, wsp, wsn, hs))
     return o
 
 
@@ -296,12 +313,13 @@ def bsmm_fp8_blockwise(a, b, scale_a, scale_b, *, out_dtype="bf16", out=None,
             f"({M}, {KB}) and scale_b should be ({KB}, {NB}). Got "
             f"scale_a.size()={tuple(scale_a.shape)} and scale_b.size()={tuple(scale_b.shape)}")
     o = _out(out, (M, N), code, a8.device)
-    wsp, wsn = _ws_args(workspace, OP_FP8_BLOCKWISE, 1, M, N, K, code, a8.device)
+    hs = _stream(stream)
+    wsp, wsn = _ws_args(workspace, OP_FP8_BLOCKWISE, 1, M, N, K, code, a8.device, stream, hs)
     _check(load().bsmm_fp8_blockwise(
         a8.data_ptr(), a8.stride(0), b8.data_ptr(), b8.stride(1),
         scale_a.data_ptr(), scale_a.stride(0), scale_a.stride(1),
         scale_b.data_ptr(), scale_b.stride(0), scale_b.stride(1),
-        o.data_ptr(), o.stride(0), code, M, N, K, wsp, wsn, _stream(stream)))
+        o.data_ptr(), o.stride(0), code, M, N, K, wsp, wsn, hs))
     return o
 
 
@@ -335,12 +353,13 @@ def bsmm_fp8_groupwise(a, b, scale_a, scale_b, *, out_dtype="bf16", out=None,
             f"should be ({M}, {KB}) and scale_b should be ({KB}, {N}). Got "
             f"scale_a.size()={tuple(scale_a.shape)} and scale_b.size()={tuple(scale_b.shape)}")
     o = _out(out, (M, N), code, a8.device)
-    wsp, wsn = _ws_args(workspace, OP_FP8_GROUPWISE, 1, M, N, K, code, a8.device)
+    hs = _stream(stream)
+    wsp, wsn = _ws_args(workspace, OP_FP8_GROUPWISE, 1, M, N, K, code, a8.device, stream, hs)
     _check(load().bsmm_fp8_groupwise(
         a8.data_ptr(), a8.stride(0), b8.data_ptr(), b8.stride(1),
         scale_a.data_ptr(), scale_a.stride(0), scale_a.stride(1),
         scale_b.data_ptr(), scale_b.stride(0), scale_b.stride(1),
-        o.data_ptr(), o.stride(0), code, M, N, K, wsp, wsn, _stream(stream)))
+        o.data_ptr(), o.stride(0), code, M, N, K, wsp, wsn, hs))
     return o
 
 
@@ -393,11 +412,12 @@ def bsmm_fp8_mx_bmm(x, w, x_scale, w_scale, *, layout="m_major", out_dtype="bf16
         o_sg, o_sm = o.stride(0), o.stride(1)
     if o.stride(2) != 1:
         raise ValueError("out must be contiguous along N")
-    wsp, wsn = _ws_args(workspace, OP_FP8_MX_BMM, G, M, N, K, code, x8.device)
+    hs = _stream(stream)
+    wsp, wsn = _ws_args(workspace, OP_FP8_MX_BMM, G, M, N, K, code, x8.device, stream, hs)
     _check(load().bsmm_fp8_mx_bmm(
         x8.data_ptr(), x_sg, x_sm, w8.data_ptr(), w8.stride(0), w8.stride(1),
         xs8.data_ptr(), xs_sg, xs_sm, ws8.data_ptr(), ws8.stride(0), ws8.stride(1),
-        o.data_ptr(), o_sg, o_sm, code, G, M, N, K, wsp, wsn, _stream(stream)))
+        o.data_ptr(), o_sg, o_sm, code, G, M, N, K, wsp, wsn, hs))
     return o
 
 
@@ -450,11 +470,12 @@ def bsmm_fp8_scaled_mm(a, b, scale_a, scale_b, *, bias=None, scale_result=None,
         sr_ptr = scale_result.data_ptr()
     o = _out(out, (M, N), code, a8.device)
     o8 = o.view(torch.uint8) if code == E4M3 else o
-    wsp, wsn = _ws_args(workspace, OP_FP8_SCALED_MM, 1, M, N, K, code, a8.device)
+    hs = _stream(stream)
+    wsp, wsn = _ws_args(workspace, OP_FP8_SCALED_MM, 1, M, N, K, code, a8.device, stream, hs)
     _check(load().bsmm_fp8_scaled_mm(
         a8.data_ptr(), a8.stride(0), b8.data_ptr(), b8.stride(1),
         scale_a.data_ptr(), sa_m, scale_b.data_ptr(), sb_n, bias_ptr, bias_code, sr_ptr,
-        o8.data_ptr(), o.stride(0), code, M, N, K, wsp, wsn, _stream(stream)))
+        o8.data_ptr(), o.stride(0), code, M, N, K, wsp, wsn, hs))
     return o
 
 
@@ -486,11 +507,12 @@ def bsmm_fp8_mx32_mm(a, b, a_scale, b_scale, *, out_dtype="bf16", out=None, work
     if KC and (sa8.stride(1) != 1 or sb8.stride(1) != 1):
         raise ValueError("scale rows must be contiguous")
     o = _out(out, (M, N), code, a8.device)
-    wsp, wsn = _ws_args(workspace, OP_FP8_MX32_MM, 1, M, N, K, code, a8.device)
+    hs = _stream(stream)
+    wsp, wsn = _ws_args(workspace, OP_FP8_MX32_MM, 1, M, N, K, code, a8.device, stream, hs)
     _check(load().bsmm_fp8_mx32_mm(
         a8.data_ptr(), a8.stride(0), b8.data_ptr(), b8.stride(1),
         sa8.data_ptr(), sa8.stride(0), sb8.data_ptr(), sb8.stride(0),
-        o.data_ptr(), o.stride(0), code, M, N, K, wsp, wsn, _stream(stream)))
+        o.data_ptr(), o.stride(0), code, M, N, K, wsp, wsn, hs))
     return o
 
 
@@ -714,6 +736,26 @@ def bsmm_query_plan(op, G, M, N, K, out_dtype, workspace_bytes=2**62):
 def bsmm_set_override(variant=None, split_k=0):
     _WS_NEED.clear()              # the plans, and so their workspace, change
     _check(load().bsmm_set_override(variant.encode() if variant else None, split_k))
+
+
+def bsmm_set_streamk_grid(workgroups=0):
+    """Grid of the stream-K kernels for the following calls (0: as many
+    workgroups as the device holds at once; tests and tuning)."""
+    _WS_NEED.clear()
+    _check(load().bsmm_set_streamk_grid(int(workgroups)))
+
+
+def bsmm_mfma_probe(kind, workgroups, iters, out, stream=None):
+    """Matrix-core throughput probe (kind 0: fp8 16x16x128, 1: int8
+    16x16x64, 2: int8 32x32x32); out: fp32 device tensor of workgroups * 256
+    elements.
+    Returns the number of flops (ops) the launch performs."""
+    if out.numel() < workgroups * 256:
+        raise ValueError("out holds fewer than workgroups * 256 floats")
+    _check(load().bsmm_mfma_probe(int(kind), int(workgroups), int(iters), out.data_ptr(),
+                                  _stream(stream)))
+    per = 32768 if kind == 1 else 65536
+    return float(workgroups) * 4 * iters * 8 * per
 
 
 def bsmm_timing_enable(enable=True):

@@ -28,11 +28,17 @@ bsmm_status fail(bsmm_status s, const char* fmt, ...) {
 }
 
 // ---- override (tests / tuning) and logging --------------------------------
+// The environment is read once; after that the planning path takes no lock
+// unless a variant or split is forced: `active` says whether one is, and
+// `gen` changes on every setter call so that cached plans made under an
+// earlier setting are not reused.
 struct Override {
-  std::mutex mu;
+  std::mutex mu;                    // guards `variant` and `split`
   std::string variant;
   int split = 0;
-  bool env_read = false;
+  std::atomic<int> active{0};       // a variant or split is forced
+  std::atomic<unsigned> gen{1};     // bumped by every setter call
+  std::atomic<int> sk_grid{0};      // stream-K grid (0: co-resident capacity)
   int log = 0;
   int tail_split_cap = 0;          // BSMM_TAIL_SPLIT: cap on the tail launch's K slices
   std::string tail_variant;        // BSMM_TAIL_VARIANT: kernel of the tail launch
@@ -42,19 +48,48 @@ Override& ovr() {
   return o;
 }
 void read_env_once() {
-  Override& o = ovr();
-  std::lock_guard<std::mutex> g(o.mu);
-  if (o.env_read) return;
-  o.env_read = true;
-  if (const char* v = getenv("BSMM_FORCE_VARIANT")) o.variant = v;
-  if (const char* v = getenv("BSMM_FORCE_SPLITK")) o.split = atoi(v);
-  if (const char* v = getenv("BSMM_LOG")) o.log = atoi(v);
-  if (const char* v = getenv("BSMM_TAIL_SPLIT")) o.tail_split_cap = atoi(v);
-  if (const char* v = getenv("BSMM_TAIL_VARIANT")) o.tail_variant = v;
+  static std::once_flag once;
+  std::call_once(once, [] {
+    Override& o = ovr();
+    std::lock_guard<std::mutex> g(o.mu);
+    if (const char* v = getenv("BSMM_FORCE_VARIANT")) o.variant = v;
+    if (const char* v = getenv("BSMM_FORCE_SPLITK")) o.split = atoi(v);
+    if (const char* v = getenv("BSMM_LOG")) o.log = atoi(v);
+    if (const char* v = getenv("BSMM_TAIL_SPLIT")) o.tail_split_cap = atoi(v);
+    if (const char* v = getenv("BSMM_TAIL_VARIANT")) o.tail_variant = v;
+    o.active.store(!o.variant.empty() || o.split > 0, std::memory_order_release);
+  });
+}
+
+// Per-thread cache of recent plans, keyed by the problem, the workspace
+// size and the override generation: a repeated call (a decode loop) skips
+// the table search and the heuristic.  Direct-mapped, no allocation.
+struct PlanKey {
+  int op, dt, G, M, N, K;
+  size_t ws;
+  unsigned gen;
+  bool operator==(const PlanKey& o) const {
+    return op == o.op && dt == o.dt && G == o.G && M == o.M && N == o.N && K == o.K &&
+           ws == o.ws && gen == o.gen;
+  }
+};
+struct PlanSlot {
+  PlanKey key{-1, -1, 0, 0, 0, 0, 0, 0};
+  Plan plan;
+};
+constexpr int kPlanCache = 16;
+thread_local PlanSlot t_plans[kPlanCache];
+unsigned plan_hash(const PlanKey& k) {
+  uint64_t h = (uint64_t)k.op * 0x9E3779B97F4A7C15ull;
+  for (uint64_t v : {(uint64_t)k.dt, (uint64_t)k.G, (uint64_t)k.M, (uint64_t)k.N,
+                     (uint64_t)k.K, (uint64_t)k.ws})
+    h = (h ^ v) * 0x100000001B3ull;
+  return (unsigned)(h >> 32) % kPlanCache;
 }
 
 constexpr int64_t kMaxDim = (int64_t)1 << 31;
 constexpr int64_t kMaxLd = (int64_t)1 << 23;    // 256 rows * ld + K < 2^32
+constexpr int64_t kMaxInt8K = 130944;           // largest multiple of 128 below 2^31 / 2^14
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -91,7 +126,7 @@ static size_t ws_bytes(int G, int rows, int N, int split) {
 
 size_t persistent_workspace(const Variant* v, bsmm_op op) {
   (void)op;   // int32 and fp32 partials are both 4 bytes
-  return (size_t)kPlanCUs * v->wg_per_cu * ((size_t)v->tile_m * v->tile_n * 4u + 8u);
+  return (size_t)kPlanCUs * v->wg_per_cu * 2 * ((size_t)v->tile_m * v->tile_n * 4u + 8u);
 }
 
 static bool plan_packed(const Plan& pl, bsmm_op op) {
@@ -150,9 +185,26 @@ static void fit_workspace(Plan& pl, bsmm_op op, int G, int M, int N, int K, bsmm
 //     at least 8192 rows (the break-even the aiter PR's dispatch uses);
 //  3  override.
 // A plan whose workspace exceeds workspace_bytes falls back to split 1.
+static Plan make_plan_uncached(bsmm_op op, int G, int M, int N, int K, bsmm_dtype dt,
+                               size_t workspace_bytes);
+
 Plan make_plan(bsmm_op op, int G, int M, int N, int K, bsmm_dtype dt,
                size_t workspace_bytes) {
   read_env_once();
+  Override& o = ovr();
+  if (o.active.load(std::memory_order_acquire))
+    return make_plan_uncached(op, G, M, N, K, dt, workspace_bytes);
+  const PlanKey key{(int)op, (int)dt, G, M, N, K, workspace_bytes,
+                    o.gen.load(std::memory_order_acquire)};
+  PlanSlot& slot = t_plans[plan_hash(key)];
+  if (slot.key == key) return slot.plan;
+  slot.plan = make_plan_uncached(op, G, M, N, K, dt, workspace_bytes);
+  slot.key = key;
+  return slot.plan;
+}
+
+static Plan make_plan_uncached(bsmm_op op, int G, int M, int N, int K, bsmm_dtype dt,
+                               size_t workspace_bytes) {
   Plan pl;
   const int KB = K / kBlockK;
   {
@@ -314,6 +366,7 @@ static bsmm_status run(const Problem& p, size_t workspace_bytes, void* ws,
   l.stream = stream;
   l.ws = ws;
   l.ws_bytes = ws ? workspace_bytes : 0;
+  l.sk_grid = ovr().sk_grid.load(std::memory_order_relaxed);
   if (plan_packed(pl, p.op) && p.K >= kBlockK) {
     const size_t pack = packed_scale_bytes(p.op, p.G, p.M, p.K, p.N);
     if (!ws || l.ws_bytes < pack) return fail(BSMM_ERR_ARG, "workspace too small for the plan");
@@ -362,7 +415,9 @@ bsmm_status bsmm_int8_rowwise(const int8_t* a, int64_t lda, const int8_t* b,
         BSMM_ERR_DTYPE, "unknown output dtype %d", (int)out_dtype);
   if (M == 0 || N == 0) return BSMM_OK;
   CHECK(K % kBlockK == 0, BSMM_ERR_UNSUPPORTED, "K=%lld is not a multiple of 128", (long long)K);
-  CHECK(K <= 133144, BSMM_ERR_UNSUPPORTED, "K=%lld may overflow the int32 accumulator", (long long)K);
+  // any int8 code, -128 included: |acc| <= K * 128^2 = K * 2^14 < 2^31
+  CHECK(K <= kMaxInt8K, BSMM_ERR_UNSUPPORTED,
+        "K=%lld may overflow the int32 accumulator (K * 2^14 >= 2^31)", (long long)K);
   CHECK(out != nullptr, BSMM_ERR_NULL, "out is NULL");
   CHECK(K == 0 || (a != nullptr && b != nullptr), BSMM_ERR_NULL, "a or b is NULL");
   if (out_dtype != BSMM_I32) {
@@ -580,6 +635,14 @@ bsmm_status bsmm_set_override(const char* variant, int split_k) {
   std::lock_guard<std::mutex> g(o.mu);
   o.variant = variant ? variant : "";
   o.split = split_k > 0 ? split_k : 0;
+  o.active.store(!o.variant.empty() || o.split > 0, std::memory_order_release);
+  o.gen.fetch_add(1, std::memory_order_acq_rel);
+  return BSMM_OK;
+}
+
+bsmm_status bsmm_set_streamk_grid(int workgroups) {
+  CHECK(workgroups >= 0, BSMM_ERR_ARG, "negative stream-K grid %d", workgroups);
+  ovr().sk_grid.store(workgroups, std::memory_order_release);
   return BSMM_OK;
 }
 

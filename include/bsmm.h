@@ -99,7 +99,9 @@ typedef enum {
  * out_dtype BSMM_I32 stores acc itself; the scales are then ignored and may
  * be NULL.  A scale stride of 0 broadcasts one scalar (tensorwise scaling).
  * a, b: int8.  scale_a, scale_b: fp32.  out: int32 / fp32 / bf16.
- * |acc| must stay below 2^31 (guaranteed for K * 127^2 < 2^31, K <= 133144).
+ * Any int8 code is accepted (-128 included), so |acc| <= K * 2^14; K above
+ * 130944 (the largest multiple of 128 with K * 2^14 < 2^31) is rejected with
+ * BSMM_ERR_UNSUPPORTED.
  */
 bsmm_status bsmm_int8_rowwise(const int8_t* a, int64_t lda,
                               const int8_t* b, int64_t ldb,
@@ -426,6 +428,34 @@ bsmm_status bsmm_query_plan(bsmm_op op, int64_t G, int64_t M, int64_t N,
  * slices and BSMM_TAIL_VARIANT names its kernel (tuning only).
  */
 bsmm_status bsmm_set_override(const char* variant, int split_k);
+
+/*
+ * Grid of the stream-K kernels (variants whose name contains "sk") for
+ * subsequent calls in this process (tests and tuning).  0, the default, uses
+ * as many workgroups as the device holds at once; any other count is also
+ * correct, since no workgroup of that kernel waits for another: a tile split
+ * over several workgroups is added up, in K order, by the last of them to
+ * finish its part.  The count is further capped by the workspace (two
+ * BM x BN partial tiles and 16 bytes per workgroup) and by the work.
+ * Returns BSMM_ERR_ARG for a negative count.
+ */
+bsmm_status bsmm_set_streamk_grid(int workgroups);
+
+/*
+ * Matrix-core throughput probe (a measurement aid for the roofline; it
+ * computes nothing of use).  Launches `workgroups` workgroups of four waves;
+ * every wave issues `iters` x 8 independent matrix instructions on register
+ * operands with no memory traffic in between: kind 0 the fp8 E4M3
+ * 16 x 16 x 128 instruction with unit e8m0 scales (65536 flops each), kind 1
+ * the int8 16 x 16 x 64 one (32768 ops each), kind 2 the int8 32 x 32 x 32
+ * one (65536 ops each).  Timing the launch gives the
+ * rate the matrix cores sustain at the clock the device holds under that
+ * load.  out: device buffer of workgroups * 256 floats (one per thread, so
+ * the work is not optimised away).  Returns BSMM_ERR_ARG for a kind outside
+ * 0..2 or a
+ * non-positive count, BSMM_ERR_NULL for a NULL out.
+ */
+bsmm_status bsmm_mfma_probe(int kind, int workgroups, int iters, float* out, void* stream);
 
 /*
  * Kernel timing for benchmarks.  While enabled (enable != 0), the main launch

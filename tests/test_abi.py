@@ -69,6 +69,10 @@ def mx(*, x=P, x_sg=512, x_sm=4096, w=P, w_sg=1 << 20, w_sn=512, xs=P, xs_sg=4,
 @pytest.mark.parametrize("kw,status", [
     (dict(M=-1), SHAPE), (dict(N=-5), SHAPE), (dict(K=-128), SHAPE),
     (dict(K=200), UNSUP), (dict(K=2**31), UNSUP), (dict(K=133248, lda=133248, ldb=133248), UNSUP),
+    # int8 codes include -128: K * 2^14 must stay below 2^31, so 130944 is the
+    # largest K (passes the size check and fails on the NULL output instead)
+    (dict(K=131072, lda=131072, ldb=131072), UNSUP),
+    (dict(K=130944, lda=130944, ldb=130944, out=None), NULL),
     (dict(dt=7), DTYPE),
     (dict(out=None), NULL), (dict(a=None), NULL), (dict(sa=None), NULL),
     (dict(sa_m=-1), SCALE), (dict(sb_n=-2), SCALE),
