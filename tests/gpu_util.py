@@ -122,3 +122,31 @@ def check_mx(p, out_dtype, y, rows=None, groups=None):
     rep = S.compare(got, ref)
     assert rep["ok"], rep
     return rep
+
+
+# ------------------------------------------------ fp32 accumulation bound --
+
+def gamma_fp32(KB, adds=8):
+    """Bound on |Y32 - C| / Bd for the fp8 kernels' binary32 result Y32 over
+    KB blocks of 128 K (Bd = sum_k |a_deq| |b_deq|).
+
+    Per block, the matrix instruction's partial.  Measured on gfx950 (see
+    test_gpu_mfma_numerics.py): the instruction adds each group of 16
+    products (in its own K order) with additions that drop the bits of the
+    smaller operand below 2**-13 of the larger operand's binade (a term
+    beside 448 keeps only whole multiples of 2**-5), and combines the group
+    sums without that loss.  A group's 15 additions then lose less than
+    15 * 2**-13 of the group's magnitude sum, and a block less than 2**-9 of
+    its share of Bd.  Then per block: the binary32 scale product (2**-24,
+    blockwise) and one rounded multiply-add or accumulation into a running
+    sum that never exceeds Bd (2**-24).  ``adds`` more roundings cover the
+    split-K / stream-K partial sums.  Valid while every scale product and
+    partial stays in the binary32 normal range."""
+    return 2.0**-9 + (KB + adds + 2) * 2.0**-24
+
+
+def check_within(y_np, res, KB, adds=8):
+    """The tight rule on an oracle Result (fp32 or bf16 bits)."""
+    rep = S.compare_within(y_np, res, gamma_fp32(KB, adds))
+    assert rep["ok"], rep
+    return rep

@@ -233,13 +233,13 @@ def test_streamk_many_segments(variant):
 
 
 def test_streamk_small_workspace_two_way_splits():
-    """A workspace that holds three slots: three workgroups, tiles split in
-    two.  Results match the oracle and repeat bit for bit."""
+    """A workspace that holds three workgroups' slots: three workgroups,
+    tiles split in two.  Results match the oracle and repeat bit for bit."""
     q = fp8_blockwise_inputs(520, 512, 1280, 504)
     a, b = dev(q["a"]), dev(q["b_nk"]).t()
     sa, sb = dev(q["scale_a"]), dev(q["scale_b"])
-    ws = torch.empty(3 * (256 * 256 * 4 + 8), dtype=torch.uint8, device=DEV)
-    say("stream-K 3-slot workspace")
+    ws = torch.empty(3 * 2 * (256 * 256 * 4 + 8), dtype=torch.uint8, device=DEV)
+    say("stream-K 3-workgroup workspace")
     with Forced("t256x256sk", 0):
         y1 = bsmm.bsmm_fp8_blockwise(a, b, sa, sb, out_dtype="f32", workspace=ws)
         y2 = bsmm.bsmm_fp8_blockwise(a, b, sa, sb, out_dtype="f32", workspace=ws)
@@ -248,17 +248,17 @@ def test_streamk_small_workspace_two_way_splits():
 
 
 def test_streamk_data_parallel_rounds_then_split_tiles():
-    """A four-slot workspace over nine 256 x 256 tiles: one data-parallel
+    """A four-workgroup workspace over nine 256 x 256 tiles: one data-parallel
     round of four whole tiles, then the other five tiles' K blocks spread
     over the four workgroups (tiles split across two of them), for every
     operation, several mx batches included; repeatable bit for bit."""
     q = fp8_blockwise_inputs(600, 640, 1280, 505)
     p = int8_rowwise_inputs(600, 640, 1280, 506)
     r = fp8_mx_bmm_inputs(3, 300, 640, 1280, 507, layout="batch_first")
-    ws = torch.empty(4 * (256 * 256 * 4 + 8), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(4 * 2 * (256 * 256 * 4 + 8), dtype=torch.uint8, device=DEV)
     a, b = dev(q["a"]), dev(q["b_nk"]).t()
     sa, sb = dev(q["scale_a"]), dev(q["scale_b"])
-    say("stream-K data-parallel rounds + split tiles (4 slots)")
+    say("stream-K data-parallel rounds + split tiles (4 workgroups)")
     with Forced("t256x256sk", 0):
         y1 = bsmm.bsmm_fp8_blockwise(a, b, sa, sb, out_dtype="bf16", workspace=ws)
         y2 = bsmm.bsmm_fp8_blockwise(a, b, sa, sb, out_dtype="bf16", workspace=ws)
@@ -386,3 +386,51 @@ def test_skinny_forced_on_tall_m_falls_back():
         y = run_int8(p, "i32")
     assert plan["variant"] != "s16x16", plan
     check_int8(p, "i32", y)
+
+
+# ----------------------------------------- stream-K grids, two streams ----
+
+@pytest.mark.parametrize("grid", [0, 5, 600])
+def test_int8_streamk_any_grid_exact(grid):
+    """The int8 stream-K kernel (the dispatcher's choice for the 8192 x 4096
+    x 4096 linear) at its default grid, at 5 workgroups and at 600, more
+    than the device holds at once: split tiles are added up by the last of
+    their segments to finish, so the int32 accumulators are bit-exact
+    whatever the grid."""
+    p = int8_rowwise_inputs(1024, 1024, 4096, 510)
+    a, b = dev(p["a"]), dev(p["b_nk"]).t()
+    sa, sb = dev(p["scale_a"]).reshape(-1, 1), dev(p["scale_b"]).reshape(1, -1)
+    ws = torch.empty(600 * 2 * (256 * 256 * 4 + 8), dtype=torch.uint8, device=DEV)
+    say(f"int8 stream-K grid {grid}")
+    bsmm.bsmm_set_streamk_grid(grid)
+    try:
+        with Forced("t256x256skp", 0):
+            yi = bsmm.bsmm_int8_rowwise(a, b, out_dtype="i32", workspace=ws)
+            yb = bsmm.bsmm_int8_rowwise(a, b, sa, sb, out_dtype="bf16", workspace=ws)
+    finally:
+        bsmm.bsmm_set_streamk_grid(0)
+    rows = np.r_[0:16, 500:520, 1000:1024]
+    check_int8(p, "i32", yi, rows=rows)
+    check_int8(p, "bf16", yb, rows=rows)
+
+
+def test_two_streams_get_their_own_workspace():
+    """Two split-K calls of the same shape queued on two streams at once:
+    the binding gives each stream its own cached workspace, so their
+    partial sums do not mix."""
+    M, N, K = 256, 512, 4096
+    plan = bsmm.bsmm_query_plan(bsmm.OP_FP8_BLOCKWISE, 1, M, N, K, "f32")
+    assert plan["split_k"] > 1 and plan["workspace"] > 0, plan
+    ps = [fp8_blockwise_inputs(M, N, K, 530 + i) for i in range(2)]
+    ins = [(dev(q["a"]), dev(q["b_nk"]).t(), dev(q["scale_a"]), dev(q["scale_b"])) for q in ps]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    say("two streams, one shape, split-K")
+    outs = [[], []]
+    for _ in range(4):
+        for i, s in enumerate(streams):
+            outs[i].append(bsmm.bsmm_fp8_blockwise(*ins[i], out_dtype="f32", stream=s))
+    torch.cuda.synchronize()
+    for i, q in enumerate(ps):
+        for y in outs[i]:
+            check_blockwise(q, "f32", y)
