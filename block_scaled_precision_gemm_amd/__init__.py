@@ -15,7 +15,8 @@ import os
 
 __all__ = [
     "load", "lib_path", "BsmmError",
-    "bsmm_int8_rowwise", "bsmm_fp8_blockwise", "bsmm_fp8_mx_bmm", "bsmm_fp8_scaled_mm",
+    "bsmm_int8_rowwise", "bsmm_fp8_blockwise", "bsmm_fp8_blockwise_scratch",
+    "bsmm_fp8_mx_bmm", "bsmm_fp8_scaled_mm",
     "bsmm_fp8_mx32_mm", "OP_FP8_MX32_MM", "bsmm_fp8_groupwise", "OP_FP8_GROUPWISE",
     "bsmm_quant_int8_rowwise", "bsmm_quant_fp8_blockwise", "bsmm_quant_fp8_mx",
     "bsmm_quant_fp8_columns", "bsmm_quant_fp8_weight", "bsmm_quant_fp8_blockwise_columns",
@@ -76,6 +77,8 @@ def load():
                                      vp, i64, st, i64, i64, i64, vp, sz, vp]
     L.bsmm_fp8_groupwise.argtypes = [vp, i64, vp, i64, vp, i64, i64, vp, i64, i64,
                                      vp, i64, st, i64, i64, i64, vp, sz, vp]
+    L.bsmm_fp8_blockwise_scratch.argtypes = [vp, i64, vp, i64, vp, i64, i64, vp, i64, i64,
+                                             vp, i64, st, i64, i64, i64, vp]
     L.bsmm_fp8_mx_bmm.argtypes = [vp, i64, i64, vp, i64, i64, vp, i64, i64, vp, i64,
                                   i64, vp, i64, i64, st, i64, i64, i64, i64, vp, sz, vp]
     L.bsmm_fp8_scaled_mm.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, vp, st, vp,
@@ -91,7 +94,8 @@ def load():
                                         vp]
     L.bsmm_quant_fp8_blockwise_columns.argtypes = [vp, i64, st, vp, i64, vp, i64, i64, vp, i64,
                                                    vp, i64, i64, i64, i64, vp]
-    for f in ("bsmm_int8_rowwise", "bsmm_fp8_blockwise", "bsmm_fp8_mx_bmm", "bsmm_fp8_scaled_mm",
+    for f in ("bsmm_int8_rowwise", "bsmm_fp8_blockwise", "bsmm_fp8_blockwise_scratch",
+              "bsmm_fp8_mx_bmm", "bsmm_fp8_scaled_mm",
               "bsmm_fp8_mx32_mm",
               "bsmm_quant_int8_rowwise", "bsmm_quant_fp8_blockwise", "bsmm_quant_fp8_mx",
               "bsmm_quant_fp8_mx32", "bsmm_quant_fp8_columns", "bsmm_quant_fp8_weight",
@@ -320,6 +324,41 @@ def bsmm_fp8_blockwise(a, b, scale_a, scale_b, *, out_dtype="bf16", out=None,
         scale_a.data_ptr(), scale_a.stride(0), scale_a.stride(1),
         scale_b.data_ptr(), scale_b.stride(0), scale_b.stride(1),
         o.data_ptr(), o.stride(0), code, M, N, K, wsp, wsn, hs))
+    return o
+
+
+def bsmm_fp8_blockwise_scratch(a, b, scale_a, scale_b, *, out_dtype="bf16", out=None,
+                               stream=None):
+    """bsmm_fp8_blockwise with the library's static device scratch as its
+    workspace: the library allocates nothing (pass ``out`` to allocate
+    nothing here either).  Same arguments and results; problems whose plan
+    needs more than the scratch holds raise BsmmError (BSMM_ERR_UNSUPPORTED).
+    Calls that overlap on one GPU race on its scratch."""
+    torch = _torch()
+    code = _dtype_code(out_dtype)
+    a8, b8 = _bytes_view(a, "a"), _bytes_view(b, "b")
+    M, K = a8.shape
+    K2, N = b8.shape
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    if K and a8.stride(1) != 1:
+        raise ValueError(f"a must be row-major, got stride {a8.stride()}")
+    if K and b8.stride(0) != 1:
+        raise ValueError(f"b must be column-major, got stride {b8.stride()}")
+    KB, NB = -(-K // 128), -(-N // 128)
+    if scale_a.dtype != torch.float32 or scale_b.dtype != torch.float32:
+        raise ValueError("blockwise scales must be fp32")
+    if tuple(scale_a.shape) != (M, KB) or tuple(scale_b.shape) != (KB, NB):
+        raise ValueError(
+            "Invalid scaling configuration. For blockwise scaling, scale_a should be "
+            f"({M}, {KB}) and scale_b should be ({KB}, {NB}). Got "
+            f"scale_a.size()={tuple(scale_a.shape)} and scale_b.size()={tuple(scale_b.shape)}")
+    o = _out(out, (M, N), code, a8.device)
+    _check(load().bsmm_fp8_blockwise_scratch(
+        a8.data_ptr(), a8.stride(0), b8.data_ptr(), b8.stride(1),
+        scale_a.data_ptr(), scale_a.stride(0), scale_a.stride(1),
+        scale_b.data_ptr(), scale_b.stride(0), scale_b.stride(1),
+        o.data_ptr(), o.stride(0), code, M, N, K, _stream(stream)))
     return o
 
 

@@ -65,7 +65,7 @@ def build(verbose: bool = False) -> str:
         jobs.append([hipcc, *COMMON, *HIP_FLAGS, f"-DBSMM_TU_OP={op}",
                      f"-DBSMM_TU_OUT={out}", "-x", "hip", "-c",
                      os.path.join(CSRC, HIP_SOURCE), "-o", o])
-    for src in ("bsmm_pack.hip", "bsmm_quant.hip", "bsmm_probe.hip"):
+    for src in ("bsmm_pack.hip", "bsmm_quant.hip", "bsmm_probe.hip", "bsmm_scratch.hip"):
         o = os.path.join(OBJDIR, src.replace(".hip", ".o"))
         jobs.append([hipcc, *COMMON, *HIP_FLAGS, "-x", "hip", "-c",
                      os.path.join(CSRC, src), "-o", o])

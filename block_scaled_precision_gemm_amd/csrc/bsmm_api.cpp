@@ -497,6 +497,30 @@ bsmm_status bsmm_fp8_blockwise(const uint8_t* a, int64_t lda, const uint8_t* b,
   return run(p, workspace ? workspace_bytes : 0, workspace, stream);
 }
 
+bsmm_status bsmm_fp8_blockwise_scratch(const uint8_t* a, int64_t lda, const uint8_t* b,
+                                       int64_t ldb, const float* scale_a, int64_t sa_m,
+                                       int64_t sa_kb, const float* scale_b, int64_t sb_kb,
+                                       int64_t sb_nb, void* out, int64_t ldo,
+                                       bsmm_dtype out_dtype, int64_t M, int64_t N, int64_t K,
+                                       void* stream) {
+  // the workspace the fastest plan wants (0 for sizes the entry point
+  // rejects or that launch nothing, which bsmm_fp8_blockwise then handles)
+  const size_t need = bsmm_workspace_bytes(BSMM_OP_FP8_BLOCKWISE, 1, M, N, K, out_dtype);
+  CHECK(need <= kScratchBytes, BSMM_ERR_UNSUPPORTED,
+        "M=%lld N=%lld K=%lld needs %zu bytes of workspace; the static scratch holds %zu "
+        "(use bsmm_fp8_blockwise with a workspace)",
+        (long long)M, (long long)N, (long long)K, need, kScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    int err = 0;
+    ws = scratch_device_ptr(&err);
+    CHECK(ws != nullptr, BSMM_ERR_HIP, "the static scratch's device address is unavailable "
+          "(hipGetSymbolAddress: error %d)", err);
+  }
+  return bsmm_fp8_blockwise(a, lda, b, ldb, scale_a, sa_m, sa_kb, scale_b, sb_kb, sb_nb, out,
+                            ldo, out_dtype, M, N, K, ws, need, stream);
+}
+
 bsmm_status bsmm_fp8_groupwise(const uint8_t* a, int64_t lda, const uint8_t* b,
                                int64_t ldb, const float* scale_a, int64_t sa_m,
                                int64_t sa_kb, const float* scale_b, int64_t sb_kb,

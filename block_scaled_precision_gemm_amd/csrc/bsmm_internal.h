@@ -172,6 +172,12 @@ struct QuantArgs {
 };
 int launch_quant(const QuantArgs& a, void* stream);
 
+// The static device scratch of the allocation-free entry point
+// (bsmm_scratch.hip): its size, and the current device's copy's address
+// (null, with *err the HIP error, on failure).
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+void* scratch_device_ptr(int* err);
+
 // Plan selection (host only).
 Plan make_plan(bsmm_op op, int G, int M, int N, int K, bsmm_dtype dt,
                size_t workspace_bytes);

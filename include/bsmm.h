@@ -137,6 +137,30 @@ bsmm_status bsmm_fp8_blockwise(const uint8_t* a, int64_t lda,
                                void* stream);
 
 /*
+ * bsmm_fp8_blockwise without a workspace argument and without allocating:
+ * for callers that cannot allocate device memory (code under stream
+ * capture, tight serving loops, harnesses that forbid allocation).  The
+ * caller passes inputs and outputs as for bsmm_fp8_blockwise; the plan's
+ * packed scales and split-K partials live in the library's static device
+ * scratch, a 64 MiB array that every GPU the library runs on holds until
+ * the process ends.  The call runs the plan bsmm_fp8_blockwise runs with a
+ * workspace of bsmm_workspace_bytes(BSMM_OP_FP8_BLOCKWISE, 1, M, N, K,
+ * out_dtype) bytes, and gives bit-identical results.  A problem whose plan
+ * needs more than 64 MiB is rejected with BSMM_ERR_UNSUPPORTED before
+ * anything is enqueued (its message gives the size).  All calls on one GPU
+ * share that GPU's scratch: calls that overlap on one GPU (different
+ * streams, or host threads without ordering) race.  Other errors as for
+ * bsmm_fp8_blockwise; BSMM_ERR_HIP if the scratch's device address cannot
+ * be obtained.  It needs no clearing: every call writes what it reads.
+ */
+bsmm_status bsmm_fp8_blockwise_scratch(const uint8_t* a, int64_t lda,
+                                       const uint8_t* b, int64_t ldb,
+                                       const float* scale_a, int64_t sa_m, int64_t sa_kb,
+                                       const float* scale_b, int64_t sb_kb, int64_t sb_nb,
+                                       void* out, int64_t ldo, bsmm_dtype out_dtype,
+                                       int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
  * fp8 E4M3FN x E4M3FN with fp32 scales per (row of A, 128-long K block) and
  * per (column of B, 128-long K block): 1 x 128 groups on both operands.
  *

@@ -58,6 +58,30 @@ def bw(*, a=P, lda=256, b=P, ldb=256, sa=P, sa_m=2, sa_kb=1, sb=P, sb_kb=1, sb_n
                                 out, ldo, dt, M, N, K, None, 0, None)
 
 
+def bws(*, a=P, lda=256, b=P, ldb=256, sa=P, sa_m=2, sa_kb=1, sb=P, sb_kb=1, sb_nb=2,
+        out=P, ldo=256, dt=bsmm.BF16, M=64, N=256, K=256):
+    L = bsmm.load()
+    return L.bsmm_fp8_blockwise_scratch(a, lda, b, ldb, sa, sa_m, sa_kb, sb, sb_kb, sb_nb,
+                                        out, ldo, dt, M, N, K, None)
+
+
+def test_blockwise_scratch_rejects_like_blockwise_and_beyond_the_scratch():
+    """The allocation-free entry validates as bsmm_fp8_blockwise does, and
+    rejects a problem whose plan wants more than the 64 MiB static scratch
+    (2048 x 3840 x 8192: 120 tiles, split K 3, 90.5 MiB of partials) before
+    any HIP call, naming the size."""
+    for kw, status in ((dict(dt=bsmm.I32), DTYPE), (dict(N=200, ldo=256), UNSUP),
+                       (dict(sa=None), NULL), (dict(ldb=255), SHAPE), (dict(b=P + 4), ALIGN)):
+        assert bws(**kw) == status == bw(**kw)
+    assert bws(M=0) == OK
+    need = bsmm.bsmm_workspace_bytes(bsmm.OP_FP8_BLOCKWISE, 1, 2048, 3840, 8192, bsmm.BF16)
+    assert need > 64 << 20
+    st = bws(M=2048, N=3840, K=8192, lda=8192, ldb=8192, ldo=3840, sa_m=64, sb_nb=64)
+    assert st == UNSUP
+    msg = bsmm.load().bsmm_last_error().decode()
+    assert str(need) in msg and str(64 << 20) in msg
+
+
 def mx(*, x=P, x_sg=512, x_sm=4096, w=P, w_sg=1 << 20, w_sn=512, xs=P, xs_sg=4,
        xs_sm=32, ws=P, ws_sg=64, ws_snb=4, out=P, o_sg=256, o_sm=2048,
        dt=bsmm.BF16, G=8, M=16, N=256, K=512):
