@@ -520,7 +520,7 @@ def mfma_peak(args):
     out = torch.empty(wgs * 256, dtype=torch.float32, device="cuda:0")
     stream = torch.cuda.current_stream()
     res = {}
-    for kind, label in ((0, "fp8"), (1, "int8"), (2, "int8_32x32x32")):
+    for kind, label in ((0, "fp8"), (1, "int8"), (2, "int8_32x32x32"), (3, "fp8_32x32x64")):
         iters = 20000
         t_settle = time.perf_counter()
         while time.perf_counter() - t_settle < args.settle:
@@ -535,9 +535,9 @@ def mfma_peak(args):
         torch.cuda.synchronize()
         ms = sorted(s0.elapsed_time(e0) for s0, e0 in ev)
         med = ms[len(ms) // 2]
-        pk = PEAK["fp8" if kind == 0 else "int8"]
+        pk = PEAK["fp8" if kind in (0, 3) else "int8"]
         res[label] = {"achieved": flops / (med * 1e-3) / 1e12, "peak": pk / 1e12,
-                      "unit": "TFLOP/s" if kind == 0 else "TOP/s",
+                      "unit": "TFLOP/s" if kind in (0, 3) else "TOP/s",
                       "frac_of_spec": flops / (med * 1e-3) / pk,
                       "launch_ms_median": med, "launch_ms_min": ms[0], "launches": len(ms),
                       "workgroups": wgs, "instructions_per_wave": iters * 8}

@@ -786,14 +786,14 @@ def bsmm_set_streamk_grid(workgroups=0):
 
 def bsmm_mfma_probe(kind, workgroups, iters, out, stream=None):
     """Matrix-core throughput probe (kind 0: fp8 16x16x128, 1: int8
-    16x16x64, 2: int8 32x32x32); out: fp32 device tensor of workgroups * 256
-    elements.
+    16x16x64, 2: int8 32x32x32, 3: fp8 32x32x64); out: fp32 device tensor of
+    workgroups * 256 elements.
     Returns the number of flops (ops) the launch performs."""
     if out.numel() < workgroups * 256:
         raise ValueError("out holds fewer than workgroups * 256 floats")
     _check(load().bsmm_mfma_probe(int(kind), int(workgroups), int(iters), out.data_ptr(),
                                   _stream(stream)))
-    per = 32768 if kind == 1 else 65536
+    per = {0: 65536, 1: 32768, 2: 65536, 3: 131072}[kind]
     return float(workgroups) * 4 * iters * 8 * per
 
 

@@ -2,9 +2,10 @@
 // of any matmul.  Every wave issues chains of independent matrix
 // instructions on register operands (no memory traffic in the loop), so the
 // launch runs at the rate the matrix cores sustain on this device, at the
-// clock it holds under that load.  Three instructions: those of the
+// clock it holds under that load.  Four instructions: those of the
 // library's K loops, the fp8 16 x 16 x 128 instruction with unit e8m0 scales
-// and the int8 16 x 16 x 64 one, and the int8 32 x 32 x 32 one.
+// and the int8 16 x 16 x 64 one, and their 32 x 32 forms (int8 32 x 32 x 32,
+// fp8 32 x 32 x 64).
 
 #include <hip/hip_runtime.h>
 
@@ -19,6 +20,7 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kChains = 8;   // independent accumulators per wave
 
@@ -44,6 +46,7 @@ __global__ void __launch_bounds__(256) mfma_probe_kernel(int iters, float* out) 
   f32x4 acc[kChains];
   i32x4 iacc[kChains];
   i32x16 wacc[KIND == 2 ? kChains : 1];
+  f32x16 facc[KIND == 3 ? kChains : 1];
 #pragma unroll
   for (int t = 0; t < kChains; ++t) {
     acc[t] = f32x4{0, 0, 0, 0};
@@ -53,6 +56,10 @@ __global__ void __launch_bounds__(256) mfma_probe_kernel(int iters, float* out) 
   for (int t = 0; t < (KIND == 2 ? kChains : 1); ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) wacc[t][r] = 0;
+#pragma unroll
+  for (int t = 0; t < (KIND == 3 ? kChains : 1); ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) facc[t][r] = 0.f;
   for (int i = 0; i < iters; ++i) {
 #pragma unroll
     for (int t = 0; t < kChains; ++t) {
@@ -63,10 +70,13 @@ __global__ void __launch_bounds__(256) mfma_probe_kernel(int iters, float* out) 
         iacc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(i32x4{a[0], a[1], a[2], a[3]},
                                                         i32x4{b[0], b[1], b[2], b[3]},
                                                         iacc[t], 0, 0, 0);
-      } else {
+      } else if constexpr (KIND == 2) {
         wacc[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(i32x4{a[0], a[1], a[2], a[3]},
                                                         i32x4{b[0], b[1], b[2], b[3]},
                                                         wacc[t], 0, 0, 0);
+      } else {
+        facc[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, facc[t], 0, 0, 0, 127,
+                                                                  0, 127);
       }
     }
   }
@@ -80,6 +90,11 @@ __global__ void __launch_bounds__(256) mfma_probe_kernel(int iters, float* out) 
     for (int t = 0; t < kChains; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s += (float)wacc[t][r];
+  if constexpr (KIND == 3)
+#pragma unroll
+    for (int t = 0; t < kChains; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s += facc[t][r];
   out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
@@ -88,7 +103,7 @@ __global__ void __launch_bounds__(256) mfma_probe_kernel(int iters, float* out) 
 
 extern "C" bsmm_status bsmm_mfma_probe(int kind, int workgroups, int iters, float* out,
                                        void* stream) {
-  if (kind < 0 || kind > 2 || workgroups <= 0 || iters <= 0) return BSMM_ERR_ARG;
+  if (kind < 0 || kind > 3 || workgroups <= 0 || iters <= 0) return BSMM_ERR_ARG;
   if (out == nullptr) return BSMM_ERR_NULL;
   hipStream_t s = (hipStream_t)stream;
   if (kind == 0)
@@ -97,8 +112,11 @@ extern "C" bsmm_status bsmm_mfma_probe(int kind, int workgroups, int iters, floa
   else if (kind == 1)
     hipLaunchKernelGGL(bsmm::mfma_probe_kernel<1>, dim3((unsigned)workgroups), dim3(256), 0, s,
                        iters, out);
-  else
+  else if (kind == 2)
     hipLaunchKernelGGL(bsmm::mfma_probe_kernel<2>, dim3((unsigned)workgroups), dim3(256), 0, s,
+                       iters, out);
+  else
+    hipLaunchKernelGGL(bsmm::mfma_probe_kernel<3>, dim3((unsigned)workgroups), dim3(256), 0, s,
                        iters, out);
   return hipGetLastError() == hipSuccess ? BSMM_OK : BSMM_ERR_HIP;
 }

@@ -472,11 +472,12 @@ bsmm_status bsmm_set_streamk_grid(int workgroups);
  * operands with no memory traffic in between: kind 0 the fp8 E4M3
  * 16 x 16 x 128 instruction with unit e8m0 scales (65536 flops each), kind 1
  * the int8 16 x 16 x 64 one (32768 ops each), kind 2 the int8 32 x 32 x 32
- * one (65536 ops each).  Timing the launch gives the
+ * one (65536 ops each), kind 3 the fp8 32 x 32 x 64 one with unit e8m0
+ * scales (131072 flops each).  Timing the launch gives the
  * rate the matrix cores sustain at the clock the device holds under that
  * load.  out: device buffer of workgroups * 256 floats (one per thread, so
  * the work is not optimised away).  Returns BSMM_ERR_ARG for a kind outside
- * 0..2 or a
+ * 0..3 or a
  * non-positive count, BSMM_ERR_NULL for a NULL out.
  */
 bsmm_status bsmm_mfma_probe(int kind, int workgroups, int iters, float* out, void* stream);
