@@ -20,7 +20,7 @@ __all__ = [
     "bsmm_fp8_mx32_mm", "OP_FP8_MX32_MM", "bsmm_fp8_groupwise", "OP_FP8_GROUPWISE",
     "bsmm_quant_int8_rowwise", "bsmm_quant_fp8_blockwise", "bsmm_quant_fp8_mx",
     "bsmm_quant_fp8_columns", "bsmm_quant_fp8_weight", "bsmm_quant_fp8_blockwise_columns",
-    "bsmm_workspace_bytes", "bsmm_query_plan", "bsmm_set_override", "bsmm_set_streamk_grid", "bsmm_mfma_probe",
+    "bsmm_workspace_bytes", "bsmm_query_plan", "bsmm_set_override", "bsmm_set_override_tail", "bsmm_set_streamk_grid", "bsmm_mfma_probe",
     "bsmm_variant_names", "bsmm_version", "bsmm_timing_enable", "bsmm_timing_read",
     "I32", "F32", "BF16", "E4M3", "OP_INT8_ROWWISE", "OP_FP8_BLOCKWISE", "OP_FP8_MX_BMM",
     "OP_FP8_SCALED_MM",
@@ -107,6 +107,8 @@ def load():
     L.bsmm_query_plan.restype = st
     L.bsmm_set_override.argtypes = [ctypes.c_char_p, st]
     L.bsmm_set_override.restype = st
+    L.bsmm_set_override_tail.argtypes = [st, ctypes.c_char_p, st]
+    L.bsmm_set_override_tail.restype = st
     L.bsmm_set_streamk_grid.argtypes = [st]
     L.bsmm_set_streamk_grid.restype = st
     L.bsmm_mfma_probe.argtypes = [st, st, st, vp, vp]
@@ -775,6 +777,16 @@ def bsmm_query_plan(op, G, M, N, K, out_dtype, workspace_bytes=2**62):
 def bsmm_set_override(variant=None, split_k=0):
     _WS_NEED.clear()              # the plans, and so their workspace, change
     _check(load().bsmm_set_override(variant.encode() if variant else None, split_k))
+
+
+def bsmm_set_override_tail(m_split=0, tail_variant=None, tail_split=1):
+    """Force an M-split (bulk rows [0, m_split), a tail launch of
+    `tail_variant` with `tail_split` K slices) for the following calls;
+    m_split 0 removes it (tests and tuning)."""
+    _WS_NEED.clear()
+    _check(load().bsmm_set_override_tail(int(m_split),
+                                         tail_variant.encode() if tail_variant else None,
+                                         int(tail_split)))
 
 
 def bsmm_set_streamk_grid(workgroups=0):

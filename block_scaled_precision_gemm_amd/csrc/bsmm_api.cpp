@@ -33,9 +33,12 @@ bsmm_status fail(bsmm_status s, const char* fmt, ...) {
 // `gen` changes on every setter call so that cached plans made under an
 // earlier setting are not reused.
 struct Override {
-  std::mutex mu;                    // guards `variant` and `split`
+  std::mutex mu;                    // guards `variant`, `split` and the tail fields
   std::string variant;
   int split = 0;
+  int m_split = 0;                  // forced M-split point (0: none)
+  std::string m_tail;               // and its tail launch's kernel and K slices
+  int m_tail_split = 1;
   std::atomic<int> active{0};       // a variant or split is forced
   std::atomic<unsigned> gen{1};     // bumped by every setter call
   std::atomic<int> sk_grid{0};      // stream-K grid (0: co-resident capacity)
@@ -210,14 +213,24 @@ static Plan make_plan_uncached(bsmm_op op, int G, int M, int N, int K, bsmm_dtyp
   {
     Override& o = ovr();
     std::lock_guard<std::mutex> g(o.mu);
-    if (!o.variant.empty() || o.split > 0) {
+    if (!o.variant.empty() || o.split > 0 || o.m_split > 0) {
       Plan h = make_plan_heuristic(op, G, M, N, K, dt);
       const Variant* v = o.variant.empty() ? h.v : find_variant(o.variant.c_str());
       if (!v || (v->max_m && M > v->max_m)) v = h.v;
       pl.v = v;
       pl.split = o.split > 0 ? o.split : (o.variant.empty() ? h.split : 1);
       if (pl.split > KB) pl.split = KB > 0 ? KB : 1;
-      if (o.variant.empty() && o.split <= 0) { pl.tail = h.tail; pl.m_split = h.m_split; }
+      // a forced M-split: bulk rows [0, m_split) on the main kernel, the rest
+      // on the tail kernel (packed-scale kernels start on a 64-row boundary)
+      const Variant* tv = o.m_tail.empty() ? nullptr : find_variant(o.m_tail.c_str());
+      if (o.m_split > 0 && o.m_split < M && o.m_split % 64 == 0 && tv && !tv->max_m &&
+          !pl.v->max_m) {
+        pl.m_split = o.m_split;
+        pl.tail = tv;
+        pl.tail_split = o.m_tail_split > 0 ? o.m_tail_split : 1;
+        if (pl.tail_split > KB) pl.tail_split = KB > 0 ? KB : 1;
+        if (tv->persistent) pl.tail_split = 1;
+      }
       pl.source = 3;
       if (pl.v->persistent || pl.v->max_m) pl.split = 1;
       fit_workspace(pl, op, G, M, N, K, dt, workspace_bytes);
@@ -659,7 +672,23 @@ bsmm_status bsmm_set_override(const char* variant, int split_k) {
   std::lock_guard<std::mutex> g(o.mu);
   o.variant = variant ? variant : "";
   o.split = split_k > 0 ? split_k : 0;
-  o.active.store(!o.variant.empty() || o.split > 0, std::memory_order_release);
+  o.active.store(!o.variant.empty() || o.split > 0 || o.m_split > 0, std::memory_order_release);
+  o.gen.fetch_add(1, std::memory_order_acq_rel);
+  return BSMM_OK;
+}
+
+bsmm_status bsmm_set_override_tail(int m_split, const char* tail_variant, int tail_split) {
+  read_env_once();
+  if (m_split > 0 && (!tail_variant || !tail_variant[0] || !find_variant(tail_variant)))
+    return fail(BSMM_ERR_ARG, "unknown tail variant '%s'", tail_variant ? tail_variant : "");
+  CHECK(m_split >= 0 && m_split % 64 == 0, BSMM_ERR_ARG,
+        "the M-split point must be a non-negative multiple of 64 (got %d)", m_split);
+  Override& o = ovr();
+  std::lock_guard<std::mutex> g(o.mu);
+  o.m_split = m_split;
+  o.m_tail = m_split > 0 ? tail_variant : "";
+  o.m_tail_split = tail_split > 0 ? tail_split : 1;
+  o.active.store(!o.variant.empty() || o.split > 0 || o.m_split > 0, std::memory_order_release);
   o.gen.fetch_add(1, std::memory_order_acq_rel);
   return BSMM_OK;
 }

@@ -454,6 +454,16 @@ bsmm_status bsmm_query_plan(bsmm_op op, int64_t G, int64_t M, int64_t N,
 bsmm_status bsmm_set_override(const char* variant, int split_k);
 
 /*
+ * Force an M-split for subsequent calls in this process (tests and tuning):
+ * rows [0, m_split) run on the main launch (the dispatcher's or the
+ * bsmm_set_override kernel), rows [m_split, M) on a second launch of
+ * `tail_variant` with `tail_split` K slices.  Applies to calls with
+ * m_split < M; m_split 0 removes it.  Returns BSMM_ERR_ARG for an unknown
+ * variant or an m_split that is not a non-negative multiple of 64.
+ */
+bsmm_status bsmm_set_override_tail(int m_split, const char* tail_variant, int tail_split);
+
+/*
  * Grid of the stream-K kernels (variants whose name contains "sk") for
  * subsequent calls in this process (tests and tuning).  0, the default, uses
  * as many workgroups as the device holds at once; any other count is also

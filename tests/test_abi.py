@@ -443,7 +443,8 @@ def test_plan_skinny_m():
 def test_tuned_table_exact_and_padded_m():
     """A tuned entry serves its exact shape (source 0) and, as the padded-M
     bucket, smaller M of the same (op, dtype, G, N, K) (source 1), but never
-    M <= 16, which keeps the skinny kernel, and never for stream-K entries."""
+    M <= 16, which keeps the skinny kernel (groupwise has none), and never
+    for stream-K entries."""
     rows = parse_table()
     q = bsmm.bsmm_query_plan
     dts = {0: "i32", 1: "f32", 2: "bf16"}
@@ -456,7 +457,8 @@ def test_tuned_table_exact_and_padded_m():
                 assert below["source"] == 2
             else:
                 assert below["source"] == 1 and below["variant"] == f[6]
-            assert q(op, G, 8, N, K, dts[dt])["variant"] == "s16x16"
+            if op != bsmm.OP_FP8_GROUPWISE:
+                assert q(op, G, 8, N, K, dts[dt])["variant"] == "s16x16"
 
 
 def test_override_roundtrip():
@@ -532,9 +534,21 @@ def test_tuner_candidates_and_table_format(tmp_path, monkeypatch):
     assert (sh["G"], sh["M"], sh["N"], sh["K"], sh["layout"]) == (8, 128, 1024, 4096, "m_major")
     names = set(bsmm.bsmm_variant_names())
     cands = tune.candidates(sh)
-    assert len(cands) > 5 and all(v in names for v, _ in cands)
-    assert all(v != "s16x16" for v, _ in cands)
-    assert ("s16x16", 1) in tune.candidates(tune.parse_shape("int8,bf16,1,4,4096,4096"))
+    assert len(cands) > 5 and all(c[0] in names for c in cands)
+    assert all(c[0] != "s16x16" for c in cands) and all(c[2] == 0 for c in cands)
+    assert ("s16x16", 1, 0, "", 1) in tune.candidates(tune.parse_shape("int8,bf16,1,4,4096,4096"))
+    # a shape the dispatcher splits in M also gets bulk + tail candidates,
+    # each one a plan the forced override really produces
+    c3 = tune.parse_shape("fp8_blockwise,bf16,1,16640,5120,8192")
+    tails = [c for c in tune.candidates(c3) if c[2]]
+    assert len(tails) > 20 and {c[2] for c in tails} == {16384, 16128}
+    assert all(c[3] in names and not c[3].startswith("s") for c in tails)
+    try:
+        tune.set_plan(tails[0])
+        p = bsmm.bsmm_query_plan(bsmm.OP_FP8_BLOCKWISE, 1, 16640, 5120, 8192, "bf16")
+        assert (p["m_split"], p["tail_variant"], p["source"]) == (tails[0][2], tails[0][3], 3)
+    finally:
+        tune.clear_plan()
     monkeypatch.setattr(tune, "TABLE", str(tmp_path / "t.inc"))
     rows = {(2, 2, 8, 128, 1024, 4096): '{2, 2, 8, 128, 1024, 4096, "t128x128", 4, 0, "", 1}'}
     tune.write_table(rows)
