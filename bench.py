@@ -365,6 +365,88 @@ def traffic(name, fdir, wdir, cfdir, cwdir):
     print(json.dumps(res))
 
 
+def counters(name, dirs):
+    """Per-launch averages of every counter collected (rocprofv3 --pmc, one
+    pass per directory) for the dominant kernel's main launch of workload
+    `name` -- the bulk launch of an M-split plan -- and derived figures:
+    clock, matrix-core busy fraction, instruction-wait fraction, L2 hit rate
+    and L2 read latency.  Durations come from the same runs' kernel traces
+    when they were collected (--kernel-trace)."""
+    import csv
+    per_call = launches_per_call(name)
+    vals = {}
+    durs = []
+    for d in dirs:
+        per = {}
+        for f in _csvs(d, "counter_collection.csv"):
+            for r in csv.DictReader(open(f)):
+                if not _main_kernel(r["Kernel_Name"]):
+                    continue
+                key = (f, int(r["Dispatch_Id"]))
+                per.setdefault(key, {}).setdefault(r["Counter_Name"], 0.0)
+                per[key][r["Counter_Name"]] += float(r["Counter_Value"])
+        keys = sorted(per)
+        for i, k in enumerate(keys):
+            if i % per_call:
+                continue                       # tail launches
+            for c, v in per[k].items():
+                vals.setdefault(c, []).append(v)
+        for f in _csvs(d, "kernel_trace.csv"):
+            rows = sorted((r for r in csv.DictReader(open(f)) if _main_kernel(r["Kernel_Name"])),
+                          key=lambda r: int(r["Dispatch_Id"]))
+            durs += [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+                     for i, r in enumerate(rows) if i % per_call == 0]
+    avg = {c: sum(v) / len(v) for c, v in vals.items()}
+    out = [f"counters per main launch ({name}; {min(len(v) for v in vals.values())} or more "
+           "launches per counter)"]
+    for c in sorted(avg):
+        out.append(f"  {c:36s} {avg[c]:18.6g}")
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count if \
+        torch.cuda.is_available() else 256
+    xcds = 8
+    der = []
+    gui = avg.get("GRBM_GUI_ACTIVE")
+    if gui and durs:
+        dur = sum(durs) / len(durs)
+        der.append(f"  launch duration (kernel trace, counter runs)  {dur * 1e6:10.2f} us")
+        der.append(f"  clock  GRBM_GUI_ACTIVE / {xcds} XCDs / duration   "
+                   f"{gui / xcds / dur / 1e9:10.3f} GHz")
+    if gui and "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+        busy = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui / xcds * cus * 4)
+        der.append(f"  matrix cores busy  SQ_VALU_MFMA_BUSY_CYCLES / (GUI_ACTIVE/{xcds} x "
+                   f"{cus} CUs x 4 SIMDs)  {busy:8.3f}")
+    for mops in ("SQ_INSTS_VALU_MFMA_MOPS_F8", "SQ_INSTS_VALU_MFMA_MOPS_I8"):
+        if mops in avg:
+            der.append(f"  matrix ops  {mops} x 512  {avg[mops] * 512:14.4g}")
+    if "SQ_WAIT_INST_ANY" in avg and "SQ_WAVE_CYCLES" in avg:
+        der.append(f"  waves waiting to issue  SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES  "
+                   f"{avg['SQ_WAIT_INST_ANY'] / avg['SQ_WAVE_CYCLES']:8.3f}")
+    if "SQ_WAIT_ANY" in avg and "SQ_WAVE_CYCLES" in avg:
+        der.append(f"  waves waiting (any)  SQ_WAIT_ANY / SQ_WAVE_CYCLES  "
+                   f"{avg['SQ_WAIT_ANY'] / avg['SQ_WAVE_CYCLES']:8.3f}")
+    if "SQ_VALU_MFMA_COEXEC_CYCLES" in avg and "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+        der.append(f"  VALU issued beside a busy matrix core  COEXEC / MFMA_BUSY  "
+                   f"{avg['SQ_VALU_MFMA_COEXEC_CYCLES'] / avg['SQ_VALU_MFMA_BUSY_CYCLES']:8.3f}")
+    if "TCC_HIT_sum" in avg and "TCC_MISS_sum" in avg:
+        h, m = avg["TCC_HIT_sum"], avg["TCC_MISS_sum"]
+        der.append(f"  L2 hit rate  TCC_HIT / (HIT + MISS)  {h / (h + m):8.3f}")
+    if "TCP_TCC_READ_REQ_LATENCY_sum" in avg and "TCP_TCC_READ_REQ_sum" in avg:
+        der.append(f"  L2 read latency  TCP_TCC_READ_REQ_LATENCY / READ_REQ  "
+                   f"{avg['TCP_TCC_READ_REQ_LATENCY_sum'] / avg['TCP_TCC_READ_REQ_sum']:8.1f} "
+                   "cycles")
+    if "TCC_EA0_RDREQ_LEVEL_sum" in avg and "TCC_EA0_RDREQ_sum" in avg:
+        der.append(f"  L2-to-fabric reads in flight per request  EA0_RDREQ_LEVEL / EA0_RDREQ  "
+                   f"{avg['TCC_EA0_RDREQ_LEVEL_sum'] / avg['TCC_EA0_RDREQ_sum']:8.1f} cycles")
+    if "TCC_EA0_RDREQ_DRAM_sum" in avg and "TCC_EA0_RDREQ_sum" in avg:
+        der.append(f"  L2 read misses sent to DRAM  EA0_RDREQ_DRAM / EA0_RDREQ  "
+                   f"{avg['TCC_EA0_RDREQ_DRAM_sum'] / avg['TCC_EA0_RDREQ_sum']:8.3f}")
+    if der:
+        out.append("derived")
+        out += der
+    print("\n".join(out))
+
+
 def quant_bytes(kind, rows, K):
     """Algorithmic HBM bytes of one quantiser call: bf16 input read once,
     1-byte codes and the scales written once."""
@@ -562,11 +644,15 @@ def main():
     ap.add_argument("--summarize", metavar="DIR")
     ap.add_argument("--traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
                                                    "COPY_WRITE_DIR"))
+    ap.add_argument("--counters", nargs="+", metavar="PMC_DIR",
+                    help="summarise rocprofv3 --pmc runs of --config's main launch")
     args = ap.parse_args()
     if args.summarize:
         return summarize(args.summarize, args.config)
     if args.traffic:
         return traffic(args.config, *args.traffic)
+    if args.counters:
+        return counters(args.config, args.counters)
     if args.copy_kernel:
         return copy_kernel()
     if args.mfma_peak:
