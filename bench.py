@@ -263,7 +263,7 @@ def _csvs(d, suffix):
 
 def _main_kernel(name):
     return any(k in name for k in ("tile_kernel", "tile4_kernel", "sk_kernel", "skinny_kernel",
-                                   "quant_"))
+                                   "narrow_kernel", "quant_"))
 
 
 def launches_per_call(name):

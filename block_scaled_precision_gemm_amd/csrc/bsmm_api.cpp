@@ -252,7 +252,7 @@ static Plan make_plan_uncached(bsmm_op op, int G, int M, int N, int K, bsmm_dtyp
   // padded-M bucket never displaces the skinny kernel for M <= 16
   const Variant* bv = best ? find_variant(best->variant) : nullptr;
   if (bv && bv->max_m && M > bv->max_m) bv = nullptr;
-  if (bv && pl.source == 1 && M <= 16 && !bv->max_m) bv = nullptr;
+  if (bv && pl.source == 1 && M <= 16 && bv->max_m != 16) bv = nullptr;
   // stream-K entries serve their exact shape only: at another M the tile
   // count may leave a stream-K phase, whose K-skewed ranges lose L2 reuse
   if (bv && pl.source == 1 && bv->persistent) bv = nullptr;

@@ -933,6 +933,332 @@ skinny_kernel(const KArgs k) {
               k.vec_out != 0, nvalid);
 }
 
+// ---------------------------------------------------------------------------
+// Narrow kernel for 16 < M <= 128 (decode batches: bound by reading B once).
+// One workgroup computes a 128-row x 32-column output tile over the whole of
+// K: no split-K partials, no reduction launch, no scale packing.  Its four
+// waves each own 32 rows (two 16-row MFMA tiles) and both 16-column tiles.
+//
+// A rows are used by one wave only, so each wave loads its own straight
+// into registers in the matrix instruction's operand layout (a lane's 32
+// bytes of its row per K block: two 16-byte loads per tile), NS K blocks
+// ahead: a ring of NS register sets, indexed by a constant in the loop,
+// which is unrolled NS times.  The 32 x 128-byte B tile of a K block is
+// shared by the four waves: it goes global -> LDS (each wave one 8-row
+// quarter, a direct-to-LDS load) into a ring of NS 4 KB slots.  At block c
+// a wave waits for its own loads of block c, the barrier makes every wave's
+// B quarter visible and frees block c - 1's B slot, and block c + NS - 1 is
+// requested into the registers and slot block c - 1 used; NS - 1 blocks
+// stay in flight.  (Direct-to-LDS loads alone kept too few bytes in flight
+// here: the A tile is 80% of each block.)  K blocks past the end run as
+// zeros with neutral scales.
+//
+// The per-block scales are staged in LDS once, before the K loop: mx: the
+// e8m0 byte of each of the 128 rows per K block, and the tile's B block
+// byte per K block; blockwise: the fp32 row scales and the B block scale.
+// The grid is G x (N / 32) workgroups in the XCD-aware order, so the
+// workgroups of one batch share an XCD and read that batch's A from its L2.
+// ---------------------------------------------------------------------------
+// f(integral_constant<int, i>) for i = B .. E - 1, unrolled
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>());
+    static_for<B + 1, E>(f);
+  }
+}
+
+namespace narrow {
+constexpr int BM = 128, BN = 32, NS = 8;
+constexpr int WB = BN * kBlockK;              // B tile bytes per K block (4 KB)
+constexpr int SCL = 20480;                    // scale region
+constexpr int LDS = NS * WB + SCL;            // 52 KB
+constexpr int LOADS = 5;                      // per wave and K block: 4 A + 1 B
+// scale region capacity in K blocks: mx x_scale [KB][BM] bytes + w_scale
+// [KB]; blockwise scale_a [KB][BM] fp32 + scale_b [KB] fp32
+constexpr int MAX_KB_MX = SCL / (BM + 1);
+constexpr int MAX_KB_BW = SCL / ((BM + 1) * 4);
+// position of row m (0..127) in a K block's scale row: a lane of wave w
+// reads rows 32 w + f and 32 w + 16 + f (f = lane % 16) as one pair
+__device__ __forceinline__ int scale_pos(int m) {
+  return (m >> 5) * 32 + (m & 15) * 2 + ((m >> 4) & 1);
+}
+template <int OP> constexpr bool supported() {
+  return OP == BSMM_OP_FP8_MX_BMM || OP == BSMM_OP_FP8_BLOCKWISE ||
+         OP == BSMM_OP_INT8_ROWWISE || OP == BSMM_OP_FP8_SCALED_MM;
+}
+}  // namespace narrow
+
+template <int OP, int OUT>
+__global__ void __launch_bounds__(256)
+narrow_kernel(const KArgs k) {
+  using namespace narrow;
+  using acc_t = typename OpT<OP>::acc_t;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS];
+  const Problem& p = k.p;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int KB = p.K / kBlockK;
+  const int nblk = p.N / BN;
+  const int u = first_unit();
+  if (u >= k.units) return;
+  const int g = u / nblk;
+  const int col0 = (u - g * nblk) * BN;
+  const int row0 = k.row_begin;
+  const int rows = k.row_end - row0;          // <= BM
+
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(
+      p.a + (int64_t)g * p.a_sg + (int64_t)row0 * p.lda, (uint64_t)rows * p.lda);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(
+      p.b + (int64_t)g * p.b_sg + (int64_t)col0 * p.ldb, (uint64_t)BN * p.ldb);
+  // The workgroup's walk over K starts at block rot and wraps: the tiles of
+  // one batch (which share an XCD) spread their requests over all of K at
+  // any moment instead of all asking for the same K block -- with row
+  // strides that are multiples of 4 KB those requests would all land on
+  // the same few L2 and HBM channels.  Step c works on block kbo(c).
+  const int rot = (int)(((int64_t)(u - g * nblk) * KB) / nblk);
+  auto kbo = [&](int c) { const int t = c + rot; return t >= KB ? t - KB : t; };
+  const __amdgpu_buffer_rsrc_t rdead = make_rsrc(p.b, 0);
+  const int fr = lane & 15, fq = lane >> 4;
+  const uint32_t lda = (uint32_t)p.lda, ldb = (uint32_t)p.ldb;
+  // A: lane's row 32 wave + 16 i + f, bytes [32 fq, 32 fq + 32) of the block
+  // (rows past the launch fall outside the resource: zeros)
+  uint32_t a_vo[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) a_vo[i] = (uint32_t)(32 * wave + 16 * i + fr) * lda + 32u * fq;
+  // B: this wave's quarter, rows 8 wave + lane / 8, chunk (lane % 8) ^ swz
+  const int b_row = wave * 8 + (lane >> 3);
+  const uint32_t b_vo = (uint32_t)b_row * ldb + ((uint32_t)((lane & 7) ^ swz(b_row)) << 4);
+  i32x4 xr[NS][2][2];            // A fragments of the NS blocks in flight
+  // block b's loads into register set / B slot s (a constant)
+  auto issue = [&](int b, auto s_c) {
+    constexpr int s = decltype(s_c)::value;
+    const bool live = b < KB;
+    const __amdgpu_buffer_rsrc_t rA = live ? ra : rdead;
+    const int kbyte = (live ? kbo(b) : 0) * kBlockK;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      xr[s][i][0] = __builtin_amdgcn_raw_buffer_load_b128(rA, a_vo[i], kbyte, 0);
+      xr[s][i][1] = __builtin_amdgcn_raw_buffer_load_b128(rA, a_vo[i] + 16, kbyte, 0);
+    }
+    const lds_ptr_t l = (lds_ptr_t)(uintptr_t)(uint32_t)(uintptr_t)(smem + s * WB + wave * 1024);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? rb : rdead, l, 16, b_vo, kbyte, 0, 0);
+  };
+
+  // The scales of every K block go to the scale region: element e =
+  // (row m, block kb), m = e / KB, of the A rows' scales (a row past the
+  // launch reads the last valid row), and the tile's B block scale of
+  // every K block (KB <= 256: one per thread).  Rows' scales beyond the
+  // first CH per thread are staged first, each round's loads then writes;
+  // the last round's loads and the B scales' are issued ahead of the
+  // prologue's loads (the empty asm keeps them there) and written after
+  // them, so those writes wait for the scales, not for the tiles.
+  uint8_t* const scl = smem + NS * WB;
+  constexpr int CH = 16;
+  using S = typename std::conditional<OP == BSMM_OP_FP8_BLOCKWISE, float, uint8_t>::type;
+  constexpr bool SCALES = OP == BSMM_OP_FP8_MX_BMM || OP == BSMM_OP_FP8_BLOCKWISE;
+  const int n_x = SCALES ? BM * KB : 0;
+  auto x_src = [&](int e) -> S {
+    const int m = e / KB, kb = e - m * KB;
+    const int64_t mm = row0 + min(m, rows - 1);
+    if constexpr (OP == BSMM_OP_FP8_MX_BMM)
+      return ((const uint8_t*)p.sa)[(int64_t)g * p.sa_sg + mm * p.sa_m + kb];
+    else
+      return ((const float*)p.sa)[mm * p.sa_m + (int64_t)kb * p.sa_kb];
+  };
+  auto x_dst = [&](int e) -> S* {
+    const int m = e / KB, kb = e - m * KB;
+    return (S*)scl + kb * BM + scale_pos(m);
+  };
+  S sv[CH];
+  S wv = S(0);
+  if constexpr (SCALES) {
+    int e0 = 0;
+    for (; e0 + 256 * CH < n_x; e0 += 256 * CH) {
+#pragma unroll
+      for (int i = 0; i < CH; ++i) sv[i] = x_src(e0 + threadIdx.x + 256 * i);
+#pragma unroll
+      for (int i = 0; i < CH; ++i) *x_dst(e0 + threadIdx.x + 256 * i) = sv[i];
+    }
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int e = e0 + threadIdx.x + 256 * i;
+      sv[i] = e < n_x ? x_src(e) : S(0);
+    }
+    const int kb = threadIdx.x;
+    if (kb < KB) {
+      if constexpr (OP == BSMM_OP_FP8_MX_BMM)
+        wv = ((const uint8_t*)p.sb)[(int64_t)g * p.sb_sg + (int64_t)(col0 / kBlockK) * p.sb_n + kb];
+      else
+        wv = ((const float*)p.sb)[(int64_t)kb * p.sb_kb + (int64_t)(col0 / kBlockK) * p.sb_n];
+    }
+    asm volatile("" ::: "memory");
+  }
+
+  // prologue: blocks 0 .. NS-1 into every register set and slot
+  static_for<0, NS>([&](auto i) { issue(decltype(i)::value, i); });
+
+  if constexpr (SCALES) {
+    const int e0 = n_x > 256 * CH ? (n_x - 1) / (256 * CH) * (256 * CH) : 0;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int e = e0 + threadIdx.x + 256 * i;
+      if (e < n_x) *x_dst(e) = sv[i];
+    }
+    if ((int)threadIdx.x < KB) ((S*)scl)[BM * KB + threadIdx.x] = wv;
+  }
+  wait_lgkm0();                            // this wave's scale writes
+
+  acc_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = acc_t{0, 0, 0, 0};
+  // B fragments: rows 16 j + f, chunks 2 fq and 2 fq + 1
+  int b_off[2][2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    b_off[j][0] = lds_off(16 * j + fr, 2 * fq);
+    b_off[j][1] = lds_off(16 * j + fr, 2 * fq + 1);
+  }
+  // B fragments and scales of a K block, into the set of the block's parity
+  struct BFrags {
+    i32x8 b[2];
+    uint32_t xs;       // mx: the lane's two row scale bytes (byte i: A tile i)
+    int ws;            // mx: the B block's scale byte
+    float sa[2], sb;   // blockwise
+  };
+  BFrags bq[2];
+  auto read_b = [&](int c, auto s_c, BFrags& f) {
+    constexpr int s = decltype(s_c)::value;
+    const uint8_t* sb_ = smem + s * WB;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const i32x4 lo = *(const i32x4*)(sb_ + b_off[j][0]);
+      const i32x4 hi = *(const i32x4*)(sb_ + b_off[j][1]);
+      f.b[j] = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    }
+    // blocks past the end: neutral scales (their products are zeros); the
+    // reads go to the last block and are selected away, so the step stays
+    // one straight-line block that the fences can pin
+    const bool live = c < KB;
+    const int cl = kbo(min(c, KB - 1));
+    f.xs = 0x7F7Fu;
+    f.ws = 127;
+    f.sa[0] = f.sa[1] = f.sb = 0.f;
+    if constexpr (OP == BSMM_OP_FP8_MX_BMM) {
+      const uint32_t xs = *(const uint16_t*)(scl + cl * BM + 32 * wave + 2 * fr);
+      const int ws = scl[BM * KB + cl];
+      f.xs = live ? xs : 0x7F7Fu;
+      f.ws = live ? ws : 127;
+    } else if constexpr (OP == BSMM_OP_FP8_BLOCKWISE) {
+      const float* sf = (const float*)scl;
+      const float2 v = *(const float2*)(sf + cl * BM + 32 * wave + 2 * fr);
+      const float sb = sf[BM * KB + cl];
+      f.sa[0] = live ? v.x : 0.f;
+      f.sa[1] = live ? v.y : 0.f;
+      f.sb = live ? sb : 0.f;
+    }
+  };
+  auto compute = [&](auto s_c, const BFrags& f) {
+    constexpr int s = decltype(s_c)::value;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const i32x4 lo = xr[s][i][0], hi = xr[s][i][1];
+      const i32x8 af = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        if constexpr (OP == BSMM_OP_INT8_ROWWISE) {
+          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+              i32x4{f.b[j][0], f.b[j][1], f.b[j][2], f.b[j][3]}, lo, acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+              i32x4{f.b[j][4], f.b[j][5], f.b[j][6], f.b[j][7]}, hi, acc[i][j], 0, 0, 0);
+        } else if constexpr (OP == BSMM_OP_FP8_MX_BMM) {
+          acc[i][j] = mfma_mx(f.b[j], af, acc[i][j], __builtin_amdgcn_readfirstlane(f.ws), i,
+                              f.xs);
+        } else if constexpr (OP == BSMM_OP_FP8_BLOCKWISE) {
+          const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              f.b[j], af, f32x4{0, 0, 0, 0}, 0, 0, 0, 127, 0, 127);
+          const float sc = f.sa[i] * f.sb;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(sc, part[r], acc[i][j][r]);
+        } else {
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              f.b[j], af, acc[i][j], 0, 0, 0, 127, 0, 127);
+        }
+      }
+    }
+  };
+  // Block 0's B fragments before the loop: every wave's loads of block 0
+  // landed, its scale writes done, then the barrier.
+  wait_vmcnt<(NS - 1) * LOADS>();
+  wait_lgkm0();
+  lds_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  read_b(0, std::integral_constant<int, 0>(), bq[0]);
+  // Step c: wait for this wave's loads of block c + 1 (the later blocks in
+  // flight may stay outstanding: NS - 2 at c = 0, then NS - 3), the
+  // barrier (every wave's B quarter of block c + 1 visible; block c - 1's
+  // B slot no longer read, its fragments were read in step c - 2), the
+  // refill of block c - 1's register set and slot with block c + NS - 1,
+  // the B fragments of block c + 1, and block c's matrix instructions on
+  // fragments read in step c - 1.  The fences keep every LDS read after its
+  // barrier.
+  auto step = [&](int c, auto s_c, auto first_c) {
+    constexpr int s = decltype(s_c)::value;
+    constexpr bool FIRST = decltype(first_c)::value;
+    constexpr int sp = (s + NS - 1) % NS, sn = (s + 1) % NS;
+    if constexpr (FIRST) wait_vmcnt<(NS - 2) * LOADS>();
+    else wait_vmcnt<(NS - 3) * LOADS>();
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (!FIRST) issue(c + NS - 1, std::integral_constant<int, sp>());
+    read_b(c + 1, std::integral_constant<int, sn>(), bq[(s + 1) & 1]);
+    compute(s_c, bq[s & 1]);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // blocks in groups of NS (register set s = c % NS); the last group's
+  // blocks past KB are zeros (dead loads) with neutral scales
+  static_assert(NS % 2 == 0, "B fragment sets alternate with the block's parity");
+  step(0, std::integral_constant<int, 0>(), std::true_type());
+  static_for<1, NS>([&](auto i) { step(decltype(i)::value, i, std::false_type()); });
+  for (int c0 = NS; c0 < KB; c0 += NS)
+    static_for<0, NS>([&](auto i) { step(c0 + decltype(i)::value, i, std::false_type()); });
+  wait_vmcnt<0>();                       // the last refills were out-of-range loads
+
+  // epilogue: lane holds row 32 wave + 16 i + f, columns 16 j + 4 fq .. + 3
+  const bool vec = k.vec_out != 0;
+  [[maybe_unused]] const ScaledEpi epi(p);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int mr = 32 * wave + 16 * i + fr;
+    if (mr >= rows) continue;
+    const int m = row0 + mr;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = col0 + 16 * j + 4 * fq;
+      float y[4];
+      int yi[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if constexpr (OP == BSMM_OP_INT8_ROWWISE) {
+          yi[r] = acc[i][j][r];
+          if constexpr (OUT != BSMM_I32)
+            y[r] = __fmul_rn(__fmul_rn((float)acc[i][j][r], ((const float*)p.sa)[(int64_t)m * p.sa_m]),
+                             ((const float*)p.sb)[(int64_t)(n + r) * p.sb_n]);
+        } else if constexpr (OP == BSMM_OP_FP8_SCALED_MM) {
+          y[r] = epi(acc[i][j][r], ((const float*)p.sa)[(int64_t)m * p.sa_m],
+                     ((const float*)p.sb)[(int64_t)(n + r) * p.sb_n], n + r);
+        } else {
+          y[r] = acc[i][j][r];
+        }
+      }
+      store4<OUT>((uint8_t*)p.out, (int64_t)g * p.o_sg + (int64_t)m * p.ldo + n, y, yi, vec, 4);
+    }
+  }
+}
+
 // Epilogue through LDS.  Stored straight from the MFMA layout, a wave's
 // store instruction writes 16 rows x 32 or 64 bytes -- sixteen partial cache
 // lines -- and a round of 256 tiles took ~13 us of pure write time.  Here
@@ -1839,6 +2165,47 @@ int launch_skinny(const Problem& p, const Launch& l) {
   return check_launch();
 }
 
+// The narrow kernel (16 < rows <= 128): one workgroup per 32 columns of each
+// batch over the whole of K.  Shapes it does not take (more rows, N not a
+// multiple of 32, more K blocks than its scale region holds, an operation
+// it lacks) run the 128 x 128 tile kernel instead.
+template <int OP, int OUT>
+int launch_narrow(const Problem& p, const Launch& l) {
+  const int rows = l.row_end - l.row_begin;
+  const int KB = p.K / kBlockK;
+  bool ok = narrow::supported<OP>() && rows <= narrow::BM && p.N % narrow::BN == 0;
+  if constexpr (OP == BSMM_OP_FP8_MX_BMM) ok = ok && KB <= narrow::MAX_KB_MX;
+  if constexpr (OP == BSMM_OP_FP8_BLOCKWISE) ok = ok && KB <= narrow::MAX_KB_BW;
+  if (!ok) {
+    Launch l2 = l;
+    l2.psa = nullptr;
+    return launch_tile<OP, OUT, 2, 1, 5, false>(p, l2);
+  }
+  if constexpr (narrow::supported<OP>()) {
+    KArgs k;
+    k.p = p;
+    k.row_begin = l.row_begin;
+    k.row_end = l.row_end;
+    k.psa = nullptr;
+    k.psa_ld = 0;
+    k.ws = nullptr;
+    k.splits = 1;
+    k.kb_per_split = KB;
+    k.tiles_m = 1;
+    k.tiles_n = p.N / narrow::BN;
+    k.vec_out = out_vec_ok<OUT>(p);
+    hipStream_t s = (hipStream_t)l.stream;
+    if (KB == 0) {
+      hipLaunchKernelGGL((zero_out<OP, OUT>), dim3(1024), dim3(256), 0, s, k);
+      return check_launch();
+    }
+    k.units = p.G * k.tiles_n;
+    hipLaunchKernelGGL((narrow_kernel<OP, OUT>), dim3((unsigned)k.units), dim3(256), 0, s, k);
+    return check_launch();
+  }
+  return 1;
+}
+
 template <int OP, int OUT, int WM, int WN, int RING, bool SK, bool PK, int KIND>
 int launch_kernel(const Problem& p, const Launch& l) {
   // the int8 and scaled_mm K loops read no scales: packed variants run the
@@ -1852,6 +2219,8 @@ int launch_kernel(const Problem& p, const Launch& l) {
     return 1;
   } else if constexpr (KIND == 2) {
     return launch_skinny<OP, OUT, RING>(p, l);
+  } else if constexpr (KIND == 3) {
+    return launch_narrow<OP, OUT>(p, l);
   } else if constexpr (KIND == 1) {
     // wide waves for int8 / mx / scaled_mm; blockwise and mx32 (per-lane
     // column scales) run the 256 x 256 eight-wave kernel

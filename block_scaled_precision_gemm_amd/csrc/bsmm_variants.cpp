@@ -43,11 +43,12 @@ int launch_variant(const Problem& p, const Launch& l) {
 constexpr unsigned kAllOps = 63u;
 
 // name, tile_m, tile_n, ops, masked tail, persistent, packed scales,
-// workgroups per CU, unpacked sibling, largest M (the skinny kernel: 16),
+// workgroups per CU, unpacked sibling, largest M (the skinny kernel: 16,
+// the narrow kernel: 128),
 // launch
 const Variant kVariants[] = {
 #define BSMM_VARIANT(NAME, TM, TN, WM, WN, RING, SK, PK, WPC, UNPACKED, KIND) \
-  {NAME, TM, TN, kAllOps, true, SK, PK, WPC, UNPACKED, KIND == 2 ? 16 : 0,                      \
+  {NAME, TM, TN, kAllOps, true, SK, PK, WPC, UNPACKED, KIND == 2 ? 16 : KIND == 3 ? 128 : 0,  \
    launch_variant<WM, WN, RING, SK, PK, KIND>},
 #include "bsmm_variants.inc"
 #undef BSMM_VARIANT

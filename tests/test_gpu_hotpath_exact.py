@@ -485,3 +485,119 @@ def test_mx_scales_land_on_their_own_blocks_bulk_and_split_tail():
         y = mx_run(p, "f32")
         rows = np.array(sorted({0, m - 1, m, min(m + 1, M - 1), 8191, 8192, M - 1}))
         mx_check(p, "f32", y, rows=rows)
+
+
+# --------------------------------------------- the narrow kernel (M <= 128) --
+
+NARROW_MS = [17, 100, 128]
+
+
+@pytest.mark.parametrize("K", [384, 1280, 1408])
+@pytest.mark.parametrize("M", NARROW_MS)
+def test_narrow_mx_bit_exact(M, K):
+    """The M <= 128 kernel: K from fewer blocks than its ring holds (3) to
+    odd and even counts beyond it, both layouts, three batches."""
+    for layout in ("m_major", "batch_first"):
+        p = mx_problem(3, M, 384, K, 51 + M + K, layout)
+        for dt in ("f32", "bf16"):
+            say(f"narrow mx exact {layout} {dt} G=3 M={M} N=384 K={K}")
+            with Forced("n128x32", 0):
+                y = mx_run(p, dt)
+            mx_check(p, dt, y, exact=True)
+
+
+@pytest.mark.parametrize("M", NARROW_MS)
+def test_narrow_blockwise_and_int8_and_scaled_mm_bit_exact(M):
+    p = bw_problem(M, 512, 1280, 52 + M)
+    for dt in ("f32", "bf16"):
+        say(f"narrow blockwise exact {dt} M={M}")
+        with Forced("n128x32", 0):
+            y = bw_run(p, dt)
+        bw_check(p, dt, y, exact=True)
+    from synth import int8_rowwise_inputs
+    from tests.gpu_util import check_int8, run_int8
+    q = int8_rowwise_inputs(M, 352, 1280, 53 + M)
+    for dt in ("i32", "f32", "bf16"):
+        say(f"narrow int8 {dt} M={M}")
+        with Forced("n128x32", 0):
+            y = run_int8(q, dt)
+        check_int8(q, dt, y)
+    from synth import fp8_scaled_mm_inputs
+    t = fp8_scaled_mm_inputs(M, 224, 1024, 54 + M, bias="f32")
+    say(f"narrow scaled_mm f32 M={M}")
+    with Forced("n128x32", 0):
+        y = bsmm.bsmm_fp8_scaled_mm(dev(t["a"]), dev(t["b_nk"]).t(), dev(t["scale_a"]),
+                                    dev(t["scale_b"]), bias=dev(t["bias"]), scale_result=0.5,
+                                    out_dtype="f32")
+    ref = S.fp8_scaled_mm(t["a"], t["b_nk"].T, t["scale_a"], t["scale_b"], bias=t["bias"],
+                          scale_result=0.5, out_dtype="f32")
+    rep = S.compare(as_f64(host_out(y)), ref)
+    assert rep["ok"], rep
+
+
+def test_narrow_falls_back_where_it_does_not_apply():
+    """More K blocks than its scale region holds (blockwise K = 5120, 40
+    blocks), more than 128 rows, N not a multiple of 32 (int8): the call
+    runs another kernel and stays exact."""
+    cases = [bw_problem(64, 256, 5120, 55), bw_problem(200, 256, 512, 56)]
+    for p in cases:
+        say(f"narrow fallback blockwise {p['a'].shape}")
+        with Forced("n128x32", 0):
+            y = bw_run(p, "f32")
+        bw_check(p, "f32", y, exact=True)
+    from synth import int8_rowwise_inputs
+    from tests.gpu_util import check_int8, run_int8
+    q = int8_rowwise_inputs(60, 200, 512, 57)
+    say("narrow fallback int8 N=200")
+    with Forced("n128x32", 0):
+        y = run_int8(q, "i32")
+    check_int8(q, "i32", y)
+
+
+@pytest.mark.parametrize("layout", ["m_major", "batch_first"])
+def test_narrow_scales_land_on_their_own_blocks(layout):
+    G, M, N, K = 3, 128, 512, 1280
+    base = mx_problem(G, M, N, K, 58, layout, codes="any", xs=(120, 134), ws=(120, 134))
+    for g, m, kb, nb, kb2 in ((0, 0, 0, 0, 0), (2, 127, 9, 3, 9), (1, 77, 4, 2, 6)):
+        p = dict(base, x_scale=base["x_scale"].copy(), w_scale=base["w_scale"].copy())
+        if layout == "m_major":
+            p["x_scale"][m, g, kb] += 20
+        else:
+            p["x_scale"][g, m, kb] += 20
+        p["w_scale"][g, nb, kb2] -= 20
+        say(f"narrow mx own block {layout} g {g} row {m} kb {kb} nb {nb}")
+        with Forced("n128x32", 0):
+            y = mx_run(p, "f32")
+        mx_check(p, "f32", y)
+    q = bw_problem(100, 384, 1024, 59, codes="any", scales=(-1, 1))
+    q["scale_a"][99, 7] *= np.float32(2.0**20)
+    q["scale_b"][3, 2] *= np.float32(2.0**-20)
+    say("narrow blockwise own block")
+    with Forced("n128x32", 0):
+        y = bw_run(q, "f32")
+    bw_check(q, "f32", y)
+
+
+@pytest.mark.parametrize("layout", ["m_major", "batch_first"])
+def test_narrow_guard_bands_and_full_range(layout):
+    G, M, N, K = 2, 90, 384, 1280
+    p = mx_problem(G, M, N, K, 60, layout, codes="any", xs=(60, 190), ws=(97, 157))
+    for dt, c0 in (("f32", 4), ("bf16", 8), ("f32", 3), ("bf16", 2)):
+        tdt = torch.float32 if dt == "f32" else torch.bfloat16
+        if layout == "m_major":
+            big = torch.full((M + 5, G + 1, N + 16), -7.0, dtype=tdt, device=DEV)
+            view = big[2:2 + M, 1:1 + G, c0:c0 + N]
+            sel = (slice(2, 2 + M), slice(1, 1 + G), slice(c0, c0 + N))
+        else:
+            big = torch.full((G + 1, M + 5, N + 16), -7.0, dtype=tdt, device=DEV)
+            view = big[1:1 + G, 2:2 + M, c0:c0 + N]
+            sel = (slice(1, 1 + G), slice(2, 2 + M), slice(c0, c0 + N))
+        say(f"narrow guard band {layout} {dt} column offset {c0}")
+        with Forced("n128x32", 0):
+            mx_run(p, dt, out=view)
+        h = host_out(big)
+        mask = np.ones(h.shape, bool)
+        mask[sel] = False
+        sentinel = host_out(torch.full((1,), -7.0, dtype=tdt, device=DEV))[0]
+        assert (h[mask] == sentinel).all()
+        mx_check(p, dt, view)
