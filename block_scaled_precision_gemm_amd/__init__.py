@@ -28,7 +28,9 @@ __all__ = [
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-lib_path = os.path.join(_PKG, "libbsmm.so")
+# BSMM_LIB_PATH: another build of the same library (the sanitized host
+# build) in place of the in-tree one
+lib_path = os.environ.get("BSMM_LIB_PATH") or os.path.join(_PKG, "libbsmm.so")
 
 I32, F32, BF16, E4M3 = 0, 1, 2, 3
 OP_INT8_ROWWISE, OP_FP8_BLOCKWISE, OP_FP8_MX_BMM, OP_FP8_SCALED_MM, OP_FP8_MX32_MM = 0, 1, 2, 3, 4
