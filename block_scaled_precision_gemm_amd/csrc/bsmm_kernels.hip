@@ -817,6 +817,11 @@ skinny_kernel(const KArgs k) {
   using acc_t = typename OpT<OP>::acc_t;
   __shared__ acc_t red[4][kWave];
   const Problem& p = k.p;
+  // the kernel arguments in one batch of loads (see the narrow kernel)
+  asm volatile("" ::"s"(k.vec_out), "s"(p.M), "s"(p.N), "s"(p.K), "s"(p.a), "s"(p.a_sg),
+               "s"(p.lda), "s"(p.b), "s"(p.b_sg), "s"(p.ldb), "s"(p.sa), "s"(p.sa_sg),
+               "s"(p.sa_m), "s"(p.sa_kb), "s"(p.sb), "s"(p.sb_sg), "s"(p.sb_n), "s"(p.sb_kb),
+               "s"(p.out), "s"(p.o_sg), "s"(p.ldo));
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int ntiles = (p.N + 15) / 16;
@@ -974,14 +979,13 @@ constexpr int WB = BN * kBlockK;              // B tile bytes per K block (4 KB)
 constexpr int SCL = 20480;                    // scale region
 constexpr int LDS = NS * WB + SCL;            // 52 KB
 constexpr int LOADS = 5;                      // per wave and K block: 4 A + 1 B
-// scale region capacity in K blocks: mx x_scale [KB][BM] bytes + w_scale
-// [KB]; blockwise scale_a [KB][BM] fp32 + scale_b [KB] fp32
-constexpr int MAX_KB_MX = SCL / (BM + 1);
-constexpr int MAX_KB_BW = SCL / ((BM + 1) * 4);
-// position of row m (0..127) in a K block's scale row: a lane of wave w
-// reads rows 32 w + f and 32 w + 16 + f (f = lane % 16) as one pair
-__device__ __forceinline__ int scale_pos(int m) {
-  return (m >> 5) * 32 + (m & 15) * 2 + ((m >> 4) & 1);
+// Staged scale rows: KB elements padded to an odd number of 4-byte words.
+template <class S> __host__ __device__ constexpr int scale_pitch(int KB) {
+  return sizeof(S) == 1 ? ((((KB + 3) >> 2) | 1) << 2) : (KB | 1);
+}
+// scale region: BM staged rows + the B scale of every K block
+template <class S> __host__ __device__ constexpr bool scales_fit(int KB) {
+  return (BM * scale_pitch<S>(KB) + KB) * (int)sizeof(S) <= SCL && KB <= 256;
 }
 template <int OP> constexpr bool supported() {
   return OP == BSMM_OP_FP8_MX_BMM || OP == BSMM_OP_FP8_BLOCKWISE ||
@@ -998,6 +1002,15 @@ narrow_kernel(const KArgs k) {
   const Problem& p = k.p;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  // Every kernel argument read below, loaded in one batch before anything
+  // else: left to the compiler, each load waits for the branch or address
+  // that first needs it, and the workgroup pays several dependent round
+  // trips to the argument buffer before its first tile load.
+  asm volatile("" ::"s"(gridDim.x), "s"(k.units), "s"(k.row_begin), "s"(k.row_end),
+               "s"(k.vec_out), "s"(p.N), "s"(p.K), "s"(p.a), "s"(p.a_sg), "s"(p.lda), "s"(p.b),
+               "s"(p.b_sg), "s"(p.ldb), "s"(p.sa), "s"(p.sa_sg), "s"(p.sa_m), "s"(p.sa_kb),
+               "s"(p.sb), "s"(p.sb_sg), "s"(p.sb_n), "s"(p.sb_kb), "s"(p.out), "s"(p.o_sg),
+               "s"(p.ldo));
   const int KB = p.K / kBlockK;
   const int nblk = p.N / BN;
   const int u = first_unit();
@@ -1016,7 +1029,7 @@ narrow_kernel(const KArgs k) {
   // any moment instead of all asking for the same K block -- with row
   // strides that are multiples of 4 KB those requests would all land on
   // the same few L2 and HBM channels.  Step c works on block kbo(c).
-  const int rot = (int)(((int64_t)(u - g * nblk) * KB) / nblk);
+  const int rot = (int)((uint32_t)(u - g * nblk) % (uint32_t)KB);
   auto kbo = [&](int c) { const int t = c + rot; return t >= KB ? t - KB : t; };
   const __amdgpu_buffer_rsrc_t rdead = make_rsrc(p.b, 0);
   const int fr = lane & 15, fq = lane >> 4;
@@ -1045,46 +1058,48 @@ narrow_kernel(const KArgs k) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? rb : rdead, l, 16, b_vo, kbyte, 0, 0);
   };
 
-  // The scales of every K block go to the scale region: element e =
-  // (row m, block kb), m = e / KB, of the A rows' scales (a row past the
-  // launch reads the last valid row), and the tile's B block scale of
-  // every K block (KB <= 256: one per thread).  Rows' scales beyond the
-  // first CH per thread are staged first, each round's loads then writes;
-  // the last round's loads and the B scales' are issued ahead of the
-  // prologue's loads (the empty asm keeps them there) and written after
-  // them, so those writes wait for the scales, not for the tiles.
+  // The scales of every K block go to the scale region once: A's as [row]
+  // [K block] with a row pitch of an odd number of 4-byte words (the loop's
+  // reads of 16 rows then fall in 16 different banks), followed by the
+  // tile's B scale of every K block.  Each wave stages its own 32 rows
+  // (only it reads them); element e of a wave is row e >> lkb, K block e &
+  // (KBP - 1) for KBP = 2^lkb >= KB, so a load instruction covers whole
+  // runs of a row's contiguous bytes, and a row past the launch reads the
+  // last valid row.  Rounds of CH loads per lane; the last round's loads and
+  // the B scales' are issued ahead of the prologue's tile loads (the empty
+  // asm keeps them there) and written after them.
   uint8_t* const scl = smem + NS * WB;
   constexpr int CH = 16;
   using S = typename std::conditional<OP == BSMM_OP_FP8_BLOCKWISE, float, uint8_t>::type;
   constexpr bool SCALES = OP == BSMM_OP_FP8_MX_BMM || OP == BSMM_OP_FP8_BLOCKWISE;
-  const int n_x = SCALES ? BM * KB : 0;
-  auto x_src = [&](int e) -> S {
-    const int m = e / KB, kb = e - m * KB;
-    const int64_t mm = row0 + min(m, rows - 1);
+  const int pitch = scale_pitch<S>(KB);          // elements per staged row
+  const int lkb = KB <= 1 ? 0 : 32 - __builtin_clz(KB - 1);
+  const int n_e = SCALES ? 32 << lkb : 0;        // elements per wave, padding included
+  auto x_load = [&](int e) -> S {
+    const int r = e >> lkb, kb = e & ((1 << lkb) - 1);
+    if (e >= n_e || kb >= KB) return S(0);
+    const int64_t mm = row0 + min(32 * wave + r, rows - 1);
     if constexpr (OP == BSMM_OP_FP8_MX_BMM)
       return ((const uint8_t*)p.sa)[(int64_t)g * p.sa_sg + mm * p.sa_m + kb];
     else
       return ((const float*)p.sa)[mm * p.sa_m + (int64_t)kb * p.sa_kb];
   };
-  auto x_dst = [&](int e) -> S* {
-    const int m = e / KB, kb = e - m * KB;
-    return (S*)scl + kb * BM + scale_pos(m);
+  auto x_store = [&](int e, S v) {
+    const int r = e >> lkb, kb = e & ((1 << lkb) - 1);
+    if (e < n_e && kb < KB) ((S*)scl)[(32 * wave + r) * pitch + kb] = v;
   };
   S sv[CH];
   S wv = S(0);
+  int e_last = 0;
   if constexpr (SCALES) {
-    int e0 = 0;
-    for (; e0 + 256 * CH < n_x; e0 += 256 * CH) {
+    for (; e_last + 64 * CH < n_e; e_last += 64 * CH) {
 #pragma unroll
-      for (int i = 0; i < CH; ++i) sv[i] = x_src(e0 + threadIdx.x + 256 * i);
+      for (int i = 0; i < CH; ++i) sv[i] = x_load(e_last + 64 * i + lane);
 #pragma unroll
-      for (int i = 0; i < CH; ++i) *x_dst(e0 + threadIdx.x + 256 * i) = sv[i];
+      for (int i = 0; i < CH; ++i) x_store(e_last + 64 * i + lane, sv[i]);
     }
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int e = e0 + threadIdx.x + 256 * i;
-      sv[i] = e < n_x ? x_src(e) : S(0);
-    }
+    for (int i = 0; i < CH; ++i) sv[i] = x_load(e_last + 64 * i + lane);
     const int kb = threadIdx.x;
     if (kb < KB) {
       if constexpr (OP == BSMM_OP_FP8_MX_BMM)
@@ -1099,13 +1114,9 @@ narrow_kernel(const KArgs k) {
   static_for<0, NS>([&](auto i) { issue(decltype(i)::value, i); });
 
   if constexpr (SCALES) {
-    const int e0 = n_x > 256 * CH ? (n_x - 1) / (256 * CH) * (256 * CH) : 0;
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int e = e0 + threadIdx.x + 256 * i;
-      if (e < n_x) *x_dst(e) = sv[i];
-    }
-    if ((int)threadIdx.x < KB) ((S*)scl)[BM * KB + threadIdx.x] = wv;
+    for (int i = 0; i < CH; ++i) x_store(e_last + 64 * i + lane, sv[i]);
+    if ((int)threadIdx.x < KB) ((S*)scl)[BM * pitch + threadIdx.x] = wv;
   }
   wait_lgkm0();                            // this wave's scale writes
 
@@ -1147,16 +1158,18 @@ narrow_kernel(const KArgs k) {
     f.ws = 127;
     f.sa[0] = f.sa[1] = f.sb = 0.f;
     if constexpr (OP == BSMM_OP_FP8_MX_BMM) {
-      const uint32_t xs = *(const uint16_t*)(scl + cl * BM + 32 * wave + 2 * fr);
-      const int ws = scl[BM * KB + cl];
+      const uint8_t* xr0 = scl + (32 * wave + fr) * pitch + cl;
+      const uint32_t xs = (uint32_t)xr0[0] | ((uint32_t)xr0[16 * pitch] << 8);
+      const int ws = scl[BM * pitch + cl];
       f.xs = live ? xs : 0x7F7Fu;
       f.ws = live ? ws : 127;
     } else if constexpr (OP == BSMM_OP_FP8_BLOCKWISE) {
       const float* sf = (const float*)scl;
-      const float2 v = *(const float2*)(sf + cl * BM + 32 * wave + 2 * fr);
-      const float sb = sf[BM * KB + cl];
-      f.sa[0] = live ? v.x : 0.f;
-      f.sa[1] = live ? v.y : 0.f;
+      const float* xr0 = sf + (32 * wave + fr) * pitch + cl;
+      const float v0 = xr0[0], v1 = xr0[16 * pitch];
+      const float sb = sf[BM * pitch + cl];
+      f.sa[0] = live ? v0 : 0.f;
+      f.sa[1] = live ? v1 : 0.f;
       f.sb = live ? sb : 0.f;
     }
   };
@@ -2174,8 +2187,8 @@ int launch_narrow(const Problem& p, const Launch& l) {
   const int rows = l.row_end - l.row_begin;
   const int KB = p.K / kBlockK;
   bool ok = narrow::supported<OP>() && rows <= narrow::BM && p.N % narrow::BN == 0;
-  if constexpr (OP == BSMM_OP_FP8_MX_BMM) ok = ok && KB <= narrow::MAX_KB_MX;
-  if constexpr (OP == BSMM_OP_FP8_BLOCKWISE) ok = ok && KB <= narrow::MAX_KB_BW;
+  if constexpr (OP == BSMM_OP_FP8_MX_BMM) ok = ok && narrow::scales_fit<uint8_t>(KB);
+  if constexpr (OP == BSMM_OP_FP8_BLOCKWISE) ok = ok && narrow::scales_fit<float>(KB);
   if (!ok) {
     Launch l2 = l;
     l2.psa = nullptr;

@@ -601,3 +601,43 @@ def test_narrow_guard_bands_and_full_range(layout):
         sentinel = host_out(torch.full((1,), -7.0, dtype=tdt, device=DEV))[0]
         assert (h[mask] == sentinel).all()
         mx_check(p, dt, view)
+
+
+@pytest.mark.parametrize("KB", [33, 56, 100, 156])
+def test_narrow_mx_many_k_blocks(KB):
+    """Scale staging in several rounds (more than 32 K blocks), up to the
+    most K blocks the scale region holds; one more falls back."""
+    G, M, N, K = 2, 100, 128, KB * 128
+    p = mx_problem(G, M, N, K, 61 + KB, "m_major")
+    say(f"narrow mx exact G={G} M={M} N={N} K={K}")
+    with Forced("n128x32", 0):
+        y = mx_run(p, "f32")
+    mx_check(p, "f32", y, exact=True)
+    q = mx_problem(G, M, N, K, 62 + KB, "batch_first", codes="any", xs=(120, 134),
+                   ws=(120, 134))
+    for g, m, kb, nb, kb2 in ((0, 0, KB - 1, 0, KB - 1), (1, 99, KB // 2, 0, min(33, KB - 1)), (1, 31, 32, 0, 0)):
+        r = dict(q, x_scale=q["x_scale"].copy(), w_scale=q["w_scale"].copy())
+        r["x_scale"][g, m, kb] += 20
+        r["w_scale"][g, nb, kb2] -= 20
+        say(f"narrow mx own block K={K} g {g} row {m} kb {kb} / kb {kb2}")
+        with Forced("n128x32", 0):
+            y = mx_run(r, "f32")
+        mx_check(r, "f32", y)
+
+
+def test_narrow_blockwise_most_k_blocks_and_beyond():
+    """Blockwise at 33 and 39 K blocks (two staging rounds; 39 is the most
+    the scale region holds) and its own-block placement there."""
+    for KB in (33, 39):
+        p = bw_problem(70, 256, KB * 128, 63 + KB)
+        say(f"narrow blockwise exact K={KB * 128}")
+        with Forced("n128x32", 0):
+            y = bw_run(p, "bf16")
+        bw_check(p, "bf16", y, exact=True)
+        q = bw_problem(70, 256, KB * 128, 64 + KB, codes="any", scales=(-1, 1))
+        q["scale_a"][69, KB - 1] *= np.float32(2.0**20)
+        q["scale_a"][3, 32] *= np.float32(2.0**20)
+        q["scale_b"][KB - 2, 1] *= np.float32(2.0**-20)
+        with Forced("n128x32", 0):
+            y = bw_run(q, "f32")
+        bw_check(q, "f32", y)
