@@ -143,10 +143,14 @@ static bool plan_packed(const Plan& pl, bsmm_op op) {
 static size_t plan_ws(const Plan& pl, bsmm_op op, int G, int M, int N, int K) {
   const size_t pack = plan_packed(pl, op) ? packed_scale_bytes(op, G, M, K, N) : 0;
   const int rows = pl.m_split ? pl.m_split : M;
-  size_t main = pl.v->persistent ? persistent_workspace(pl.v, op) : ws_bytes(G, rows, N, pl.split);
+  auto launch_ws = [&](const Variant* v, int r, int split) {
+    if (v->persistent) return persistent_workspace(v, op);
+    if (v->kind == 3 || v->kind == 4) return narrow_workspace(G, N, v->tile_n, split);
+    return ws_bytes(G, r, N, split);
+  };
+  size_t main = launch_ws(pl.v, rows, pl.split);
   if (pl.tail && pl.m_split) {
-    const size_t t = pl.tail->persistent ? persistent_workspace(pl.tail, op)
-                                         : ws_bytes(G, M - pl.m_split, N, pl.tail_split);
+    const size_t t = launch_ws(pl.tail, M - pl.m_split, pl.tail_split);
     if (t > main) main = t;
   }
   return pack + main;
@@ -232,7 +236,7 @@ static Plan make_plan_uncached(bsmm_op op, int G, int M, int N, int K, bsmm_dtyp
         if (tv->persistent) pl.tail_split = 1;
       }
       pl.source = 3;
-      if (pl.v->persistent || pl.v->max_m) pl.split = 1;
+      if (pl.v->persistent || pl.v->kind == 2) pl.split = 1;   // no split-K in these kernels
       fit_workspace(pl, op, G, M, N, K, dt, workspace_bytes);
       return pl;
     }
@@ -271,7 +275,7 @@ static Plan make_plan_uncached(bsmm_op op, int G, int M, int N, int K, bsmm_dtyp
     pl.source = 2;
   }
   if (pl.split > KB) pl.split = KB > 0 ? KB : 1;
-  if (pl.v->persistent || pl.v->max_m) pl.split = 1;
+  if (pl.v->persistent || pl.v->kind == 2) pl.split = 1;   // no split-K in these kernels
   fit_workspace(pl, op, G, M, N, K, dt, workspace_bytes);
   return pl;
 }

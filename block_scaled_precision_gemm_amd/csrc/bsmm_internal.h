@@ -79,8 +79,19 @@ struct Variant {
   int wg_per_cu;        // workgroups one CU holds (LDS / registers)
   const char* unpacked; // the same kernel without packed scales (or null)
   int max_m;            // largest M the kernel takes in one launch (0: any)
+  int kind;             // 0 tile, 1 wide-wave tile, 2 skinny, 3 / 4 narrow (32 / 64 columns)
   LaunchFn launch;
 };
+
+// Workspace of a narrow-kernel launch split into S K ranges: S partial
+// 128 x tile_n tiles (4-byte elements) per output tile, then one 64-bit
+// counter per output tile.  It also covers the split-K partials of the tile
+// kernel the narrow launch falls back to (at most 128 rows).
+inline size_t narrow_workspace(int G, int N, int tile_n, int split) {
+  if (split <= 1) return 0;
+  const size_t tiles = (size_t)G * (size_t)((N + tile_n - 1) / tile_n);
+  return (size_t)split * tiles * 128u * (size_t)tile_n * 4u + tiles * 8u;
+}
 
 // Packed scale_a for the fp8 kernels: K block major, rows padded to a
 // multiple of 256, and within every 64 rows the element of row

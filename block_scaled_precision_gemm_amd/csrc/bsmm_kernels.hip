@@ -101,6 +101,7 @@ struct KArgs {
   const void* psa;    // packed scale_a [G][KB][psa_ld] (packed-scale kernels)
   int64_t psa_ld;
   int units;          // tiles_m * tiles_n * G * splits work units of the launch
+  uint64_t epoch;     // narrow split-K: distinct per launch (tags its counters)
 };
 
 template <int OP> struct OpT;
@@ -940,28 +941,40 @@ skinny_kernel(const KArgs k) {
 
 // ---------------------------------------------------------------------------
 // Narrow kernel for 16 < M <= 128 (decode batches: bound by reading B once).
-// One workgroup computes a 128-row x 32-column output tile over the whole of
-// K: no split-K partials, no reduction launch, no scale packing.  Its four
-// waves each own 32 rows (two 16-row MFMA tiles) and both 16-column tiles.
+// One workgroup computes a 128-row x BN-column output tile (BN = 32 or 64)
+// over its share of K: the whole of K, or one of S contiguous K ranges whose
+// partial tiles the last-arriving workgroup adds (below).  Its four waves
+// each own 32 rows (two 16-row MFMA tiles) and all BN / 16 column tiles.
 //
 // A rows are used by one wave only, so each wave loads its own straight
 // into registers in the matrix instruction's operand layout (a lane's 32
 // bytes of its row per K block: two 16-byte loads per tile), NS K blocks
 // ahead: a ring of NS register sets, indexed by a constant in the loop,
-// which is unrolled NS times.  The 32 x 128-byte B tile of a K block is
-// shared by the four waves: it goes global -> LDS (each wave one 8-row
-// quarter, a direct-to-LDS load) into a ring of NS 4 KB slots.  At block c
-// a wave waits for its own loads of block c, the barrier makes every wave's
-// B quarter visible and frees block c - 1's B slot, and block c + NS - 1 is
-// requested into the registers and slot block c - 1 used; NS - 1 blocks
-// stay in flight.  (Direct-to-LDS loads alone kept too few bytes in flight
-// here: the A tile is 80% of each block.)  K blocks past the end run as
-// zeros with neutral scales.
+// which is unrolled NS times.  The BN x 128-byte B tile of a K block is
+// shared by the four waves: it goes global -> LDS (each wave a quarter, by
+// direct-to-LDS loads) into a ring of NS slots.  At block c a wave waits for
+// its own loads of block c + 1, the barrier makes every wave's quarter of
+// block c + 1 visible and frees block c - 1's slot, block c + NS - 1 is
+// requested into the registers and slot block c - 1 used, the B fragments
+// of block c + 1 are read, and block c's matrix instructions run on the
+// fragments read one step earlier.  (Direct-to-LDS loads alone kept too few
+// bytes in flight: A is two thirds or more of each block.)  Steps past the
+// end run dead loads (zeros) with neutral scales.
 //
-// The per-block scales are staged in LDS once, before the K loop: mx: the
-// e8m0 byte of each of the 128 rows per K block, and the tile's B block
-// byte per K block; blockwise: the fp32 row scales and the B block scale.
-// The grid is G x (N / 32) workgroups in the XCD-aware order, so the
+// The per-block scales of the workgroup's K range are staged in LDS once,
+// before the K loop: mx: the e8m0 byte of each of the 128 rows per K block
+// and the tile's B block byte per K block; blockwise: the fp32 row scales
+// and the B block scale.
+//
+// Split K (S > 1): every workgroup stores its fp32 / int32 partial tile in
+// a slot of the workspace and then counts itself in the tile's counter with
+// a global atomic; the one that brings the count to S adds the S partials in
+// ascending K order and runs the epilogue.  No
+// workgroup waits for another.  A counter holds the launch's 40-bit tag
+// above a 24-bit count; a value with another tag counts as zero, so the
+// counters need no clearing between launches.
+//
+// The grid is G x (N / BN) x S workgroups in the XCD-aware order, so the
 // workgroups of one batch share an XCD and read that batch's A from its L2.
 // ---------------------------------------------------------------------------
 // f(integral_constant<int, i>) for i = B .. E - 1, unrolled
@@ -974,11 +987,17 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 namespace narrow {
-constexpr int BM = 128, BN = 32, NS = 8;
-constexpr int WB = BN * kBlockK;              // B tile bytes per K block (4 KB)
-constexpr int SCL = 20480;                    // scale region
-constexpr int LDS = NS * WB + SCL;            // 52 KB
-constexpr int LOADS = 5;                      // per wave and K block: 4 A + 1 B
+constexpr int BM = 128;
+constexpr int SCL = 20480;                       // scale region
+template <int BN> struct Cfg {
+  static_assert(BN == 32 || BN == 64, "tile widths");
+  static constexpr int NS = BN == 32 ? 8 : 6;    // K blocks in the ring
+  static constexpr int WB = BN * kBlockK;        // B tile bytes per K block
+  static constexpr int BL = BN / 32;             // B loads per wave and K block
+  static constexpr int LOADS = 4 + BL;           // per wave and K block: 4 A + B
+  static constexpr int TJ = BN / 16;             // 16-column MFMA tiles
+  static constexpr int LDS = NS * WB + SCL;
+};
 // Staged scale rows: KB elements padded to an odd number of 4-byte words.
 template <class S> __host__ __device__ constexpr int scale_pitch(int KB) {
   return sizeof(S) == 1 ? ((((KB + 3) >> 2) | 1) << 2) : (KB | 1);
@@ -992,31 +1011,46 @@ template <int OP> constexpr bool supported() {
          OP == BSMM_OP_INT8_ROWWISE || OP == BSMM_OP_FP8_SCALED_MM;
 }
 }  // namespace narrow
+constexpr int kNarrowLds = narrow::Cfg<32>::LDS > narrow::Cfg<64>::LDS ? narrow::Cfg<32>::LDS
+                                                                        : narrow::Cfg<64>::LDS;
 
-template <int OP, int OUT>
+template <int OP, int OUT, int BN>
 __global__ void __launch_bounds__(256)
 narrow_kernel(const KArgs k) {
   using namespace narrow;
+  using C = Cfg<BN>;
+  constexpr int NS = C::NS, WB = C::WB, BL = C::BL, LOADS = C::LOADS, TJ = C::TJ;
   using acc_t = typename OpT<OP>::acc_t;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS];
+  typedef typename OpT<OP>::elem_t E;
+  // LDS sized for the wider tile (one workgroup per CU either way)
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kNarrowLds];
+  static_assert(C::LDS <= kNarrowLds, "LDS");
   const Problem& p = k.p;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   // Every kernel argument read below, loaded in one batch before anything
   // else: left to the compiler, each load waits for the branch or address
   // that first needs it, and the workgroup pays several dependent round
   // trips to the argument buffer before its first tile load.
   asm volatile("" ::"s"(gridDim.x), "s"(k.units), "s"(k.row_begin), "s"(k.row_end),
-               "s"(k.vec_out), "s"(p.N), "s"(p.K), "s"(p.a), "s"(p.a_sg), "s"(p.lda), "s"(p.b),
-               "s"(p.b_sg), "s"(p.ldb), "s"(p.sa), "s"(p.sa_sg), "s"(p.sa_m), "s"(p.sa_kb),
-               "s"(p.sb), "s"(p.sb_sg), "s"(p.sb_n), "s"(p.sb_kb), "s"(p.out), "s"(p.o_sg),
-               "s"(p.ldo));
+               "s"(k.vec_out), "s"(k.splits), "s"(k.kb_per_split), "s"(p.N), "s"(p.K), "s"(p.a), "s"(p.a_sg),
+               "s"(p.lda), "s"(p.b), "s"(p.b_sg), "s"(p.ldb), "s"(p.sa), "s"(p.sa_sg),
+               "s"(p.sa_m), "s"(p.sa_kb), "s"(p.sb), "s"(p.sb_sg), "s"(p.sb_n), "s"(p.sb_kb),
+               "s"(p.out), "s"(p.o_sg), "s"(p.ldo));
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int KB = p.K / kBlockK;
   const int nblk = p.N / BN;
+  const int S = k.splits;
   const int u = first_unit();
   if (u >= k.units) return;
-  const int g = u / nblk;
-  const int col0 = (u - g * nblk) * BN;
+  const int g = u / (nblk * S);
+  const int rem = u - g * nblk * S;
+  const int jt = rem / S;                      // column tile
+  const int ks = rem - jt * S;                 // K range
+  const int col0 = jt * BN;
+  // K ranges of kb_per_split blocks, the last one shorter (the launch
+  // picks S so that none is empty)
+  const int kb0 = ks * k.kb_per_split;
+  const int nk = min(k.kb_per_split, KB - kb0);
   const int row0 = k.row_begin;
   const int rows = k.row_end - row0;          // <= BM
 
@@ -1024,13 +1058,14 @@ narrow_kernel(const KArgs k) {
       p.a + (int64_t)g * p.a_sg + (int64_t)row0 * p.lda, (uint64_t)rows * p.lda);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(
       p.b + (int64_t)g * p.b_sg + (int64_t)col0 * p.ldb, (uint64_t)BN * p.ldb);
-  // The workgroup's walk over K starts at block rot and wraps: the tiles of
-  // one batch (which share an XCD) spread their requests over all of K at
-  // any moment instead of all asking for the same K block -- with row
-  // strides that are multiples of 4 KB those requests would all land on
-  // the same few L2 and HBM channels.  Step c works on block kbo(c).
-  const int rot = (int)((uint32_t)(u - g * nblk) % (uint32_t)KB);
-  auto kbo = [&](int c) { const int t = c + rot; return t >= KB ? t - KB : t; };
+  // The workgroup's walk over its K range starts at local block rot and
+  // wraps: the tiles of one batch (which share an XCD) spread their requests
+  // over K at any moment instead of all asking for the same K block -- with
+  // row strides that are multiples of 4 KB those would all land on the same
+  // few L2 and HBM channels.  Step c works on local block kbo(c), global
+  // block kb0 + kbo(c).
+  const int rot = (int)((uint32_t)jt % (uint32_t)nk);
+  auto kbo = [&](int c) { const int t = c + rot; return t >= nk ? t - nk : t; };
   const __amdgpu_buffer_rsrc_t rdead = make_rsrc(p.b, 0);
   const int fr = lane & 15, fq = lane >> 4;
   const uint32_t lda = (uint32_t)p.lda, ldb = (uint32_t)p.ldb;
@@ -1039,57 +1074,69 @@ narrow_kernel(const KArgs k) {
   uint32_t a_vo[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) a_vo[i] = (uint32_t)(32 * wave + 16 * i + fr) * lda + 32u * fq;
-  // B: this wave's quarter, rows 8 wave + lane / 8, chunk (lane % 8) ^ swz
-  const int b_row = wave * 8 + (lane >> 3);
-  const uint32_t b_vo = (uint32_t)b_row * ldb + ((uint32_t)((lane & 7) ^ swz(b_row)) << 4);
+  // B: this wave's quarter, BL groups of 8 rows; group q = BL wave + t holds
+  // rows 8 q + lane / 8, chunk (lane % 8) ^ swz, at slot bytes 1024 q
+  // (a fixed size: with a BN-dependent one the host-side pass drops the
+  // kernel template, with no stub and no error, where a lambda hands an
+  // element to the buffer builtin)
+  uint32_t b_vo[2];
+#pragma unroll
+  for (int t = 0; t < BL; ++t) {
+    const int b_row = (BL * wave + t) * 8 + (lane >> 3);
+    b_vo[t] = (uint32_t)b_row * ldb + ((uint32_t)((lane & 7) ^ swz(b_row)) << 4);
+  }
   i32x4 xr[NS][2][2];            // A fragments of the NS blocks in flight
-  // block b's loads into register set / B slot s (a constant)
+  // step b's loads into register set / B slot s (a constant)
   auto issue = [&](int b, auto s_c) {
     constexpr int s = decltype(s_c)::value;
-    const bool live = b < KB;
+    const bool live = b < nk;
     const __amdgpu_buffer_rsrc_t rA = live ? ra : rdead;
-    const int kbyte = (live ? kbo(b) : 0) * kBlockK;
+    const int kbyte = (live ? kb0 + kbo(b) : 0) * kBlockK;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       xr[s][i][0] = __builtin_amdgcn_raw_buffer_load_b128(rA, a_vo[i], kbyte, 0);
       xr[s][i][1] = __builtin_amdgcn_raw_buffer_load_b128(rA, a_vo[i] + 16, kbyte, 0);
     }
-    const lds_ptr_t l = (lds_ptr_t)(uintptr_t)(uint32_t)(uintptr_t)(smem + s * WB + wave * 1024);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? rb : rdead, l, 16, b_vo, kbyte, 0, 0);
+#pragma unroll
+    for (int t = 0; t < BL; ++t) {
+      const lds_ptr_t l = (lds_ptr_t)(uintptr_t)(uint32_t)(uintptr_t)(
+          smem + s * WB + (BL * wave + t) * 1024);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? rb : rdead, l, 16, b_vo[t], kbyte, 0, 0);
+    }
   };
 
-  // The scales of every K block go to the scale region once: A's as [row]
-  // [K block] with a row pitch of an odd number of 4-byte words (the loop's
-  // reads of 16 rows then fall in 16 different banks), followed by the
-  // tile's B scale of every K block.  Each wave stages its own 32 rows
-  // (only it reads them); element e of a wave is row e >> lkb, K block e &
-  // (KBP - 1) for KBP = 2^lkb >= KB, so a load instruction covers whole
-  // runs of a row's contiguous bytes, and a row past the launch reads the
-  // last valid row.  Rounds of CH loads per lane; the last round's loads and
-  // the B scales' are issued ahead of the prologue's tile loads (the empty
-  // asm keeps them there) and written after them.
+  // The scales of the K range go to the scale region once: A's as [row]
+  // [local K block] with a row pitch of an odd number of 4-byte words (the
+  // loop's reads of 16 rows then fall in 16 different banks), followed by
+  // the tile's B scale of every local K block.  Each wave stages its own 32
+  // rows (only it reads them); element e of a wave is row e >> lkb, local
+  // K block e & (KBP - 1) for KBP = 2^lkb >= nk, so a load instruction
+  // covers whole runs of a row's contiguous bytes, and a row past the launch
+  // reads the last valid row.  Rounds of CH loads per lane; the last round's
+  // loads and the B scales' are issued ahead of the prologue's tile loads
+  // (the empty asm keeps them there) and written after them.
   uint8_t* const scl = smem + NS * WB;
   constexpr int CH = 16;
-  using S = typename std::conditional<OP == BSMM_OP_FP8_BLOCKWISE, float, uint8_t>::type;
+  using SC = typename std::conditional<OP == BSMM_OP_FP8_BLOCKWISE, float, uint8_t>::type;
   constexpr bool SCALES = OP == BSMM_OP_FP8_MX_BMM || OP == BSMM_OP_FP8_BLOCKWISE;
-  const int pitch = scale_pitch<S>(KB);          // elements per staged row
-  const int lkb = KB <= 1 ? 0 : 32 - __builtin_clz(KB - 1);
+  const int pitch = scale_pitch<SC>(nk);         // elements per staged row
+  const int lkb = nk <= 1 ? 0 : 32 - __builtin_clz(nk - 1);
   const int n_e = SCALES ? 32 << lkb : 0;        // elements per wave, padding included
-  auto x_load = [&](int e) -> S {
+  auto x_load = [&](int e) -> SC {
     const int r = e >> lkb, kb = e & ((1 << lkb) - 1);
-    if (e >= n_e || kb >= KB) return S(0);
+    if (e >= n_e || kb >= nk) return SC(0);
     const int64_t mm = row0 + min(32 * wave + r, rows - 1);
     if constexpr (OP == BSMM_OP_FP8_MX_BMM)
-      return ((const uint8_t*)p.sa)[(int64_t)g * p.sa_sg + mm * p.sa_m + kb];
+      return ((const uint8_t*)p.sa)[(int64_t)g * p.sa_sg + mm * p.sa_m + kb0 + kb];
     else
-      return ((const float*)p.sa)[mm * p.sa_m + (int64_t)kb * p.sa_kb];
+      return ((const float*)p.sa)[mm * p.sa_m + (int64_t)(kb0 + kb) * p.sa_kb];
   };
-  auto x_store = [&](int e, S v) {
+  auto x_store = [&](int e, SC v) {
     const int r = e >> lkb, kb = e & ((1 << lkb) - 1);
-    if (e < n_e && kb < KB) ((S*)scl)[(32 * wave + r) * pitch + kb] = v;
+    if (e < n_e && kb < nk) ((SC*)scl)[(32 * wave + r) * pitch + kb] = v;
   };
-  S sv[CH];
-  S wv = S(0);
+  SC sv[CH];
+  SC wv = SC(0);
   int e_last = 0;
   if constexpr (SCALES) {
     for (; e_last + 64 * CH < n_e; e_last += 64 * CH) {
@@ -1101,40 +1148,41 @@ narrow_kernel(const KArgs k) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) sv[i] = x_load(e_last + 64 * i + lane);
     const int kb = threadIdx.x;
-    if (kb < KB) {
+    if (kb < nk) {
       if constexpr (OP == BSMM_OP_FP8_MX_BMM)
-        wv = ((const uint8_t*)p.sb)[(int64_t)g * p.sb_sg + (int64_t)(col0 / kBlockK) * p.sb_n + kb];
+        wv = ((const uint8_t*)p.sb)[(int64_t)g * p.sb_sg + (int64_t)(col0 / kBlockK) * p.sb_n +
+                                    kb0 + kb];
       else
-        wv = ((const float*)p.sb)[(int64_t)kb * p.sb_kb + (int64_t)(col0 / kBlockK) * p.sb_n];
+        wv = ((const float*)p.sb)[(int64_t)(kb0 + kb) * p.sb_kb + (int64_t)(col0 / kBlockK) * p.sb_n];
     }
     asm volatile("" ::: "memory");
   }
 
-  // prologue: blocks 0 .. NS-1 into every register set and slot
+  // prologue: steps 0 .. NS-1 into every register set and slot
   static_for<0, NS>([&](auto i) { issue(decltype(i)::value, i); });
 
   if constexpr (SCALES) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) x_store(e_last + 64 * i + lane, sv[i]);
-    if ((int)threadIdx.x < KB) ((S*)scl)[BM * pitch + threadIdx.x] = wv;
+    if ((int)threadIdx.x < nk) ((SC*)scl)[BM * pitch + threadIdx.x] = wv;
   }
   wait_lgkm0();                            // this wave's scale writes
 
-  acc_t acc[2][2];
+  acc_t acc[2][TJ];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = acc_t{0, 0, 0, 0};
+    for (int j = 0; j < TJ; ++j) acc[i][j] = acc_t{0, 0, 0, 0};
   // B fragments: rows 16 j + f, chunks 2 fq and 2 fq + 1
-  int b_off[2][2];
+  int b_off[TJ][2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < TJ; ++j) {
     b_off[j][0] = lds_off(16 * j + fr, 2 * fq);
     b_off[j][1] = lds_off(16 * j + fr, 2 * fq + 1);
   }
-  // B fragments and scales of a K block, into the set of the block's parity
+  // B fragments and scales of a step, into the set of the step's parity
   struct BFrags {
-    i32x8 b[2];
+    i32x8 b[TJ];
     uint32_t xs;       // mx: the lane's two row scale bytes (byte i: A tile i)
     int ws;            // mx: the B block's scale byte
     float sa[2], sb;   // blockwise
@@ -1144,16 +1192,16 @@ narrow_kernel(const KArgs k) {
     constexpr int s = decltype(s_c)::value;
     const uint8_t* sb_ = smem + s * WB;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < TJ; ++j) {
       const i32x4 lo = *(const i32x4*)(sb_ + b_off[j][0]);
       const i32x4 hi = *(const i32x4*)(sb_ + b_off[j][1]);
       f.b[j] = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
     }
-    // blocks past the end: neutral scales (their products are zeros); the
+    // steps past the end: neutral scales (their products are zeros); the
     // reads go to the last block and are selected away, so the step stays
     // one straight-line block that the fences can pin
-    const bool live = c < KB;
-    const int cl = kbo(min(c, KB - 1));
+    const bool live = c < nk;
+    const int cl = kbo(min(c, nk - 1));
     f.xs = 0x7F7Fu;
     f.ws = 127;
     f.sa[0] = f.sa[1] = f.sb = 0.f;
@@ -1180,7 +1228,7 @@ narrow_kernel(const KArgs k) {
       const i32x4 lo = xr[s][i][0], hi = xr[s][i][1];
       const i32x8 af = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < TJ; ++j) {
         if constexpr (OP == BSMM_OP_INT8_ROWWISE) {
           acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
               i32x4{f.b[j][0], f.b[j][1], f.b[j][2], f.b[j][3]}, lo, acc[i][j], 0, 0, 0);
@@ -1202,21 +1250,20 @@ narrow_kernel(const KArgs k) {
       }
     }
   };
-  // Block 0's B fragments before the loop: every wave's loads of block 0
+  // Step 0's B fragments before the loop: every wave's loads of step 0
   // landed, its scale writes done, then the barrier.
   wait_vmcnt<(NS - 1) * LOADS>();
   wait_lgkm0();
   lds_barrier();
   __builtin_amdgcn_sched_barrier(0);
   read_b(0, std::integral_constant<int, 0>(), bq[0]);
-  // Step c: wait for this wave's loads of block c + 1 (the later blocks in
-  // flight may stay outstanding: NS - 2 at c = 0, then NS - 3), the
-  // barrier (every wave's B quarter of block c + 1 visible; block c - 1's
-  // B slot no longer read, its fragments were read in step c - 2), the
-  // refill of block c - 1's register set and slot with block c + NS - 1,
-  // the B fragments of block c + 1, and block c's matrix instructions on
-  // fragments read in step c - 1.  The fences keep every LDS read after its
-  // barrier.
+  // Step c: wait for this wave's loads of step c + 1 (the later steps in
+  // flight may stay outstanding: NS - 2 at c = 0, then NS - 3), the barrier
+  // (every wave's B quarter of step c + 1 visible; step c - 1's slot no
+  // longer read, its fragments were read in step c - 2), the refill of step
+  // c - 1's register set and slot with step c + NS - 1, the B fragments of
+  // step c + 1, and step c's matrix instructions on fragments read in step
+  // c - 1.  The fences keep every LDS read after its barrier.
   auto step = [&](int c, auto s_c, auto first_c) {
     constexpr int s = decltype(s_c)::value;
     constexpr bool FIRST = decltype(first_c)::value;
@@ -1231,14 +1278,76 @@ narrow_kernel(const KArgs k) {
     compute(s_c, bq[s & 1]);
     __builtin_amdgcn_sched_barrier(0);
   };
-  // blocks in groups of NS (register set s = c % NS); the last group's
-  // blocks past KB are zeros (dead loads) with neutral scales
-  static_assert(NS % 2 == 0, "B fragment sets alternate with the block's parity");
+  // steps in groups of NS (register set s = c % NS); the last group's steps
+  // past nk are zeros (dead loads) with neutral scales
+  static_assert(NS % 2 == 0, "B fragment sets alternate with the step's parity");
   step(0, std::integral_constant<int, 0>(), std::true_type());
   static_for<1, NS>([&](auto i) { step(decltype(i)::value, i, std::false_type()); });
-  for (int c0 = NS; c0 < KB; c0 += NS)
+  for (int c0 = NS; c0 < nk; c0 += NS)
     static_for<0, NS>([&](auto i) { step(c0 + decltype(i)::value, i, std::false_type()); });
   wait_vmcnt<0>();                       // the last refills were out-of-range loads
+
+  if (S > 1) {
+    // Publish this K range's partial in slot (tile, ks): the lane's 16
+    // bytes of MFMA tile (wave, i, j) at ((wave * 2 + i) * TJ + j) * 1024 +
+    // 16 lane, so each store instruction writes 1 KB of whole lines, and
+    // the last arriver's lanes read the same positions of every slot.  The
+    // partials and the counter are touched only through agent-scope
+    // (sc1) accesses: those stores write through to the device's coherence
+    // point and those loads read from it, and a store has reached it once
+    // the wave's vmcnt wait covers it.  So the waits below order the
+    // partials before the count (and the count before the reads) without a
+    // fence's L2 write-back and invalidate, which serialise across an
+    // XCD's workgroups and cost more than the K loop.
+    constexpr int SLOT = BM * BN * 4;
+    constexpr int SC1 = 16;                    // buffer cache policy: agent scope
+    const int tile = g * nblk + jt;
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc((uint8_t*)k.ws + (size_t)tile * S * SLOT,
+                                                (uint64_t)S * SLOT);
+    uint64_t* const counters = (uint64_t*)((uint8_t*)k.ws + (size_t)k.units * SLOT);
+    auto pos = [&](int i, int j) { return (uint32_t)(((wave * 2 + i) * TJ + j) * 1024 + 16 * lane); };
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, acc[i][j]), rw, pos(i, j),
+                                               ks * SLOT, SC1);
+    wait_vmcnt<0>();     // this wave's partial has reached the coherence point
+    __syncthreads();     // ... every wave's; the ring is idle
+    int* const last_arrival = (int*)smem;
+    if (threadIdx.x == 0) {
+      const uint64_t tag = k.epoch & ((1ull << 40) - 1);
+      uint64_t* ctr = counters + tile;
+      uint64_t old = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      uint64_t now;
+      // lock-free: a failed exchange means another range's succeeded, so
+      // at most S attempts
+      do {
+        now = (old >> 24) == tag ? old + 1 : ((tag << 24) | 1u);
+      } while (!__hip_atomic_compare_exchange_strong(ctr, &old, now, __ATOMIC_RELAXED,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      *last_arrival = (int)(now & 0xFFFFFFu) == S;
+    }
+    __syncthreads();
+    if (!*last_arrival) return;
+    // the S partials in ascending K order, this workgroup's own read back
+    // like the others (choosing between it and a load would put the
+    // accumulators in scratch memory)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        acc_t sum = __builtin_bit_cast(acc_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  rw, pos(i, j), 0, SC1));
+        for (int s2 = 1; s2 < S; ++s2) {
+          const acc_t v = __builtin_bit_cast(
+              acc_t, __builtin_amdgcn_raw_buffer_load_b128(rw, pos(i, j), s2 * SLOT, SC1));
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sum[r] += v[r];
+        }
+        acc[i][j] = sum;
+      }
+  }
 
   // epilogue: lane holds row 32 wave + 16 i + f, columns 16 j + 4 fq .. + 3
   const bool vec = k.vec_out != 0;
@@ -1249,7 +1358,7 @@ narrow_kernel(const KArgs k) {
     if (mr >= rows) continue;
     const int m = row0 + mr;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < TJ; ++j) {
       const int n = col0 + 16 * j + 4 * fq;
       float y[4];
       int yi[4];
@@ -2178,17 +2287,23 @@ int launch_skinny(const Problem& p, const Launch& l) {
   return check_launch();
 }
 
-// The narrow kernel (16 < rows <= 128): one workgroup per 32 columns of each
-// batch over the whole of K.  Shapes it does not take (more rows, N not a
-// multiple of 32, more K blocks than its scale region holds, an operation
-// it lacks) run the 128 x 128 tile kernel instead.
-template <int OP, int OUT>
+// The narrow kernel (16 < rows <= 128): one workgroup per BN columns of each
+// batch and K range.  Shapes it does not take (more rows, N not a multiple
+// of BN, more K blocks per range than its scale region holds, an operation
+// it lacks) run the 128 x 128 tile kernel instead.  A split the workspace
+// cannot hold (or more ranges than K blocks) is reduced.
+template <int OP, int OUT, int BN>
 int launch_narrow(const Problem& p, const Launch& l) {
   const int rows = l.row_end - l.row_begin;
   const int KB = p.K / kBlockK;
-  bool ok = narrow::supported<OP>() && rows <= narrow::BM && p.N % narrow::BN == 0;
-  if constexpr (OP == BSMM_OP_FP8_MX_BMM) ok = ok && narrow::scales_fit<uint8_t>(KB);
-  if constexpr (OP == BSMM_OP_FP8_BLOCKWISE) ok = ok && narrow::scales_fit<float>(KB);
+  int S = l.split < 1 ? 1 : (l.split > KB ? (KB > 0 ? KB : 1) : l.split);
+  if (S > 1 && (!l.ws || l.ws_bytes < narrow_workspace(p.G, p.N, BN, S))) S = 1;
+  // ranges of ceil(KB / S) blocks; as many as that leaves non-empty
+  const int nk_max = KB > 0 ? (KB + S - 1) / S : 0;
+  if (nk_max > 0) S = (KB + nk_max - 1) / nk_max;
+  bool ok = narrow::supported<OP>() && rows <= narrow::BM && p.N % BN == 0;
+  if constexpr (OP == BSMM_OP_FP8_MX_BMM) ok = ok && narrow::scales_fit<uint8_t>(nk_max);
+  if constexpr (OP == BSMM_OP_FP8_BLOCKWISE) ok = ok && narrow::scales_fit<float>(nk_max);
   if (!ok) {
     Launch l2 = l;
     l2.psa = nullptr;
@@ -2201,19 +2316,20 @@ int launch_narrow(const Problem& p, const Launch& l) {
     k.row_end = l.row_end;
     k.psa = nullptr;
     k.psa_ld = 0;
-    k.ws = nullptr;
-    k.splits = 1;
-    k.kb_per_split = KB;
+    k.ws = S > 1 ? l.ws : nullptr;
+    k.splits = S;
+    k.kb_per_split = nk_max;
     k.tiles_m = 1;
-    k.tiles_n = p.N / narrow::BN;
+    k.tiles_n = p.N / BN;
     k.vec_out = out_vec_ok<OUT>(p);
+    k.epoch = S > 1 ? next_epoch() : 0;
     hipStream_t s = (hipStream_t)l.stream;
     if (KB == 0) {
       hipLaunchKernelGGL((zero_out<OP, OUT>), dim3(1024), dim3(256), 0, s, k);
       return check_launch();
     }
-    k.units = p.G * k.tiles_n;
-    hipLaunchKernelGGL((narrow_kernel<OP, OUT>), dim3((unsigned)k.units), dim3(256), 0, s, k);
+    k.units = p.G * k.tiles_n * S;
+    hipLaunchKernelGGL((narrow_kernel<OP, OUT, BN>), dim3((unsigned)k.units), dim3(256), 0, s, k);
     return check_launch();
   }
   return 1;
@@ -2232,8 +2348,8 @@ int launch_kernel(const Problem& p, const Launch& l) {
     return 1;
   } else if constexpr (KIND == 2) {
     return launch_skinny<OP, OUT, RING>(p, l);
-  } else if constexpr (KIND == 3) {
-    return launch_narrow<OP, OUT>(p, l);
+  } else if constexpr (KIND == 3 || KIND == 4) {
+    return launch_narrow<OP, OUT, KIND == 3 ? 32 : 64>(p, l);
   } else if constexpr (KIND == 1) {
     // wide waves for int8 / mx / scaled_mm; blockwise and mx32 (per-lane
     // column scales) run the 256 x 256 eight-wave kernel

@@ -44,11 +44,11 @@ constexpr unsigned kAllOps = 63u;
 
 // name, tile_m, tile_n, ops, masked tail, persistent, packed scales,
 // workgroups per CU, unpacked sibling, largest M (the skinny kernel: 16,
-// the narrow kernel: 128),
-// launch
+// the narrow kernels: 128), kind, launch
 const Variant kVariants[] = {
 #define BSMM_VARIANT(NAME, TM, TN, WM, WN, RING, SK, PK, WPC, UNPACKED, KIND) \
-  {NAME, TM, TN, kAllOps, true, SK, PK, WPC, UNPACKED, KIND == 2 ? 16 : KIND == 3 ? 128 : 0,  \
+  {NAME, TM, TN, kAllOps, true, SK, PK, WPC, UNPACKED,                                      \
+   KIND == 2 ? 16 : (KIND == 3 || KIND == 4) ? 128 : 0, KIND,                                \
    launch_variant<WM, WN, RING, SK, PK, KIND>},
 #include "bsmm_variants.inc"
 #undef BSMM_VARIANT

@@ -641,3 +641,94 @@ def test_narrow_blockwise_most_k_blocks_and_beyond():
         with Forced("n128x32", 0):
             y = bw_run(q, "f32")
         bw_check(q, "f32", y)
+
+
+# ------------------------- the narrow kernel: 64 columns and split K --
+
+NARROW_PLANS = [("n128x32", 2), ("n128x32", 3), ("n128x64", 1), ("n128x64", 2), ("n128x64", 5)]
+
+
+@pytest.mark.parametrize("variant,split", NARROW_PLANS)
+def test_narrow_split_mx_bit_exact(variant, split):
+    """Both widths, K split into 1 to 5 ranges added in the kernel (10 K
+    blocks: ranges of 2 to 5 blocks, the last one shorter), both layouts,
+    three batches."""
+    for layout in ("m_major", "batch_first"):
+        p = mx_problem(3, 100, 384, 1280, 70 + split, layout)
+        for dt in ("f32", "bf16"):
+            say(f"narrow mx exact {variant} split {split} {layout} {dt}")
+            with Forced(variant, split):
+                plan = bsmm.bsmm_query_plan(bsmm.OP_FP8_MX_BMM, 3, 100, 384, 1280, dt)
+                assert plan["variant"] == variant and plan["split_k"] == split, plan
+                y = mx_run(p, dt)
+            mx_check(p, dt, y, exact=True)
+
+
+@pytest.mark.parametrize("variant,split", [("n128x64", 1), ("n128x64", 3), ("n128x32", 4)])
+def test_narrow_split_blockwise_int8_scaled_mm_bit_exact(variant, split):
+    p = bw_problem(77, 512, 1280, 71 + split)
+    for dt in ("f32", "bf16"):
+        say(f"narrow blockwise exact {variant} split {split} {dt}")
+        with Forced(variant, split):
+            y = bw_run(p, dt)
+        bw_check(p, dt, y, exact=True)
+    from synth import fp8_scaled_mm_inputs, int8_rowwise_inputs
+    from tests.gpu_util import check_int8, run_int8
+    q = int8_rowwise_inputs(77, 320, 1280, 72 + split)
+    for dt in ("i32", "bf16"):
+        say(f"narrow int8 {variant} split {split} {dt}")
+        with Forced(variant, split):
+            y = run_int8(q, dt)
+        check_int8(q, dt, y)
+    t = fp8_scaled_mm_inputs(77, 192, 1024, 73 + split, bias="f32")
+    say(f"narrow scaled_mm {variant} split {split}")
+    with Forced(variant, split):
+        y = bsmm.bsmm_fp8_scaled_mm(dev(t["a"]), dev(t["b_nk"]).t(), dev(t["scale_a"]),
+                                    dev(t["scale_b"]), bias=dev(t["bias"]), scale_result=0.5,
+                                    out_dtype="f32")
+    want = S.fp8_scaled_mm(t["a"], t["b_nk"].T, t["scale_a"], t["scale_b"], bias=t["bias"],
+                           scale_result=0.5, out_dtype="f32")
+    rep = S.compare(as_f64(host_out(y)), want)
+    assert rep["ok"], rep
+
+
+def test_narrow_split_scales_land_on_their_own_blocks():
+    """10 K blocks split into 3 ranges (4, 4 and 2 blocks): a raised scale
+    at the first and last block of every range shows only in its own
+    block."""
+    G, M, N, K = 2, 128, 256, 1280
+    base = mx_problem(G, M, N, K, 74, "m_major", codes="any", xs=(120, 134), ws=(120, 134))
+    for kb in (0, 3, 4, 7, 8, 9):
+        p = dict(base, x_scale=base["x_scale"].copy(), w_scale=base["w_scale"].copy())
+        p["x_scale"][kb * 11 % M, kb % G, kb] += 20
+        p["w_scale"][(kb + 1) % G, kb % 2, kb] -= 20
+        say(f"narrow split own block kb {kb}")
+        with Forced("n128x64", 3):
+            y = mx_run(p, "f32")
+        mx_check(p, "f32", y)
+    q = bw_problem(90, 256, 1280, 75, codes="any", scales=(-1, 1))
+    q["scale_a"][89, 3] *= np.float32(2.0**20)
+    q["scale_b"][6, 1] *= np.float32(2.0**-20)
+    with Forced("n128x64", 3):
+        y = bw_run(q, "f32")
+    bw_check(q, "f32", y)
+
+
+def test_narrow_split_counters_across_calls_and_small_workspace():
+    """Launches in a row share the workspace's counters (each launch tags
+    its own); a workspace too small for the split runs unsplit."""
+    ps = [mx_problem(2, 90, 256, 1280, 76 + i, "batch_first") for i in range(3)]
+    with Forced("n128x64", 4):
+        plan = bsmm.bsmm_query_plan(bsmm.OP_FP8_MX_BMM, 2, 90, 256, 1280, "f32")
+        assert plan["variant"] == "n128x64" and plan["split_k"] == 4, plan
+        ws = torch.empty(plan["workspace"], dtype=torch.uint8, device=DEV)
+        ys = [mx_run(p, "f32", workspace=ws) for p in ps]
+    for p, y in zip(ps, ys):
+        mx_check(p, "f32", y, exact=True)
+    small = torch.empty(1024, dtype=torch.uint8, device=DEV)
+    with Forced("n128x64", 4):
+        plan = bsmm.bsmm_query_plan(bsmm.OP_FP8_MX_BMM, 2, 90, 256, 1280, "f32",
+                                    workspace_bytes=1024)
+        y = mx_run(ps[0], "f32", workspace=small)
+    assert plan["split_k"] == 1, plan
+    mx_check(ps[0], "f32", y, exact=True)
