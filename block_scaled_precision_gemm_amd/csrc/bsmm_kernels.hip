@@ -1498,18 +1498,17 @@ __device__ __forceinline__ void store_staged(const KArgs& k, int s, int g, int r
       if (MODE != kSlot && (m >= k.row_end || nvalid <= 0)) continue;
       const int64_t e = og + (int64_t)m * ldo + n;
       if constexpr (MODE == kOutAdd) {
-        typedef E e4 __attribute__((ext_vector_type(4)));
         const int64_t off = (int64_t)(m - row0) * BN + (n - col0);
         const i32x4 mine = v;
         for (int q2 = 0; q2 < sl.count; ++q2) {
           i32x4 t = mine;
           if (q2 != sl.own) {
-            const e4 s = *(const e4*)((const E*)sl.base + sl.slot(q2) * sl.stride + off);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              if constexpr (OP == BSMM_OP_INT8_ROWWISE) t[c] = s[c];
-              else t[c] = __float_as_int(s[c]);
-            }
+            // agent-scope (sc1) loads: they read the partials from the
+            // device's coherence point, where their agent-scope stores put
+            // them (every slot lies within 4 GB of slot 0)
+            t = __builtin_amdgcn_raw_buffer_load_b128(
+                make_rsrc(sl.base, 0xFFFFFFF0ull),
+                (uint32_t)((sl.slot(q2) * sl.stride + off) * (int64_t)sizeof(E)), 0, 16);
           }
           if (q2 == 0) {
             v = t;
@@ -1562,10 +1561,17 @@ __device__ __forceinline__ void store_staged(const KArgs& k, int s, int g, int r
           yi[c] = v[c];
         }
       }
-      if constexpr (PARTIAL)
+      if constexpr (MODE == kSlot) {
+        // agent-scope (sc1) stores: written through to the device's
+        // coherence point (the stream-K protocol orders them with vmcnt
+        // waits alone); the staged values are the partial's bits
+        __builtin_amdgcn_raw_buffer_store_b128(v, make_rsrc(obase, (uint64_t)BM * BN * sizeof(E)),
+                                               (uint32_t)(e * (int64_t)sizeof(E)), 0, 16);
+      } else if constexpr (PARTIAL) {
         store4<OP == BSMM_OP_INT8_ROWWISE ? BSMM_I32 : BSMM_F32>(obase, e, y, yi, vec, nvalid);
-      else
+      } else {
         store4<OUT>(obase, e, y, yi, vec, nvalid);
+      }
     }
   }
 }
@@ -1825,6 +1831,12 @@ tile_kernel(const KArgs k) {
 // workgroup ever waits for another, so the result does not depend on how
 // many of the grid's workgroups the device holds at once, and the fixed K
 // order makes it deterministic.
+// The partials and the counters are touched only through agent-scope
+// atomics, whose stores write through to the device's coherence point and
+// whose loads read from it; a wave's vmcnt wait after its stores orders them
+// before the count, and the adds read after the count.  That gives the
+// ordering of a release and an acquire without a fence's L2 write-back and
+// invalidate, which serialise across an XCD's workgroups.
 // A counter holds the launch's 40-bit tag above a 24-bit count; a value with
 // another tag (an earlier launch, or whatever the workspace held) counts as
 // zero, so the counters need no clearing between launches.
@@ -1926,8 +1938,8 @@ sk_kernel(const KArgs k, const SkArgs sk) {
       mine.base = slots + sl.slot(sl.own) * SLOT_ELEMS;
       store_staged<OP, OUT, WM * WN, WN, kSlot, T::BM, T::BN>(k, 0, g, row0, col0, acc, smem,
                                                               mine);
-      __threadfence();     // the partial is visible device-wide before the count
-      __syncthreads();
+      wait_vmcnt<0>();     // this wave's part of the partial has reached the
+      __syncthreads();     // coherence point (agent-scope stores), every wave's
       if (tid == 0) {
         uint64_t* ctr = counters + (tile - sk.dp_tiles);
         uint64_t old = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1936,14 +1948,14 @@ sk_kernel(const KArgs k, const SkArgs sk) {
         // so at most count attempts
         do {
           now = (old >> 24) == tag ? old + 1 : ((tag << 24) | 1u);
-        } while (!__hip_atomic_compare_exchange_strong(ctr, &old, now, __ATOMIC_ACQ_REL,
+        } while (!__hip_atomic_compare_exchange_strong(ctr, &old, now, __ATOMIC_RELAXED,
                                                        __ATOMIC_RELAXED,
                                                        __HIP_MEMORY_SCOPE_AGENT));
         *last_arrival = (int)(now & 0xFFFFFFu) == sl.count;
       }
       __syncthreads();
       if (*last_arrival) {   // store_staged's first barrier precedes any LDS write
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // the other partials
+        // the other partials are read with agent-scope loads (no fence)
         store_staged<OP, OUT, WM * WN, WN, kOutAdd, T::BM, T::BN>(k, 0, g, row0, col0, acc, smem,
                                                                   sl);
       }
