@@ -986,6 +986,23 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
+// Count one arrival in a tile's counter and return the count it makes.  A
+// counter holds a launch's 40-bit tag above a 24-bit count; a value with
+// another tag (an earlier launch, or whatever the workspace held) counts as
+// zero.  The first exchange guesses that this is the last of n arrivals,
+// so the last one, whose adds follow, needs a single atomic round trip; a
+// wrong guess costs one more, and every failure after it means another
+// arrival's exchange succeeded, so at most n + 1 attempts.
+__device__ __forceinline__ int count_arrival(uint64_t* ctr, uint64_t tag, int n) {
+  uint64_t old = (tag << 24) | (uint64_t)(n - 1);
+  uint64_t now;
+  do {
+    now = (old >> 24) == tag ? old + 1 : ((tag << 24) | 1u);
+  } while (!__hip_atomic_compare_exchange_strong(ctr, &old, now, __ATOMIC_RELAXED,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  return (int)(now & 0xFFFFFFu);
+}
+
 namespace narrow {
 constexpr int BM = 128;
 constexpr int SCL = 20480;                       // scale region
@@ -1315,21 +1332,23 @@ narrow_kernel(const KArgs k) {
     wait_vmcnt<0>();     // this wave's partial has reached the coherence point
     __syncthreads();     // ... every wave's; the ring is idle
     int* const last_arrival = (int*)smem;
-    if (threadIdx.x == 0) {
-      const uint64_t tag = k.epoch & ((1ull << 40) - 1);
-      uint64_t* ctr = counters + tile;
-      uint64_t old = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      uint64_t now;
-      // lock-free: a failed exchange means another range's succeeded, so
-      // at most S attempts
-      do {
-        now = (old >> 24) == tag ? old + 1 : ((tag << 24) | 1u);
-      } while (!__hip_atomic_compare_exchange_strong(ctr, &old, now, __ATOMIC_RELAXED,
-                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-      *last_arrival = (int)(now & 0xFFFFFFu) == S;
-    }
+    if (threadIdx.x == 0)
+      *last_arrival = count_arrival(counters + tile, k.epoch & ((1ull << 40) - 1), S) == S;
     __syncthreads();
     if (!*last_arrival) return;
+    if (S == 2) {
+      // two partials: this workgroup's, in registers, plus the other one
+      // (the sum of two does not depend on which of them adds)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          const acc_t v = __builtin_bit_cast(
+              acc_t, __builtin_amdgcn_raw_buffer_load_b128(rw, pos(i, j), (1 - ks) * SLOT, SC1));
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][j][r] = acc[i][j][r] + v[r];
+        }
+    } else {
     // the S partials in ascending K order, this workgroup's own read back
     // like the others (choosing between it and a load would put the
     // accumulators in scratch memory)
@@ -1347,6 +1366,7 @@ narrow_kernel(const KArgs k) {
         }
         acc[i][j] = sum;
       }
+    }
   }
 
   // epilogue: lane holds row 32 wave + 16 i + f, columns 16 j + 4 fq .. + 3
@@ -1940,19 +1960,8 @@ sk_kernel(const KArgs k, const SkArgs sk) {
                                                               mine);
       wait_vmcnt<0>();     // this wave's part of the partial has reached the
       __syncthreads();     // coherence point (agent-scope stores), every wave's
-      if (tid == 0) {
-        uint64_t* ctr = counters + (tile - sk.dp_tiles);
-        uint64_t old = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        uint64_t now;
-        // lock-free: a failed exchange means another segment's succeeded,
-        // so at most count attempts
-        do {
-          now = (old >> 24) == tag ? old + 1 : ((tag << 24) | 1u);
-        } while (!__hip_atomic_compare_exchange_strong(ctr, &old, now, __ATOMIC_RELAXED,
-                                                       __ATOMIC_RELAXED,
-                                                       __HIP_MEMORY_SCOPE_AGENT));
-        *last_arrival = (int)(now & 0xFFFFFFu) == sl.count;
-      }
+      if (tid == 0)
+        *last_arrival = count_arrival(counters + (tile - sk.dp_tiles), tag, sl.count) == sl.count;
       __syncthreads();
       if (*last_arrival) {   // store_staged's first barrier precedes any LDS write
         // the other partials are read with agent-scope loads (no fence)
