@@ -53,6 +53,7 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 constexpr int kWave = 64;
 constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer, dword format
 constexpr uint32_t kOob = 0xFFFFFFF0u;         // a voffset past any range
+constexpr int kSc0 = 1;                        // buffer cache policy bit sc0
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
                                                            uint64_t bytes) {
@@ -251,7 +252,10 @@ __device__ __forceinline__ void load_row_group(__amdgpu_buffer_rsrc_t rs,
   // the LDS address is the low word of the generic one; formed as an
   // integer it needs no null check of the generic pointer
   const lds_ptr_t l = (lds_ptr_t)(uintptr_t)(uint32_t)(uintptr_t)(dst + q * 1024);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? rs : dead, l, 16, vo, (int)kbyte, 0, 0);
+  // sc0: the loads miss in the CU's L1 instead of allocating there -- every
+  // byte goes to LDS once, and the tiles' re-use is in L2 (mx 8 x 8192 x
+  // 1024 x 4096: 1.7% faster; the other workloads unchanged)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? rs : dead, l, 16, vo, (int)kbyte, 0, kSc0);
 }
 
 // mx MFMA: scale byte-select `sel` (0..3, a constant after unrolling) picks the
