@@ -46,6 +46,7 @@ namespace {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -392,8 +393,21 @@ __device__ __forceinline__ void store4(uint8_t* base, int64_t e, const float* y,
 template <int OP, int WM, int WN, int RING, bool PK>
 struct Mainloop {
   using T = Tile<OP, WM, WN, RING>;
-  using acc_t = typename OpT<OP>::acc_t;
-  static constexpr int TI = T::TI, TJ = T::TJ;
+  // int8 with at most four waves per workgroup (one wave per SIMD) runs
+  // 32 x 32 x 32 matrix instructions (1.4 times the 16 x 16 x 64 one's rate
+  // on gfx950): a wave's 64 x 128 sub-tile is 2 x 4 blocks of 32 x 32 with
+  // 16 int32 accumulators per lane each (17-37% faster than 16 x 16 x 64 on
+  // int8 8192 x 4096 x 4096 with those kernels).  The eight-wave kernels keep
+  // 16 x 16 x 64, which measured 12% faster there than 32 x 32 x 32 with two
+  // waves per SIMD.  The fp8 operations run 16 x 16 x 128 tiles (4 x 8 of
+  // them, 4 accumulators per lane each).
+  static constexpr bool W32 = OP == BSMM_OP_INT8_ROWWISE && WM * WN <= 4;
+  using acc_t = std::conditional_t<W32, i32x16, typename OpT<OP>::acc_t>;
+  static constexpr int TI = W32 ? 2 : T::TI, TJ = W32 ? 4 : T::TJ;
+  // refill slots per wave and K block: one after each 16 x 16 tile's
+  // instructions, or after each 32 x 32 x 32 instruction
+  static constexpr int NQ = 32;
+  static_assert(W32 || T::TI * T::TJ == NQ, "one refill slot per 16 x 16 tile");
   static constexpr int kLoadsPerBlock = T::LA + T::LB;   // per wave
   // shared memory: the ring, or the epilogue's 32-row strips of every wave
   // if those need more (a four-slot ring of 256 x 256 tiles does)
@@ -620,8 +634,22 @@ struct Mainloop {
     // column j computes.
     const uint8_t* SA = smem;
     const uint8_t* SB = smem;
-    i32x8 af[TI];
+    i32x8 af[T::TI];
     i32x8 bcur;          // B tile of the current column
+    // int8 (32 x 32 x 32): lane l holds row l % 32 of a block and, of each
+    // 32-byte K step s, the 16 bytes of LDS chunk 2 s + l / 32 (the K order
+    // is the same for both operands, which is all an exact integer sum needs)
+    const int r32 = lane & 31, h32 = lane >> 5;
+    const int a32 = (wm * T::WTM + r32) << 7, b32 = (wn * T::WTN + r32) << 7;
+    int c32[4];
+  #pragma unroll
+    for (int q = 0; q < 4; ++q) c32[q] = ((2 * q + h32) ^ swz(r32)) << 4;
+    i32x4 af32[2][4];    // A blocks 0, 1 of the K block, by K step
+    i32x4 bc32[4];       // B block of the current column block, by K step
+    auto read_b32 = [&](int bj, i32x4 (&f)[4]) {
+  #pragma unroll
+      for (int q = 0; q < 4; ++q) f[q] = *(const i32x4*)(SB + b32 + bj * 4096 + c32[q]);
+    };
     auto read_b = [&](int j) {
       const i32x4 lo = *(const i32x4*)(SB + b_off0 + j * 2048);
       const i32x4 hi = *(const i32x4*)(SB + b_off1 + j * 2048);
@@ -642,12 +670,21 @@ struct Mainloop {
   #pragma unroll
         for (int i = 0; i < TI; ++i) sc[i] = v[i];
       }
-      bcur = read_b(0);
+      if constexpr (W32) {
+        read_b32(0, bc32);
   #pragma unroll
-      for (int i = 0; i < TI; ++i) {
-        const i32x4 lo = *(const i32x4*)(SA + a_off0 + i * 2048);
-        const i32x4 hi = *(const i32x4*)(SA + a_off1 + i * 2048);
-        af[i] = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        for (int bi = 0; bi < 2; ++bi)
+  #pragma unroll
+          for (int q = 0; q < 4; ++q)
+            af32[bi][q] = *(const i32x4*)(SA + a32 + bi * 4096 + c32[q]);
+      } else {
+        bcur = read_b(0);
+  #pragma unroll
+        for (int i = 0; i < T::TI; ++i) {
+          const i32x4 lo = *(const i32x4*)(SA + a_off0 + i * 2048);
+          const i32x4 hi = *(const i32x4*)(SA + a_off1 + i * 2048);
+          af[i] = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        }
       }
     };
 
@@ -672,7 +709,7 @@ struct Mainloop {
       // right behind its own MFMA, which serialises MFMA and VALU.
       auto tile = [&](int i, int j) {
         const int tt = j * TI + i;
-        if constexpr (OP == BSMM_OP_INT8_ROWWISE) {
+        if constexpr (OP == BSMM_OP_INT8_ROWWISE && !W32) {
           const i32x4 alo = i32x4{af[i][0], af[i][1], af[i][2], af[i][3]};
           const i32x4 ahi = i32x4{af[i][4], af[i][5], af[i][6], af[i][7]};
           const i32x4 blo = i32x4{bcur[0], bcur[1], bcur[2], bcur[3]};
@@ -700,11 +737,38 @@ struct Mainloop {
               bcur, af[i], f32x4{0, 0, 0, 0}, 0, 0, 0, 127, 0, 127);
         } else if constexpr (OP == BSMM_OP_FP8_MX32_MM) {
           acc[i][j] = mfma_mx32(bcur, af[i], acc[i][j], wc_cur[j >> 2], j & 3, xs_cur, i);
-        } else {
+        } else if constexpr (OP != BSMM_OP_INT8_ROWWISE) {    // mx; scaled_mm with unit scales
           acc[i][j] = mfma_mx(bcur, af[i], acc[i][j], ws_cur, i, xs_cur);
         }
         __builtin_amdgcn_sched_barrier(0);
       };
+      if constexpr (W32) {
+        // int8: per column block bj, its first instruction, then the next
+        // column block's B reads and the refills, then the other seven;
+        // consecutive instructions alternate between the two accumulators
+  #pragma unroll
+        for (int bj = 0; bj < TJ; ++bj) {
+          i32x4 bn32[4];
+  #pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const int q = t >> 1, bi = t & 1;
+            acc[bi][bj] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bc32[q], af32[bi][q],
+                                                                acc[bi][bj], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            if (t == 0) {
+              if (bj + 1 < TJ) read_b32(bj + 1, bn32);
+              else {
+  #pragma unroll
+                for (int q2 = 0; q2 < 4; ++q2) bn32[q2] = bc32[q2];
+              }
+            }
+            refill(bj * 8 + t);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+  #pragma unroll
+          for (int q2 = 0; q2 < 4; ++q2) bc32[q2] = bn32[q2];
+        }
+      } else {
   #pragma unroll
       for (int j = 0; j < TJ; ++j) {
         tile(0, j);
@@ -742,6 +806,7 @@ struct Mainloop {
             acc[ui][uj][r] = __builtin_fmaf(__fmul_rn(sc[ui], sbp[r]), ring[u % D][r],
                                             acc[ui][uj][r]);
         }
+      }
       }
     };
 
@@ -785,9 +850,8 @@ struct Mainloop {
         // taken into use after its last MFMA.
         load_scales(kb0 + min(c + 1, nkb - 1));
         __builtin_amdgcn_sched_barrier(0);
-        columns([&](int q) {   // after the block's MFMA q of TI * TJ
+        columns([&](int q) {   // at the block's refill slot q of NQ
           if constexpr (LOADER) {
-            constexpr int NQ = TI * TJ;
     #pragma unroll
             for (int u = kLoadsPerBlock * q / NQ; u < kLoadsPerBlock * (q + 1) / NQ; ++u) {
               if (u < L1) issue_load(h1, slot1, u);
@@ -1446,12 +1510,19 @@ template <int OP, int OUT, int NW, int WN, int MODE, int BM, int BN, int TI, int
 __device__ __forceinline__ void store_staged(const KArgs& k, int s, int g, int row0, int col0,
                                              const acc_t (&acc)[TI][TJ], uint8_t* smem,
                                              const SlotRef& sl = SlotRef()) {
+  // accumulator blocks: 16 x 16 (4 values per lane: row l % 16, columns
+  // 4 (l / 16) .. + 3) or, for int8, 32 x 32 (16 values per lane: row l % 32,
+  // columns 8 q + 4 (l / 32) .. + 3 for q = 0 .. 3)
+  constexpr bool W32 = sizeof(acc_t) == 64;
+  constexpr int TW = W32 ? 32 : 16;              // rows and columns of a block
   constexpr int ROWS = 32;                       // staged rows per pass
-  constexpr int PITCH = 16 * TJ * 4 + 16;        // bytes per staged row
-  constexpr int GROUPS = ROWS * 16 * TJ / 4;     // 4-element groups per pass
-  constexpr int PER_ROW = 16 * TJ / 4;           // groups per row
+  constexpr int WCOLS = TW * TJ;                 // the wave's columns
+  constexpr int PITCH = WCOLS * 4 + 16;          // bytes per staged row
+  constexpr int PER_ROW = WCOLS / 4;             // 4-element groups per row
+  constexpr int GROUPS = ROWS * PER_ROW;         // per pass
+  constexpr int NPASS = TW * TI / ROWS;
   constexpr bool PARTIAL = MODE == kSplitK || MODE == kSlot;
-  static_assert(TI % 2 == 0 && GROUPS % kWave == 0, "staging layout");
+  static_assert((TW * TI) % ROWS == 0 && GROUPS % kWave == 0, "staging layout");
   typedef typename OpT<OP>::elem_t E;
   const Problem& p = k.p;
   const int lane = threadIdx.x & 63;
@@ -1459,7 +1530,7 @@ __device__ __forceinline__ void store_staged(const KArgs& k, int s, int g, int r
   const int wm = wave / WN, wn = wave % WN;
   uint8_t* st = smem + wave * (ROWS * PITCH);
   const int fr = lane & 15, fq = lane >> 4;
-  const int wrow0 = row0 + wm * 16 * TI, wcol0 = col0 + wn * 16 * TJ;
+  const int wrow0 = row0 + wm * TW * TI, wcol0 = col0 + wn * WCOLS;
   const bool vec = k.vec_out != 0;
   uint8_t* obase;
   int64_t og, ldo;
@@ -1488,7 +1559,29 @@ __device__ __forceinline__ void store_staged(const KArgs& k, int s, int g, int r
   [[maybe_unused]] const ScaledEpi epi(p);
   lds_barrier();     // every wave's K-loop reads of LDS are done
 #pragma unroll
-  for (int pass = 0; pass < TI / 2; ++pass) {
+  for (int pass = 0; pass < NPASS; ++pass) {
+    if constexpr (W32) {
+      // block row `pass`: the lane's row l % 32, four runs of four columns
+      // per 32-column block
+      const int r32 = lane & 31, h32 = lane >> 5;
+      float sa_m = 1.f;
+      if constexpr (SCALE_A_STAGED)
+        sa_m = ((const float*)p.sa)[(int64_t)min(wrow0 + 32 * pass + r32, k.row_end - 1) * p.sa_m];
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          i32x4 v;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            if constexpr (SCALE_A_STAGED)
+              v[r] = __float_as_int(__fmul_rn((float)acc[pass][j][4 * q + r], sa_m));
+            else
+              v[r] = acc[pass][j][4 * q + r];
+          }
+          *(i32x4*)(st + r32 * PITCH + (32 * j + 8 * q + 4 * h32) * 4) = v;
+        }
+    } else {
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii) {
       const int i = 2 * pass + ii;
@@ -1509,6 +1602,7 @@ __device__ __forceinline__ void store_staged(const KArgs& k, int s, int g, int r
         }
         *(i32x4*)(st + (16 * ii + fr) * PITCH + (16 * j + 4 * fq) * 4) = v;
       }
+    }
     }
 #pragma unroll
     for (int q = 0; q < GROUPS / kWave; ++q) {
@@ -1834,7 +1928,7 @@ tile_kernel(const KArgs k) {
 #pragma unroll
     for (int i = 0; i < M::TI; ++i)
 #pragma unroll
-      for (int j = 0; j < M::TJ; ++j) acc[i][j] = typename M::acc_t{0, 0, 0, 0};
+      for (int j = 0; j < M::TJ; ++j) acc[i][j] = typename M::acc_t{};
     M::run(k, smem, t.g, row0, col0, kb0, nkb, acc);
     if (k.splits > 1)
       store_staged<OP, OUT, WM * WN, WN, kSplitK, T::BM, T::BN>(k, t.s, t.g, row0, col0, acc, smem);
@@ -1941,7 +2035,7 @@ sk_kernel(const KArgs k, const SkArgs sk) {
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int j = 0; j < TJ; ++j) acc[i][j] = acc_t{0, 0, 0, 0};
+      for (int j = 0; j < TJ; ++j) acc[i][j] = acc_t{};
     M::run(k, smem, g, row0, col0, kb_a, kb_b - kb_a, acc);
 
     if (kb_a == 0 && kb_b == KB) {
