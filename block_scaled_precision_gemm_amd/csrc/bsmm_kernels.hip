@@ -48,6 +48,7 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -81,12 +82,13 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu))
-    return (u >> 16) | 0x0040u;                       // quiet NaN
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+// Two fp32 values to a packed pair of bf16 (a in the low half) with the
+// hardware conversion (v_cvt_pk_bf16_f32): round to nearest even, as the
+// kernels' float mode (round to nearest even, denormals kept) sets it; a NaN
+// input is unsupported.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{a, b}), bf16x2_t));
 }
 
 // ---------------------------------------------------------------------------
@@ -367,11 +369,11 @@ __device__ __forceinline__ void store4(uint8_t* base, int64_t e, const float* y,
     uint16_t* o = (uint16_t*)base + e;
     if (vec && nvalid == 4) {
       u32x2 v;
-      v.x = f32_to_bf16_rne(y[0]) | (f32_to_bf16_rne(y[1]) << 16);
-      v.y = f32_to_bf16_rne(y[2]) | (f32_to_bf16_rne(y[3]) << 16);
+      v.x = bf16x2(y[0], y[1]);
+      v.y = bf16x2(y[2], y[3]);
       __builtin_nontemporal_store(v, (u32x2*)o);
     } else {
-      for (int r = 0; r < nvalid; ++r) o[r] = (uint16_t)f32_to_bf16_rne(y[r]);
+      for (int r = 0; r < nvalid; ++r) o[r] = (uint16_t)bf16x2(y[r], 0.f);
     }
   } else if (OUT == BSMM_F32) {
     float* o = (float*)base + e;
