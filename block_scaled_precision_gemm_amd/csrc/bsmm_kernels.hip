@@ -1558,6 +1558,22 @@ __device__ __forceinline__ void store_staged(const KArgs& k, int s, int g, int r
   // (stream-K) adds
   constexpr bool SCALED = OP == BSMM_OP_FP8_SCALED_MM && !PARTIAL;
   const bool sb_vec = (SCALE || SCALED) && p.sb_n == 1 && (((uintptr_t)p.sb) & 15u) == 0;
+  // the column scales of the lane's four columns, the same in every group
+  // the lane stores (group q of a pass covers row q kWave / PER_ROW + lane /
+  // PER_ROW and columns 4 (lane % PER_ROW) ..), loaded once per tile
+  static_assert(kWave % PER_ROW == 0, "a lane's groups share their columns");
+  float sb_l[4] = {1.f, 1.f, 1.f, 1.f};
+  if constexpr (SCALE || SCALED) {
+    const int n_l = wcol0 + 4 * (lane % PER_ROW);
+    if (sb_vec && p.N - n_l >= 4) {
+      const f32x4 t = *(const f32x4*)((const float*)p.sb + n_l);
+      sb_l[0] = t[0]; sb_l[1] = t[1]; sb_l[2] = t[2]; sb_l[3] = t[3];
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        sb_l[c] = ((const float*)p.sb)[(int64_t)max(0, min(n_l + c, p.N - 1)) * p.sb_n];
+    }
+  }
   [[maybe_unused]] const ScaledEpi epi(p);
   lds_barrier();     // every wave's K-loop reads of LDS are done
 #pragma unroll
@@ -1644,28 +1660,12 @@ __device__ __forceinline__ void store_staged(const KArgs& k, int s, int g, int r
       float y[4];
       int yi[4];
       if constexpr (SCALED) {
-        float sb[4];
-        if (sb_vec && nvalid == 4) {
-          const f32x4 t = *(const f32x4*)((const float*)p.sb + n);
-          sb[0] = t[0]; sb[1] = t[1]; sb[2] = t[2]; sb[3] = t[3];
-        } else {
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-            sb[c] = ((const float*)p.sb)[(int64_t)min(n + c, p.N - 1) * p.sb_n];
-        }
+        const float* sb = sb_l;
         const float sa_m = ((const float*)p.sa)[(int64_t)m * p.sa_m];
 #pragma unroll
         for (int c = 0; c < 4; ++c) y[c] = epi(__int_as_float(v[c]), sa_m, sb[c], min(n + c, p.N - 1));
       } else if constexpr (SCALE) {
-        float sb[4];
-        if (sb_vec && nvalid == 4) {
-          const f32x4 t = *(const f32x4*)((const float*)p.sb + n);
-          sb[0] = t[0]; sb[1] = t[1]; sb[2] = t[2]; sb[3] = t[3];
-        } else {
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-            sb[c] = ((const float*)p.sb)[(int64_t)min(n + c, p.N - 1) * p.sb_n];
-        }
+        const float* sb = sb_l;
         if constexpr (SCALE_A_STAGED) {
 #pragma unroll
           for (int c = 0; c < 4; ++c) y[c] = __fmul_rn(__int_as_float(v[c]), sb[c]);
